@@ -1,0 +1,325 @@
+"""Pins for the CPU oracle: facts that do not come from the oracle itself.
+
+Each test names the passage or the mathematical fact it checks; each is
+chosen so that a plausible slip in the oracle (a dropped term, a wrong sign
+or index, a transposed operand, a wrong inverse) fails at least one of them.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+import moe_inputs as mi
+from oracle import moe_oracle as o
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _distinct_logits(rng, T, E):
+    while True:
+        l = rng.standard_normal((T, E)).astype(np.float32)
+        if all(len(set(r.tolist())) == E for r in l):
+            return l
+
+
+def _tiny(T=24, H=16, E=6, k=2, I=8, **kw):
+    cfg = mi.MoEShape("pin", T=T, H=H, E=E, k=k, I=I, dtype="f32", **kw)
+    rng = np.random.default_rng(7)
+    lg = _distinct_logits(rng, T, E)
+    x = rng.standard_normal((T, H))
+    w13 = rng.standard_normal((E, 2 * I, H)) * 0.3
+    w2 = rng.standard_normal((E, H, I)) * 0.3
+    return cfg, lg, x, w13, w2
+
+
+# ---------------------------------------------------------------- printed facts
+def test_token_flow_printed_example():
+    """8 tokens, 64 experts, top-2 -> 16 expert executions, 16 outputs
+    combined into 8 ("Follow one token through an MoE layer")."""
+    g = _gold("serving_moe_token_flow.json")["token_flow"]
+    cfg = mi.WORKLOADS["tiny_fp32"]
+    assert (cfg.T, cfg.E, cfg.k) == (g["tokens"], g["experts"], g["top_k"])
+    lg = mi.logits(cfg)
+    x = mi.values_f64(mi.x(cfg), cfg.dtype)
+    E, I, H = cfg.E, cfg.I, cfg.H
+    rng = np.random.default_rng(0)
+    w13 = rng.standard_normal((E, 2 * I, H)) * 0.02
+    w2 = rng.standard_normal((E, H, I)) * 0.02
+    r = o.layer_forward(cfg, lg, x, w13, w2)
+    assert r["ids"].size == g["expert_executions"]
+    assert r["y_perm"].shape[0] == g["expert_executions"]
+    assert r["out"].shape[0] == g["outputs_combined_into"]
+    assert int(r["seg_offsets"][-1]) == 16
+    # "roughly 3 percent of its expert parameters" per token
+    assert abs(cfg.k / cfg.E - _gold("serving_moe_token_flow.json")["expert_fraction_per_token_approx"]) < 0.005
+
+
+def test_balancedness_worked_example():
+    """Counts 22,14,7,6,5,4,3,3 on 4 ranks of 2 contiguous experts: loads
+    36,13,9,6, mean 16, balancedness 16/36 ~ 0.44; the repack gives max 25
+    ("Worked example: balance the busiest rank")."""
+    g = _gold("serving_moe_worked_example.json")
+    counts = np.array(g["expert_counts"])
+    per = g["experts_per_rank"]
+    loads = counts.reshape(-1, per).sum(axis=1)
+    assert loads.tolist() == g["rank_loads"]
+    b = o.balancedness(loads)
+    num, den = g["balancedness_per_rank_exact"]
+    assert b == np.float32(num / den)
+    assert round(float(b), 2) == g["balancedness_per_rank_approx"]
+    repacked = [counts[list(p)].sum() for p in g["repacked_pairs"]]
+    assert repacked == g["repacked_rank_loads"]
+    assert o.balancedness(repacked) == np.float32(16 / 25)
+    # per logical expert (the unit used for one layer on one GPU): 8/22
+    assert o.balancedness(counts) == np.float32(8 / 22)
+    assert o.balancedness(o.expert_counts(np.repeat(np.arange(8), 8), 8)) == g["perfect_balance"]
+
+
+def test_uniform_routing_balancedness_is_one():
+    """A perfectly balanced deployment logs 1.0 ("The slowest expert sets
+    the pace"): token t routed to experts 2t mod E and 2t+1 mod E."""
+    T, E, k = 64, 16, 2
+    lg = np.empty((T, E), dtype=np.float32)
+    for t in range(T):
+        lg[t] = -np.arange(E, dtype=np.float32) / 100.0 - 1.0
+        lg[t, (2 * t) % E] = 5.0
+        lg[t, (2 * t + 1) % E] = 4.0
+    ids, _ = o.route_flat(lg, k)
+    assert all(ids[t].tolist() == [(2 * t) % E, (2 * t + 1) % E] for t in range(T))
+    c = o.expert_counts(ids, E)
+    assert (c == T * k // E).all()
+    assert o.balancedness(c) == np.float32(1.0)
+
+
+def test_empty_experts_are_normal():
+    """An expert may get no token at all (Zepp section 2): its segment stays in
+    the list with length 0 and the mean still counts it."""
+    cfg, lg, x, w13, w2 = _tiny(T=4, E=12, k=1)
+    r = o.layer_forward(cfg, lg, x, w13, w2)
+    lens = np.diff(r["seg_offsets"])
+    assert len(lens) == 12 and (lens == 0).sum() >= 8
+    assert r["balancedness"] == np.float32((4 / 12) / r["counts"].max())
+
+
+# ---------------------------------------------------------------- routing
+@pytest.mark.parametrize("E,k,seed", [(5, 1, 0), (6, 2, 1), (9, 3, 2), (12, 4, 3), (7, 7, 4)])
+def test_route_flat_brute_force(E, k, seed):
+    """The chosen set maximises the sum of logits over all C(E,k) subsets
+    (unique: values are distinct); slots are in descending logit order."""
+    rng = np.random.default_rng(seed)
+    lg = _distinct_logits(rng, 10, E)
+    ids, w = o.route_flat(lg, k)
+    for t in range(10):
+        best = max(itertools.combinations(range(E), k), key=lambda c: sum(float(lg[t, e]) for e in c))
+        assert set(ids[t].tolist()) == set(best)
+        vals = lg[t, ids[t]]
+        assert all(vals[j] > vals[j + 1] for j in range(k - 1))
+        # softmax over the winners: ratios exp(l_i - l_j), sum 1
+        assert abs(w[t].sum() - 1.0) < 1e-15
+        for i in range(k):
+            for j in range(k):
+                assert np.isclose(w[t, i] / w[t, j], np.exp(float(vals[i]) - float(vals[j])), rtol=1e-13)
+
+
+def test_route_flat_k2_closed_form():
+    """k = 2: w0 = 1 / (1 + exp(l1 - l0))."""
+    lg = _distinct_logits(np.random.default_rng(11), 50, 64)
+    ids, w = o.route_flat(lg, 2)
+    l0 = lg[np.arange(50), ids[:, 0]].astype(np.float64)
+    l1 = lg[np.arange(50), ids[:, 1]].astype(np.float64)
+    np.testing.assert_allclose(w[:, 0], scipy.special.expit(l0 - l1), rtol=1e-14)
+
+
+def test_route_flat_without_renormalising_is_full_softmax():
+    lg = _distinct_logits(np.random.default_rng(12), 20, 10)
+    ids, w = o.route_flat(lg, 3, renormalize=False)
+    p = scipy.special.softmax(lg.astype(np.float64), axis=1)
+    np.testing.assert_allclose(w, np.take_along_axis(p, ids.astype(np.int64), 1), rtol=1e-13)
+
+
+def test_route_grouped_brute_force():
+    """E=16 in 4 groups, keep 2 groups, top-3: enumerate every group pair by
+    the sum of its group scores (score = sum of the 2 best member sigmoids),
+    then every 3-subset of the pair's experts."""
+    rng = np.random.default_rng(5)
+    lg = _distinct_logits(rng, 40, 16)
+    ids, w, gap = o.route_grouped(lg, 3, n_group=4, topk_group=2, topn=2)
+    s = scipy.special.expit(lg.astype(np.float64))
+    for t in range(40):
+        gsc = [sum(sorted(s[t, 4 * g:4 * g + 4])[-2:]) for g in range(4)]
+        pair = max(itertools.combinations(range(4), 2), key=lambda p: gsc[p[0]] + gsc[p[1]])
+        members = [e for g in pair for e in range(4 * g, 4 * g + 4)]
+        best = max(itertools.combinations(members, 3), key=lambda c: sum(float(lg[t, e]) for e in c))
+        assert set(ids[t].tolist()) == set(best), t
+        assert list(lg[t, ids[t]]) == sorted(lg[t, ids[t]], reverse=True)
+        np.testing.assert_allclose(w[t], s[t, ids[t]] / s[t, ids[t]].sum(), rtol=1e-14)
+        assert gap[t] > 0
+
+
+def test_route_grouped_one_group_is_flat_sigmoid_topk():
+    lg = _distinct_logits(np.random.default_rng(6), 30, 24)
+    ids_g, w_g, _ = o.route_grouped(lg, 5, n_group=1, topk_group=1)
+    ids_f, _ = o.route_flat(lg, 5)
+    assert (ids_g == ids_f).all()
+    s = scipy.special.expit(lg.astype(np.float64))
+    sel = np.take_along_axis(s, ids_f.astype(np.int64), 1)
+    np.testing.assert_allclose(w_g, sel / sel.sum(1, keepdims=True), rtol=1e-14)
+
+
+def test_group_scores_are_fp32_sums_of_best_members():
+    """fp32 group scores lie within 2 ulp of the exact top-2 sigmoid sums."""
+    lg = _distinct_logits(np.random.default_rng(8), 16, 64)
+    gs = o.group_scores_f32(lg, 8, 2)
+    s = scipy.special.expit(lg.astype(np.float64))
+    for t in range(16):
+        for g in range(8):
+            exact = sum(sorted(s[t, 8 * g:8 * g + 8])[-2:])
+            assert abs(float(gs[t, g]) - exact) <= 2 * np.spacing(np.float32(exact))
+
+
+# ---------------------------------------------------------------- permutation
+def _counting_sort_rows(seg_of_a, S):
+    rows = []
+    for s in range(S):
+        for a in range(len(seg_of_a)):
+            if seg_of_a[a] == s:
+                rows.append(a)
+    return np.array(rows)
+
+
+@pytest.mark.parametrize("T,E,k,hot,ways", [(24, 6, 2, 0, 1), (37, 8, 3, 2, 2), (50, 5, 5, 0, 1), (33, 9, 2, 3, 3)])
+def test_permutation_is_stable_bijection(T, E, k, hot, ways):
+    """Rows of a segment are its assignments in increasing a = t*k+j; the
+    permutation is a bijection; segment lengths merge back to the expert
+    histogram ("Follow one token through an MoE layer", step 1)."""
+    cfg, lg, x, w13, w2 = _tiny(T=T, E=E, k=k, n_hot_split=hot, split_ways=ways)
+    r = o.layer_forward(cfg, lg, x, w13, w2)
+    A = T * k
+    r2a, a2r = r["row_to_assign"], r["assign_to_row"]
+    assert sorted(r2a.tolist()) == list(range(A))
+    assert (a2r[r2a] == np.arange(A)).all()
+    S = len(r["seg_expert"])
+    seg_of_a = o.segment_of_assignments(r["ids"], r["seg_expert"], r["seg_replica"], ways)
+    assert (r2a == _counting_sort_rows(seg_of_a.tolist(), S)).all()
+    lens = np.diff(r["seg_offsets"])
+    merged = np.zeros(E, dtype=np.int64)
+    np.add.at(merged, r["seg_expert"], lens)
+    assert (merged == np.bincount(r["ids"].ravel(), minlength=E)).all()
+    assert (r["row_to_token"] == r2a // k).all()
+    assert (r["x_perm"] == x[r["row_to_token"]]).all()
+    # every row of a segment really belongs to that segment's expert
+    for s in range(S):
+        for row in range(r["seg_offsets"][s], r["seg_offsets"][s + 1]):
+            a = r2a[row]
+            assert r["ids"][a // k, a % k] == r["seg_expert"][s]
+            if r["seg_replica"][s] >= 0:
+                assert (a // k) % ways == r["seg_replica"][s]
+
+
+def test_hot_experts_are_the_largest_counts():
+    counts = np.array([5, 9, 9, 1, 0, 9, 3, 7])
+    assert o.hot_experts(counts, 3) == [1, 2, 5]
+    assert o.hot_experts(counts, 4) == [1, 2, 5, 7]
+    se, sr = o.segment_list(counts, 2, 2)
+    assert se.tolist() == [0, 1, 1, 2, 2, 3, 4, 5, 6, 7]
+    assert sr.tolist() == [-1, 0, 1, 0, 1, -1, -1, -1, -1, -1]
+
+
+# ---------------------------------------------------------------- expert MLP
+def test_swiglu_hand_example():
+    """x = [1, 2]; W_gate column [0.5, 0.25] -> g = 1; W_up column [1, -1]
+    -> u = -1; h = silu(1) * -1 = -1/(1+e^-1); W_down row [2, 3]."""
+    x = np.array([[1.0, 2.0]])
+    w13 = np.array([[0.5, 0.25], [1.0, -1.0]])       # [2I=2, H=2]
+    w2 = np.array([[2.0], [3.0]])                      # [H=2, I=1]
+    h = -0.7310585786300049                            # -sigmoid(1)
+    np.testing.assert_allclose(o.swiglu(x, w13, w2), [[2 * h, 3 * h]], rtol=1e-15)
+    assert o.silu(np.array([0.0]))[0] == 0.0
+    assert o.silu(np.array([-800.0]))[0] == 0.0
+    assert o.silu(np.array([40.0]))[0] == 40.0
+
+
+def _dense(x, w13, w2):
+    I = w13.shape[0] // 2
+    g = x @ w13[:I].T
+    return (g * scipy.special.expit(g) * (x @ w13[I:].T)) @ w2.T
+
+
+def test_identical_experts_reduce_to_dense_mlp():
+    """With every expert equal and weights renormalised, the routed layer is
+    the dense SwiGLU MLP: routing, permutation and combine cancel out."""
+    cfg, lg, x, w13, w2 = _tiny(T=31, E=7, k=3, n_hot_split=2, split_ways=2)
+    w13[:] = w13[0]
+    w2[:] = w2[0]
+    r = o.layer_forward(cfg, lg, x, w13, w2)
+    np.testing.assert_allclose(r["out"], _dense(x, w13[0], w2[0]), rtol=1e-12, atol=1e-12)
+
+
+def test_one_expert_top1_is_dense_mlp():
+    cfg, lg, x, w13, w2 = _tiny(T=9, E=1, k=1)
+    r = o.layer_forward(cfg, lg, x, w13, w2)
+    assert (r["w"] == 1.0).all()
+    np.testing.assert_allclose(r["out"], _dense(x, w13[0], w2[0]), rtol=1e-12, atol=1e-12)
+
+
+def test_scaling_down_projection_by_two_doubles_output_exactly():
+    cfg, lg, x, w13, w2 = _tiny(T=20, E=5, k=2)
+    a = o.layer_forward(cfg, lg, x, w13, w2)["out"]
+    b = o.layer_forward(cfg, lg, x, w13, 2.0 * w2)["out"]
+    assert (b == 2.0 * a).all()
+
+
+def test_identity_experts_recover_tokens():
+    """If every expert returned its input row, the weighted combine of a
+    token's k rows (weights summing to 1) gives back the token: pins that
+    combine reads assign_to_row as the inverse of the packing."""
+    cfg, lg, x, w13, w2 = _tiny(T=40, E=6, k=3, n_hot_split=2, split_ways=2)
+    ids, w, _ = o.route(cfg, lg)
+    p = o.plan(cfg, ids)
+    x_perm = x[p["row_to_token"]]
+    out = o.combine(x_perm, p["assign_to_row"], w)
+    np.testing.assert_allclose(out, x, rtol=1e-13, atol=1e-14)
+    # and with distinct per-slot weights the pairing of slot and row matters
+    y = x_perm * (1.0 + p["row_to_assign"][:, None] % cfg.k)
+    out2 = o.combine(y, p["assign_to_row"], w)
+    np.testing.assert_allclose(out2, x * (w * (1.0 + np.arange(cfg.k))).sum(1, keepdims=True), rtol=1e-13)
+
+
+def test_replica_segments_do_not_change_the_output():
+    """Replication "preserves the model's logical expert selections and
+    routing weights" (Zepp section 4.1): splitting hot experts by token parity
+    gives the same output, bit for bit, in the oracle."""
+    cfg, lg, x, w13, w2 = _tiny(T=45, E=6, k=3, n_hot_split=2, split_ways=2)
+    a = o.layer_forward(cfg, lg, x, w13, w2)
+    b = o.layer_forward(cfg.replace(n_hot_split=0, split_ways=1), lg, x, w13, w2)
+    assert len(a["seg_expert"]) == 8 and len(b["seg_expert"]) == 6
+    assert (a["out"] == b["out"]).all()
+
+
+def test_shared_expert_is_added_with_weight_one():
+    """Shared experts process every token, independent of routing ("MoE
+    architecture recap")."""
+    cfg, lg, x, w13, w2 = _tiny(T=12, E=4, k=2)
+    rng = np.random.default_rng(3)
+    sw13 = rng.standard_normal((2 * 8, 16)) * 0.3
+    sw2 = rng.standard_normal((16, 8)) * 0.3
+    a = o.layer_forward(cfg, lg, x, w13, w2)
+    b = o.layer_forward(cfg, lg, x, w13, w2, sw13, sw2)
+    np.testing.assert_allclose(b["out"] - a["out"], _dense(x, sw13, sw2), rtol=1e-11, atol=1e-12)
+
+
+def test_token_outputs_match_whole_layer():
+    """The sampled per-token form equals the permuted whole-layer form."""
+    cfg, lg, x, w13, w2 = _tiny(T=30, E=6, k=3, n_hot_split=1, split_ways=2)
+    r = o.layer_forward(cfg, lg, x, w13, w2)
+    toks = [0, 7, 29]
+    out = o.token_outputs(toks, x[toks], r["ids"][toks], r["w"][toks], lambda e: (w13[e], w2[e]))
+    np.testing.assert_allclose(out, r["out"][toks], rtol=1e-12, atol=1e-13)
