@@ -1,0 +1,261 @@
+"""Benchmark of the single-GPU MoE layer forward on one MI355X.
+
+One step = one moe_layer_forward (route -> permute -> grouped SwiGLU ->
+combine, plus balancedness) over one batch of seeded synthetic inputs that
+are resident in HBM before timing starts.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--no-cpu-baseline]
+
+The roofline object is for the grouped expert FFN (the two persistent
+grouped-GEMM launches that dominate the step), timed live with HIP events on
+the stream it runs on.  The cpu_baseline object times the float64 CPU oracle
+on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import moe_inputs as mi  # noqa: E402
+
+METRIC = "MoE-layer tokens/s and grouped-GEMM TFLOP/s (% MFMA/HBM roofline), 1 MI355X"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+FP32_PEAK_TFLOPS = 157.3
+
+
+# ------------------------------------------------------------------ accounting
+def dispatch_bytes(cfg, assignments: int | None = None) -> int:
+    """Bytes of one dispatch: one hidden-size row per assignment ("Price one
+    dispatch": 2 B x hidden per routed activation; count assignments, not
+    tokens)."""
+    A = cfg.A if assignments is None else assignments
+    return A * cfg.H * cfg.elem_bytes
+
+
+def ffn_flops(cfg) -> int:
+    """Algorithmic flops of the expert MLPs: 6*H*I per assignment (gate, up
+    and down projections), plus 6*H*shared_I per token for a shared expert."""
+    return 6 * cfg.H * cfg.I * cfg.A + 6 * cfg.H * cfg.shared_I * cfg.T
+
+
+def ffn_bytes(cfg, active_experts: int) -> int:
+    """Algorithmic HBM bytes of the grouped FFN: the weights of every active
+    expert read once, x_perm read, h written and read, y_perm written (and the
+    shared expert's weights and rows)."""
+    eb = cfg.elem_bytes
+    w = active_experts * 3 * cfg.H * cfg.I * eb
+    act = cfg.A * (cfg.H * 2 + cfg.I * 2) * eb
+    if cfg.shared_I:
+        w += 3 * cfg.H * cfg.shared_I * eb
+        act += cfg.T * (cfg.H * 2 + cfg.shared_I * 2) * eb
+    return w + act
+
+
+# ------------------------------------------------------------------ device inputs
+def device_inputs(cfg, keep_experts=()):
+    """Seeded inputs in HBM.  Returns (dict of tensors, {e: (w13, w2)} host
+    copies of the experts listed in keep_experts)."""
+    import torch
+    dev = torch.device("cuda:0")
+    tdt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+
+    def up(a):
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a))
+
+    d = dict(logits=torch.from_numpy(mi.logits(cfg)).to(dev), x=up(mi.x(cfg)).to(dev))
+    d["w13"] = torch.empty((cfg.E, 2 * cfg.I, cfg.H), dtype=tdt, device=dev)
+    d["w2"] = torch.empty((cfg.E, cfg.H, cfg.I), dtype=tdt, device=dev)
+    kept = {}
+    keep = set(keep_experts)
+
+    def put(e, a, b):
+        d["w13"][e].copy_(up(a))
+        d["w2"][e].copy_(up(b))
+        if e in keep:
+            kept[e] = (a, b)
+
+    mi.for_each_expert(cfg, put)
+    d["sw13"] = d["sw2"] = None
+    if cfg.shared_I:
+        d["sw13"] = up(mi.shared_w13(cfg)).to(dev)
+        d["sw2"] = up(mi.shared_w2(cfg)).to(dev)
+    torch.cuda.synchronize()
+    return d, kept
+
+
+# ------------------------------------------------------------------ cpu baseline
+def cpu_baseline(cfg, logits, kept, active, budget_s=20.0):
+    """The float64 oracle on the host: routing and permutation of every token,
+    the expert MLP of a sample of active experts; the total is scaled to the
+    whole layer by the number of active experts (every expert costs the same
+    weight traffic; rows are few in decode)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import moe_oracle as orc
+    threads = max(1, min(16, os.cpu_count() or 1))
+    with threadpool_limits(limits=threads):
+        x64 = mi.values_f64(mi.x(cfg), cfg.dtype)
+        t0 = time.perf_counter()
+        ids, w, _ = orc.route(cfg, logits)
+        p = orc.plan(cfg, ids)
+        x_perm = x64[p["row_to_token"]]
+        t_route = time.perf_counter() - t0
+        seg_off, seg_exp = p["seg_offsets"], p["seg_expert"]
+        t_ffn, done = 0.0, []
+        for e in sorted(kept):
+            w13 = mi.values_f64(kept[e][0], cfg.dtype)
+            w2 = mi.values_f64(kept[e][1], cfg.dtype)
+            t0 = time.perf_counter()
+            for s in np.nonzero(seg_exp == e)[0]:
+                r0, r1 = int(seg_off[s]), int(seg_off[s + 1])
+                if r1 > r0:
+                    orc.swiglu(x_perm[r0:r1], w13, w2)
+            t_ffn += time.perf_counter() - t0
+            done.append(e)
+            if t_ffn > budget_s:
+                break
+        t0 = time.perf_counter()
+        y = np.zeros((cfg.A, cfg.H))
+        orc.combine(y, p["assign_to_row"], w)
+        t_comb = time.perf_counter() - t0
+    est = t_route + t_ffn * active / max(1, len(done)) + t_comb
+    return {"value": cfg.T / est, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"float64 numpy oracle: routing, permutation and combine of all {cfg.T} "
+                       f"tokens; expert MLP of {len(done)} of {active} active experts "
+                       f"({t_ffn:.1f} s), scaled by {active}/{len(done)}; "
+                       f"estimated {est:.1f} s per layer")}
+
+
+# ------------------------------------------------------------------ main
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_bf16", choices=sorted(mi.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by expert parallelism across GPUs, which is not built here)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import mixture_experts_layer_segments_amd as moe
+    cfg = mi.WORKLOADS[args.workload]
+    print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
+    from oracle import moe_oracle as orc  # routing only, to choose the oracle sample
+    logits = mi.logits(cfg)
+    ids_ref, _, _ = orc.route(cfg, logits)
+    counts_ref = orc.expert_counts(ids_ref, cfg.E)
+    active = int((counts_ref > 0).sum())
+    act_ids = np.nonzero(counts_ref > 0)[0]
+    keep = act_ids[:: max(1, len(act_ids) // 8)][:8] if not args.no_cpu_baseline else []
+    d, kept = device_inputs(cfg, keep)
+
+    dev = torch.device("cuda:0")
+    tdt = d["x"].dtype
+    out = torch.empty((cfg.T, cfg.H), dtype=tdt, device=dev)
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
+    w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
+    counts = torch.empty((cfg.E,), dtype=torch.int32, device=dev)
+    bal = torch.empty((1,), dtype=torch.float32, device=dev)
+    ws = torch.empty((moe.moe_workspace_size(cfg),), dtype=torch.uint8, device=dev)
+
+    def step():
+        moe.moe_layer_forward(cfg, d["logits"], d["x"], d["w13"], d["w2"], d["sw13"], d["sw2"],
+                              out, ids, w, counts, bal, ws)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    assert (counts.cpu().numpy() == counts_ref).all(), "device counts differ from the oracle"
+
+    # dominant kernels: the grouped FFN on the permuted rows of this batch
+    S = moe.moe_num_segments(cfg)
+    A = cfg.A
+    x_perm = torch.empty((A, cfg.H), dtype=tdt, device=dev)
+    y_perm = torch.empty((A, cfg.H), dtype=tdt, device=dev)
+    so = torch.empty((S + 1,), dtype=torch.int32, device=dev)
+    se = torch.empty((S,), dtype=torch.int32, device=dev)
+    a2r = torch.empty((A,), dtype=torch.int32, device=dev)
+    r2t = torch.empty((A,), dtype=torch.int32, device=dev)
+    moe.moe_permute(cfg, d["x"], ids, x_perm, so, se, a2r, r2t, counts, bal, ws)
+    for _ in range(2):
+        moe.moe_grouped_ffn(cfg, x_perm, so, se, d["w13"], d["w2"], None, y_perm, ws)
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    f0.record(stream)
+    for _ in range(args.steps):
+        moe.moe_grouped_ffn(cfg, x_perm, so, se, d["w13"], d["w2"], None, y_perm, ws)
+    f1.record(stream)
+    torch.cuda.synchronize()
+    ffn_ms = f0.elapsed_time(f1) / args.steps
+
+    routed = cfg.replace(shared_I=0)
+    fl = ffn_flops(routed)
+    by = ffn_bytes(routed, active)
+    gbs = by / (ffn_ms * 1e-3) / 1e9
+    tflops = fl / (ffn_ms * 1e-3) / 1e12
+    hbm_bound = fl / (BF16_PEAK_TFLOPS * 1e12) < by / (HBM_PEAK_GBS * 1e9)
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    roof["kernel"] = "grouped FFN (gemm_tiled_kernel gate/up+SwiGLU and down+scale)"
+    roof["ms_per_launch"] = round(ffn_ms, 4)
+    roof["algorithmic_bytes"] = by
+    roof["algorithmic_flops"] = fl
+
+    res = {
+        "metric": METRIC, "value": round(cfg.T / (ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded; random-init weights)",
+        "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "experts": cfg.E,
+                   "top_k": cfg.k, "intermediate": cfg.I, "shared_intermediate": cfg.shared_I,
+                   "assignments": cfg.A, "active_experts": active,
+                   "balancedness": float(bal.item())},
+        "grouped_gemm_tflops": round(tflops, 2),
+        "grouped_gemm_frac_mfma": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "grouped_gemm_frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+        "wall_s_timed": round(wall, 3),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(cfg, logits, kept, active)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,185 @@
+/*
+ * moe.h -- C ABI of libmoe: the forward pass of one Mixture-of-Experts layer on
+ * one AMD Instinct MI355X (gfx950), as hand-written HIP kernels.
+ *
+ * The layer follows the four runtime steps of "Serving Mixture-of-Experts
+ * Models" (section "Follow one token through an MoE layer"), minus the network
+ * send: (1) the router's top-k expert ids and weights per token; (2) a
+ * histogram / prefix-sum permutation that packs token rows into contiguous
+ * per-expert segments; (3) every expert's segment through its SwiGLU MLP as a
+ * grouped matrix multiplication; (4) the inverse permutation with a
+ * router-weighted sum.  It also reports balancedness = mean / max tokens per
+ * expert (same chapter, section "The slowest expert sets the pace").
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless marked "host".  The caller allocates
+ *    and frees every buffer, including the workspace; the library never
+ *    allocates, frees or synchronises, and keeps no state between calls other
+ *    than a per-device cache of the compute-unit count.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream).  Calls on different streams may run concurrently if they use
+ *    different workspaces and outputs.
+ *  - Argument checks run on the host before anything is launched and return a
+ *    negative status synchronously; nothing is written then.  A failed launch
+ *    returns MOE_ERR_HIP.  Faults inside kernels surface at the caller's next
+ *    synchronisation, as for any asynchronous GPU API.
+ *  - Device index arrays are int32, row-major.  Assignment a = t*k + j is slot
+ *    j of token t.  Activations x, weights and outputs share one element type
+ *    (cfg->act_dtype): fp32 or bf16; arithmetic accumulates in fp32.
+ *  - T == 0 is an empty batch: every call returns MOE_OK and touches nothing.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment */
+  MOE_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels handle */
+  MOE_ERR_WORKSPACE = -3,   /* workspace_bytes too small */
+  MOE_ERR_HIP = -4          /* a HIP launch failed */
+} moe_status;
+
+typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 } moe_dtype;
+
+typedef enum {
+  MOE_SCORE_SOFTMAX = 0, /* flat top-k, softmax weights */
+  MOE_SCORE_SIGMOID = 1  /* group-limited top-k on sigmoid scores */
+} moe_score;
+
+/* Layer description, a host struct read by every call (never retained). */
+typedef struct moe_config {
+  int32_t T;  /* tokens in the batch (>= 0) */
+  int32_t H;  /* hidden size */
+  int32_t E;  /* routed (logical) experts, 1..1024 */
+  int32_t k;  /* experts per token, 1..min(E, 32) */
+  int32_t I;  /* expert intermediate size */
+  int32_t score;            /* moe_score */
+  int32_t n_group;          /* expert groups (contiguous, E % n_group == 0); 1 = flat */
+  int32_t topk_group;       /* groups kept per token (sigmoid mode) */
+  int32_t group_score_topn; /* a group's score = sum of its best n member scores */
+  int32_t renormalize;      /* 1: the k weights are renormalised to sum to 1 */
+  int32_t n_hot_split;      /* hottest experts given replica segments (0 = none) */
+  int32_t split_ways;       /* replicas per hot expert: token index mod ways (1..4) */
+  int32_t shared_I;         /* 0, or the shared expert's intermediate size */
+  int32_t act_dtype;        /* moe_dtype of x, weights, x_perm, y_perm, out */
+} moe_config;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_string(moe_status s);
+
+/* Number of segments S = E + min(n_hot_split, E) * (split_ways - 1)
+ * (split_ways > 1 only); -1 if cfg is NULL or invalid. */
+int32_t moe_num_segments(const moe_config* cfg);
+
+/* Bytes of device workspace that suffices for every call below with this
+ * configuration (moe_layer_forward needs all of it; moe_permute and
+ * moe_grouped_ffn need a leading part of it and accept any size at least
+ * that large).  0 if cfg is invalid. */
+size_t moe_workspace_size(const moe_config* cfg);
+
+/* Step 1 -- top-k gating ("Follow one token through an MoE layer": the router
+ * gives expert ids and weights for every token; the MoE inference blog's
+ * "MoE architecture recap": top-k experts, or a few expert groups first and
+ * then the top experts inside them).
+ *   logits   [T, E] fp32, finite.
+ *   topk_ids [T, k] out: expert ids in descending logit order; an exact tie
+ *            goes to the lower id.
+ *   topk_w   [T, k] out, fp32: softmax mode -- softmax over the k winners
+ *            (renormalize = 1) or the full-E softmax of each winner;
+ *            sigmoid mode -- groups are scored by the sum of their best
+ *            group_score_topn sigmoid scores (fp32), the topk_group best
+ *            groups are kept (lower group id on a tie), the k largest logits
+ *            of the kept groups win, and weights are s_j / sum(s)
+ *            (renormalize = 1) or s_j.  Weights are computed in fp64 and
+ *            rounded once to fp32. */
+moe_status moe_route_topk(const moe_config* cfg, const float* logits,
+                          int32_t* topk_ids, float* topk_w, void* stream);
+
+/* Step 2 -- histogram / prefix-sum permutation into contiguous per-expert
+ * segments ("Follow one token through an MoE layer", step 1).
+ *   x             [T, H]  act_dtype.
+ *   topk_ids      [T, k]  ids in [0, E); an id outside is dropped (its
+ *                          assign_to_row is -1 and it joins no segment).
+ *   x_perm        [T*k, H] out: x_perm[r] = x[row_to_token[r]] byte for byte,
+ *                          for r < seg_offsets[S]; later rows untouched.
+ *   seg_offsets   [S+1]   out: exclusive prefix sum of segment lengths.
+ *   seg_expert    [S]     out: logical expert of each segment.  Segments are
+ *                          in ascending expert order; a hot expert (one of the
+ *                          n_hot_split largest counts, lower id on a tie) has
+ *                          split_ways adjacent replica segments, replica p
+ *                          holding its assignments with t mod split_ways == p
+ *                          (replicas keep the logical selection and weights,
+ *                          Zepp section 4.1).  Empty segments stay listed.
+ *   assign_to_row [T*k]   out: row of each assignment (-1 if dropped).
+ *   row_to_token  [T*k]   out: token of each row (rows < seg_offsets[S]).
+ *   counts        [E]     out: assignments per logical expert.
+ *   balancedness  [1]     out, fp32: (sum(counts) / E) / max(counts), from
+ *                          exact integers by one fp64 division ("The slowest
+ *                          expert sets the pace"); 0 if every id was dropped.
+ * Rows of a segment are its assignments in increasing a (a stable counting
+ * sort), so every output is deterministic.  H * element size must be a
+ * multiple of 16 bytes and x / x_perm 16-byte aligned. */
+moe_status moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_ids,
+                       void* x_perm, int32_t* seg_offsets, int32_t* seg_expert,
+                       int32_t* assign_to_row, int32_t* row_to_token, int32_t* counts,
+                       float* balancedness, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Step 3 -- every segment through its expert as one grouped matrix
+ * multiplication ("Follow one token through an MoE layer", step 3; the MoE
+ * inference blog's "Optimized kernels for MoE": one kernel over many experts
+ * with different token counts).  Per row r of segment s, e = seg_expert[s]:
+ *   h = silu(x_perm[r] . W_gate[e]) * (x_perm[r] . W_up[e])   (fp32, rounded
+ *       to act_dtype), y_perm[r] = row_scale[r] * (h . W_down[e]).
+ *   x_perm      [T*k, H]  rows as produced by moe_permute.
+ *   seg_offsets [S+1], seg_expert [S] as produced by moe_permute (read on the
+ *               device; the host never needs the counts).
+ *   w13         [E, 2I, H] act_dtype, K-contiguous: rows 0..I-1 of expert e
+ *               are W_gate[e]^T, rows I..2I-1 are W_up[e]^T.
+ *   w2          [E, H, I]  act_dtype, W_down[e]^T.
+ *   row_scale   [T*k] fp32 indexed by row, or NULL for 1.0.
+ *   y_perm      [T*k, H] out (rows < seg_offsets[S]).
+ * bf16 needs H and I multiples of 64; all pointers 16-byte aligned. */
+moe_status moe_grouped_ffn(const moe_config* cfg, const void* x_perm,
+                           const int32_t* seg_offsets, const int32_t* seg_expert,
+                           const void* w13, const void* w2, const float* row_scale,
+                           void* y_perm, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Step 4 -- inverse permutation and router-weighted sum ("Follow one token
+ * through an MoE layer", step 4):
+ *   out[t] = sum_{j<k} w[t,j] * y_perm[assign_to_row[t*k+j]] (+ shared_y[t]),
+ * accumulated in fp32 in slot order j = 0..k-1 and rounded once.
+ *   topk_w    [T, k] fp32, or NULL when y_perm rows are already scaled.
+ *   shared_y  [T, H] or NULL (the shared expert, added with weight 1).
+ *   out       [T, H] out.  A dropped slot (assign_to_row -1) adds nothing. */
+moe_status moe_unpermute_combine(const moe_config* cfg, const void* y_perm,
+                                 const int32_t* assign_to_row, const float* topk_w,
+                                 const void* shared_y, void* out, void* stream);
+
+/* The whole layer: steps 1-4 plus the shared expert (if cfg->shared_I > 0;
+ * "MoE architecture recap": shared experts process every token), with no host
+ * synchronisation between steps (segment lengths never leave the device).
+ *   logits [T, E] fp32; x [T, H]; w13 [E, 2I, H]; w2 [E, H, I];
+ *   shared_w13 [2*shared_I, H] and shared_w2 [H, shared_I] (NULL if none);
+ *   out [T, H] out; topk_ids [T, k], topk_w [T, k], counts [E],
+ *   balancedness [1] out (as in the step calls).
+ *   workspace: at least moe_workspace_size(cfg) bytes, 256-byte aligned. */
+moe_status moe_layer_forward(const moe_config* cfg, const float* logits, const void* x,
+                             const void* w13, const void* w2, const void* shared_w13,
+                             const void* shared_w2, void* out, int32_t* topk_ids,
+                             float* topk_w, int32_t* counts, float* balancedness,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

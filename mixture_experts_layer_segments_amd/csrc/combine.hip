@@ -1,0 +1,115 @@
+// Inverse permutation with a router-weighted sum ("Serving Mixture-of-Experts
+// Models", section "Follow one token through an MoE layer", step 4):
+// out[t] = sum_j w[t,j] * y_perm[assign_to_row[t*k+j]] (+ shared_y[t]).
+// One wave per token; each lane owns 16-byte chunks of the row, accumulates
+// the k rows in fp32 in slot order and rounds once.  No atomics.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ void unpack_bf16x8(const uint4& u, float* f) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint4 pack_bf16x8(const float* f) {
+  uint4 u;
+  u.x = bf16_bits_rne(f[0]) | (bf16_bits_rne(f[1]) << 16);
+  u.y = bf16_bits_rne(f[2]) | (bf16_bits_rne(f[3]) << 16);
+  u.z = bf16_bits_rne(f[4]) | (bf16_bits_rne(f[5]) << 16);
+  u.w = bf16_bits_rne(f[6]) | (bf16_bits_rne(f[7]) << 16);
+  return u;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ y,
+                                                      const int32_t* __restrict__ a2r,
+                                                      const float* __restrict__ w,
+                                                      const uint4* __restrict__ shared_y,
+                                                      int T, int k, int row_chunks,
+                                                      uint4* __restrict__ out) {
+  constexpr int EPC = BF16 ? 8 : 4;  // elements per 16-byte chunk
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int32_t* rows = a2r + (size_t)t * k;  // wave-uniform: scalar loads
+  const float* wt = w ? w + (size_t)t * k : nullptr;
+  for (int c = lane; c < row_chunks; c += 64) {
+    float acc[EPC];
+#pragma unroll
+    for (int i = 0; i < EPC; ++i) acc[i] = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int r = rows[j];
+      if (r < 0) continue;
+      const float wj = wt ? wt[j] : 1.0f;
+      const uint4 u = y[(size_t)r * row_chunks + c];
+      float f[EPC];
+      if constexpr (BF16) {
+        unpack_bf16x8(u, f);
+      } else {
+        f[0] = __uint_as_float(u.x);
+        f[1] = __uint_as_float(u.y);
+        f[2] = __uint_as_float(u.z);
+        f[3] = __uint_as_float(u.w);
+      }
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) acc[i] = fmaf(wj, f[i], acc[i]);
+    }
+    if (shared_y) {
+      const uint4 u = shared_y[(size_t)t * row_chunks + c];
+      float f[EPC];
+      if constexpr (BF16) {
+        unpack_bf16x8(u, f);
+      } else {
+        f[0] = __uint_as_float(u.x);
+        f[1] = __uint_as_float(u.y);
+        f[2] = __uint_as_float(u.z);
+        f[3] = __uint_as_float(u.w);
+      }
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) acc[i] += f[i];
+    }
+    uint4 o;
+    if constexpr (BF16) {
+      o = pack_bf16x8(acc);
+    } else {
+      o.x = __float_as_uint(acc[0]);
+      o.y = __float_as_uint(acc[1]);
+      o.z = __float_as_uint(acc[2]);
+      o.w = __float_as_uint(acc[3]);
+    }
+    out[(size_t)t * row_chunks + c] = o;
+  }
+}
+
+}  // namespace
+
+void launch_combine(const moe_config& c, const void* y_perm, const int32_t* a2r,
+                    const float* w, const void* shared_y, void* out, hipStream_t s) {
+  const bool bf16 = c.act_dtype == MOE_DT_BF16;
+  const int row_chunks = c.H * (bf16 ? 2 : 4) / 16;
+  dim3 grid((c.T + 3) / 4);
+  if (bf16)
+    combine_kernel<true><<<grid, 256, 0, s>>>(
+        reinterpret_cast<const uint4*>(y_perm), a2r, w,
+        reinterpret_cast<const uint4*>(shared_y), c.T, c.k, row_chunks,
+        reinterpret_cast<uint4*>(out));
+  else
+    combine_kernel<false><<<grid, 256, 0, s>>>(
+        reinterpret_cast<const uint4*>(y_perm), a2r, w,
+        reinterpret_cast<const uint4*>(shared_y), c.T, c.k, row_chunks,
+        reinterpret_cast<uint4*>(out));
+}
+
+}  // namespace moe

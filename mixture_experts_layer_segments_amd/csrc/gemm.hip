@@ -1,0 +1,428 @@
+// Grouped SwiGLU expert MLP over ragged segments ("Serving Mixture-of-Experts
+// Models", section "Follow one token through an MoE layer", step 3: one kernel
+// runs every expert's segment as a matrix with its own row count; the MoE
+// inference blog, "Optimized kernels for MoE": grouped GEMM).
+//
+//   GEMM 1: [g | u] = X_s . [W_gate[e] | W_up[e]],  h = silu(g) * u
+//   GEMM 2: y = row_scale * (h . W_down[e])
+//
+// bf16 path: persistent MFMA kernels.  A device-side tile table (exclusive
+// prefix of tiles per segment) is built from the segment offsets, so segment
+// lengths never travel to the host.  Each workgroup walks the tile list with a
+// fixed stride; tiles are ordered segment-major, then by output column block,
+// then by row block, and the workgroup -> tile mapping is remapped so that
+// consecutive tiles (which share the same weight slice) land on the same XCD
+// and therefore the same L2.  The K loop double-buffers LDS tiles; operands
+// are XOR-swizzled in 16-byte chunks so that MFMA operand reads avoid bank
+// conflicts.  fp32 path: a plain FMA kernel (the fp32 layer is tiny).
+#include <math.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct GemmProblem {
+  const uint16_t* A;        // [rows, K] bf16 bits
+  const uint16_t* B;        // [n_w][NB, K]
+  uint16_t* C;              // [rows, N]
+  const float* scale;       // nullable, by row
+  const int32_t* seg_offsets;  // nullable: one segment [0, rows)
+  const int32_t* seg_expert;   // nullable: expert 0
+  int32_t n_seg, rows, N, K;
+  int32_t up_off;           // GEMM 1: row offset of W_up inside B
+  int64_t b_stride;         // elements per expert in B
+};
+
+struct GemmArgs {
+  GemmProblem p[2];
+  int32_t n_probs;
+  int32_t n_seg_total;
+  const int32_t* tiles;     // [n_seg_total + 1] exclusive prefix of tiles
+};
+
+__device__ __forceinline__ void seg_range(const GemmProblem& P, int s, int& r0, int& len,
+                                          int& e) {
+  if (P.seg_offsets) {
+    r0 = P.seg_offsets[s];
+    len = P.seg_offsets[s + 1] - r0;
+    e = P.seg_expert[s];
+  } else {
+    r0 = 0;
+    len = P.rows;
+    e = 0;
+  }
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// ---------------------------------------------------------------- tile table
+// tiles[s] = exclusive prefix over all segments of ceil(len/BM) * ceil(N/BN).
+__global__ __launch_bounds__(1024) void tile_plan_kernel(GemmArgs a1, int bm1, int bn1,
+                                                         GemmArgs a2, int bm2, int bn2,
+                                                         int32_t* tiles1, int32_t* tiles2) {
+  __shared__ int v1[kMaxSegments + 2];
+  __shared__ int v2[kMaxSegments + 2];
+  __shared__ int wt[2][17];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = a1.n_seg_total;
+  for (int g = tid; g < n; g += 1024) {
+    int p = 0, s = g;
+    if (s >= a1.p[0].n_seg) {
+      p = 1;
+      s -= a1.p[0].n_seg;
+    }
+    int r0, len, e;
+    seg_range(a1.p[p], s, r0, len, e);
+    const int mt1 = (len + bm1 - 1) / bm1, mt2 = (len + bm2 - 1) / bm2;
+    v1[g] = mt1 * ((a1.p[p].N + bn1 - 1) / bn1);
+    v2[g] = mt2 * ((a2.p[p].N + bn2 - 1) / bn2);
+  }
+  __syncthreads();
+  // exclusive scans of v1 and v2 (n <= 4097)
+  const int per = (n + 1023) / 1024;
+  const int lo = min(n, tid * per), hi = min(n, lo + per);
+  int s1 = 0, s2 = 0;
+  for (int i = lo; i < hi; ++i) {
+    s1 += v1[i];
+    s2 += v2[i];
+  }
+  int i1 = s1, i2 = s2;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int o1 = __shfl_up(i1, off), o2 = __shfl_up(i2, off);
+    if (lane >= off) {
+      i1 += o1;
+      i2 += o2;
+    }
+  }
+  if (lane == 63) {
+    wt[0][wv] = i1;
+    wt[1][wv] = i2;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int r1 = 0, r2 = 0;
+    for (int w = 0; w < 16; ++w) {
+      int t1 = wt[0][w], t2 = wt[1][w];
+      wt[0][w] = r1;
+      wt[1][w] = r2;
+      r1 += t1;
+      r2 += t2;
+    }
+    wt[0][16] = r1;
+    wt[1][16] = r2;
+  }
+  __syncthreads();
+  int run1 = wt[0][wv] + i1 - s1, run2 = wt[1][wv] + i2 - s2;
+  for (int i = lo; i < hi; ++i) {
+    tiles1[i] = run1;
+    tiles2[i] = run2;
+    run1 += v1[i];
+    run2 += v2[i];
+  }
+  if (tid == 0) {
+    tiles1[n] = wt[0][16];
+    tiles2[n] = wt[1][16];
+  }
+}
+
+// ---------------------------------------------------------------- bf16 MFMA
+// MODE 0: GEMM 1 with the SwiGLU epilogue.  The B tile holds BN rows: the
+//         first BN/2 are W_gate rows n0.., the rest W_up rows n0.. (output
+//         columns per tile = BN/2).  Each wave owns matching gate and up
+//         columns, so silu(g) * u is formed in registers.
+// MODE 1: GEMM 2 with the row-scale epilogue (BN output columns per tile).
+template <int MODE, int BM, int BN, int BK>
+__global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs args) {
+  constexpr int WM = BM / 2, WN = BN / 2;   // wave tile (2 x 2 waves)
+  constexpr int TM = WM / 16, TN = WN / 16; // MFMA 16x16 subtiles per wave
+  constexpr int KCH = BK / 8;               // 16-byte chunks per row
+  constexpr int A_LOADS = BM * KCH / 256, B_LOADS = BN * KCH / 256;
+  static_assert(KCH == 8, "swizzle assumes 8 chunks per row");
+
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * BK];
+  extern __shared__ int tiles_l[];  // [n_seg_total + 1], dynamic
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv >> 1, wn = wv & 1;
+  const int nst = args.n_seg_total;
+  for (int i = tid; i <= nst; i += 256) tiles_l[i] = args.tiles[i];
+  __syncthreads();
+  const int total = tiles_l[nst];
+
+  // XCD-aware persistent order: consecutive logical ids share an XCD.
+  const int G = gridDim.x;
+  const int logical = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+
+  for (int tile = logical; tile < total; tile += G) {
+    // segment of this tile: last s with tiles_l[s] <= tile
+    int lo = 0, hi = nst - 1;
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (tiles_l[mid] <= tile) lo = mid; else hi = mid - 1;
+    }
+    const int gs = lo;
+    const int pi = gs < args.p[0].n_seg ? 0 : 1;
+    const GemmProblem& P = args.p[pi];
+    const int s = gs - (pi ? args.p[0].n_seg : 0);
+    int r0, len, e;
+    seg_range(P, s, r0, len, e);
+    const int mt = (len + BM - 1) / BM;
+    const int local = tile - tiles_l[gs];
+    const int m_idx = local % mt, n_idx = local / mt;
+    const int m0 = m_idx * BM;
+    const int ncols = MODE == 0 ? BN / 2 : BN;
+    const int n0 = n_idx * ncols;
+    const int K = P.K, N = P.N;
+    const uint16_t* Ab = P.A + (size_t)r0 * K;
+    const uint16_t* Bb = P.B + (size_t)e * P.b_stride;
+
+    // per-thread global source pointers for this tile
+    const uint16_t* a_src[A_LOADS];
+    int a_dst[A_LOADS];
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) {
+      const int c = tid + 256 * i, row = c >> 3, kc = c & 7;
+      const int gr = min(m0 + row, len - 1);
+      a_src[i] = Ab + (size_t)gr * K + kc * 8;
+      a_dst[i] = row * BK + ((kc ^ (row & 7)) * 8);
+    }
+    const uint16_t* b_src[B_LOADS];
+    int b_dst[B_LOADS];
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) {
+      const int c = tid + 256 * i, row = c >> 3, kc = c & 7;
+      int brow;
+      if (MODE == 0) {
+        const int col = min(n0 + (row % (BN / 2)), N - 1);
+        brow = row < BN / 2 ? col : P.up_off + col;
+      } else {
+        brow = min(n0 + row, N - 1);
+      }
+      b_src[i] = Bb + (size_t)brow * K + kc * 8;
+      b_dst[i] = row * BK + ((kc ^ (row & 7)) * 8);
+    }
+
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 ra[A_LOADS], rb[B_LOADS];
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_src[i]);
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) rb[i] = *reinterpret_cast<const u32x4*>(b_src[i]);
+    __syncthreads();  // previous tile's epilogue done with LDS
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) *reinterpret_cast<u32x4*>(&As[0][a_dst[i]]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) *reinterpret_cast<u32x4*>(&Bs[0][b_dst[i]]) = rb[i];
+    __syncthreads();
+
+    // B-tile row of each of this wave's n subtiles
+    int brow_of[TN];
+#pragma unroll
+    for (int ni = 0; ni < TN; ++ni) {
+      if (MODE == 0)
+        brow_of[ni] = (ni < TN / 2) ? wn * (WN / 2) + ni * 16
+                                    : BN / 2 + wn * (WN / 2) + (ni - TN / 2) * 16;
+      else
+        brow_of[ni] = wn * WN + ni * 16;
+    }
+
+    const int KT = K / BK;
+    for (int kt = 0; kt < KT; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < KT) {
+        const int koff = (kt + 1) * BK;
+#pragma unroll
+        for (int i = 0; i < A_LOADS; ++i)
+          ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + koff);
+#pragma unroll
+        for (int i = 0; i < B_LOADS; ++i)
+          rb[i] = *reinterpret_cast<const u32x4*>(b_src[i] + koff);
+      }
+#pragma unroll
+      for (int kk = 0; kk < BK / 32; ++kk) {
+        const int ch = kk * 4 + (lane >> 4);
+        bf16x8 af[TM], bfr[TN];
+#pragma unroll
+        for (int mi = 0; mi < TM; ++mi) {
+          const int row = wm * WM + mi * 16 + (lane & 15);
+          af[mi] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(&As[cur][row * BK + ((ch ^ (row & 7)) * 8)]));
+        }
+#pragma unroll
+        for (int ni = 0; ni < TN; ++ni) {
+          const int row = brow_of[ni] + (lane & 15);
+          bfr[ni] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(&Bs[cur][row * BK + ((ch ^ (row & 7)) * 8)]));
+        }
+#pragma unroll
+        for (int mi = 0; mi < TM; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < TN; ++ni)
+            acc[mi][ni] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+      }
+      if (kt + 1 < KT) {
+        const int nxt = cur ^ 1;
+#pragma unroll
+        for (int i = 0; i < A_LOADS; ++i) *reinterpret_cast<u32x4*>(&As[nxt][a_dst[i]]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < B_LOADS; ++i) *reinterpret_cast<u32x4*>(&Bs[nxt][b_dst[i]]) = rb[i];
+      }
+      __syncthreads();
+    }
+
+    // epilogue: lane holds D[row = 4*(lane/16) + i][col = lane % 16]
+    uint16_t* Cb = P.C + (size_t)r0 * N;
+#pragma unroll
+    for (int mi = 0; mi < TM; ++mi) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = m0 + wm * WM + mi * 16 + (lane >> 4) * 4 + i;
+        if (row >= len) continue;
+        if (MODE == 0) {
+#pragma unroll
+          for (int ni = 0; ni < TN / 2; ++ni) {
+            const int col = n0 + wn * (WN / 2) + ni * 16 + (lane & 15);
+            if (col < N) {
+              const float g = acc[mi][ni][i], u = acc[mi][ni + TN / 2][i];
+              Cb[(size_t)row * N + col] = to_bf16(silu(g) * u);
+            }
+          }
+        } else {
+          const float sc = P.scale ? P.scale[r0 + row] : 1.0f;
+#pragma unroll
+          for (int ni = 0; ni < TN; ++ni) {
+            const int col = n0 + wn * WN + ni * 16 + (lane & 15);
+            if (col < N) Cb[(size_t)row * N + col] = to_bf16(acc[mi][ni][i] * sc);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- fp32 path
+// One thread per output element.  GEMM 1 writes h, GEMM 2 writes y.
+__device__ int find_segment(const int32_t* off, int n, int r) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A,
+                                                       const float* __restrict__ B,
+                                                       float* __restrict__ C,
+                                                       const float* __restrict__ scale,
+                                                       const int32_t* __restrict__ seg_offsets,
+                                                       const int32_t* __restrict__ seg_expert,
+                                                       int n_seg, int rows, int N, int K,
+                                                       int up_off, int64_t b_stride) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int row = (int)(idx / N), col = (int)(idx % N);
+  if (row >= rows) return;
+  int e = 0;
+  if (seg_offsets) {
+    if (row >= seg_offsets[n_seg]) return;
+    e = seg_expert[find_segment(seg_offsets, n_seg, row)];
+  }
+  const float* a = A + (size_t)row * K;
+  const float* b = B + (size_t)e * b_stride;
+  if (MODE == 0) {
+    const float* bg = b + (size_t)col * K;
+    const float* bu = b + (size_t)(up_off + col) * K;
+    float g = 0.f, u = 0.f;
+    for (int kk = 0; kk < K; ++kk) {
+      g = fmaf(a[kk], bg[kk], g);
+      u = fmaf(a[kk], bu[kk], u);
+    }
+    C[(size_t)row * N + col] = silu(g) * u;
+  } else {
+    const float* bd = b + (size_t)col * K;
+    float y = 0.f;
+    for (int kk = 0; kk < K; ++kk) y = fmaf(a[kk], bd[kk], y);
+    C[(size_t)row * N + col] = y * (scale ? scale[row] : 1.0f);
+  }
+}
+
+constexpr int BM1 = 128, BN1 = 128, BM2 = 128, BN2 = 128, BKT = 64;
+
+}  // namespace
+
+void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_probs,
+                        int32_t* tiles1, int32_t* tiles2, hipStream_t s) {
+  const int H = c.H;
+  if (c.act_dtype == MOE_DT_F32) {
+    for (int p = 0; p < n_probs; ++p) {
+      const FfnProblem& P = probs[p];
+      const int Iw = P.Iw;
+      int64_t n1 = (int64_t)P.rows * Iw, n2 = (int64_t)P.rows * H;
+      gemm_f32_kernel<0><<<(unsigned)((n1 + 255) / 256), 256, 0, s>>>(
+          (const float*)P.A, (const float*)P.w13, (float*)P.h, nullptr, P.seg_offsets,
+          P.seg_expert, P.n_seg, P.rows, Iw, H, Iw, (int64_t)2 * Iw * H);
+      gemm_f32_kernel<1><<<(unsigned)((n2 + 255) / 256), 256, 0, s>>>(
+          (const float*)P.h, (const float*)P.w2, (float*)P.y, P.row_scale, P.seg_offsets,
+          P.seg_expert, P.n_seg, P.rows, H, Iw, 0, (int64_t)H * Iw);
+    }
+    return;
+  }
+  GemmArgs g1{}, g2{};
+  int nst = 0;
+  for (int p = 0; p < n_probs; ++p) {
+    const FfnProblem& P = probs[p];
+    GemmProblem& a = g1.p[p];
+    a.A = (const uint16_t*)P.A;
+    a.B = (const uint16_t*)P.w13;
+    a.C = (uint16_t*)P.h;
+    a.scale = nullptr;
+    a.seg_offsets = P.seg_offsets;
+    a.seg_expert = P.seg_expert;
+    a.n_seg = P.n_seg;
+    a.rows = P.rows;
+    a.N = P.Iw;
+    a.K = H;
+    a.up_off = P.Iw;
+    a.b_stride = (int64_t)2 * P.Iw * H;
+    GemmProblem& b = g2.p[p];
+    b = a;
+    b.A = (const uint16_t*)P.h;
+    b.B = (const uint16_t*)P.w2;
+    b.C = (uint16_t*)P.y;
+    b.scale = P.row_scale;
+    b.N = H;
+    b.K = P.Iw;
+    b.up_off = 0;
+    b.b_stride = (int64_t)H * P.Iw;
+    nst += P.n_seg;
+  }
+  g1.n_probs = g2.n_probs = n_probs;
+  g1.n_seg_total = g2.n_seg_total = nst;
+  g1.tiles = tiles1;
+  g2.tiles = tiles2;
+  tile_plan_kernel<<<1, 1024, 0, s>>>(g1, BM1, BN1 / 2, g2, BM2, BN2, tiles1, tiles2);
+  const int grid = device_cu_count() * 2 / 8 * 8;
+  const size_t lds_tiles = (size_t)(nst + 1) * sizeof(int);
+  gemm_tiled_kernel<0, BM1, BN1, BKT><<<grid, 256, lds_tiles, s>>>(g1);
+  gemm_tiled_kernel<1, BM2, BN2, BKT><<<grid, 256, lds_tiles, s>>>(g2);
+}
+
+}  // namespace moe

@@ -1,0 +1,277 @@
+// C ABI of libmoe: argument checks, workspace layout and launch order.
+// Every check runs on the host before any HIP call, so a bad call returns a
+// status without touching the GPU (and can be tested on a machine without
+// one).
+#include <string.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+int32_t num_segments(const moe_config& c) {
+  if (c.n_hot_split > 0 && c.split_ways > 1)
+    return c.E + (c.n_hot_split < c.E ? c.n_hot_split : c.E) * (c.split_ways - 1);
+  return c.E;
+}
+
+Layout make_layout(const moe_config& c) {
+  Layout L{};
+  const size_t A = (size_t)c.T * c.k;
+  const size_t eb = c.act_dtype == MOE_DT_F32 ? 4 : 2;
+  const int ways = c.n_hot_split > 0 ? c.split_ways : 1;
+  const size_t nbins = (size_t)c.E * ways;
+  const size_t nb = (size_t)num_chunks((int64_t)A);
+  const size_t S = (size_t)num_segments(c);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  L.cnt_bin = take(nbins * nb * 4);
+  L.blk_off = take(S * nb * 4);
+  L.seg_of_bin = take(nbins * 4);
+  L.p_end = o;
+  L.tiles1 = take((S + 2) * 4);
+  L.tiles2 = take((S + 2) * 4);
+  L.h = take(A * c.I * eb);
+  L.shared_h = take((size_t)c.T * c.shared_I * eb);
+  L.g_end = o;
+  L.x_perm = take(A * c.H * eb);
+  L.y_perm = take(A * c.H * eb);
+  L.shared_y = take(c.shared_I > 0 ? (size_t)c.T * c.H * eb : 0);
+  L.seg_offsets = take((S + 1) * 4);
+  L.seg_expert = take(S * 4);
+  L.assign_to_row = take(A * 4);
+  L.row_to_token = take(A * 4);
+  L.row_w = take(A * 4);
+  L.l_end = o;
+  return L;
+}
+
+int device_cu_count() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+namespace {
+
+moe_status check_config(const moe_config* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->T < 0 || c->H <= 0 || c->E <= 0 || c->k <= 0 || c->I <= 0) return MOE_ERR_INVALID_ARG;
+  if (c->E > kMaxE || c->k > kMaxK) return MOE_ERR_UNSUPPORTED;
+  if (c->k > c->E) return MOE_ERR_INVALID_ARG;
+  if (c->act_dtype != MOE_DT_F32 && c->act_dtype != MOE_DT_BF16) return MOE_ERR_INVALID_ARG;
+  if (c->score != MOE_SCORE_SOFTMAX && c->score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (c->n_group <= 0 || c->E % c->n_group != 0) return MOE_ERR_INVALID_ARG;
+  if (c->n_group > 64) return MOE_ERR_UNSUPPORTED;
+  if (c->n_group > 1) {
+    if (c->score != MOE_SCORE_SIGMOID) return MOE_ERR_UNSUPPORTED;
+    const int per = c->E / c->n_group;
+    if (c->topk_group <= 0 || c->topk_group > c->n_group) return MOE_ERR_INVALID_ARG;
+    if ((int64_t)c->topk_group * per < c->k) return MOE_ERR_INVALID_ARG;
+    if (c->group_score_topn <= 0 || c->group_score_topn > per) return MOE_ERR_INVALID_ARG;
+  }
+  if (c->n_hot_split < 0 || c->split_ways < 1) return MOE_ERR_INVALID_ARG;
+  if (c->split_ways > kMaxWays) return MOE_ERR_UNSUPPORTED;
+  if (c->shared_I < 0) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)c->T * c->k > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED;
+  if (c->act_dtype == MOE_DT_BF16) {
+    if (c->H % 64 || c->I % 64 || c->shared_I % 64) return MOE_ERR_UNSUPPORTED;
+  } else {
+    if (c->H % 4) return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+moe_status launch_status() {
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t moe_num_segments(const moe_config* cfg) {
+  if (check_config(cfg) != MOE_OK) return -1;
+  return num_segments(*cfg);
+}
+
+size_t moe_workspace_size(const moe_config* cfg) {
+  if (check_config(cfg) != MOE_OK) return 0;
+  return make_layout(*cfg).l_end;
+}
+
+moe_status moe_route_topk(const moe_config* cfg, const float* logits, int32_t* topk_ids,
+                          float* topk_w, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->T == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4))
+    return MOE_ERR_INVALID_ARG;
+  launch_route(*cfg, logits, topk_ids, topk_w, (hipStream_t)stream);
+  return launch_status();
+}
+
+moe_status moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_ids,
+                       void* x_perm, int32_t* seg_offsets, int32_t* seg_expert,
+                       int32_t* assign_to_row, int32_t* row_to_token, int32_t* counts,
+                       float* balancedness, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->T == 0) return MOE_OK;
+  if (!x || !topk_ids || !x_perm || !seg_offsets || !seg_expert || !assign_to_row ||
+      !row_to_token || !counts || !balancedness || !workspace)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(x_perm, 16) || !aligned(workspace, kAlign) ||
+      !aligned(topk_ids, 4) || !aligned(seg_offsets, 4) || !aligned(seg_expert, 4) ||
+      !aligned(assign_to_row, 4) || !aligned(row_to_token, 4) || !aligned(counts, 4) ||
+      !aligned(balancedness, 4))
+    return MOE_ERR_INVALID_ARG;
+  const Layout L = make_layout(*cfg);
+  if (workspace_bytes < L.p_end) return MOE_ERR_WORKSPACE;
+  launch_permute(*cfg, x, topk_ids, x_perm, seg_offsets, seg_expert, assign_to_row,
+                 row_to_token, counts, balancedness, nullptr, nullptr, (char*)workspace, L,
+                 (hipStream_t)stream);
+  return launch_status();
+}
+
+moe_status moe_grouped_ffn(const moe_config* cfg, const void* x_perm,
+                           const int32_t* seg_offsets, const int32_t* seg_expert,
+                           const void* w13, const void* w2, const float* row_scale,
+                           void* y_perm, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->T == 0) return MOE_OK;
+  if (!x_perm || !seg_offsets || !seg_expert || !w13 || !w2 || !y_perm || !workspace)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(x_perm, 16) || !aligned(w13, 16) || !aligned(w2, 16) || !aligned(y_perm, 16) ||
+      !aligned(workspace, kAlign) || !aligned(seg_offsets, 4) || !aligned(seg_expert, 4) ||
+      (row_scale && !aligned(row_scale, 4)))
+    return MOE_ERR_INVALID_ARG;
+  const Layout L = make_layout(*cfg);
+  if (workspace_bytes < L.g_end) return MOE_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  FfnProblem p{};
+  p.A = x_perm;
+  p.w13 = w13;
+  p.w2 = w2;
+  p.h = ws + L.h;
+  p.y = y_perm;
+  p.row_scale = row_scale;
+  p.seg_offsets = seg_offsets;
+  p.seg_expert = seg_expert;
+  p.n_seg = num_segments(*cfg);
+  p.rows = cfg->T * cfg->k;
+  p.Iw = cfg->I;
+  launch_grouped_ffn(*cfg, &p, 1, (int32_t*)(ws + L.tiles1), (int32_t*)(ws + L.tiles2),
+                     (hipStream_t)stream);
+  return launch_status();
+}
+
+moe_status moe_unpermute_combine(const moe_config* cfg, const void* y_perm,
+                                 const int32_t* assign_to_row, const float* topk_w,
+                                 const void* shared_y, void* out, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->T == 0) return MOE_OK;
+  if (!y_perm || !assign_to_row || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned(y_perm, 16) || !aligned(out, 16) || (shared_y && !aligned(shared_y, 16)) ||
+      !aligned(assign_to_row, 4) || (topk_w && !aligned(topk_w, 4)))
+    return MOE_ERR_INVALID_ARG;
+  launch_combine(*cfg, y_perm, assign_to_row, topk_w, shared_y, out, (hipStream_t)stream);
+  return launch_status();
+}
+
+moe_status moe_layer_forward(const moe_config* cfg, const float* logits, const void* x,
+                             const void* w13, const void* w2, const void* shared_w13,
+                             const void* shared_w2, void* out, int32_t* topk_ids,
+                             float* topk_w, int32_t* counts, float* balancedness,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->T == 0) return MOE_OK;
+  const bool shared = cfg->shared_I > 0;
+  if (!logits || !x || !w13 || !w2 || !out || !topk_ids || !topk_w || !counts ||
+      !balancedness || !workspace || (shared && (!shared_w13 || !shared_w2)))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w13, 16) || !aligned(w2, 16) || !aligned(out, 16) ||
+      (shared && (!aligned(shared_w13, 16) || !aligned(shared_w2, 16))) ||
+      !aligned(workspace, kAlign) || !aligned(logits, 4) || !aligned(topk_ids, 4) ||
+      !aligned(topk_w, 4) || !aligned(counts, 4) || !aligned(balancedness, 4))
+    return MOE_ERR_INVALID_ARG;
+  const Layout L = make_layout(*cfg);
+  if (workspace_bytes < L.l_end) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  int32_t* seg_offsets = (int32_t*)(ws + L.seg_offsets);
+  int32_t* seg_expert = (int32_t*)(ws + L.seg_expert);
+  int32_t* a2r = (int32_t*)(ws + L.assign_to_row);
+  int32_t* r2t = (int32_t*)(ws + L.row_to_token);
+  float* row_w = (float*)(ws + L.row_w);
+
+  launch_route(*cfg, logits, topk_ids, topk_w, s);
+  launch_permute(*cfg, x, topk_ids, ws + L.x_perm, seg_offsets, seg_expert, a2r, r2t, counts,
+                 balancedness, topk_w, row_w, ws, L, s);
+  FfnProblem p[2]{};
+  p[0].A = ws + L.x_perm;
+  p[0].w13 = w13;
+  p[0].w2 = w2;
+  p[0].h = ws + L.h;
+  p[0].y = ws + L.y_perm;
+  p[0].row_scale = row_w;
+  p[0].seg_offsets = seg_offsets;
+  p[0].seg_expert = seg_expert;
+  p[0].n_seg = num_segments(*cfg);
+  p[0].rows = cfg->T * cfg->k;
+  p[0].Iw = cfg->I;
+  if (shared) {
+    p[1].A = x;
+    p[1].w13 = shared_w13;
+    p[1].w2 = shared_w2;
+    p[1].h = ws + L.shared_h;
+    p[1].y = ws + L.shared_y;
+    p[1].row_scale = nullptr;
+    p[1].seg_offsets = nullptr;
+    p[1].seg_expert = nullptr;
+    p[1].n_seg = 1;
+    p[1].rows = cfg->T;
+    p[1].Iw = cfg->shared_I;
+  }
+  launch_grouped_ffn(*cfg, p, shared ? 2 : 1, (int32_t*)(ws + L.tiles1),
+                     (int32_t*)(ws + L.tiles2), s);
+  launch_combine(*cfg, ws + L.y_perm, a2r, nullptr, shared ? ws + L.shared_y : nullptr, out,
+                 s);
+  return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Internal declarations shared by the HIP translation units of libmoe.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 32;
+constexpr int kMaxWays = 4;
+constexpr int kMaxBins = kMaxE * kMaxWays;
+constexpr int kMaxSegments = kMaxE * kMaxWays;
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
+
+// Assignment chunk of one histogram / rank block: a multiple of 64, at least
+// 256, grown so that there are at most ~256 chunks.
+inline int chunk_len(int64_t A) {
+  int64_t c = (A + 255) / 256;
+  c = (c + 63) / 64 * 64;
+  if (c < 256) c = 256;
+  return (int)c;
+}
+inline int num_chunks(int64_t A) { return (int)((A + chunk_len(A) - 1) / chunk_len(A)); }
+
+// Offsets of the workspace regions (bytes).  P: permutation scratch;
+// G: grouped-FFN scratch (tile tables, h); L: layer intermediates.
+struct Layout {
+  size_t cnt_bin, blk_off, seg_of_bin, p_end;                 // region P
+  size_t tiles1, tiles2, h, shared_h, g_end;                  // region G
+  size_t x_perm, y_perm, shared_y, seg_offsets, seg_expert,   // region L
+      assign_to_row, row_to_token, row_w, l_end;
+};
+Layout make_layout(const moe_config& c);
+int32_t num_segments(const moe_config& c);
+
+// ---- launchers (all asynchronous on `s`) ----
+void launch_route(const moe_config& c, const float* logits, int32_t* ids, float* w,
+                  hipStream_t s);
+void launch_permute(const moe_config& c, const void* x, const int32_t* ids, void* x_perm,
+                    int32_t* seg_offsets, int32_t* seg_expert, int32_t* a2r, int32_t* r2t,
+                    int32_t* counts, float* bal, const float* w, float* row_w, char* ws,
+                    const Layout& L, hipStream_t s);
+
+// One grouped-FFN problem: segments [seg_offsets[s], seg_offsets[s+1]) of
+// the rows of A, or (shared) one segment of all `rows` rows.
+struct FfnProblem {
+  const void* A;          // [rows, K1] act dtype
+  const void* w13;        // [n_w, 2*Iw, K1]
+  const void* w2;         // [n_w, K1, Iw]
+  void* h;                // [rows, Iw] scratch
+  void* y;                // [rows, K1] out
+  const float* row_scale; // nullable, by row
+  const int32_t* seg_offsets;  // nullable: shared problem = one segment
+  const int32_t* seg_expert;
+  int32_t n_seg;          // segments (1 for shared)
+  int32_t rows;           // max rows (A rows)
+  int32_t Iw;             // intermediate size of this problem
+};
+void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_probs,
+                        int32_t* tiles1, int32_t* tiles2, hipStream_t s);
+void launch_combine(const moe_config& c, const void* y_perm, const int32_t* a2r,
+                    const float* w, const void* shared_y, void* out, hipStream_t s);
+
+int device_cu_count();
+
+}  // namespace moe

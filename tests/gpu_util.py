@@ -1,0 +1,131 @@
+"""Helpers shared by the GPU parity tests: seeded inputs on the device, the
+C-ABI calls, and the oracle's expected values (computed on the host from the
+same seeded inputs; nothing expected ever comes from the GPU)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import moe_inputs as mi
+from oracle import moe_oracle as orc
+
+BF16_REL = 1.5e-2   # max|gpu - oracle| <= BF16_REL * max|oracle|  (bf16 layers)
+F32_REL = 1e-4      # same, fp32 layers
+W_TOL = 2.0 ** -24  # routing weights: fp64 math rounded once to fp32
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def tdtype(cfg):
+    return torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+
+
+def to_dev(a: np.ndarray, dtype: str):
+    """Host input (fp32 array or bf16 bits) -> device tensor of that type."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev()).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev())
+
+
+def host_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-300))
+
+
+def rel_tol(cfg) -> float:
+    return F32_REL if cfg.dtype == "f32" else BF16_REL
+
+
+def empty(shape, dtype):
+    return torch.empty(shape, dtype=dtype, device=dev())
+
+
+class SmallCase:
+    """A layer small enough for the whole oracle: all inputs on host and
+    device, and every intermediate of the oracle."""
+
+    def __init__(self, cfg, logits=None, ids_override=None):
+        self.cfg = cfg
+        self.logits = mi.logits(cfg) if logits is None else logits
+        self.xb = mi.x(cfg)
+        self.w13b = np.stack([mi.w13(cfg, e) for e in range(cfg.E)])
+        self.w2b = np.stack([mi.w2(cfg, e) for e in range(cfg.E)])
+        self.sw13b = mi.shared_w13(cfg) if cfg.shared_I else None
+        self.sw2b = mi.shared_w2(cfg) if cfg.shared_I else None
+        f = lambda a: None if a is None else mi.values_f64(a, cfg.dtype)  # noqa: E731
+        self.x64, self.w13_64, self.w2_64 = f(self.xb), f(self.w13b), f(self.w2b)
+        self.sw13_64, self.sw2_64 = f(self.sw13b), f(self.sw2b)
+        self.ref = orc.layer_forward(cfg, self.logits, self.x64, self.w13_64, self.w2_64,
+                                     self.sw13_64, self.sw2_64)
+
+    def device_inputs(self):
+        c = self.cfg
+        d = dict(logits=torch.from_numpy(self.logits).to(dev()), x=to_dev(self.xb, c.dtype),
+                 w13=to_dev(self.w13b, c.dtype), w2=to_dev(self.w2b, c.dtype),
+                 sw13=None, sw2=None)
+        if c.shared_I:
+            d["sw13"] = to_dev(self.sw13b, c.dtype)
+            d["sw2"] = to_dev(self.sw2b, c.dtype)
+        return d
+
+
+def run_layer(moe, cfg, d):
+    """moe_layer_forward on device inputs d; returns its outputs."""
+    o = dict(out=empty((cfg.T, cfg.H), tdtype(cfg)), ids=empty((cfg.T, cfg.k), torch.int32),
+             w=empty((cfg.T, cfg.k), torch.float32), counts=empty((cfg.E,), torch.int32),
+             bal=empty((1,), torch.float32))
+    ws = empty((moe.moe_workspace_size(cfg),), torch.uint8)
+    moe.moe_layer_forward(cfg, d["logits"], d["x"], d["w13"], d["w2"], d["sw13"], d["sw2"],
+                          o["out"], o["ids"], o["w"], o["counts"], o["bal"], ws)
+    torch.cuda.synchronize()
+    return o
+
+
+def run_permute(moe, cfg, x_d, ids_d):
+    S = moe.moe_num_segments(cfg)
+    A = cfg.T * cfg.k
+    o = dict(x_perm=empty((A, cfg.H), tdtype(cfg)), seg_offsets=empty((S + 1,), torch.int32),
+             seg_expert=empty((S,), torch.int32), a2r=empty((A,), torch.int32),
+             r2t=empty((A,), torch.int32), counts=empty((cfg.E,), torch.int32),
+             bal=empty((1,), torch.float32))
+    ws = empty((moe.moe_workspace_size(cfg),), torch.uint8)
+    moe.moe_permute(cfg, x_d, ids_d, o["x_perm"], o["seg_offsets"], o["seg_expert"], o["a2r"],
+                    o["r2t"], o["counts"], o["bal"], ws)
+    torch.cuda.synchronize()
+    return o
+
+
+def check_plan(gpu: dict, ref: dict, n_rows: int | None = None):
+    """Bit-exact permutation outputs against the oracle."""
+    assert (gpu["counts"].cpu().numpy() == ref["counts"]).all(), "counts"
+    assert (gpu["seg_offsets"].cpu().numpy() == ref["seg_offsets"]).all(), "seg_offsets"
+    assert (gpu["seg_expert"].cpu().numpy() == ref["seg_expert"]).all(), "seg_expert"
+    assert (gpu["a2r"].cpu().numpy() == ref["assign_to_row"]).all(), "assign_to_row"
+    R = int(ref["seg_offsets"][-1])
+    assert (gpu["r2t"].cpu().numpy()[:R] == ref["row_to_token"][:R]).all(), "row_to_token"
+    assert gpu["bal"].cpu().numpy()[0] == ref["balancedness"], "balancedness"
+
+
+def check_routing(cfg, ids_gpu: np.ndarray, w_gpu: np.ndarray, ids_ref, w_ref, gap,
+                  logits=None):
+    """ids bit-exact, except tokens whose kept-group choice sits within a few
+    fp32 ulp of another (gap <= 4 ulp), where any choice among the tied groups
+    is correct; there the chosen groups must all score within the tie band."""
+    mism = np.nonzero((ids_gpu != ids_ref).any(axis=1))[0]
+    if mism.size:
+        assert cfg.score == "sigmoid", f"flat routing differs at tokens {mism[:10]}"
+        gs = orc.group_scores_f32(logits[mism], cfg.n_group, cfg.group_score_topn)
+        per = cfg.E // cfg.n_group
+        for i, t in enumerate(mism):
+            band = 4 * float(np.spacing(np.float32(np.sort(gs[i])[-cfg.topk_group])))
+            assert gap[t] <= band, f"token {t}: ids differ but the group gap {gap[t]} is not a tie"
+            thr = np.sort(gs[i])[-cfg.topk_group] - band
+            assert all(gs[i][e // per] >= thr for e in ids_gpu[t]), f"token {t}: invalid groups"
+    ok = np.setdiff1d(np.arange(cfg.T), mism)
+    assert np.abs(w_gpu[ok].astype(np.float64) - w_ref[ok]).max() <= W_TOL
+    return mism

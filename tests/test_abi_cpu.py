@@ -1,0 +1,121 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every symbol
+that include/moe.h declares, and rejects bad arguments synchronously with a
+status code before launching anything (every call here fails validation, so
+no kernel is ever launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_inputs as mi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import mixture_experts_layer_segments_amd as m
+    return m
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "moe.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\S.*?\b(moe_[a-z_]+)\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(moe):
+    names = _declared()
+    assert set(names) == set(moe.EXPORTED_SYMBOLS), names
+    for n in names:
+        assert hasattr(moe.lib, n), n
+
+
+def test_status_strings(moe):
+    for s in (0, -1, -2, -3, -4):
+        assert moe.moe_status_string(s)
+    assert moe.moe_status_string(-99) == "unknown status"
+
+
+def test_segments_and_workspace_of_the_workloads(moe):
+    expect = {"tiny_fp32": 64, "decode_bf16": 64, "prefill_skew_bf16": 64,
+              "deepseek_v3_bf16": 256, "ragged_stress_bf16": 136}
+    for name, S in expect.items():
+        cfg = mi.WORKLOADS[name]
+        assert moe.moe_num_segments(cfg) == S == cfg.S
+        ws = moe.moe_workspace_size(cfg)
+        eb = cfg.elem_bytes
+        # at least x_perm, y_perm and h of every assignment
+        assert ws >= cfg.A * (2 * cfg.H + cfg.I) * eb
+
+
+FAKE = 1 << 20          # 256-byte aligned non-null address, never dereferenced
+
+
+def _layer(moe, cfg, ws_bytes=None, **override):
+    c = moe.make_config(cfg)
+    args = dict(logits=FAKE, x=FAKE, w13=FAKE, w2=FAKE, sw13=None, sw2=None, out=FAKE,
+                ids=FAKE, w=FAKE, counts=FAKE, bal=FAKE, ws=FAKE)
+    args.update(override)
+    wsb = moe.moe_workspace_size(cfg) if ws_bytes is None else ws_bytes
+    return moe.lib.moe_layer_forward(ctypes.byref(c), args["logits"], args["x"], args["w13"],
+                                     args["w2"], args["sw13"], args["sw2"], args["out"],
+                                     args["ids"], args["w"], args["counts"], args["bal"],
+                                     args["ws"], wsb, None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("E", 0, -1), ("k", 0, -1), ("H", -8, -1), ("I", 0, -1), ("T", -1, -1),
+    ("k", 65, -2), ("E", 2048, -2), ("act_dtype", 7, -1), ("score", 3, -1),
+    ("n_group", 3, -1), ("split_ways", 9, -2), ("H", 100, -2), ("I", 96, -2),
+    ("shared_I", 32, -2), ("renormalize", 2, -1),
+])
+def test_bad_config_is_rejected(moe, field, value, status):
+    c = moe.make_config(mi.WORKLOADS["decode_bf16"])
+    setattr(c, field, value)
+    assert moe.lib.moe_route_topk(ctypes.byref(c), FAKE, FAKE, FAKE, None) == status
+    assert moe.lib.moe_workspace_size(ctypes.byref(c)) == 0
+    assert moe.lib.moe_num_segments(ctypes.byref(c)) == -1
+
+
+def test_grouped_softmax_and_bad_groups_are_rejected(moe):
+    base = mi.WORKLOADS["deepseek_v3_bf16"]
+    for kw, st in [(dict(score="softmax"), -2), (dict(topk_group=0), -1),
+                   (dict(topk_group=9), -1), (dict(group_score_topn=33), -1),
+                   (dict(k=8, topk_group=1, n_group=64), -1)]:
+        c = moe.make_config(base.replace(**kw))
+        assert moe.lib.moe_route_topk(ctypes.byref(c), FAKE, FAKE, FAKE, None) == st, kw
+
+
+def test_null_misaligned_and_small_workspace(moe):
+    cfg = mi.WORKLOADS["decode_bf16"]
+    assert _layer(moe, cfg, out=None) == -1
+    assert _layer(moe, cfg, x=FAKE + 8) == -1             # 16-byte alignment
+    assert _layer(moe, cfg, ws=FAKE + 64) == -1           # 256-byte alignment
+    assert _layer(moe, cfg, ws_bytes=moe.moe_workspace_size(cfg) - 1) == -3
+    shared = mi.WORKLOADS["deepseek_v3_bf16"]
+    assert _layer(moe, shared) == -1                       # shared weights missing
+    c = moe.make_config(cfg)
+    assert moe.lib.moe_permute(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               FAKE, FAKE, 16, None) == -3
+    assert moe.lib.moe_grouped_ffn(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                   FAKE, 16, None) == -3
+    assert moe.lib.moe_unpermute_combine(ctypes.byref(c), FAKE, None, None, None, FAKE,
+                                         None) == -1
+
+
+def test_empty_batch_returns_ok_without_launching(moe):
+    cfg = mi.WORKLOADS["decode_bf16"].replace(T=0)
+    c = moe.make_config(cfg)
+    assert moe.lib.moe_route_topk(ctypes.byref(c), None, None, None, None) == 0
+    assert _layer(moe, cfg, out=None) == 0
+
+
+def test_config_struct_matches_header(moe):
+    with open(os.path.join(ROOT, "include", "moe.h")) as f:
+        text = f.read()
+    body = text[text.index("typedef struct moe_config"):text.index("} moe_config;")]
+    fields = re.findall(r"int32_t\s+([^;]+);", body)
+    names = [n.strip() for grp in fields for n in grp.split(",")]
+    assert names == [f for f, _ in moe.MoEConfig._fields_]

@@ -1,0 +1,192 @@
+"""GPU parity of every C-ABI call against the CPU oracle on small layers that
+the whole oracle finishes in seconds, spanning several tiles with ragged
+tails, plus the degenerate cases (one expert, k = E, one hot expert taking
+every token, replica splits, dropped ids, an empty batch)."""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+from oracle import moe_oracle as orc
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = {
+    "tiny_fp32": mi.WORKLOADS["tiny_fp32"],
+    "bf16_tiles_hot_split": mi.MoEShape("t1", T=300, H=576, E=16, k=4, I=320, zipf_s=1.2,
+                                        n_hot_split=3, split_ways=2, seed=11),
+    "bf16_grouped_shared": mi.MoEShape("t2", T=200, H=256, E=32, k=4, I=128, score="sigmoid",
+                                       n_group=4, topk_group=2, shared_I=192, zipf_s=1.0,
+                                       seed=12),
+    "f32_ragged": mi.MoEShape("t3", T=50, H=132, E=10, k=3, I=70, dtype="f32", seed=13),
+    "bf16_one_expert": mi.MoEShape("t4", T=70, H=128, E=1, k=1, I=64, seed=14),
+    "bf16_k_equals_E": mi.MoEShape("t5", T=33, H=192, E=4, k=4, I=128, seed=15),
+    "bf16_three_way_split": mi.MoEShape("t6", T=257, H=128, E=12, k=3, I=64, zipf_s=1.5,
+                                        n_hot_split=2, split_ways=3, seed=16),
+    "bf16_single_token": mi.MoEShape("t7", T=1, H=512, E=64, k=8, I=256, seed=17),
+    "bf16_no_renorm_sigmoid": mi.MoEShape("t8", T=90, H=256, E=64, k=6, I=128, score="sigmoid",
+                                          n_group=8, topk_group=3, renormalize=0, seed=18),
+    "bf16_no_renorm_softmax": mi.MoEShape("t9", T=90, H=256, E=48, k=5, I=128, renormalize=0,
+                                          seed=19),
+}
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import mixture_experts_layer_segments_amd as m
+    return m
+
+
+@pytest.fixture(scope="module", params=sorted(SHAPES))
+def case(request):
+    print(f"\n[case] {request.param}", flush=True)
+    return gu.SmallCase(SHAPES[request.param])
+
+
+def test_route(moe, case):
+    c, d = case.cfg, case.device_inputs()
+    ids = gu.empty((c.T, c.k), torch.int32)
+    w = gu.empty((c.T, c.k), torch.float32)
+    moe.moe_route_topk(c, d["logits"], ids, w)
+    torch.cuda.synchronize()
+    mism = gu.check_routing(c, ids.cpu().numpy(), w.cpu().numpy(), case.ref["ids"],
+                            case.ref["w"], case.ref["group_gap"], case.logits)
+    assert mism.size == 0
+
+
+def test_permute(moe, case):
+    c, d = case.cfg, case.device_inputs()
+    ids_d = torch.from_numpy(case.ref["ids"]).to(gu.dev())
+    g = gu.run_permute(moe, c, d["x"], ids_d)
+    gu.check_plan(g, case.ref)
+    R = int(case.ref["seg_offsets"][-1])
+    xp = g["x_perm"][:R].cpu()
+    expect = d["x"].cpu()[torch.from_numpy(case.ref["row_to_token"][:R]).long()]
+    assert torch.equal(xp.view(torch.int16) if c.dtype == "bf16" else xp.view(torch.int32),
+                       expect.view(torch.int16) if c.dtype == "bf16" else expect.view(torch.int32))
+
+
+def test_grouped_ffn(moe, case):
+    c, d = case.cfg, case.device_inputs()
+    r = case.ref
+    R = int(r["seg_offsets"][-1])
+    x_perm = gu.to_dev(case.xb[r["row_to_token"]], c.dtype)
+    so = torch.from_numpy(r["seg_offsets"]).to(gu.dev())
+    se = torch.from_numpy(r["seg_expert"]).to(gu.dev())
+    y = gu.empty((c.T * c.k, c.H), gu.tdtype(c))
+    ws = gu.empty((moe.moe_workspace_size(c),), torch.uint8)
+    moe.moe_grouped_ffn(c, x_perm, so, se, d["w13"], d["w2"], None, y, ws)
+    torch.cuda.synchronize()
+    err = gu.rel_err(gu.host_f64(y[:R]), r["y_perm"][:R])
+    assert err <= gu.rel_tol(c), err
+    # router weight applied in the epilogue
+    row_w = r["w"].reshape(-1)[r["row_to_assign"]].astype(np.float32)
+    moe.moe_grouped_ffn(c, x_perm, so, se, d["w13"], d["w2"],
+                        torch.from_numpy(row_w).to(gu.dev()), y, ws)
+    torch.cuda.synchronize()
+    ref_s = r["y_perm"][:R] * row_w[:R, None].astype(np.float64)
+    err = gu.rel_err(gu.host_f64(y[:R]), ref_s)
+    assert err <= gu.rel_tol(c), err
+
+
+def test_combine(moe, case):
+    c, d = case.cfg, case.device_inputs()
+    r = case.ref
+    y_enc = mi.bf16_bits(r["y_perm"].astype(np.float32)) if c.dtype == "bf16" \
+        else r["y_perm"].astype(np.float32)
+    y_in = mi.values_f64(y_enc, c.dtype)
+    sh_enc = sh_in = None
+    if r["shared_y"] is not None:
+        sh_enc = mi.bf16_bits(r["shared_y"].astype(np.float32)) if c.dtype == "bf16" \
+            else r["shared_y"].astype(np.float32)
+        sh_in = mi.values_f64(sh_enc, c.dtype)
+    out = gu.empty((c.T, c.H), gu.tdtype(c))
+    w32 = r["w"].astype(np.float32)
+    moe.moe_unpermute_combine(c, gu.to_dev(y_enc, c.dtype),
+                              torch.from_numpy(r["assign_to_row"]).to(gu.dev()),
+                              torch.from_numpy(w32).to(gu.dev()),
+                              None if sh_enc is None else gu.to_dev(sh_enc, c.dtype), out)
+    torch.cuda.synchronize()
+    ref = orc.combine(y_in, r["assign_to_row"], w32.astype(np.float64), sh_in)
+    # fp32 accumulation of k + 1 terms, one final rounding to the output type
+    tol = (2.0 ** -8 if c.dtype == "bf16" else 2.0 ** -20) * np.abs(ref).max()
+    assert np.abs(gu.host_f64(out) - ref).max() <= tol
+
+
+def test_layer_forward(moe, case):
+    c, d = case.cfg, case.device_inputs()
+    o = gu.run_layer(moe, c, d)
+    r = case.ref
+    gu.check_routing(c, o["ids"].cpu().numpy(), o["w"].cpu().numpy(), r["ids"], r["w"],
+                     r["group_gap"], case.logits)
+    assert (o["counts"].cpu().numpy() == r["counts"]).all()
+    assert o["bal"].cpu().numpy()[0] == r["balancedness"]
+    err = gu.rel_err(gu.host_f64(o["out"]), r["out"])
+    print(f"  layer rel err {err:.3e}")
+    assert err <= gu.rel_tol(c), err
+    # deterministic: a second run is bit-identical
+    o2 = gu.run_layer(moe, c, d)
+    assert torch.equal(o["out"].view(torch.int16) if c.dtype == "bf16" else o["out"],
+                       o2["out"].view(torch.int16) if c.dtype == "bf16" else o2["out"])
+
+
+def test_one_hot_expert_takes_every_token(moe):
+    """Every token routes first to expert 5: one segment holds every slot-0
+    row and most segments are empty."""
+    cfg = mi.MoEShape("hot", T=333, H=256, E=16, k=2, I=128, seed=21)
+    lg = mi.logits(cfg)
+    lg[:, 5] = lg.max(axis=1) + 1.0
+    case = gu.SmallCase(cfg, logits=lg)
+    o = gu.run_layer(moe, cfg, case.device_inputs())
+    assert o["counts"].cpu().numpy()[5] == cfg.T
+    assert (o["counts"].cpu().numpy() == case.ref["counts"]).all()
+    assert o["bal"].cpu().numpy()[0] == case.ref["balancedness"]
+    assert gu.rel_err(gu.host_f64(o["out"]), case.ref["out"]) <= gu.BF16_REL
+
+
+def test_dropped_ids(moe):
+    """Ids outside [0, E) join no segment and get assign_to_row = -1."""
+    cfg = mi.MoEShape("drop", T=40, H=128, E=6, k=3, I=64, n_hot_split=1, split_ways=2, seed=22)
+    rng = np.random.default_rng(0)
+    ids = rng.integers(0, cfg.E, size=(cfg.T, cfg.k)).astype(np.int32)
+    bad = rng.random((cfg.T, cfg.k)) < 0.2
+    ids[bad] = np.where(rng.random(bad.sum()) < 0.5, -1, cfg.E)
+    x = mi.x(cfg)
+    g = gu.run_permute(moe, cfg, gu.to_dev(x, cfg.dtype), torch.from_numpy(ids).to(gu.dev()))
+    valid = ~bad.ravel()
+    counts = np.bincount(ids.ravel()[valid], minlength=cfg.E)
+    se, sr = orc.segment_list(counts, cfg.n_hot_split, cfg.split_ways)
+    seg = orc.segment_of_assignments(np.where(bad, 0, ids), se, sr, cfg.split_ways)
+    seg = np.where(valid, seg, len(se))   # dropped -> a sentinel past the end
+    so, r2a, a2r, r2t = orc.permutation(seg, len(se) + 1, cfg.k)
+    a2r = np.where(valid, a2r, -1)
+    assert (g["counts"].cpu().numpy() == counts).all()
+    assert (g["seg_offsets"].cpu().numpy() == so[:len(se) + 1]).all()
+    assert (g["a2r"].cpu().numpy() == a2r).all()
+    R = int(so[len(se)])
+    assert (g["r2t"].cpu().numpy()[:R] == r2t[:R]).all()
+    assert g["bal"].cpu().numpy()[0] == orc.balancedness(counts)
+
+
+@pytest.mark.parametrize("E,k,groups,topk_group", [(1024, 32, 1, 1), (100, 7, 1, 1),
+                                                   (256, 8, 64, 16), (130, 3, 1, 1)])
+def test_route_extremes(moe, E, k, groups, topk_group):
+    score = "sigmoid" if groups > 1 else "softmax"
+    cfg = mi.MoEShape("rx", T=77, H=64, E=E, k=k, I=64, score=score, n_group=groups,
+                      topk_group=topk_group, seed=23)
+    lg = mi.logits(cfg)
+    ids_r, w_r, gap = orc.route(cfg, lg)
+    ids = gu.empty((cfg.T, cfg.k), torch.int32)
+    w = gu.empty((cfg.T, cfg.k), torch.float32)
+    moe.moe_route_topk(cfg, torch.from_numpy(lg).to(gu.dev()), ids, w)
+    torch.cuda.synchronize()
+    gu.check_routing(cfg, ids.cpu().numpy(), w.cpu().numpy(), ids_r, w_r, gap, lg)
+
+
+def test_empty_batch_is_a_noop(moe):
+    cfg = mi.MoEShape("empty", T=0, H=128, E=8, k=2, I=64)
+    sentinel = torch.full((4,), 7, dtype=torch.int32, device=gu.dev())
+    moe.moe_route_topk(cfg, None, sentinel, None)
+    torch.cuda.synchronize()
+    assert (sentinel.cpu() == 7).all()
