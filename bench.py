@@ -62,9 +62,8 @@ def ffn_bytes(cfg, active_experts: int) -> int:
 
 
 # ------------------------------------------------------------------ device inputs
-def device_inputs(cfg, keep_experts=()):
-    """Seeded inputs in HBM.  Returns (dict of tensors, {e: (w13, w2)} host
-    copies of the experts listed in keep_experts)."""
+def device_inputs(cfg):
+    """Seeded inputs resident in HBM (dict of tensors)."""
     import torch
     dev = torch.device("cuda:0")
     tdt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
@@ -77,14 +76,9 @@ def device_inputs(cfg, keep_experts=()):
     d = dict(logits=torch.from_numpy(mi.logits(cfg)).to(dev), x=up(mi.x(cfg)).to(dev))
     d["w13"] = torch.empty((cfg.E, 2 * cfg.I, cfg.H), dtype=tdt, device=dev)
     d["w2"] = torch.empty((cfg.E, cfg.H, cfg.I), dtype=tdt, device=dev)
-    kept = {}
-    keep = set(keep_experts)
-
     def put(e, a, b):
         d["w13"][e].copy_(up(a))
         d["w2"][e].copy_(up(b))
-        if e in keep:
-            kept[e] = (a, b)
 
     mi.for_each_expert(cfg, put)
     d["sw13"] = d["sw2"] = None
@@ -92,15 +86,17 @@ def device_inputs(cfg, keep_experts=()):
         d["sw13"] = up(mi.shared_w13(cfg)).to(dev)
         d["sw2"] = up(mi.shared_w2(cfg)).to(dev)
     torch.cuda.synchronize()
-    return d, kept
+    return d
 
 
 # ------------------------------------------------------------------ cpu baseline
-def cpu_baseline(cfg, logits, kept, active, budget_s=20.0):
-    """The float64 oracle on the host: routing and permutation of every token,
-    the expert MLP of a sample of active experts; the total is scaled to the
-    whole layer by the number of active experts (every expert costs the same
-    weight traffic; rows are few in decode)."""
+def cpu_baseline(cfg, logits, budget_s=20.0):
+    """The float64 oracle as it stands, on the host cores: routing,
+    permutation and combine of every token, and the expert MLP of active
+    experts in a spread order until ~budget_s of MLP time (all of them when
+    that fits).  Expert weights are regenerated and converted to float64
+    outside the timed region (they are the oracle's inputs).  The MLP time
+    is scaled to all active experts."""
     from threadpoolctl import threadpool_limits
 
     from oracle import moe_oracle as orc
@@ -113,29 +109,39 @@ def cpu_baseline(cfg, logits, kept, active, budget_s=20.0):
         x_perm = x64[p["row_to_token"]]
         t_route = time.perf_counter() - t0
         seg_off, seg_exp = p["seg_offsets"], p["seg_expert"]
-        t_ffn, done = 0.0, []
-        for e in sorted(kept):
-            w13 = mi.values_f64(kept[e][0], cfg.dtype)
-            w2 = mi.values_f64(kept[e][1], cfg.dtype)
-            t0 = time.perf_counter()
+        active_experts = np.nonzero(p["counts"] > 0)[0].tolist()
+        n = len(active_experts)
+        order = [active_experts[(i * 37) % n] for i in range(n)] if n % 37 else list(active_experts)
+        t_ffn, done = [0.0], []
+        y = np.zeros((cfg.A, cfg.H))
+
+        def run(e, a, b):
+            if t_ffn[0] > budget_s:
+                return
+            w13, w2 = mi.values_f64(a, cfg.dtype), mi.values_f64(b, cfg.dtype)
+            t1 = time.perf_counter()
             for s in np.nonzero(seg_exp == e)[0]:
                 r0, r1 = int(seg_off[s]), int(seg_off[s + 1])
                 if r1 > r0:
-                    orc.swiglu(x_perm[r0:r1], w13, w2)
-            t_ffn += time.perf_counter() - t0
+                    y[r0:r1] = orc.swiglu(x_perm[r0:r1], w13, w2)
+            t_ffn[0] += time.perf_counter() - t1
             done.append(e)
-            if t_ffn > budget_s:
+
+        for i in range(0, n, 8):
+            if t_ffn[0] > budget_s:
                 break
+            mi.for_each_expert(cfg, run, experts=order[i:i + 8])
         t0 = time.perf_counter()
-        y = np.zeros((cfg.A, cfg.H))
         orc.combine(y, p["assign_to_row"], w)
         t_comb = time.perf_counter() - t0
-    est = t_route + t_ffn * active / max(1, len(done)) + t_comb
+    est = t_route + t_ffn[0] * n / max(1, len(done)) + t_comb
+    scope = ("the whole layer" if len(done) == n else
+             f"expert MLP of {len(done)} of {n} active experts ({t_ffn[0]:.1f} s), "
+             f"scaled by {n}/{len(done)}")
     return {"value": cfg.T / est, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": (f"float64 numpy oracle: routing, permutation and combine of all {cfg.T} "
-                       f"tokens; expert MLP of {len(done)} of {active} active experts "
-                       f"({t_ffn:.1f} s), scaled by {active}/{len(done)}; "
-                       f"estimated {est:.1f} s per layer")}
+            "sample": (f"{cfg.name}: float64 numpy oracle, routing + permutation + combine of all "
+                       f"{cfg.T} tokens and {scope}; {est:.2f} s per layer (weight generation "
+                       f"and bf16->f64 conversion untimed)")}
 
 
 # ------------------------------------------------------------------ main
@@ -158,14 +164,7 @@ def main(argv=None):
     import mixture_experts_layer_segments_amd as moe
     cfg = mi.WORKLOADS[args.workload]
     print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
-    from oracle import moe_oracle as orc  # routing only, to choose the oracle sample
-    logits = mi.logits(cfg)
-    ids_ref, _, _ = orc.route(cfg, logits)
-    counts_ref = orc.expert_counts(ids_ref, cfg.E)
-    active = int((counts_ref > 0).sum())
-    act_ids = np.nonzero(counts_ref > 0)[0]
-    keep = act_ids[:: max(1, len(act_ids) // 8)][:8] if not args.no_cpu_baseline else []
-    d, kept = device_inputs(cfg, keep)
+    d = device_inputs(cfg)
 
     dev = torch.device("cuda:0")
     tdt = d["x"].dtype
@@ -195,7 +194,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / args.steps
-    assert (counts.cpu().numpy() == counts_ref).all(), "device counts differ from the oracle"
+    active = int((counts.cpu() > 0).sum())   # experts whose weights the step must read
 
     # dominant kernels: the grouped FFN on the permuted rows of this batch
     S = moe.moe_num_segments(cfg)
@@ -252,7 +251,7 @@ def main(argv=None):
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(cfg, logits, kept, active)
+        res["cpu_baseline"] = cpu_baseline(cfg, mi.logits(cfg))
     print(json.dumps(res), flush=True)
     return 0
 

@@ -4,6 +4,11 @@ from __future__ import annotations
 import ctypes
 import os
 
+# torch first: its HIP runtime must be the one libmoe.so binds to.  Loading
+# libmoe.so first would pull in a second copy of libamdhip64 (same soname,
+# different file) that does not share torch's device state.
+import torch  # noqa: F401
+
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4

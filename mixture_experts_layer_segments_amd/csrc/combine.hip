@@ -1,8 +1,8 @@
 // Inverse permutation with a router-weighted sum ("Serving Mixture-of-Experts
 // Models", section "Follow one token through an MoE layer", step 4):
 // out[t] = sum_j w[t,j] * y_perm[assign_to_row[t*k+j]] (+ shared_y[t]).
-// One wave per token; each lane owns 16-byte chunks of the row, accumulates
-// the k rows in fp32 in slot order and rounds once.  No atomics.
+// One thread per 16-byte chunk of an output row: it accumulates the chunk of
+// the token's k rows in fp32 in slot order and rounds once.  No atomics.
 #include "moe_internal.h"
 
 namespace moe {
@@ -40,12 +40,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
                                                       int T, int k, int row_chunks,
                                                       uint4* __restrict__ out) {
   constexpr int EPC = BF16 ? 8 : 4;  // elements per 16-byte chunk
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const int32_t* rows = a2r + (size_t)t * k;  // wave-uniform: scalar loads
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)T * row_chunks) return;
+  const int t = (int)(idx / row_chunks);
+  const int c = (int)(idx % row_chunks);
+  const int32_t* rows = a2r + (size_t)t * k;
   const float* wt = w ? w + (size_t)t * k : nullptr;
-  for (int c = lane; c < row_chunks; c += 64) {
+  {
     float acc[EPC];
 #pragma unroll
     for (int i = 0; i < EPC; ++i) acc[i] = 0.0f;
@@ -99,7 +100,8 @@ void launch_combine(const moe_config& c, const void* y_perm, const int32_t* a2r,
                     const float* w, const void* shared_y, void* out, hipStream_t s) {
   const bool bf16 = c.act_dtype == MOE_DT_BF16;
   const int row_chunks = c.H * (bf16 ? 2 : 4) / 16;
-  dim3 grid((c.T + 3) / 4);
+  const int64_t n = (int64_t)c.T * row_chunks;
+  dim3 grid((unsigned)((n + 255) / 256));
   if (bf16)
     combine_kernel<true><<<grid, 256, 0, s>>>(
         reinterpret_cast<const uint4*>(y_perm), a2r, w,

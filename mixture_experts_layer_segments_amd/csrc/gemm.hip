@@ -364,7 +364,196 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
   }
 }
 
+// ---------------------------------------------------------------- bf16 decode tiles
+// Segments of a few rows (decode): the FFN is bound by reading each active
+// expert's weights once, and HBM only reaches its practical rate with many
+// waves per CU each keeping loads in flight.  So the tile is small -- 16
+// activation rows x BN weight rows -- and so is its footprint: one LDS stage
+// holds the BN x BK weight slice (loaded coalesced, whole rows, and
+// XOR-swizzled), the next stage is prefetched in registers while the current
+// one is consumed, and activation fragments come straight from L2 into MFMA
+// registers (rows past the segment end are never loaded).  The four waves
+// split each stage's K and reduce their partial sums through LDS at the end
+// of the tile, so every wave issues MFMAs even on one-row segments.
+#ifndef MOE_DWAVES
+#define MOE_DWAVES 6
+#endif
+#ifndef MOE_DECODE_ROWS
+#define MOE_DECODE_ROWS 16  // mean rows per segment up to which the decode tiles are used
+#endif
+template <int MODE, int BN, int BK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_DWAVES)))
+void gemm_decode_kernel(GemmArgs args) {
+  constexpr int BM = 16;
+  constexpr int KCH = BK / 8;                    // 16-byte chunks per row
+  constexpr int B_CH = BN * KCH / 256;           // chunks per thread per stage
+  constexpr int KPW = BK / 32 / 4;               // MFMA K steps per wave per stage
+  constexpr int TN = BN / 16;                    // n subtiles
+  static_assert(KPW >= 1 && B_CH >= 1, "tile shape");
+  __shared__ u32x4 Bs[BN * KCH];
+  extern __shared__ int tiles_l[];
+  f32x4 (*red)[TN][64] = reinterpret_cast<f32x4 (*)[TN][64]>(&Bs[0]);  // after the K loop
+  static_assert(sizeof(f32x4) * 4 * TN * 64 <= sizeof(u32x4) * BN * KCH, "reduction fits");
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nst = args.n_seg_total;
+  for (int i = tid; i <= nst; i += 256) tiles_l[i] = args.tiles[i];
+  __syncthreads();
+  const int total = tiles_l[nst];
+  const int G = gridDim.x;
+  const int logical = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+  const int r = lane & 15, q = lane >> 4;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+
+  for (int tile = logical; tile < total; tile += G) {
+    int lo = 0, hi = nst - 1;
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (tiles_l[mid] <= tile) lo = mid; else hi = mid - 1;
+    }
+    const int gs = lo;
+    const int pi = gs < args.p[0].n_seg ? 0 : 1;
+    const GemmProblem& P = args.p[pi];
+    int r0, len, e;
+    seg_range(P, gs - (pi ? args.p[0].n_seg : 0), r0, len, e);
+    const int mt = (len + BM - 1) / BM;
+    const int local = tile - tiles_l[gs];
+    const int m0 = (local % mt) * BM;
+    const int n0 = (local / mt) * (MODE == 0 ? BN / 2 : BN);
+    const int K = P.K, N = P.N;
+    const uint16_t* Bb = P.B + (size_t)e * P.b_stride;
+
+    // element offsets (within this expert's matrix) of this thread's chunks
+    uint32_t b_off[B_CH];
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      const int c = tid + 256 * i, row = c / KCH, kc = c % KCH;
+      int brow;
+      if (MODE == 0) {
+        const int col = min(n0 + (row % (BN / 2)), N - 1);
+        brow = row < BN / 2 ? col : P.up_off + col;
+      } else {
+        brow = min(n0 + row, N - 1);
+      }
+      b_off[i] = (uint32_t)brow * (uint32_t)K + kc * 8;
+    }
+    // this lane's activation row and its K offsets inside a stage
+    const bool a_ok = m0 + r < len;
+    const uint16_t* a_src = P.A + (size_t)(r0 + min(m0 + r, len - 1)) * K + (wv * KPW * 32 + q * 8);
+
+    f32x4 acc[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 rb[B_CH], ra[KPW];
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4*>(Bb + b_off[i]);
+#pragma unroll
+    for (int jj = 0; jj < KPW; ++jj)
+      ra[jj] = a_ok ? *reinterpret_cast<const u32x4*>(a_src + jj * 32) : zero;
+
+    const int KT = K / BK;
+    for (int kt = 0; kt < KT; ++kt) {
+      __syncthreads();  // everyone done with the previous stage (or tile)
+#pragma unroll
+      for (int i = 0; i < B_CH; ++i) {
+        const int c = tid + 256 * i, row = c / KCH, kc = c % KCH;
+        Bs[row * KCH + (kc ^ (row & 7))] = rb[i];
+      }
+      __syncthreads();
+      u32x4 ac[KPW];
+#pragma unroll
+      for (int jj = 0; jj < KPW; ++jj) ac[jj] = ra[jj];
+      if (kt + 1 < KT) {
+        const int koff = (kt + 1) * BK;
+#pragma unroll
+        for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4*>(Bb + b_off[i] + koff);
+#pragma unroll
+        for (int jj = 0; jj < KPW; ++jj)
+          ra[jj] = a_ok ? *reinterpret_cast<const u32x4*>(a_src + koff + jj * 32) : zero;
+      }
+#pragma unroll
+      for (int jj = 0; jj < KPW; ++jj) {
+        const int ch = (wv * KPW + jj) * 4 + q;
+        const bf16x8 a = __builtin_bit_cast(bf16x8, ac[jj]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int row = j * 16 + r;
+          const bf16x8 b = __builtin_bit_cast(bf16x8, Bs[row * KCH + (ch ^ (row & 7))]);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+        }
+      }
+    }
+
+    // split-K reduction over the four waves, then the epilogue on wave 0
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < TN; ++j) red[wv][j][lane] = acc[j];
+    __syncthreads();
+    if (wv == 0) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[j] = acc[j] + red[1][j][lane] + red[2][j][lane] + red[3][j][lane];
+      uint16_t* Cb = P.C + (size_t)r0 * N;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = m0 + q * 4 + i;
+        if (row >= len) continue;
+        if (MODE == 0) {
+#pragma unroll
+          for (int j = 0; j < TN / 2; ++j) {
+            const int col = n0 + j * 16 + r;
+            if (col < N) Cb[(size_t)row * N + col] = to_bf16(silu(acc[j][i]) * acc[j + TN / 2][i]);
+          }
+        } else {
+          const float sc = P.scale ? P.scale[r0 + row] : 1.0f;
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int col = n0 + j * 16 + r;
+            if (col < N) Cb[(size_t)row * N + col] = to_bf16(acc[j][i] * sc);
+          }
+        }
+      }
+    }
+  }
+}
+
 constexpr int BM1 = 128, BN1 = 128, BM2 = 128, BN2 = 128, BKT = 64;
+// decode tiles: GEMM 1 32 weight rows (16 h columns) x K 256; GEMM 2 32 rows x K 256
+#ifndef MOE_DBN1
+#define MOE_DBN1 32
+#define MOE_DBK1 256
+#define MOE_DBN2 32
+#define MOE_DBK2 256
+#endif
+constexpr int DBN1 = MOE_DBN1, DBK1 = MOE_DBK1, DBN2 = MOE_DBN2, DBK2 = MOE_DBK2;
+
+// Persistent grid: as many workgroups as can be resident at once (a larger
+// grid would run its excess only after others finish), a multiple of 8 so
+// that the XCD remap is a bijection.  The occupancy query's own error (it
+// refuses some large-LDS kernels that launch fine) is cleared so that it is
+// not reported as a launch failure; `fallback` workgroups per CU are used
+// then.  Results are cached per kernel and LDS size.
+template <typename Kern>
+int persistent_grid(Kern kernel, size_t dyn_lds, int fallback) {
+  struct Entry { const void* k; size_t lds; int dev; int per_cu; };
+  static Entry cache[32];
+  static int n_cache = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  const void* key = reinterpret_cast<const void*>(kernel);
+  int per_cu = 0;
+  for (int i = 0; i < n_cache; ++i)
+    if (cache[i].k == key && cache[i].lds == dyn_lds && cache[i].dev == dev) per_cu = cache[i].per_cu;
+  if (per_cu == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, dyn_lds) != hipSuccess ||
+        per_cu < 1) {
+      (void)hipGetLastError();
+      per_cu = fallback;
+    }
+    if (n_cache < 32) cache[n_cache++] = Entry{key, dyn_lds, dev, per_cu};
+  }
+  const int g = device_cu_count() * per_cu / 8 * 8;
+  return g > 8 ? g : 8;
+}
 
 }  // namespace
 
@@ -418,11 +607,34 @@ void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_prob
   g1.n_seg_total = g2.n_seg_total = nst;
   g1.tiles = tiles1;
   g2.tiles = tiles2;
-  tile_plan_kernel<<<1, 1024, 0, s>>>(g1, BM1, BN1 / 2, g2, BM2, BN2, tiles1, tiles2);
-  const int grid = device_cu_count() * 2 / 8 * 8;
+  int max_rows = 0;
+  bool k_ok = H % DBK1 == 0;
+  for (int p = 0; p < n_probs; ++p) {
+    max_rows += probs[p].rows;
+    k_ok = k_ok && probs[p].Iw % DBK2 == 0;
+  }
   const size_t lds_tiles = (size_t)(nst + 1) * sizeof(int);
-  gemm_tiled_kernel<0, BM1, BN1, BKT><<<grid, 256, lds_tiles, s>>>(g1);
-  gemm_tiled_kernel<1, BM2, BN2, BKT><<<grid, 256, lds_tiles, s>>>(g2);
+  // Few rows per segment on average: weight streaming with 16-row tiles.
+  if (k_ok && (int64_t)max_rows <= (int64_t)MOE_DECODE_ROWS * nst) {
+    tile_plan_kernel<<<1, 1024, 0, s>>>(g1, 16, DBN1 / 2, g2, 16, DBN2, tiles1, tiles2);
+    auto k1 = gemm_decode_kernel<0, DBN1, DBK1>;
+    auto k2 = gemm_decode_kernel<1, DBN2, DBK2>;
+    k1<<<persistent_grid(k1, lds_tiles, 4), 256, lds_tiles, s>>>(g1);
+    k2<<<persistent_grid(k2, lds_tiles, 4), 256, lds_tiles, s>>>(g2);
+    return;
+  }
+  MOE_DBG("before tile plan");
+  tile_plan_kernel<<<1, 1024, 0, s>>>(g1, BM1, BN1 / 2, g2, BM2, BN2, tiles1, tiles2);
+  MOE_DBG("tile plan");
+  auto k1 = gemm_tiled_kernel<0, BM1, BN1, BKT>;
+  auto k2 = gemm_tiled_kernel<1, BM2, BN2, BKT>;
+  const int grid1 = persistent_grid(k1, lds_tiles, 2);
+  MOE_DBG("occupancy 1");
+  k1<<<grid1, 256, lds_tiles, s>>>(g1);
+  MOE_DBG("gemm 1");
+  const int grid2 = persistent_grid(k2, lds_tiles, 2);
+  k2<<<grid2, 256, lds_tiles, s>>>(g2);
+  MOE_DBG("gemm 2");
 }
 
 }  // namespace moe

@@ -239,9 +239,12 @@ moe_status moe_layer_forward(const moe_config* cfg, const float* logits, const v
   int32_t* r2t = (int32_t*)(ws + L.row_to_token);
   float* row_w = (float*)(ws + L.row_w);
 
+  MOE_DBG("layer entry");
   launch_route(*cfg, logits, topk_ids, topk_w, s);
+  MOE_DBG("route");
   launch_permute(*cfg, x, topk_ids, ws + L.x_perm, seg_offsets, seg_expert, a2r, r2t, counts,
                  balancedness, topk_w, row_w, ws, L, s);
+  MOE_DBG("permute");
   FfnProblem p[2]{};
   p[0].A = ws + L.x_perm;
   p[0].w13 = w13;

@@ -7,6 +7,21 @@
 
 #include "moe.h"
 
+// Build with -DMOE_DEBUG_LAUNCH to print the pending HIP error after each
+// launch point (diagnostics only; off in normal builds).
+#ifdef MOE_DEBUG_LAUNCH
+#include <stdio.h>
+#define MOE_DBG(tag)                                                              \
+  do {                                                                            \
+    hipError_t e_ = hipPeekAtLastError();                                         \
+    if (e_ != hipSuccess) fprintf(stderr, "[moe] %s: %s\n", tag, hipGetErrorString(e_)); \
+  } while (0)
+#else
+#define MOE_DBG(tag) \
+  do {               \
+  } while (0)
+#endif
+
 namespace moe {
 
 constexpr int kWave = 64;

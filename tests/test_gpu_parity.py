@@ -29,6 +29,11 @@ SHAPES = {
                                           n_group=8, topk_group=3, renormalize=0, seed=18),
     "bf16_no_renorm_softmax": mi.MoEShape("t9", T=90, H=256, E=48, k=5, I=128, renormalize=0,
                                           seed=19),
+    # few rows per segment and K a multiple of 1024 / 512: the weight-streaming kernels
+    "bf16_decode_stream": mi.MoEShape("t10", T=40, H=1024, E=32, k=2, I=512, seed=20),
+    "bf16_decode_stream_shared": mi.MoEShape("t11", T=24, H=2048, E=16, k=2, I=512,
+                                             score="sigmoid", n_group=4, topk_group=2,
+                                             shared_I=1024, seed=24),
 }
 
 

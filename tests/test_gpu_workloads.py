@@ -1,0 +1,114 @@
+"""GPU parity at the full sizes of the five workloads, in the launch
+configuration the benchmark times (moe_layer_forward on the whole batch).
+
+Routing ids, expert counts, balancedness and the whole permutation
+(seg_offsets, seg_expert, assign_to_row, row_to_token) are compared with the
+oracle bit for bit over the full batch.  The layer output and the grouped-FFN
+rows are compared on a sample of tokens (first, last, random, tokens of the
+hottest expert and of both replicas of a split expert), each computed by the
+oracle from the definition out[t] = sum_j w_tj SwiGLU_e(x_t) (+ shared)."""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+from oracle import moe_oracle as orc
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_tokens(cfg, ids, rng):
+    T = cfg.T
+    toks = {0, T - 1} | set(rng.choice(T, size=min(T, 10), replace=False).tolist())
+    counts = np.bincount(ids.ravel(), minlength=cfg.E)
+    hot = int(np.argmax(counts))
+    users = np.nonzero((ids == hot).any(axis=1))[0]
+    for parity in (0, 1):
+        sel = users[users % 2 == parity]
+        toks |= set(sel[:2].tolist())
+    return np.array(sorted(toks))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["tiny_fp32", "decode_bf16", "prefill_skew_bf16",
+                                  "ragged_stress_bf16", "deepseek_v3_bf16"])
+def test_workload_full_size(name):
+    import mixture_experts_layer_segments_amd as moe
+    cfg = mi.WORKLOADS[name]
+    print(f"\n[workload] {name}: routing on the host", flush=True)
+    logits = mi.logits(cfg)
+    ids_r, w_r, gap = orc.route(cfg, logits)
+    plan_r = orc.plan(cfg, ids_r)
+    rng = np.random.default_rng(cfg.seed)
+    toks = _sample_tokens(cfg, ids_r, rng)
+    xb = mi.x(cfg)
+    x64_s = mi.values_f64(xb[toks], cfg.dtype)
+    need = {}
+    for i, t in enumerate(toks):
+        for j, e in enumerate(ids_r[t].tolist()):
+            need.setdefault(e, []).append((i, j))
+
+    dev = gu.dev()
+    tdt = gu.tdtype(cfg)
+    w13_d = torch.empty((cfg.E, 2 * cfg.I, cfg.H), dtype=tdt, device=dev)
+    w2_d = torch.empty((cfg.E, cfg.H, cfg.I), dtype=tdt, device=dev)
+    y_ref = {}   # (i, j) -> oracle expert output row (unweighted)
+
+    def put(e, a, b):
+        w13_d[e].copy_(gu.to_dev(a, cfg.dtype))
+        w2_d[e].copy_(gu.to_dev(b, cfg.dtype))
+        if e in need:
+            rows = [i for i, _ in need[e]]
+            y = orc.swiglu(x64_s[rows], mi.values_f64(a, cfg.dtype), mi.values_f64(b, cfg.dtype))
+            for n, (i, j) in enumerate(need[e]):
+                y_ref[(i, j)] = y[n]
+
+    print(f"[workload] {name}: generating {cfg.E} experts", flush=True)
+    mi.for_each_expert(cfg, put)
+    out_ref = np.zeros((len(toks), cfg.H))
+    for (i, j), y in y_ref.items():
+        out_ref[i] += w_r[toks[i], j] * y
+    d = dict(logits=torch.from_numpy(logits).to(dev), x=gu.to_dev(xb, cfg.dtype), w13=w13_d,
+             w2=w2_d, sw13=None, sw2=None)
+    if cfg.shared_I:
+        s13, s2 = mi.shared_w13(cfg), mi.shared_w2(cfg)
+        out_ref += orc.swiglu(x64_s, mi.values_f64(s13, cfg.dtype), mi.values_f64(s2, cfg.dtype))
+        d["sw13"], d["sw2"] = gu.to_dev(s13, cfg.dtype), gu.to_dev(s2, cfg.dtype)
+    torch.cuda.synchronize()
+
+    print(f"[workload] {name}: layer forward", flush=True)
+    o = gu.run_layer(moe, cfg, d)
+    ids_g = o["ids"].cpu().numpy()
+    mism = gu.check_routing(cfg, ids_g, o["w"].cpu().numpy(), ids_r, w_r, gap, logits)
+    assert (o["counts"].cpu().numpy() == plan_r["counts"]).all()
+    assert o["bal"].cpu().numpy()[0] == plan_r["balancedness"]
+    got = gu.host_f64(o["out"][torch.from_numpy(toks).to(dev)])
+    ok = ~np.isin(toks, mism)
+    err = gu.rel_err(got[ok], out_ref[ok])
+    print(f"[workload] {name}: sampled {ok.sum()} tokens, rel err {err:.3e}, "
+          f"balancedness {o['bal'].item():.4f}", flush=True)
+    assert err <= gu.rel_tol(cfg), err
+
+    if mism.size == 0:
+        print(f"[workload] {name}: permutation + grouped FFN steps", flush=True)
+        g = gu.run_permute(moe, cfg, d["x"], o["ids"])
+        gu.check_plan(g, plan_r)
+        a2r = plan_r["assign_to_row"]
+        rows = torch.from_numpy(np.array([a2r[t * cfg.k + j] for t in toks
+                                          for j in range(cfg.k)])).long().to(dev)
+        tok_rows = torch.from_numpy(np.repeat(toks, cfg.k)).long().to(dev)
+        xv = g["x_perm"][rows].cpu()
+        xs = d["x"][tok_rows].cpu()
+        assert torch.equal(xv.view(torch.int16) if cfg.dtype == "bf16" else xv,
+                           xs.view(torch.int16) if cfg.dtype == "bf16" else xs)
+        y = torch.empty_like(g["x_perm"])
+        ws = gu.empty((moe.moe_workspace_size(cfg),), torch.uint8)
+        moe.moe_grouped_ffn(cfg, g["x_perm"], g["seg_offsets"], g["seg_expert"], w13_d, w2_d,
+                            None, y, ws)
+        torch.cuda.synchronize()
+        yg = gu.host_f64(y[rows]).reshape(len(toks), cfg.k, cfg.H)
+        yr = np.stack([np.stack([y_ref[(i, j)] for j in range(cfg.k)]) for i in range(len(toks))])
+        err = gu.rel_err(yg, yr)
+        print(f"[workload] {name}: grouped FFN sampled rows rel err {err:.3e}", flush=True)
+        assert err <= gu.rel_tol(cfg), err
