@@ -9,10 +9,10 @@
 // bf16 path: persistent MFMA kernels.  A device-side tile table (exclusive
 // prefix of tiles per segment) is built from the segment offsets, so segment
 // lengths never travel to the host.  Each workgroup walks the tile list with a
-// fixed stride; tiles are ordered segment-major, then by output column block,
-// then by row block, and the workgroup -> tile mapping is remapped so that
-// consecutive tiles (which share the same weight slice) land on the same XCD
-// and therefore the same L2.  The K loop double-buffers LDS tiles; operands
+// fixed stride; tiles are ordered segment-major, then in groups of 8 row
+// blocks that walk every column block, and the workgroup -> tile mapping is
+// remapped so that consecutive tiles (which share weight slices and
+// activation rows) land on the same XCD and therefore the same L2.  The K loop double-buffers LDS tiles; operands
 // are XOR-swizzled in 16-byte chunks so that MFMA operand reads avoid bank
 // conflicts.  fp32 path: a plain FMA kernel (the fp32 layer is tiny).
 #include <math.h>
@@ -56,6 +56,20 @@ __device__ __forceinline__ void seg_range(const GemmProblem& P, int s, int& r0, 
     len = P.rows;
     e = 0;
   }
+}
+
+#ifndef MOE_GROUP_M
+#define MOE_GROUP_M 8
+#endif
+#ifndef MOE_XCD_REMAP
+#define MOE_XCD_REMAP 1
+#endif
+constexpr int kGroupM = MOE_GROUP_M;  // row tiles that share a weight slice in the tile order
+
+// Workgroup ids are dealt round-robin to the 8 XCDs; renumber them so that
+// consecutive logical ids share an XCD (and its L2).
+__device__ __forceinline__ int xcd_logical(int bid, int G) {
+  return MOE_XCD_REMAP ? (bid % 8) * (G / 8) + bid / 8 : bid;
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
@@ -136,17 +150,22 @@ __global__ __launch_bounds__(1024) void tile_plan_kernel(GemmArgs a1, int bm1, i
 }
 
 // ---------------------------------------------------------------- bf16 MFMA
+// Block tile BM x BN (weight rows) x BK over NTHR/64 waves laid out
+// WAVES_M x WAVES_N; 128 x 128 with 2 x 2 waves for moderate segments, and
+// 256 x 256 with 4 x 2 waves of 64 x 128 for large ones (half the operand
+// traffic per flop).
 // MODE 0: GEMM 1 with the SwiGLU epilogue.  The B tile holds BN rows: the
 //         first BN/2 are W_gate rows n0.., the rest W_up rows n0.. (output
 //         columns per tile = BN/2).  Each wave owns matching gate and up
 //         columns, so silu(g) * u is formed in registers.
 // MODE 1: GEMM 2 with the row-scale epilogue (BN output columns per tile).
-template <int MODE, int BM, int BN, int BK>
-__global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs args) {
-  constexpr int WM = BM / 2, WN = BN / 2;   // wave tile (2 x 2 waves)
+template <int MODE, int BM, int BN, int BK, int NTHR, int WAVES_M, int OCC>
+__global__ __launch_bounds__(NTHR, OCC) void gemm_tiled_kernel(GemmArgs args) {
+  constexpr int WAVES_N = NTHR / 64 / WAVES_M;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;   // wave tile
   constexpr int TM = WM / 16, TN = WN / 16; // MFMA 16x16 subtiles per wave
   constexpr int KCH = BK / 8;               // 16-byte chunks per row
-  constexpr int A_LOADS = BM * KCH / 256, B_LOADS = BN * KCH / 256;
+  constexpr int A_LOADS = BM * KCH / NTHR, B_LOADS = BN * KCH / NTHR;
   static_assert(KCH == 8, "swizzle assumes 8 chunks per row");
 
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * BK];
@@ -154,15 +173,15 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs args) {
   extern __shared__ int tiles_l[];  // [n_seg_total + 1], dynamic
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wm = wv / WAVES_N, wn = wv % WAVES_N;
   const int nst = args.n_seg_total;
-  for (int i = tid; i <= nst; i += 256) tiles_l[i] = args.tiles[i];
+  for (int i = tid; i <= nst; i += NTHR) tiles_l[i] = args.tiles[i];
   __syncthreads();
   const int total = tiles_l[nst];
 
   // XCD-aware persistent order: consecutive logical ids share an XCD.
   const int G = gridDim.x;
-  const int logical = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+  const int logical = xcd_logical(blockIdx.x, G);
 
   for (int tile = logical; tile < total; tile += G) {
     // segment of this tile: last s with tiles_l[s] <= tile
@@ -178,10 +197,19 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs args) {
     int r0, len, e;
     seg_range(P, s, r0, len, e);
     const int mt = (len + BM - 1) / BM;
-    const int local = tile - tiles_l[gs];
-    const int m_idx = local % mt, n_idx = local / mt;
-    const int m0 = m_idx * BM;
     const int ncols = MODE == 0 ? BN / 2 : BN;
+    const int nt = (P.N + ncols - 1) / ncols;
+    // grouped order: runs of GM row tiles share one weight slice, and a
+    // group's row tiles are revisited for every column block before the
+    // next group starts, so both operands stay in L2 across the ~64
+    // consecutive tiles that one XCD works on at a time
+    const int local = tile - tiles_l[gs];
+    const int grp = local / (kGroupM * nt);
+    const int first_m = grp * kGroupM;
+    const int gm = min(kGroupM, mt - first_m);
+    const int lg = local - grp * kGroupM * nt;
+    const int m_idx = first_m + lg % gm, n_idx = lg / gm;
+    const int m0 = m_idx * BM;
     const int n0 = n_idx * ncols;
     const int K = P.K, N = P.N;
     const uint16_t* Ab = P.A + (size_t)r0 * K;
@@ -192,7 +220,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs args) {
     int a_dst[A_LOADS];
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, kc = c & 7;
+      const int c = tid + NTHR * i, row = c >> 3, kc = c & 7;
       const int gr = min(m0 + row, len - 1);
       a_src[i] = Ab + (size_t)gr * K + kc * 8;
       a_dst[i] = row * BK + ((kc ^ (row & 7)) * 8);
@@ -201,7 +229,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs args) {
     int b_dst[B_LOADS];
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, kc = c & 7;
+      const int c = tid + NTHR * i, row = c >> 3, kc = c & 7;
       int brow;
       if (MODE == 0) {
         const int col = min(n0 + (row % (BN / 2)), N - 1);
@@ -378,6 +406,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 #ifndef MOE_DWAVES
 #define MOE_DWAVES 6
 #endif
+#ifndef MOE_BIG_ROWS
+#define MOE_BIG_ROWS 256  // mean rows per segment from which 256 x 256 tiles are used
+#endif
 #ifndef MOE_DECODE_ROWS
 #define MOE_DECODE_ROWS 16  // mean rows per segment up to which the decode tiles are used
 #endif
@@ -401,7 +432,7 @@ void gemm_decode_kernel(GemmArgs args) {
   __syncthreads();
   const int total = tiles_l[nst];
   const int G = gridDim.x;
-  const int logical = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+  const int logical = xcd_logical(blockIdx.x, G);
   const int r = lane & 15, q = lane >> 4;
   const u32x4 zero = {0u, 0u, 0u, 0u};
 
@@ -516,7 +547,6 @@ void gemm_decode_kernel(GemmArgs args) {
   }
 }
 
-constexpr int BM1 = 128, BN1 = 128, BM2 = 128, BN2 = 128, BKT = 64;
 // decode tiles: GEMM 1 32 weight rows (16 h columns) x K 256; GEMM 2 32 rows x K 256
 #ifndef MOE_DBN1
 #define MOE_DBN1 32
@@ -533,7 +563,7 @@ constexpr int DBN1 = MOE_DBN1, DBK1 = MOE_DBK1, DBN2 = MOE_DBN2, DBK2 = MOE_DBK2
 // not reported as a launch failure; `fallback` workgroups per CU are used
 // then.  Results are cached per kernel and LDS size.
 template <typename Kern>
-int persistent_grid(Kern kernel, size_t dyn_lds, int fallback) {
+int persistent_grid(Kern kernel, size_t dyn_lds, int fallback, int threads = 256) {
   struct Entry { const void* k; size_t lds; int dev; int per_cu; };
   static Entry cache[32];
   static int n_cache = 0;
@@ -544,7 +574,7 @@ int persistent_grid(Kern kernel, size_t dyn_lds, int fallback) {
   for (int i = 0; i < n_cache; ++i)
     if (cache[i].k == key && cache[i].lds == dyn_lds && cache[i].dev == dev) per_cu = cache[i].per_cu;
   if (per_cu == 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, dyn_lds) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, dyn_lds) != hipSuccess ||
         per_cu < 1) {
       (void)hipGetLastError();
       per_cu = fallback;
@@ -553,6 +583,21 @@ int persistent_grid(Kern kernel, size_t dyn_lds, int fallback) {
   }
   const int g = device_cu_count() * per_cu / 8 * 8;
   return g > 8 ? g : 8;
+}
+
+template <int BM, int BN, int NTHR, int WAVES_M, int OCC>
+void launch_tiled(const GemmArgs& g1, const GemmArgs& g2, int nst, int32_t* tiles1,
+                  int32_t* tiles2, hipStream_t s) {
+  constexpr int BK = 64;
+  tile_plan_kernel<<<1, 1024, 0, s>>>(g1, BM, BN / 2, g2, BM, BN, tiles1, tiles2);
+  MOE_DBG("tile plan");
+  const size_t lds_tiles = (size_t)(nst + 1) * sizeof(int);
+  auto k1 = gemm_tiled_kernel<0, BM, BN, BK, NTHR, WAVES_M, OCC>;
+  auto k2 = gemm_tiled_kernel<1, BM, BN, BK, NTHR, WAVES_M, OCC>;
+  k1<<<persistent_grid(k1, lds_tiles, OCC, NTHR), NTHR, lds_tiles, s>>>(g1);
+  MOE_DBG("gemm 1");
+  k2<<<persistent_grid(k2, lds_tiles, OCC, NTHR), NTHR, lds_tiles, s>>>(g2);
+  MOE_DBG("gemm 2");
 }
 
 }  // namespace
@@ -623,18 +668,10 @@ void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_prob
     k2<<<persistent_grid(k2, lds_tiles, 4), 256, lds_tiles, s>>>(g2);
     return;
   }
-  MOE_DBG("before tile plan");
-  tile_plan_kernel<<<1, 1024, 0, s>>>(g1, BM1, BN1 / 2, g2, BM2, BN2, tiles1, tiles2);
-  MOE_DBG("tile plan");
-  auto k1 = gemm_tiled_kernel<0, BM1, BN1, BKT>;
-  auto k2 = gemm_tiled_kernel<1, BM2, BN2, BKT>;
-  const int grid1 = persistent_grid(k1, lds_tiles, 2);
-  MOE_DBG("occupancy 1");
-  k1<<<grid1, 256, lds_tiles, s>>>(g1);
-  MOE_DBG("gemm 1");
-  const int grid2 = persistent_grid(k2, lds_tiles, 2);
-  k2<<<grid2, 256, lds_tiles, s>>>(g2);
-  MOE_DBG("gemm 2");
+  if ((int64_t)max_rows >= (int64_t)MOE_BIG_ROWS * nst)
+    launch_tiled<256, 256, 512, 4, 1>(g1, g2, nst, tiles1, tiles2, s);
+  else
+    launch_tiled<128, 128, 256, 2, 2>(g1, g2, nst, tiles1, tiles2, s);
 }
 
 }  // namespace moe

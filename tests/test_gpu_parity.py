@@ -34,6 +34,9 @@ SHAPES = {
     "bf16_decode_stream_shared": mi.MoEShape("t11", T=24, H=2048, E=16, k=2, I=512,
                                              score="sigmoid", n_group=4, topk_group=2,
                                              shared_I=1024, seed=24),
+    # many rows per segment (256 x 256 tiles), N and K tails in both GEMMs
+    "bf16_big_tiles": mi.MoEShape("t12", T=1100, H=320, E=3, k=1, I=192, zipf_s=1.0,
+                                  seed=25),
 }
 
 
