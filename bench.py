@@ -34,7 +34,12 @@ GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_segments_amd", "csrc", "gem
 # WRITE_SIZE (summed over the GEMM kernels of one call, each counter scaled by
 # what it reads for a plain 1 GiB device copy), keyed by workload.  An entry
 # only applies while gemm.hip still has the hash it was measured with.
-MEASURED_TRAFFIC = {}
+MEASURED_TRAFFIC = {
+    "decode_bf16": {"gemm_src_sha256_16": "403a7ded73497828", "bytes": 5550855409},
+    "prefill_skew_bf16": {"gemm_src_sha256_16": "403a7ded73497828", "bytes": 7641518073},
+    "deepseek_v3_bf16": {"gemm_src_sha256_16": "403a7ded73497828", "bytes": 38977864637},
+    "ragged_stress_bf16": {"gemm_src_sha256_16": "403a7ded73497828", "bytes": 13954352255},
+}
 
 
 def _src_hash(path=GEMM_SRC) -> str:
