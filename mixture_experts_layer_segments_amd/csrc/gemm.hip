@@ -64,7 +64,8 @@ __device__ __forceinline__ void seg_range(const GemmProblem& P, int s, int& r0, 
 #ifndef MOE_XCD_REMAP
 #define MOE_XCD_REMAP 1
 #endif
-constexpr int kGroupM = MOE_GROUP_M;  // row tiles that share a weight slice in the tile order
+constexpr int kGroupM = MOE_GROUP_M;
+constexpr size_t kMaxLdsBytes = 160 * 1024;  // LDS per workgroup on gfx950  // row tiles that share a weight slice in the tile order
 
 // Workgroup ids are dealt round-robin to the 8 XCDs; renumber them so that
 // consecutive logical ids share an XCD (and its L2).
@@ -149,28 +150,63 @@ __global__ __launch_bounds__(1024) void tile_plan_kernel(GemmArgs a1, int bm1, i
   }
 }
 
-// ---------------------------------------------------------------- bf16 MFMA
-// Block tile BM x BN (weight rows) x BK over NTHR/64 waves laid out
-// WAVES_M x WAVES_N; 128 x 128 with 2 x 2 waves for moderate segments, and
-// 256 x 256 with 4 x 2 waves of 64 x 128 for large ones (half the operand
-// traffic per flop).
+// ---------------------------------------------------------------- bf16 MFMA tiles
+// Segments of many rows.  Block tile BM x BN (weight rows) x 64 over NTHR/64
+// waves laid out WAVES_M x WAVES_N, each wave a grid of 16x16x32 MFMAs with
+// fp32 accumulators; 128 x 256 over 2 x 4 waves with a 3-stage ring for
+// moderate segments (HBM-bound), 256 x 256 over 4 x 2 waves with 2 stages for
+// large ones (half the operand traffic per flop).  LDS rows are 128-byte
+// pieces of 8 chunks of 16 bytes, XOR-swizzled by row.
+//
 // MODE 0: GEMM 1 with the SwiGLU epilogue.  The B tile holds BN rows: the
-//         first BN/2 are W_gate rows n0.., the rest W_up rows n0.. (output
-//         columns per tile = BN/2).  Each wave owns matching gate and up
+//         first BN/2 are W_gate rows n0.., the rest W_up rows n0.. (BN/2
+//         output columns per tile).  Each wave owns matching gate and up
 //         columns, so silu(g) * u is formed in registers.
 // MODE 1: GEMM 2 with the row-scale epilogue (BN output columns per tile).
-template <int MODE, int BM, int BN, int BK, int NTHR, int WAVES_M, int OCC>
-__global__ __launch_bounds__(NTHR, OCC) void gemm_tiled_kernel(GemmArgs args) {
-  constexpr int WAVES_N = NTHR / 64 / WAVES_M;
-  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;   // wave tile
-  constexpr int TM = WM / 16, TN = WN / 16; // MFMA 16x16 subtiles per wave
-  constexpr int KCH = BK / 8;               // 16-byte chunks per row
-  constexpr int A_LOADS = BM * KCH / NTHR, B_LOADS = BN * KCH / NTHR;
-  static_assert(KCH == 8, "swizzle assumes 8 chunks per row");
+//
+// Global -> LDS copies go straight into a STAGES-deep LDS ring (global_load_lds_dwordx4: each wave instruction
+// fills one contiguous 1 KiB block of 8 swizzled 128-byte row pieces), so the
+// copies for the next STAGES-1 K stages stay in flight while the current one
+// feeds the MFMAs, with no registers spent on staging.  Completion is tracked
+// with explicit vmcnt waits: a wave waits until at most the copies it issued
+// for later stages are outstanding, then a plain s_barrier (without the
+// memory fence of __syncthreads, which would wait for every copy) makes the
+// stage visible to all waves and frees the slot read one stage earlier.
+#define MOE_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * BK];
-  extern __shared__ int tiles_l[];  // [n_seg_total + 1], dynamic
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Copy K stage kt of this wave's LPW 1 KiB blocks into its ring slot.
+template <int LPW, int NW, int STAGES, int STAGE_CH, int BK>
+__device__ __forceinline__ void ring_issue(const uint16_t* const* src, u32x4* ring, int kt,
+                                           int wv) {
+  u32x4* slot = ring + (kt % STAGES) * STAGE_CH;
+#pragma unroll
+  for (int i = 0; i < LPW; ++i)
+    __builtin_amdgcn_global_load_lds(src[i] + kt * BK, MOE_LDS_PTR(slot + (i * NW + wv) * 64), 16,
+                                     0, 0);
+}
+
+template <int MODE, int BM, int BN, int NTHR, int WAVES_M, int STAGES, int OCC>
+__global__ __launch_bounds__(NTHR, OCC) void gemm_ring_kernel(GemmArgs args) {
+  constexpr int BK = 64;
+  constexpr int NW = NTHR / 64;
+  constexpr int WAVES_N = NW / WAVES_M;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;   // wave tile
+  constexpr int TM = WM / 16, TN = WN / 16;
+  constexpr int ROWS = BM + BN;         // A rows then B rows in one stage
+  constexpr int STAGE_CH = ROWS * 8;    // 16-byte chunks per stage
+  constexpr int LPW = ROWS / 8 / NW;    // 1 KiB copy instructions per wave per stage
+  static_assert((ROWS / 8) % NW == 0 && STAGES >= 2 && STAGES <= 4, "ring shape");
+  static_assert(LPW * (STAGES - 2) < 64, "vmcnt range");
+
+  __shared__ u32x4 ring[STAGES * STAGE_CH];
+  extern __shared__ int tiles_l[];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv / WAVES_N, wn = wv % WAVES_N;
@@ -178,13 +214,20 @@ __global__ __launch_bounds__(NTHR, OCC) void gemm_tiled_kernel(GemmArgs args) {
   for (int i = tid; i <= nst; i += NTHR) tiles_l[i] = args.tiles[i];
   __syncthreads();
   const int total = tiles_l[nst];
-
-  // XCD-aware persistent order: consecutive logical ids share an XCD.
   const int G = gridDim.x;
   const int logical = xcd_logical(blockIdx.x, G);
 
+  int brow_of[TN];
+#pragma unroll
+  for (int ni = 0; ni < TN; ++ni) {
+    if (MODE == 0)
+      brow_of[ni] = (ni < TN / 2) ? wn * (WN / 2) + ni * 16
+                                  : BN / 2 + wn * (WN / 2) + (ni - TN / 2) * 16;
+    else
+      brow_of[ni] = wn * WN + ni * 16;
+  }
+
   for (int tile = logical; tile < total; tile += G) {
-    // segment of this tile: last s with tiles_l[s] <= tile
     int lo = 0, hi = nst - 1;
     while (lo < hi) {
       int mid = (lo + hi + 1) >> 1;
@@ -193,52 +236,41 @@ __global__ __launch_bounds__(NTHR, OCC) void gemm_tiled_kernel(GemmArgs args) {
     const int gs = lo;
     const int pi = gs < args.p[0].n_seg ? 0 : 1;
     const GemmProblem& P = args.p[pi];
-    const int s = gs - (pi ? args.p[0].n_seg : 0);
     int r0, len, e;
-    seg_range(P, s, r0, len, e);
+    seg_range(P, gs - (pi ? args.p[0].n_seg : 0), r0, len, e);
     const int mt = (len + BM - 1) / BM;
     const int ncols = MODE == 0 ? BN / 2 : BN;
     const int nt = (P.N + ncols - 1) / ncols;
-    // grouped order: runs of GM row tiles share one weight slice, and a
-    // group's row tiles are revisited for every column block before the
-    // next group starts, so both operands stay in L2 across the ~64
-    // consecutive tiles that one XCD works on at a time
     const int local = tile - tiles_l[gs];
     const int grp = local / (kGroupM * nt);
     const int first_m = grp * kGroupM;
     const int gm = min(kGroupM, mt - first_m);
     const int lg = local - grp * kGroupM * nt;
-    const int m_idx = first_m + lg % gm, n_idx = lg / gm;
-    const int m0 = m_idx * BM;
-    const int n0 = n_idx * ncols;
+    const int m0 = (first_m + lg % gm) * BM;
+    const int n0 = (lg / gm) * ncols;
     const int K = P.K, N = P.N;
     const uint16_t* Ab = P.A + (size_t)r0 * K;
     const uint16_t* Bb = P.B + (size_t)e * P.b_stride;
 
-    // per-thread global source pointers for this tile
-    const uint16_t* a_src[A_LOADS];
-    int a_dst[A_LOADS];
+    // source of this lane's 16 bytes in each of the wave's copy instructions
+    const uint16_t* src[LPW];
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-      const int c = tid + NTHR * i, row = c >> 3, kc = c & 7;
-      const int gr = min(m0 + row, len - 1);
-      a_src[i] = Ab + (size_t)gr * K + kc * 8;
-      a_dst[i] = row * BK + ((kc ^ (row & 7)) * 8);
-    }
-    const uint16_t* b_src[B_LOADS];
-    int b_dst[B_LOADS];
-#pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) {
-      const int c = tid + NTHR * i, row = c >> 3, kc = c & 7;
-      int brow;
-      if (MODE == 0) {
-        const int col = min(n0 + (row % (BN / 2)), N - 1);
-        brow = row < BN / 2 ? col : P.up_off + col;
+    for (int i = 0; i < LPW; ++i) {
+      const int row = (i * NW + wv) * 8 + (lane >> 3);
+      const int kc = (lane & 7) ^ (row & 7);
+      if ((i * NW + wv) * 8 < BM) {
+        src[i] = Ab + (size_t)min(m0 + row, len - 1) * K + kc * 8;
       } else {
-        brow = min(n0 + row, N - 1);
+        const int br = row - BM;
+        int brow;
+        if (MODE == 0) {
+          const int col = min(n0 + (br % (BN / 2)), N - 1);
+          brow = br < BN / 2 ? col : P.up_off + col;
+        } else {
+          brow = min(n0 + br, N - 1);
+        }
+        src[i] = Bb + (size_t)brow * K + kc * 8;
       }
-      b_src[i] = Bb + (size_t)brow * K + kc * 8;
-      b_dst[i] = row * BK + ((kc ^ (row & 7)) * 8);
     }
 
     f32x4 acc[TM][TN];
@@ -247,41 +279,21 @@ __global__ __launch_bounds__(NTHR, OCC) void gemm_tiled_kernel(GemmArgs args) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 ra[A_LOADS], rb[B_LOADS];
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_src[i]);
-#pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) rb[i] = *reinterpret_cast<const u32x4*>(b_src[i]);
-    __syncthreads();  // previous tile's epilogue done with LDS
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) *reinterpret_cast<u32x4*>(&As[0][a_dst[i]]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) *reinterpret_cast<u32x4*>(&Bs[0][b_dst[i]]) = rb[i];
-    __syncthreads();
-
-    // B-tile row of each of this wave's n subtiles
-    int brow_of[TN];
-#pragma unroll
-    for (int ni = 0; ni < TN; ++ni) {
-      if (MODE == 0)
-        brow_of[ni] = (ni < TN / 2) ? wn * (WN / 2) + ni * 16
-                                    : BN / 2 + wn * (WN / 2) + (ni - TN / 2) * 16;
-      else
-        brow_of[ni] = wn * WN + ni * 16;
-    }
-
     const int KT = K / BK;
+    wait_vmcnt<0>();   // this wave's earlier stores and copies are done
+    raw_barrier();     // every wave is done reading the ring
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+      if (st < KT) ring_issue<LPW, NW, STAGES, STAGE_CH, BK>(src, ring, st, wv);
     for (int kt = 0; kt < KT; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < KT) {
-        const int koff = (kt + 1) * BK;
-#pragma unroll
-        for (int i = 0; i < A_LOADS; ++i)
-          ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + koff);
-#pragma unroll
-        for (int i = 0; i < B_LOADS; ++i)
-          rb[i] = *reinterpret_cast<const u32x4*>(b_src[i] + koff);
-      }
+      // stage kt has landed once only the copies of later stages remain
+      const int later = min(STAGES - 2, KT - 1 - kt);
+      if (later >= 2) wait_vmcnt<2 * LPW>();
+      else if (later == 1) wait_vmcnt<LPW>();
+      else wait_vmcnt<0>();
+      raw_barrier();
+      if (kt + STAGES - 1 < KT) ring_issue<LPW, NW, STAGES, STAGE_CH, BK>(src, ring, kt + STAGES - 1, wv);
+      const u32x4* slot = ring + (kt % STAGES) * STAGE_CH;
 #pragma unroll
       for (int kk = 0; kk < BK / 32; ++kk) {
         const int ch = kk * 4 + (lane >> 4);
@@ -289,14 +301,12 @@ __global__ __launch_bounds__(NTHR, OCC) void gemm_tiled_kernel(GemmArgs args) {
 #pragma unroll
         for (int mi = 0; mi < TM; ++mi) {
           const int row = wm * WM + mi * 16 + (lane & 15);
-          af[mi] = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(&As[cur][row * BK + ((ch ^ (row & 7)) * 8)]));
+          af[mi] = __builtin_bit_cast(bf16x8, slot[row * 8 + (ch ^ (row & 7))]);
         }
 #pragma unroll
         for (int ni = 0; ni < TN; ++ni) {
-          const int row = brow_of[ni] + (lane & 15);
-          bfr[ni] = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(&Bs[cur][row * BK + ((ch ^ (row & 7)) * 8)]));
+          const int row = BM + brow_of[ni] + (lane & 15);
+          bfr[ni] = __builtin_bit_cast(bf16x8, slot[row * 8 + (ch ^ (row & 7))]);
         }
 #pragma unroll
         for (int mi = 0; mi < TM; ++mi)
@@ -305,17 +315,8 @@ __global__ __launch_bounds__(NTHR, OCC) void gemm_tiled_kernel(GemmArgs args) {
             acc[mi][ni] =
                 __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
       }
-      if (kt + 1 < KT) {
-        const int nxt = cur ^ 1;
-#pragma unroll
-        for (int i = 0; i < A_LOADS; ++i) *reinterpret_cast<u32x4*>(&As[nxt][a_dst[i]]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < B_LOADS; ++i) *reinterpret_cast<u32x4*>(&Bs[nxt][b_dst[i]]) = rb[i];
-      }
-      __syncthreads();
     }
 
-    // epilogue: lane holds D[row = 4*(lane/16) + i][col = lane % 16]
     uint16_t* Cb = P.C + (size_t)r0 * N;
 #pragma unroll
     for (int mi = 0; mi < TM; ++mi) {
@@ -412,10 +413,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 #ifndef MOE_DECODE_ROWS
 #define MOE_DECODE_ROWS 16  // mean rows per segment up to which the decode tiles are used
 #endif
-template <int MODE, int BN, int BK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_DWAVES)))
+template <int MODE, int BN, int BK, int MT, int WAVES>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES)))
 void gemm_decode_kernel(GemmArgs args) {
-  constexpr int BM = 16;
+  constexpr int BM = 16 * MT;                    // rows per tile (MT subtiles of 16)
   constexpr int KCH = BK / 8;                    // 16-byte chunks per row
   constexpr int B_CH = BN * KCH / 256;           // chunks per thread per stage
   constexpr int KPW = BK / 32 / 4;               // MFMA K steps per wave per stage
@@ -469,18 +470,28 @@ void gemm_decode_kernel(GemmArgs args) {
       b_off[i] = (uint32_t)brow * (uint32_t)K + kc * 8;
     }
     // this lane's activation row and its K offsets inside a stage
-    const bool a_ok = m0 + r < len;
-    const uint16_t* a_src = P.A + (size_t)(r0 + min(m0 + r, len - 1)) * K + (wv * KPW * 32 + q * 8);
-
-    f32x4 acc[TN];
+    bool a_ok[MT];
+    uint32_t a_off[MT];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x4 rb[B_CH], ra[KPW];
+    for (int mi = 0; mi < MT; ++mi) {
+      a_ok[mi] = m0 + mi * 16 + r < len;
+      a_off[mi] = (uint32_t)(r0 + min(m0 + mi * 16 + r, len - 1)) * (uint32_t)K +
+                  (wv * KPW * 32 + q * 8);
+    }
+
+    f32x4 acc[MT][TN];
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[mi][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 rb[B_CH], ra[MT][KPW];
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4*>(Bb + b_off[i]);
 #pragma unroll
-    for (int jj = 0; jj < KPW; ++jj)
-      ra[jj] = a_ok ? *reinterpret_cast<const u32x4*>(a_src + jj * 32) : zero;
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int jj = 0; jj < KPW; ++jj)
+        ra[mi][jj] = a_ok[mi] ? *reinterpret_cast<const u32x4*>(P.A + a_off[mi] + jj * 32) : zero;
 
     const int KT = K / BK;
     for (int kt = 0; kt < KT; ++kt) {
@@ -491,55 +502,68 @@ void gemm_decode_kernel(GemmArgs args) {
         Bs[row * KCH + (kc ^ (row & 7))] = rb[i];
       }
       __syncthreads();
-      u32x4 ac[KPW];
+      u32x4 ac[MT][KPW];
 #pragma unroll
-      for (int jj = 0; jj < KPW; ++jj) ac[jj] = ra[jj];
+      for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+        for (int jj = 0; jj < KPW; ++jj) ac[mi][jj] = ra[mi][jj];
       if (kt + 1 < KT) {
         const int koff = (kt + 1) * BK;
 #pragma unroll
         for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4*>(Bb + b_off[i] + koff);
 #pragma unroll
-        for (int jj = 0; jj < KPW; ++jj)
-          ra[jj] = a_ok ? *reinterpret_cast<const u32x4*>(a_src + koff + jj * 32) : zero;
+        for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+          for (int jj = 0; jj < KPW; ++jj)
+            ra[mi][jj] =
+                a_ok[mi] ? *reinterpret_cast<const u32x4*>(P.A + a_off[mi] + koff + jj * 32) : zero;
       }
 #pragma unroll
       for (int jj = 0; jj < KPW; ++jj) {
         const int ch = (wv * KPW + jj) * 4 + q;
-        const bf16x8 a = __builtin_bit_cast(bf16x8, ac[jj]);
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int row = j * 16 + r;
           const bf16x8 b = __builtin_bit_cast(bf16x8, Bs[row * KCH + (ch ^ (row & 7))]);
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+#pragma unroll
+          for (int mi = 0; mi < MT; ++mi)
+            acc[mi][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, ac[mi][jj]), b, acc[mi][j], 0, 0, 0);
         }
       }
     }
 
-    // split-K reduction over the four waves, then the epilogue on wave 0
-    __syncthreads();
+    // split-K reduction over the four waves, one 16-row subtile at a time,
+    // then the epilogue on wave 0
+    uint16_t* Cb = P.C + (size_t)r0 * N;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) red[wv][j][lane] = acc[j];
-    __syncthreads();
-    if (wv == 0) {
+    for (int mi = 0; mi < MT; ++mi) {
+      if (m0 + mi * 16 >= len) break;  // uniform over the workgroup
+      __syncthreads();
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[j] = acc[j] + red[1][j][lane] + red[2][j][lane] + red[3][j][lane];
-      uint16_t* Cb = P.C + (size_t)r0 * N;
+      for (int j = 0; j < TN; ++j) red[wv][j][lane] = acc[mi][j];
+      __syncthreads();
+      if (wv == 0) {
+        f32x4 v[TN];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = m0 + q * 4 + i;
-        if (row >= len) continue;
-        if (MODE == 0) {
+        for (int j = 0; j < TN; ++j) v[j] = acc[mi][j] + red[1][j][lane] + red[2][j][lane] + red[3][j][lane];
 #pragma unroll
-          for (int j = 0; j < TN / 2; ++j) {
-            const int col = n0 + j * 16 + r;
-            if (col < N) Cb[(size_t)row * N + col] = to_bf16(silu(acc[j][i]) * acc[j + TN / 2][i]);
-          }
-        } else {
-          const float sc = P.scale ? P.scale[r0 + row] : 1.0f;
+        for (int i = 0; i < 4; ++i) {
+          const int row = m0 + mi * 16 + q * 4 + i;
+          if (row >= len) continue;
+          if (MODE == 0) {
 #pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            const int col = n0 + j * 16 + r;
-            if (col < N) Cb[(size_t)row * N + col] = to_bf16(acc[j][i] * sc);
+            for (int j = 0; j < TN / 2; ++j) {
+              const int col = n0 + j * 16 + r;
+              if (col < N) Cb[(size_t)row * N + col] = to_bf16(silu(v[j][i]) * v[j + TN / 2][i]);
+            }
+          } else {
+            const float sc = P.scale ? P.scale[r0 + row] : 1.0f;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+              const int col = n0 + j * 16 + r;
+              if (col < N) Cb[(size_t)row * N + col] = to_bf16(v[j][i] * sc);
+            }
           }
         }
       }
@@ -585,19 +609,15 @@ int persistent_grid(Kern kernel, size_t dyn_lds, int fallback, int threads = 256
   return g > 8 ? g : 8;
 }
 
-template <int BM, int BN, int NTHR, int WAVES_M, int OCC>
-void launch_tiled(const GemmArgs& g1, const GemmArgs& g2, int nst, int32_t* tiles1,
-                  int32_t* tiles2, hipStream_t s) {
-  constexpr int BK = 64;
+template <int BM, int BN, int NTHR, int WAVES_M, int STAGES, int OCC>
+void launch_ring(const GemmArgs& g1, const GemmArgs& g2, int nst, int32_t* tiles1,
+                 int32_t* tiles2, hipStream_t s) {
   tile_plan_kernel<<<1, 1024, 0, s>>>(g1, BM, BN / 2, g2, BM, BN, tiles1, tiles2);
-  MOE_DBG("tile plan");
   const size_t lds_tiles = (size_t)(nst + 1) * sizeof(int);
-  auto k1 = gemm_tiled_kernel<0, BM, BN, BK, NTHR, WAVES_M, OCC>;
-  auto k2 = gemm_tiled_kernel<1, BM, BN, BK, NTHR, WAVES_M, OCC>;
+  auto k1 = gemm_ring_kernel<0, BM, BN, NTHR, WAVES_M, STAGES, OCC>;
+  auto k2 = gemm_ring_kernel<1, BM, BN, NTHR, WAVES_M, STAGES, OCC>;
   k1<<<persistent_grid(k1, lds_tiles, OCC, NTHR), NTHR, lds_tiles, s>>>(g1);
-  MOE_DBG("gemm 1");
   k2<<<persistent_grid(k2, lds_tiles, OCC, NTHR), NTHR, lds_tiles, s>>>(g2);
-  MOE_DBG("gemm 2");
 }
 
 }  // namespace
@@ -662,16 +682,18 @@ void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_prob
   // Few rows per segment on average: weight streaming with 16-row tiles.
   if (k_ok && (int64_t)max_rows <= (int64_t)MOE_DECODE_ROWS * nst) {
     tile_plan_kernel<<<1, 1024, 0, s>>>(g1, 16, DBN1 / 2, g2, 16, DBN2, tiles1, tiles2);
-    auto k1 = gemm_decode_kernel<0, DBN1, DBK1>;
-    auto k2 = gemm_decode_kernel<1, DBN2, DBK2>;
+    auto k1 = gemm_decode_kernel<0, DBN1, DBK1, 1, MOE_DWAVES>;
+    auto k2 = gemm_decode_kernel<1, DBN2, DBK2, 1, MOE_DWAVES>;
     k1<<<persistent_grid(k1, lds_tiles, 4), 256, lds_tiles, s>>>(g1);
     k2<<<persistent_grid(k2, lds_tiles, 4), 256, lds_tiles, s>>>(g2);
     return;
   }
   if ((int64_t)max_rows >= (int64_t)MOE_BIG_ROWS * nst)
-    launch_tiled<256, 256, 512, 4, 1>(g1, g2, nst, tiles1, tiles2, s);
-  else
-    launch_tiled<128, 128, 256, 2, 2>(g1, g2, nst, tiles1, tiles2, s);
+    launch_ring<256, 256, 512, 4, 2, 1>(g1, g2, nst, tiles1, tiles2, s);   // 4 x 2 waves of 64 x 128
+  else if ((size_t)(nst + 1) * sizeof(int) + 3 * 384 * 128 <= kMaxLdsBytes)
+    launch_ring<128, 256, 512, 2, 3, 1>(g1, g2, nst, tiles1, tiles2, s);   // 2 x 4 waves of 64 x 64
+  else  // a tile table this long leaves no room for the third stage
+    launch_ring<128, 256, 512, 2, 2, 1>(g1, g2, nst, tiles1, tiles2, s);
 }
 
 }  // namespace moe
