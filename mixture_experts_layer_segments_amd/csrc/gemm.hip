@@ -33,6 +33,7 @@ struct GemmProblem {
   const float* scale;       // nullable, by row
   const int32_t* seg_offsets;  // nullable: one segment [0, rows)
   const int32_t* seg_expert;   // nullable: expert 0
+  const int32_t* a_rows;       // nullable: row r of the problem is row a_rows[r] of A
   int32_t n_seg, rows, N, K;
   int32_t up_off;           // GEMM 1: row offset of W_up inside B
   int64_t b_stride;         // elements per expert in B
@@ -249,7 +250,6 @@ __global__ __launch_bounds__(NTHR, OCC) void gemm_ring_kernel(GemmArgs args) {
     const int m0 = (first_m + lg % gm) * BM;
     const int n0 = (lg / gm) * ncols;
     const int K = P.K, N = P.N;
-    const uint16_t* Ab = P.A + (size_t)r0 * K;
     const uint16_t* Bb = P.B + (size_t)e * P.b_stride;
 
     // source of this lane's 16 bytes in each of the wave's copy instructions
@@ -259,7 +259,8 @@ __global__ __launch_bounds__(NTHR, OCC) void gemm_ring_kernel(GemmArgs args) {
       const int row = (i * NW + wv) * 8 + (lane >> 3);
       const int kc = (lane & 7) ^ (row & 7);
       if ((i * NW + wv) * 8 < BM) {
-        src[i] = Ab + (size_t)min(m0 + row, len - 1) * K + kc * 8;
+        const int ar = r0 + min(m0 + row, len - 1);
+        src[i] = P.A + (size_t)(P.a_rows ? P.a_rows[ar] : ar) * K + kc * 8;
       } else {
         const int br = row - BM;
         int brow;
@@ -364,6 +365,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
                                                        const float* __restrict__ scale,
                                                        const int32_t* __restrict__ seg_offsets,
                                                        const int32_t* __restrict__ seg_expert,
+                                                       const int32_t* __restrict__ a_rows,
                                                        int n_seg, int rows, int N, int K,
                                                        int up_off, int64_t b_stride) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -374,7 +376,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
     if (row >= seg_offsets[n_seg]) return;
     e = seg_expert[find_segment(seg_offsets, n_seg, row)];
   }
-  const float* a = A + (size_t)row * K;
+  const float* a = A + (size_t)(a_rows ? a_rows[row] : row) * K;
   const float* b = B + (size_t)e * b_stride;
   if (MODE == 0) {
     const float* bg = b + (size_t)col * K;
@@ -475,7 +477,8 @@ void gemm_decode_kernel(GemmArgs args) {
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) {
       a_ok[mi] = m0 + mi * 16 + r < len;
-      a_off[mi] = (uint32_t)(r0 + min(m0 + mi * 16 + r, len - 1)) * (uint32_t)K +
+      const int ar = r0 + min(m0 + mi * 16 + r, len - 1);
+      a_off[mi] = (uint32_t)(P.a_rows ? P.a_rows[ar] : ar) * (uint32_t)K +
                   (wv * KPW * 32 + q * 8);
     }
 
@@ -632,10 +635,10 @@ void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_prob
       int64_t n1 = (int64_t)P.rows * Iw, n2 = (int64_t)P.rows * H;
       gemm_f32_kernel<0><<<(unsigned)((n1 + 255) / 256), 256, 0, s>>>(
           (const float*)P.A, (const float*)P.w13, (float*)P.h, nullptr, P.seg_offsets,
-          P.seg_expert, P.n_seg, P.rows, Iw, H, Iw, (int64_t)2 * Iw * H);
+          P.seg_expert, P.a_rows, P.n_seg, P.rows, Iw, H, Iw, (int64_t)2 * Iw * H);
       gemm_f32_kernel<1><<<(unsigned)((n2 + 255) / 256), 256, 0, s>>>(
           (const float*)P.h, (const float*)P.w2, (float*)P.y, P.row_scale, P.seg_offsets,
-          P.seg_expert, P.n_seg, P.rows, H, Iw, 0, (int64_t)H * Iw);
+          P.seg_expert, nullptr, P.n_seg, P.rows, H, Iw, 0, (int64_t)H * Iw);
     }
     return;
   }
@@ -650,6 +653,7 @@ void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_prob
     a.scale = nullptr;
     a.seg_offsets = P.seg_offsets;
     a.seg_expert = P.seg_expert;
+    a.a_rows = P.a_rows;
     a.n_seg = P.n_seg;
     a.rows = P.rows;
     a.N = P.Iw;
@@ -659,6 +663,7 @@ void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_prob
     GemmProblem& b = g2.p[p];
     b = a;
     b.A = (const uint16_t*)P.h;
+    b.a_rows = nullptr;
     b.B = (const uint16_t*)P.w2;
     b.C = (uint16_t*)P.y;
     b.scale = P.row_scale;

@@ -37,7 +37,6 @@ Layout make_layout(const moe_config& c) {
   L.h = take(A * c.I * eb);
   L.shared_h = take((size_t)c.T * c.shared_I * eb);
   L.g_end = o;
-  L.x_perm = take(A * c.H * eb);
   L.y_perm = take(A * c.H * eb);
   L.shared_y = take(c.shared_I > 0 ? (size_t)c.T * c.H * eb : 0);
   L.seg_offsets = take((S + 1) * 4);
@@ -86,6 +85,11 @@ moe_status check_config(const moe_config* c) {
   if (c->split_ways > kMaxWays) return MOE_ERR_UNSUPPORTED;
   if (c->shared_I < 0) return MOE_ERR_INVALID_ARG;
   if ((int64_t)c->T * c->k > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED;
+  // 32-bit element offsets inside the kernels
+  if ((int64_t)c->T * c->k * c->H >= (int64_t)1 << 32 ||
+      (int64_t)2 * c->I * c->H >= (int64_t)1 << 32 ||
+      (int64_t)2 * c->shared_I * c->H >= (int64_t)1 << 32)
+    return MOE_ERR_UNSUPPORTED;
   if (c->act_dtype == MOE_DT_BF16) {
     if (c->H % 64 || c->I % 64 || c->shared_I % 64) return MOE_ERR_UNSUPPORTED;
   } else {
@@ -242,11 +246,13 @@ moe_status moe_layer_forward(const moe_config* cfg, const float* logits, const v
   MOE_DBG("layer entry");
   launch_route(*cfg, logits, topk_ids, topk_w, s);
   MOE_DBG("route");
-  launch_permute(*cfg, x, topk_ids, ws + L.x_perm, seg_offsets, seg_expert, a2r, r2t, counts,
+  // no x_perm: GEMM 1 gathers its rows from x through row_to_token
+  launch_permute(*cfg, x, topk_ids, nullptr, seg_offsets, seg_expert, a2r, r2t, counts,
                  balancedness, topk_w, row_w, ws, L, s);
   MOE_DBG("permute");
   FfnProblem p[2]{};
-  p[0].A = ws + L.x_perm;
+  p[0].A = x;
+  p[0].a_rows = r2t;
   p[0].w13 = w13;
   p[0].w2 = w2;
   p[0].h = ws + L.h;

@@ -49,7 +49,7 @@ inline int num_chunks(int64_t A) { return (int)((A + chunk_len(A) - 1) / chunk_l
 struct Layout {
   size_t cnt_bin, blk_off, seg_of_bin, p_end;                 // region P
   size_t tiles1, tiles2, h, shared_h, g_end;                  // region G
-  size_t x_perm, y_perm, shared_y, seg_offsets, seg_expert,   // region L
+  size_t y_perm, shared_y, seg_offsets, seg_expert,           // region L
       assign_to_row, row_to_token, row_w, l_end;
 };
 Layout make_layout(const moe_config& c);
@@ -74,6 +74,7 @@ struct FfnProblem {
   const float* row_scale; // nullable, by row
   const int32_t* seg_offsets;  // nullable: shared problem = one segment
   const int32_t* seg_expert;
+  const int32_t* a_rows;  // nullable: GEMM 1 reads row a_rows[r] of A for row r
   int32_t n_seg;          // segments (1 for shared)
   int32_t rows;           // max rows (A rows)
   int32_t Iw;             // intermediate size of this problem

@@ -281,6 +281,7 @@ void launch_permute(const moe_config& c, const void* x, const int32_t* ids, void
                                  seg_expert, seg_of_bin, blk_off, bal);
   rank_kernel<<<nb, 64, S * sizeof(int), s>>>(ids, A, c.k, c.E, ways, chunk, nb, S,
                                               seg_of_bin, blk_off, a2r, r2t, w, row_w);
+  if (!x_perm) return;  // the caller reads rows of x through row_to_token
   const int eb = c.act_dtype == MOE_DT_F32 ? 4 : 2;
   const int row_chunks = c.H * eb / 16;
   gather_kernel<<<(A + 3) / 4, 256, 0, s>>>(reinterpret_cast<const uint4*>(x), r2t,
