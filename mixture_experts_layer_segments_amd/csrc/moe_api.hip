@@ -32,8 +32,7 @@ Layout make_layout(const moe_config& c) {
   L.blk_off = take(S * nb * 4);
   L.seg_of_bin = take(nbins * 4);
   L.p_end = o;
-  L.tiles1 = take((S + 2) * 4);
-  L.tiles2 = take((S + 2) * 4);
+  L.tiles = take(4 * (S + 2) * 4);
   L.h = take(A * c.I * eb);
   L.shared_h = take((size_t)c.T * c.shared_I * eb);
   L.g_end = o;
@@ -197,8 +196,7 @@ moe_status moe_grouped_ffn(const moe_config* cfg, const void* x_perm,
   p.n_seg = num_segments(*cfg);
   p.rows = cfg->T * cfg->k;
   p.Iw = cfg->I;
-  launch_grouped_ffn(*cfg, &p, 1, (int32_t*)(ws + L.tiles1), (int32_t*)(ws + L.tiles2),
-                     (hipStream_t)stream);
+  launch_grouped_ffn(*cfg, &p, 1, (int32_t*)(ws + L.tiles), (hipStream_t)stream);
   return launch_status();
 }
 
@@ -244,12 +242,16 @@ moe_status moe_layer_forward(const moe_config* cfg, const float* logits, const v
   float* row_w = (float*)(ws + L.row_w);
 
   MOE_DBG("layer entry");
-  launch_route(*cfg, logits, topk_ids, topk_w, s);
-  MOE_DBG("route");
   // no x_perm: GEMM 1 gathers its rows from x through row_to_token
-  launch_permute(*cfg, x, topk_ids, nullptr, seg_offsets, seg_expert, a2r, r2t, counts,
-                 balancedness, topk_w, row_w, ws, L, s);
-  MOE_DBG("permute");
+  if (cfg->T * cfg->k <= kSmallA) {
+    launch_route_permute_small(*cfg, logits, topk_ids, topk_w, counts, seg_offsets, seg_expert,
+                               a2r, r2t, row_w, balancedness, s);
+  } else {
+    launch_route(*cfg, logits, topk_ids, topk_w, s);
+    launch_permute(*cfg, x, topk_ids, nullptr, seg_offsets, seg_expert, a2r, r2t, counts,
+                   balancedness, topk_w, row_w, ws, L, s);
+  }
+  MOE_DBG("route + permute");
   FfnProblem p[2]{};
   p[0].A = x;
   p[0].a_rows = r2t;
@@ -276,8 +278,7 @@ moe_status moe_layer_forward(const moe_config* cfg, const float* logits, const v
     p[1].rows = cfg->T;
     p[1].Iw = cfg->shared_I;
   }
-  launch_grouped_ffn(*cfg, p, shared ? 2 : 1, (int32_t*)(ws + L.tiles1),
-                     (int32_t*)(ws + L.tiles2), s);
+  launch_grouped_ffn(*cfg, p, shared ? 2 : 1, (int32_t*)(ws + L.tiles), s);
   launch_combine(*cfg, ws + L.y_perm, a2r, nullptr, shared ? ws + L.shared_y : nullptr, out,
                  s);
   return launch_status();

@@ -31,6 +31,7 @@ constexpr int kMaxWays = 4;
 constexpr int kMaxBins = kMaxE * kMaxWays;
 constexpr int kMaxSegments = kMaxE * kMaxWays;
 constexpr size_t kAlign = 256;
+constexpr int kSmallA = 1024;  // assignments up to which one workgroup routes and permutes
 
 inline size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
 
@@ -48,7 +49,7 @@ inline int num_chunks(int64_t A) { return (int)((A + chunk_len(A) - 1) / chunk_l
 // G: grouped-FFN scratch (tile tables, h); L: layer intermediates.
 struct Layout {
   size_t cnt_bin, blk_off, seg_of_bin, p_end;                 // region P
-  size_t tiles1, tiles2, h, shared_h, g_end;                  // region G
+  size_t tiles, h, shared_h, g_end;                           // region G
   size_t y_perm, shared_y, seg_offsets, seg_expert,           // region L
       assign_to_row, row_to_token, row_w, l_end;
 };
@@ -62,6 +63,14 @@ void launch_permute(const moe_config& c, const void* x, const int32_t* ids, void
                     int32_t* seg_offsets, int32_t* seg_expert, int32_t* a2r, int32_t* r2t,
                     int32_t* counts, float* bal, const float* w, float* row_w, char* ws,
                     const Layout& L, hipStream_t s);
+
+// Routing and permutation in one single-workgroup launch, for T*k <= kSmallA
+// (no x_perm; writes ids, w, counts, seg_offsets, seg_expert, assign_to_row,
+// row_to_token, row_w and balancedness).
+void launch_route_permute_small(const moe_config& c, const float* logits, int32_t* ids,
+                                float* w, int32_t* counts, int32_t* seg_offsets,
+                                int32_t* seg_expert, int32_t* a2r, int32_t* r2t, float* row_w,
+                                float* bal, hipStream_t s);
 
 // One grouped-FFN problem: segments [seg_offsets[s], seg_offsets[s+1]) of
 // the rows of A, or (shared) one segment of all `rows` rows.
@@ -79,8 +88,9 @@ struct FfnProblem {
   int32_t rows;           // max rows (A rows)
   int32_t Iw;             // intermediate size of this problem
 };
+// `tiles`: 4 * (total segments + 1) int32 of scratch for the tile tables.
 void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_probs,
-                        int32_t* tiles1, int32_t* tiles2, hipStream_t s);
+                        int32_t* tiles, hipStream_t s);
 void launch_combine(const moe_config& c, const void* y_perm, const int32_t* a2r,
                     const float* w, const void* shared_y, void* out, hipStream_t s);
 

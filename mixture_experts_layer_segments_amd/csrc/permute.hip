@@ -14,19 +14,11 @@
 //             time; lanes of one segment get consecutive rows from a ballot
 //             mask, so rows of a segment are in increasing assignment order.
 //  4. gather: x_perm[r] = x[row_to_token[r]] with 16-byte loads and stores.
-#include "moe_internal.h"
+#include "plan_dev.h"
+#include "route_dev.h"
 
 namespace moe {
 namespace {
-
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int o = __shfl_up(v, off);
-    if (lane >= off) v += o;
-  }
-  return v;
-}
 
 __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ ids, int A,
                                                    int k, int E, int ways, int chunk, int nb,
@@ -46,114 +38,33 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
   for (int i = threadIdx.x; i < nbins; i += blockDim.x) cnt_bin[(size_t)i * nb + b] = h[i];
 }
 
-// In-place exclusive scan of n <= 4096 ints in LDS by 1024 threads; returns
-// the total to every thread.
-__device__ int block_exclusive_scan(int* data, int n, int* wave_tot) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int per = (n + 1023) / 1024;
-  const int lo = min(n, tid * per), hi = min(n, lo + per);
-  int sum = 0;
-  for (int i = lo; i < hi; ++i) sum += data[i];
-  int incl = wave_incl_scan(sum, lane);
-  if (lane == 63) wave_tot[wv] = incl;
-  __syncthreads();
-  if (wv == 0) {
-    int x = lane < 16 ? wave_tot[lane] : 0;
-    int xi = wave_incl_scan(x, lane);
-    if (lane < 16) wave_tot[lane] = xi - x;
-    if (lane == 15) wave_tot[16] = xi;
-  }
-  __syncthreads();
-  int run = wave_tot[wv] + incl - sum;
-  for (int i = lo; i < hi; ++i) {
-    int v = data[i];
-    data[i] = run;
-    run += v;
-  }
-  const int total = wave_tot[16];
-  __syncthreads();
-  return total;
-}
-
 __global__ __launch_bounds__(1024) void plan_kernel(
     const int32_t* __restrict__ cnt_bin, int nb, int E, int ways, int n_hot,
     int32_t* __restrict__ counts, int32_t* __restrict__ seg_offsets,
     int32_t* __restrict__ seg_expert, int32_t* __restrict__ seg_of_bin,
     int32_t* __restrict__ blk_off, float* __restrict__ bal) {
-  __shared__ int tot[kMaxBins];
-  __shared__ int cnt_e[kMaxE];
-  __shared__ int seg_first[kMaxE + 1];
-  __shared__ int seg_len[kMaxSegments + 1];
-  __shared__ int seg_exp[kMaxSegments];
-  __shared__ int wave_tot[17];
-  __shared__ int red[2][16];
-
+  __shared__ plan_dev::PlanLds L;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nbins = E * ways;
 
-  // 1. bin totals: one wave per bin, coalesced over chunks
+  // bin totals: one wave per bin, coalesced over chunks
   for (int bin = wv; bin < nbins; bin += 16) {
     int s = 0;
     for (int b = lane; b < nb; b += 64) s += cnt_bin[(size_t)bin * nb + b];
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-    if (lane == 0) tot[bin] = s;
+    if (lane == 0) L.tot[bin] = s;
   }
   __syncthreads();
+  const int S = plan_dev::plan_segments(L, E, ways, n_hot, counts, seg_offsets, seg_expert,
+                                        seg_of_bin, bal);
 
-  // 2. logical expert counts
-  for (int e = tid; e < E; e += 1024) {
-    int s = 0;
-    for (int p = 0; p < ways; ++p) s += tot[e * ways + p];
-    cnt_e[e] = s;
-    counts[e] = s;
-  }
-  __syncthreads();
-
-  // 3. hot experts: rank by (count desc, id asc); segments per expert
-  const bool split = n_hot > 0 && ways > 1;
-  for (int e = tid; e < E; e += 1024) {
-    int nseg = 1;
-    if (split) {
-      const int ce = cnt_e[e];
-      int rank = 0;
-      for (int o = 0; o < E; ++o) {
-        const int co = cnt_e[o];
-        rank += (co > ce) || (co == ce && o < e);
-      }
-      if (rank < n_hot) nseg = ways;
-    }
-    seg_first[e] = nseg;
-  }
-  __syncthreads();
-  const int S = block_exclusive_scan(seg_first, E, wave_tot);
-  if (tid == 0) seg_first[E] = S;
-  __syncthreads();
-
-  // 4. segment list, lengths, bin -> segment map
-  for (int e = tid; e < E; e += 1024) {
-    const int f = seg_first[e];
-    const int nseg = seg_first[e + 1] - f;
-    for (int p = 0; p < nseg; ++p) {
-      seg_exp[f + p] = e;
-      seg_expert[f + p] = e;
-      seg_len[f + p] = nseg > 1 ? tot[e * ways + p] : cnt_e[e];
-    }
-    for (int p = 0; p < ways; ++p) seg_of_bin[e * ways + p] = nseg > 1 ? f + p : f;
-  }
-  __syncthreads();
-
-  // 5. segment offsets
-  const int total = block_exclusive_scan(seg_len, S, wave_tot);
-  for (int s = tid; s < S; s += 1024) seg_offsets[s] = seg_len[s];
-  if (tid == 0) seg_offsets[S] = total;
-
-  // 6. per-(segment, chunk) bases: one wave per segment scans over chunks
+  // per-(segment, chunk) bases: one wave per segment scans over chunks
   for (int s = wv; s < S; s += 16) {
-    const int e = seg_exp[s];
-    const int f = seg_first[e];
-    const bool hot = seg_first[e + 1] - f > 1;
-    int carry = seg_len[s];
+    const int e = L.seg_exp[s];
+    const int f = L.seg_first[e];
+    const bool hot = L.seg_first[e + 1] - f > 1;
+    int carry = L.seg_off[s];
     for (int b0 = 0; b0 < nb; b0 += 64) {
       const int b = b0 + lane;
       int v = 0;
@@ -164,35 +75,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(
           for (int p = 0; p < ways; ++p) v += cnt_bin[(size_t)(e * ways + p) * nb + b];
         }
       }
-      const int incl = wave_incl_scan(v, lane);
+      const int incl = plan_dev::wave_incl_scan(v, lane);
       if (b < nb) blk_off[(size_t)s * nb + b] = carry + incl - v;
       carry += __shfl(incl, 63);
     }
-  }
-
-  // 7. balancedness = (sum / E) / max, one fp64 division of exact integers
-  int mx = 0, sm = 0;
-  for (int e = tid; e < E; e += 1024) {
-    mx = max(mx, cnt_e[e]);
-    sm += cnt_e[e];
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    mx = max(mx, __shfl_xor(mx, off));
-    sm += __shfl_xor(sm, off);
-  }
-  if (lane == 0) {
-    red[0][wv] = mx;
-    red[1][wv] = sm;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int m = 0, su = 0;
-    for (int i = 0; i < 16; ++i) {
-      m = max(m, red[0][i]);
-      su += red[1][i];
-    }
-    bal[0] = m > 0 ? (float)(((double)su / (double)E) / (double)m) : 0.0f;
   }
 }
 
@@ -239,6 +125,56 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ id
   }
 }
 
+// Small batches (decode): routing, histogram, plan and the stable rank in one
+// workgroup -- one launch instead of four.  Each wave routes tokens; every
+// assignment is binned by LDS atomics (counts do not depend on the order);
+// the plan is the one above; and the row of assignment a is its segment's
+// offset plus the number of earlier assignments in the same segment, counted
+// directly over the at most kSmallA assignments.
+template <int VPL>
+__global__ __launch_bounds__(1024) void route_permute_small_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int score, int n_group,
+    int topk_group, int topn, int renorm, int ways, int n_hot, int32_t* __restrict__ ids,
+    float* __restrict__ w, int32_t* __restrict__ counts, int32_t* __restrict__ seg_offsets,
+    int32_t* __restrict__ seg_expert, int32_t* __restrict__ a2r, int32_t* __restrict__ r2t,
+    float* __restrict__ row_w, float* __restrict__ bal) {
+  __shared__ plan_dev::PlanLds L;
+  __shared__ int seg_of_bin[kMaxBins];
+  __shared__ int id_a[kSmallA];
+  __shared__ float w_a[kSmallA];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int A = T * k;
+  for (int i = tid; i < E * ways; i += 1024) L.tot[i] = 0;
+  __syncthreads();
+  for (int t = wv; t < T; t += 16) {
+    int my_id;
+    float my_w;
+    route_dev::route_token<VPL>(logits + (size_t)t * E, E, k, score, n_group, topk_group, topn,
+                                renorm, lane, my_id, my_w);
+    if (lane < k) {
+      const int a = t * k + lane;
+      ids[a] = my_id;
+      w[a] = my_w;
+      id_a[a] = my_id;
+      w_a[a] = my_w;
+      atomicAdd(&L.tot[my_id * ways + t % ways], 1);
+    }
+  }
+  __syncthreads();
+  plan_dev::plan_segments(L, E, ways, n_hot, counts, seg_offsets, seg_expert, seg_of_bin, bal);
+  for (int a = tid; a < A; a += 1024) id_a[a] = seg_of_bin[id_a[a] * ways + (a / k) % ways];
+  __syncthreads();
+  for (int a = tid; a < A; a += 1024) {
+    const int sa = id_a[a];
+    int before = 0;
+    for (int b = 0; b < a; ++b) before += id_a[b] == sa;
+    const int row = L.seg_off[sa] + before;
+    a2r[a] = row;
+    r2t[row] = a / k;
+    row_w[row] = w_a[a];
+  }
+}
+
 // x_perm[r] = x[row_to_token[r]]: one wave per row, 16-byte chunks.
 __global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x,
                                                      const int32_t* __restrict__ r2t,
@@ -262,7 +198,35 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x
   for (; c < row_chunks; c += 64) dst[c] = src[c];
 }
 
+template <int VPL>
+void launch_small_vpl(const moe_config& c, const float* logits, int32_t* ids, float* w,
+                      int32_t* counts, int32_t* seg_offsets, int32_t* seg_expert, int32_t* a2r,
+                      int32_t* r2t, float* row_w, float* bal, hipStream_t s) {
+  const int ways = c.n_hot_split > 0 ? c.split_ways : 1;
+  route_permute_small_kernel<VPL><<<1, 1024, 0, s>>>(
+      logits, c.T, c.E, c.k, c.score, c.n_group, c.topk_group, c.group_score_topn,
+      c.renormalize, ways, c.n_hot_split, ids, w, counts, seg_offsets, seg_expert, a2r, r2t,
+      row_w, bal);
+}
+
 }  // namespace
+
+void launch_route_permute_small(const moe_config& c, const float* logits, int32_t* ids,
+                                float* w, int32_t* counts, int32_t* seg_offsets,
+                                int32_t* seg_expert, int32_t* a2r, int32_t* r2t, float* row_w,
+                                float* bal, hipStream_t s) {
+  const int vpl = (c.E + 63) / 64;
+  if (vpl <= 1)
+    launch_small_vpl<1>(c, logits, ids, w, counts, seg_offsets, seg_expert, a2r, r2t, row_w, bal, s);
+  else if (vpl <= 2)
+    launch_small_vpl<2>(c, logits, ids, w, counts, seg_offsets, seg_expert, a2r, r2t, row_w, bal, s);
+  else if (vpl <= 4)
+    launch_small_vpl<4>(c, logits, ids, w, counts, seg_offsets, seg_expert, a2r, r2t, row_w, bal, s);
+  else if (vpl <= 8)
+    launch_small_vpl<8>(c, logits, ids, w, counts, seg_offsets, seg_expert, a2r, r2t, row_w, bal, s);
+  else
+    launch_small_vpl<16>(c, logits, ids, w, counts, seg_offsets, seg_expert, a2r, r2t, row_w, bal, s);
+}
 
 void launch_permute(const moe_config& c, const void* x, const int32_t* ids, void* x_perm,
                     int32_t* seg_offsets, int32_t* seg_expert, int32_t* a2r, int32_t* r2t,

@@ -1,0 +1,147 @@
+// Device-side planning shared by the permutation kernels: block scans and
+// the step from bin totals to the segment list ("Serving Mixture-of-Experts
+// Models", section "Follow one token through an MoE layer", step 1, and
+// section "The slowest expert sets the pace" for balancedness).  Every
+// function here is called by all 1024 threads of one workgroup.
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace plan_dev {
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int o = __shfl_up(v, off);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// In-place exclusive scan of n <= 4096 ints in LDS by 1024 threads; returns
+// the total to every thread.
+__device__ inline int block_exclusive_scan(int* data, int n, int* wave_tot) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int per = (n + 1023) / 1024;
+  const int lo = min(n, tid * per), hi = min(n, lo + per);
+  int sum = 0;
+  for (int i = lo; i < hi; ++i) sum += data[i];
+  int incl = wave_incl_scan(sum, lane);
+  if (lane == 63) wave_tot[wv] = incl;
+  __syncthreads();
+  if (wv == 0) {
+    int x = lane < 16 ? wave_tot[lane] : 0;
+    int xi = wave_incl_scan(x, lane);
+    if (lane < 16) wave_tot[lane] = xi - x;
+    if (lane == 15) wave_tot[16] = xi;
+  }
+  __syncthreads();
+  int run = wave_tot[wv] + incl - sum;
+  for (int i = lo; i < hi; ++i) {
+    int v = data[i];
+    data[i] = run;
+    run += v;
+  }
+  const int total = wave_tot[16];
+  __syncthreads();
+  return total;
+}
+
+// LDS scratch of plan_segments, declared by the calling kernel.
+struct PlanLds {
+  int tot[kMaxBins];            // in: assignments per bin (expert, t mod ways)
+  int cnt_e[kMaxE];             // assignments per logical expert
+  int seg_first[kMaxE + 1];     // first segment of each expert; [E] = S
+  int seg_off[kMaxSegments + 1];  // out: exclusive offsets of the segments
+  int seg_exp[kMaxSegments];    // expert of each segment
+  int wave_tot[17];
+  int red[2][16];
+};
+
+// From bin totals to expert counts, the hot experts (the n_hot largest
+// counts, lower id on a tie) with `ways` replica segments each, segment
+// offsets, the bin -> segment map and balancedness = (sum/E) / max by one fp64
+// division of exact integers.  Writes counts[E], seg_offsets[S+1],
+// seg_expert[S], seg_of_bin[E*ways] and bal[0]; returns S.
+__device__ inline int plan_segments(PlanLds& L, int E, int ways, int n_hot,
+                                    int32_t* __restrict__ counts,
+                                    int32_t* __restrict__ seg_offsets,
+                                    int32_t* __restrict__ seg_expert, int32_t* seg_of_bin,
+                                    float* __restrict__ bal) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int e = tid; e < E; e += 1024) {
+    int s = 0;
+    for (int p = 0; p < ways; ++p) s += L.tot[e * ways + p];
+    L.cnt_e[e] = s;
+    counts[e] = s;
+  }
+  __syncthreads();
+
+  const bool split = n_hot > 0 && ways > 1;
+  for (int e = tid; e < E; e += 1024) {
+    int nseg = 1;
+    if (split) {
+      const int ce = L.cnt_e[e];
+      int rank = 0;
+      for (int o = 0; o < E; ++o) {
+        const int co = L.cnt_e[o];
+        rank += (co > ce) || (co == ce && o < e);
+      }
+      if (rank < n_hot) nseg = ways;
+    }
+    L.seg_first[e] = nseg;
+  }
+  __syncthreads();
+  const int S = block_exclusive_scan(L.seg_first, E, L.wave_tot);
+  if (tid == 0) L.seg_first[E] = S;
+  __syncthreads();
+
+  for (int e = tid; e < E; e += 1024) {
+    const int f = L.seg_first[e];
+    const int nseg = L.seg_first[e + 1] - f;
+    for (int p = 0; p < nseg; ++p) {
+      L.seg_exp[f + p] = e;
+      seg_expert[f + p] = e;
+      L.seg_off[f + p] = nseg > 1 ? L.tot[e * ways + p] : L.cnt_e[e];
+    }
+    for (int p = 0; p < ways; ++p) seg_of_bin[e * ways + p] = nseg > 1 ? f + p : f;
+  }
+  __syncthreads();
+
+  const int total = block_exclusive_scan(L.seg_off, S, L.wave_tot);
+  for (int s = tid; s < S; s += 1024) seg_offsets[s] = L.seg_off[s];
+  if (tid == 0) {
+    seg_offsets[S] = total;
+    L.seg_off[S] = total;
+  }
+
+  int mx = 0, sm = 0;
+  for (int e = tid; e < E; e += 1024) {
+    mx = max(mx, L.cnt_e[e]);
+    sm += L.cnt_e[e];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    mx = max(mx, __shfl_xor(mx, off));
+    sm += __shfl_xor(sm, off);
+  }
+  if (lane == 0) {
+    L.red[0][wv] = mx;
+    L.red[1][wv] = sm;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int m = 0, su = 0;
+    for (int i = 0; i < 16; ++i) {
+      m = max(m, L.red[0][i]);
+      su += L.red[1][i];
+    }
+    bal[0] = m > 0 ? (float)(((double)su / (double)E) / (double)m) : 0.0f;
+  }
+  __syncthreads();
+  return S;
+}
+
+}  // namespace plan_dev
+}  // namespace moe

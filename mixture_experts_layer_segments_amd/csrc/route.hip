@@ -1,46 +1,9 @@
-// Top-k gating: one wave64 per token, the token's logits held in registers
-// (VPL = ceil(E/64) per lane, expert e = lane + 64*i), k rounds of a
-// wave-wide (value desc, id asc) arg-max butterfly.
-//
-// Flat mode: the k largest logits; weights softmax over the winners.  Grouped
-// mode (the MoE inference blog, "MoE architecture recap": a few expert groups
-// first, then the top experts inside them): sigmoid scores, each group scored
-// by the fp32 sum of its best `topn` member scores, the `topk_group` best
-// groups kept, then the k largest logits inside them; weights s_j / sum(s).
-// Sigmoid and weights are evaluated in fp64 and rounded once, so the fp32
-// group scores (the values that decide which groups are kept) are the
-// correctly rounded sigmoid in all but vanishingly rare cases.
-#include <math.h>
-
-#include "moe_internal.h"
+// Top-k gating kernel: one wave64 per token (the per-token logic is in
+// route_dev.h).
+#include "route_dev.h"
 
 namespace moe {
 namespace {
-
-constexpr int kNoId = 0x7fffffff;
-
-__device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
-  return av > bv || (av == bv && ai < bi);
-}
-
-// Wave-wide arg-max of (value desc, id asc); every lane returns the winner.
-__device__ __forceinline__ void wave_argmax(float& v, int& id) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    float ov = __shfl_xor(v, off);
-    int oi = __shfl_xor(id, off);
-    if (better(ov, oi, v, id)) {
-      v = ov;
-      id = oi;
-    }
-  }
-}
-
-__device__ __forceinline__ double wave_sum(double x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-  return x;
-}
 
 template <int VPL>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T,
@@ -51,125 +14,13 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-
-  float v[VPL];
-  bool avail[VPL];
-  const float* row = logits + (size_t)t * E;
-#pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    int e = lane + 64 * i;
-    float x = e < E ? row[e] : -INFINITY;
-    if (x != x) x = -INFINITY;  // a NaN logit never wins over a number
-    v[i] = x;
-    avail[i] = e < E;
-  }
-
-  if (score == MOE_SCORE_SIGMOID && n_group > 1) {
-    const int per = E / n_group;
-    float s32[VPL];
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) s32[i] = (float)(1.0 / (1.0 + exp(-(double)v[i])));
-    float my_gs = -INFINITY;  // lane g holds group g's score
-    for (int g = 0; g < n_group; ++g) {
-      bool used[VPL];
-#pragma unroll
-      for (int i = 0; i < VPL; ++i) used[i] = false;
-      float acc = 0.0f;
-      for (int r = 0; r < topn; ++r) {
-        float bv = -INFINITY;
-        int bi = kNoId;
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-          int e = lane + 64 * i;
-          if (avail[i] && !used[i] && e / per == g && better(v[i], e, bv, bi)) {
-            bv = v[i];
-            bi = e;
-          }
-        }
-        wave_argmax(bv, bi);
-        if (bi == kNoId) break;  // group smaller than topn
-        const int slot = bi >> 6, owner = bi & 63;
-        float mine = 0.0f;
-#pragma unroll
-        for (int i = 0; i < VPL; ++i)
-          if (i == slot) mine = s32[i];
-        acc = acc + __shfl(mine, owner);
-        if (lane == owner) {
-#pragma unroll
-          for (int i = 0; i < VPL; ++i)
-            if (i == slot) used[i] = true;
-        }
-      }
-      if (lane == g) my_gs = acc;
-    }
-    // keep the topk_group best groups
-    uint64_t kept = 0;
-    bool gtaken = false;
-    for (int r = 0; r < topk_group; ++r) {
-      float bv = (lane < n_group && !gtaken) ? my_gs : -INFINITY;
-      int bi = (lane < n_group && !gtaken) ? lane : kNoId;
-      wave_argmax(bv, bi);
-      if (bi == kNoId) break;
-      kept |= 1ull << bi;
-      if (lane == bi) gtaken = true;
-    }
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      int e = lane + 64 * i;
-      if (avail[i] && !((kept >> (e / per)) & 1ull)) avail[i] = false;
-    }
-  }
-
-  // k rounds of arg-max over the remaining experts
-  int my_id = 0;
-  float my_v = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = kNoId;
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      int e = lane + 64 * i;
-      if (avail[i] && better(v[i], e, bv, bi)) {
-        bv = v[i];
-        bi = e;
-      }
-    }
-    wave_argmax(bv, bi);
-    if (lane == j) {
-      my_id = bi;
-      my_v = bv;
-    }
-    if (lane == (bi & 63)) {
-      const int slot = bi >> 6;
-#pragma unroll
-      for (int i = 0; i < VPL; ++i)
-        if (i == slot) avail[i] = false;
-    }
-  }
-
-  // weights in fp64, rounded once
-  const double top0 = (double)__shfl(my_v, 0);
-  double p = 0.0;
-  if (score == MOE_SCORE_SIGMOID) {
-    p = lane < k ? 1.0 / (1.0 + exp(-(double)my_v)) : 0.0;
-    if (renorm) p = p / wave_sum(p);
-  } else {
-    p = lane < k ? exp((double)my_v - top0) : 0.0;
-    double denom;
-    if (renorm) {
-      denom = wave_sum(p);
-    } else {
-      double part = 0.0;
-#pragma unroll
-      for (int i = 0; i < VPL; ++i)
-        if (lane + 64 * i < E) part += exp((double)v[i] - top0);
-      denom = wave_sum(part);
-    }
-    p = p / denom;
-  }
+  int my_id;
+  float my_w;
+  route_dev::route_token<VPL>(logits + (size_t)t * E, E, k, score, n_group, topk_group, topn,
+                              renorm, lane, my_id, my_w);
   if (lane < k) {
     ids[(size_t)t * k + lane] = my_id;
-    w[(size_t)t * k + lane] = (float)p;
+    w[(size_t)t * k + lane] = my_w;
   }
 }
 
