@@ -1,0 +1,57 @@
+"""Seeded random small layers through moe_layer_forward against the oracle:
+shapes, dtypes, routing modes and replica splits drawn at random, so that
+every kernel path (fused small-batch routing, multi-kernel permutation,
+decode tiles, both ring tile shapes, fp32) meets shapes nobody picked by
+hand.  Routing is compared bit for bit, outputs within the layer tolerance."""
+import numpy as np
+import pytest
+
+import moe_inputs as mi
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _random_shape(rng, i):
+    dtype = "f32" if rng.random() < 0.2 else "bf16"
+    E = int(rng.choice([1, 2, 3, 5, 8, 13, 16, 32, 40, 64]))
+    k = int(rng.integers(1, min(E, 6) + 1))
+    T = int(rng.choice([1, 2, 7, 33, 64, 100, 257, 600, 1100]))
+    H = int(rng.choice([64, 128, 192, 320, 512, 1024]))
+    I = int(rng.choice([64, 128, 192, 256, 512]))
+    if dtype == "f32":
+        H = int(rng.choice([4, 12, 64, 100]))
+        I = int(rng.choice([3, 16, 70]))
+    kw = dict(zipf_s=float(rng.choice([0.0, 1.0, 1.5])))
+    if E % 4 == 0 and E >= 8 and rng.random() < 0.4:
+        groups = 4
+        kw.update(score="sigmoid", n_group=groups, topk_group=int(rng.integers(1, groups + 1)))
+        per = E // groups
+        k = min(k, kw["topk_group"] * per)
+        kw["group_score_topn"] = int(rng.integers(1, min(per, 3) + 1))
+    if rng.random() < 0.4 and E >= 2:
+        kw.update(n_hot_split=int(rng.integers(1, min(E, 4) + 1)), split_ways=int(rng.integers(2, 4)))
+    if dtype == "bf16" and rng.random() < 0.2:
+        kw["shared_I"] = int(rng.choice([64, 128, 256]))
+    if rng.random() < 0.2:
+        kw["renormalize"] = 0
+    return mi.MoEShape(f"rand{i}", T=T, H=H, E=E, k=k, I=I, dtype=dtype, seed=1000 + i,
+                       x_std=0.5, **kw)
+
+
+@pytest.mark.timeout(600)
+def test_random_layers():
+    import mixture_experts_layer_segments_amd as moe
+    rng = np.random.default_rng(2024)
+    for i in range(32):
+        cfg = _random_shape(rng, i)
+        print(f"\n[random] {i}: {cfg}", flush=True)
+        case = gu.SmallCase(cfg)
+        o = gu.run_layer(moe, cfg, case.device_inputs())
+        r = case.ref
+        gu.check_routing(cfg, o["ids"].cpu().numpy(), o["w"].cpu().numpy(), r["ids"], r["w"],
+                         r["group_gap"], case.logits)
+        assert (o["counts"].cpu().numpy() == r["counts"]).all(), i
+        assert o["bal"].cpu().numpy()[0] == r["balancedness"], i
+        err = gu.rel_err(gu.host_f64(o["out"]), r["out"])
+        assert err <= gu.rel_tol(cfg), (i, err)
