@@ -35,10 +35,10 @@ GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_segments_amd", "csrc", "gem
 # what it reads for a plain 1 GiB device copy), keyed by workload.  An entry
 # only applies while gemm.hip still has the hash it was measured with.
 MEASURED_TRAFFIC = {
-    "decode_bf16": {"gemm_src_sha256_16": "c6c28c0f9f8c83cf", "bytes": 5550756449},
-    "prefill_skew_bf16": {"gemm_src_sha256_16": "c6c28c0f9f8c83cf", "bytes": 8072902543},
-    "deepseek_v3_bf16": {"gemm_src_sha256_16": "c6c28c0f9f8c83cf", "bytes": 25014576372},
-    "ragged_stress_bf16": {"gemm_src_sha256_16": "c6c28c0f9f8c83cf", "bytes": 13650536576},
+    "decode_bf16": {"gemm_src_sha256_16": "c6a263b8612806d1", "bytes": 5550795800},
+    "prefill_skew_bf16": {"gemm_src_sha256_16": "c6a263b8612806d1", "bytes": 8073820945},
+    "deepseek_v3_bf16": {"gemm_src_sha256_16": "c6a263b8612806d1", "bytes": 22972953148},
+    "ragged_stress_bf16": {"gemm_src_sha256_16": "c6a263b8612806d1", "bytes": 12891357114},
 }
 
 
