@@ -164,18 +164,23 @@ __global__ __launch_bounds__(1024) void tile_plan_kernel(GemmArgs a1, GemmArgs a
 //         columns, so silu(g) * u is formed in registers.
 // MODE 1: GEMM 2 with the row-scale epilogue (BN output columns per tile).
 //
-// Global -> LDS copies go straight into a STAGES-deep LDS ring (global_load_lds_dwordx4: each wave instruction
-// fills one contiguous 1 KiB block of 8 swizzled 128-byte row pieces), so the
-// copies for the next STAGES-1 K stages stay in flight while the current one
-// feeds the MFMAs, with no registers spent on staging.  Completion is tracked
-// with explicit vmcnt waits: a wave waits until at most the copies it issued
-// for later stages are outstanding, then a plain s_barrier (without the
-// memory fence of __syncthreads, which would wait for every copy) makes the
-// stage visible to all waves and frees the slot read one stage earlier.
+// Global -> LDS copies go straight into a STAGES-deep LDS ring
+// (global_load_lds_dwordx4: each wave instruction fills one contiguous 1 KiB
+// block of 8 swizzled 128-byte row pieces), so the copies for the next
+// STAGES-1 K stages stay in flight while the current one feeds the MFMAs,
+// with no registers spent on staging.  Completion is tracked with explicit
+// vmcnt waits: a wave waits until at most the copies it issued for later
+// stages are outstanding, then a plain s_barrier (without the memory fence of
+// __syncthreads, which would wait for every copy) makes the stage visible to
+// all waves and frees the slot read one stage earlier.
+//
+// Inside a stage the MFMA operands are double-buffered in registers: the
+// fragments of the second 32-deep K step are read from LDS while the MFMAs of
+// the first run, one read slotted between every few MFMAs
+// (sched_group_barrier), so a wave waits on LDS once per K step instead of
+// once per fragment -- left to itself the compiler reloads one fragment at a
+// time to save registers (measured 3-6% faster on the large tiles).
 #define MOE_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
-#ifndef MOE_MFMA_PRIO
-#define MOE_MFMA_PRIO 0
-#endif
 #ifndef MOE_SWZ8
 #define MOE_SWZ8(row) (((row) >> 1) & 7)
 #endif
@@ -220,8 +225,21 @@ __device__ __forceinline__ void ring_issue(const uint16_t* const* src, u32x4* ri
                                      0, 0);
 }
 
-template <int MODE, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES, int OCC>
-__global__ __launch_bounds__(NTHR, OCC) void gemm_ring_kernel(GemmArgs args) {
+// Ring-tile geometry shared by the per-tile body and the kernels that size
+// the ring.
+template <int BM, int BN, int BK, int STAGES>
+struct RingShape {
+  static constexpr int KCH = BK / 8;                      // 16-byte chunks per row piece
+  static constexpr int STAGE_CH = (BM + BN) * KCH;        // 16-byte chunks per stage
+  static constexpr int RING_CH = STAGES * STAGE_CH;       // 16-byte chunks of the ring
+};
+
+// One output tile (`tile` in the numbering of the tile table `tiles_l`, which
+// holds args.n_seg_total + 1 prefix entries) through the LDS ring `ring`.
+// Every thread of the workgroup calls it with the same tile.
+template <int MODE, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
+__device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles_l, int tile,
+                                          u32x4* ring) {
   constexpr int KCH = BK / 8;           // 16-byte chunks per row piece
   constexpr int RPB = 64 / KCH;         // row pieces per 1 KiB copy block
   constexpr int NW = NTHR / 64;
@@ -235,17 +253,9 @@ __global__ __launch_bounds__(NTHR, OCC) void gemm_ring_kernel(GemmArgs args) {
   static_assert((ROWS / RPB) % NW == 0 && STAGES >= 2 && STAGES <= 6, "ring shape");
   static_assert(LPW * (STAGES - 2) < 64, "vmcnt range");
 
-  __shared__ u32x4 ring[STAGES * STAGE_CH];
-  extern __shared__ int tiles_l[];
-
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv / WAVES_N, wn = wv % WAVES_N;
   const int nst = args.n_seg_total;
-  for (int i = tid; i <= nst; i += NTHR) tiles_l[i] = args.tiles[i];
-  __syncthreads();
-  const int total = tiles_l[nst];
-  const int G = gridDim.x;
-  const int logical = xcd_logical(blockIdx.x, G);
 
   int brow_of[TN];
 #pragma unroll
@@ -257,123 +267,185 @@ __global__ __launch_bounds__(NTHR, OCC) void gemm_ring_kernel(GemmArgs args) {
       brow_of[ni] = wn * WN + ni * 16;
   }
 
-  for (int tile = logical; tile < total; tile += G) {
-    int lo = 0, hi = nst - 1;
-    while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (tiles_l[mid] <= tile) lo = mid; else hi = mid - 1;
-    }
-    const int gs = lo;
-    const int pi = gs < args.p[0].n_seg ? 0 : 1;
-    const GemmProblem& P = args.p[pi];
-    int r0, len, e;
-    seg_range(P, gs - (pi ? args.p[0].n_seg : 0), r0, len, e);
-    const int mt = (len + BM - 1) / BM;
-    const int ncols = MODE == 0 ? BN / 2 : BN;
-    const int nt = (P.N + ncols - 1) / ncols;
-    const int local = tile - tiles_l[gs];
-    const int grp = local / (kGroupM * nt);
-    const int first_m = grp * kGroupM;
-    const int gm = min(kGroupM, mt - first_m);
-    const int lg = local - grp * kGroupM * nt;
-    const int m0 = (first_m + lg % gm) * BM;
-    const int n0 = (lg / gm) * ncols;
-    const int K = P.K, N = P.N;
-    const uint16_t* Bb = P.B + (size_t)e * P.b_stride;
+  int lo = 0, hi = nst - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (tiles_l[mid] <= tile) lo = mid; else hi = mid - 1;
+  }
+  const int gs = lo;
+  const int pi = gs < args.p[0].n_seg ? 0 : 1;
+  const GemmProblem& P = args.p[pi];
+  int r0, len, e;
+  seg_range(P, gs - (pi ? args.p[0].n_seg : 0), r0, len, e);
+  const int mt = (len + BM - 1) / BM;
+  const int ncols = MODE == 0 ? BN / 2 : BN;
+  const int nt = (P.N + ncols - 1) / ncols;
+  const int local = tile - tiles_l[gs];
+  const int grp = local / (kGroupM * nt);
+  const int first_m = grp * kGroupM;
+  const int gm = min(kGroupM, mt - first_m);
+  const int lg = local - grp * kGroupM * nt;
+  const int m0 = (first_m + lg % gm) * BM;
+  const int n0 = (lg / gm) * ncols;
+  const int K = P.K, N = P.N;
+  const uint16_t* Bb = P.B + (size_t)e * P.b_stride;
 
-    // source of this lane's 16 bytes in each of the wave's copy instructions
-    const uint16_t* src[LPW];
+  // source of this lane's 16 bytes in each of the wave's copy instructions
+  const uint16_t* src[LPW];
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int row = (i * NW + wv) * RPB + lane / KCH;
-      const int kc = (lane % KCH) ^ swz<KCH>(row);
-      if ((i * NW + wv) * RPB < BM) {
-        const int ar = r0 + min(m0 + row, len - 1);
-        src[i] = P.A + (size_t)(P.a_rows ? P.a_rows[ar] : ar) * K + kc * 8;
+  for (int i = 0; i < LPW; ++i) {
+    const int row = (i * NW + wv) * RPB + lane / KCH;
+    const int kc = (lane % KCH) ^ swz<KCH>(row);
+    if ((i * NW + wv) * RPB < BM) {
+      const int ar = r0 + min(m0 + row, len - 1);
+      src[i] = P.A + (size_t)(P.a_rows ? P.a_rows[ar] : ar) * K + kc * 8;
+    } else {
+      const int br = row - BM;
+      int brow;
+      if (MODE == 0) {
+        const int col = min(n0 + (br % (BN / 2)), N - 1);
+        brow = br < BN / 2 ? col : P.up_off + col;
       } else {
-        const int br = row - BM;
-        int brow;
-        if (MODE == 0) {
-          const int col = min(n0 + (br % (BN / 2)), N - 1);
-          brow = br < BN / 2 ? col : P.up_off + col;
-        } else {
-          brow = min(n0 + br, N - 1);
+        brow = min(n0 + br, N - 1);
+      }
+      src[i] = Bb + (size_t)brow * K + kc * 8;
+    }
+  }
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int KT = K / BK;
+  wait_vmcnt<0>();   // this wave's earlier stores and copies are done
+  raw_barrier();     // every wave is done reading the ring
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < KT) ring_issue<LPW, NW, STAGES, STAGE_CH, BK>(src, ring, st, wv);
+  for (int kt = 0; kt < KT; ++kt) {
+    // stage kt has landed once only the copies of later stages remain
+    wait_stages<LPW, STAGES - 2>(min(STAGES - 2, KT - 1 - kt));
+    raw_barrier();
+    if (kt + STAGES - 1 < KT) ring_issue<LPW, NW, STAGES, STAGE_CH, BK>(src, ring, kt + STAGES - 1, wv);
+    const u32x4* slot = ring + (kt % STAGES) * STAGE_CH;
+    // Fragments of K step kk + 1 are read while the MFMAs of step kk run:
+    // two register sets, and the scheduler is told to interleave the LDS
+    // reads one by one among the MFMAs.
+    bf16x8 af[2][TM], bfr[2][TN];
+    auto load_frags = [&](int kk, bf16x8* a, bf16x8* b) {
+      const int ch = kk * 4 + (lane >> 4);
+#pragma unroll
+      for (int mi = 0; mi < TM; ++mi) {
+        const int row = wm * WM + mi * 16 + (lane & 15);
+        a[mi] = __builtin_bit_cast(bf16x8, slot[row * KCH + (ch ^ swz<KCH>(row))]);
+      }
+#pragma unroll
+      for (int ni = 0; ni < TN; ++ni) {
+        const int row = BM + brow_of[ni] + (lane & 15);
+        b[ni] = __builtin_bit_cast(bf16x8, slot[row * KCH + (ch ^ swz<KCH>(row))]);
+      }
+    };
+    load_frags(0, af[0], bfr[0]);
+#pragma unroll
+    for (int kk = 0; kk < BK / 32; ++kk) {
+      const int cur = kk & 1;
+      if (kk + 1 < BK / 32) load_frags(kk + 1, af[cur ^ 1], bfr[cur ^ 1]);
+#pragma unroll
+      for (int mi = 0; mi < TM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < TN; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[cur][mi], bfr[cur][ni],
+                                                                acc[mi][ni], 0, 0, 0);
+      if (kk == 0) {
+        // first: this step's own fragment reads
+        __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
+      }
+      if (kk + 1 < BK / 32) {
+        constexpr int per = (TM * TN) / (TM + TN);
+#pragma unroll
+        for (int i = 0; i < TM + TN; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, per, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        src[i] = Bb + (size_t)brow * K + kc * 8;
+        __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - per * (TM + TN), 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
       }
     }
+  }
 
-    f32x4 acc[TM][TN];
+  uint16_t* Cb = P.C + (size_t)r0 * N;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+  for (int mi = 0; mi < TM; ++mi) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int KT = K / BK;
-    wait_vmcnt<0>();   // this wave's earlier stores and copies are done
-    raw_barrier();     // every wave is done reading the ring
+    for (int i = 0; i < 4; ++i) {
+      const int row = m0 + wm * WM + mi * 16 + (lane >> 4) * 4 + i;
+      if (row >= len) continue;
+      if (MODE == 0) {
 #pragma unroll
-    for (int st = 0; st < STAGES - 1; ++st)
-      if (st < KT) ring_issue<LPW, NW, STAGES, STAGE_CH, BK>(src, ring, st, wv);
-    for (int kt = 0; kt < KT; ++kt) {
-      // stage kt has landed once only the copies of later stages remain
-      wait_stages<LPW, STAGES - 2>(min(STAGES - 2, KT - 1 - kt));
-      raw_barrier();
-      if (kt + STAGES - 1 < KT) ring_issue<LPW, NW, STAGES, STAGE_CH, BK>(src, ring, kt + STAGES - 1, wv);
-      const u32x4* slot = ring + (kt % STAGES) * STAGE_CH;
-#pragma unroll
-      for (int kk = 0; kk < BK / 32; ++kk) {
-        const int ch = kk * 4 + (lane >> 4);
-        bf16x8 af[TM], bfr[TN];
-#pragma unroll
-        for (int mi = 0; mi < TM; ++mi) {
-          const int row = wm * WM + mi * 16 + (lane & 15);
-          af[mi] = __builtin_bit_cast(bf16x8, slot[row * KCH + (ch ^ swz<KCH>(row))]);
+        for (int ni = 0; ni < TN / 2; ++ni) {
+          const int col = n0 + wn * (WN / 2) + ni * 16 + (lane & 15);
+          if (col < N) {
+            const float g = acc[mi][ni][i], u = acc[mi][ni + TN / 2][i];
+            Cb[(size_t)row * N + col] = to_bf16(silu(g) * u);
+          }
         }
+      } else {
+        const float sc = P.scale ? P.scale[r0 + row] : 1.0f;
 #pragma unroll
         for (int ni = 0; ni < TN; ++ni) {
-          const int row = BM + brow_of[ni] + (lane & 15);
-          bfr[ni] = __builtin_bit_cast(bf16x8, slot[row * KCH + (ch ^ swz<KCH>(row))]);
-        }
-        if (MOE_MFMA_PRIO) __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int mi = 0; mi < TM; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < TN; ++ni)
-            acc[mi][ni] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
-        if (MOE_MFMA_PRIO) __builtin_amdgcn_s_setprio(0);
-      }
-    }
-
-    uint16_t* Cb = P.C + (size_t)r0 * N;
-#pragma unroll
-    for (int mi = 0; mi < TM; ++mi) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = m0 + wm * WM + mi * 16 + (lane >> 4) * 4 + i;
-        if (row >= len) continue;
-        if (MODE == 0) {
-#pragma unroll
-          for (int ni = 0; ni < TN / 2; ++ni) {
-            const int col = n0 + wn * (WN / 2) + ni * 16 + (lane & 15);
-            if (col < N) {
-              const float g = acc[mi][ni][i], u = acc[mi][ni + TN / 2][i];
-              Cb[(size_t)row * N + col] = to_bf16(silu(g) * u);
-            }
-          }
-        } else {
-          const float sc = P.scale ? P.scale[r0 + row] : 1.0f;
-#pragma unroll
-          for (int ni = 0; ni < TN; ++ni) {
-            const int col = n0 + wn * WN + ni * 16 + (lane & 15);
-            if (col < N) Cb[(size_t)row * N + col] = to_bf16(acc[mi][ni][i] * sc);
-          }
+          const int col = n0 + wn * WN + ni * 16 + (lane & 15);
+          if (col < N) Cb[(size_t)row * N + col] = to_bf16(acc[mi][ni][i] * sc);
         }
       }
     }
   }
 }
+
+// Static schedule: workgroup l (XCD-remapped) takes tiles l, l + G, l + 2G...
+template <int MODE, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES, int OCC>
+__global__ __launch_bounds__(NTHR, OCC) void gemm_ring_kernel(GemmArgs args) {
+  __shared__ u32x4 ring[RingShape<BM, BN, BK, STAGES>::RING_CH];
+  extern __shared__ int tiles_l[];
+  const int nst = args.n_seg_total;
+  for (int i = threadIdx.x; i <= nst; i += NTHR) tiles_l[i] = args.tiles[i];
+  __syncthreads();
+  const int total = tiles_l[nst];
+  const int G = gridDim.x;
+  for (int tile = xcd_logical(blockIdx.x, G); tile < total; tile += G)
+    ring_tile<MODE, BM, BN, BK, NTHR, WAVES_M, STAGES>(args, tiles_l, tile, ring);
+}
+
+
+// Ring-tile shapes: BM, BN, BK, threads, waves along M, ring stages.  "big"
+// for segments of at least MOE_BIG_ROWS rows, "mid" for the rest.
+#ifndef MOE_MID_TILE
+#define MOE_MID_TILE 128, 256, 64, 512, 2, 3   // 2 x 4 waves of 64 x 64
+#endif
+#ifndef MOE_BIG_TILE
+#define MOE_BIG_TILE 256, 256, 64, 512, 4, 2   // 4 x 2 waves of 64 x 128
+#endif
+#ifndef MOE_BIG_ROWS
+#define MOE_BIG_ROWS 256
+#endif
+template <int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
+struct TileCfg {
+  static constexpr int kRingBytes = RingShape<BM, BN, BK, STAGES>::RING_CH * 16;
+  static constexpr int kThreads = NTHR;
+  static constexpr int kBM = BM, kBN = BN, kBK = BK, kWM = WAVES_M;
+};
+#ifndef MOE_MID1_TILE
+#define MOE_MID1_TILE MOE_MID_TILE
+#endif
+#ifndef MOE_MID2_TILE
+#define MOE_MID2_TILE MOE_MID_TILE
+#endif
+using Mid1Cfg = TileCfg<MOE_MID1_TILE>;   // GEMM 1 and GEMM 2 may differ
+using Mid2Cfg = TileCfg<MOE_MID2_TILE>;
+using BigCfg = TileCfg<MOE_BIG_TILE>;
+
 
 // ---------------------------------------------------------------- fp32 path
 // One thread per output element.  GEMM 1 writes h, GEMM 2 writes y.
@@ -436,26 +508,6 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 // of the tile, so every wave issues MFMAs even on one-row segments.
 #ifndef MOE_DWAVES
 #define MOE_DWAVES 6
-#endif
-// Ring-tile shapes: BM, BN, BK, threads, waves along M, ring stages,
-// workgroups per CU.  "mid" for segments below MOE_BIG_ROWS rows, "big" for
-// the rest.
-#ifndef MOE_MID_BM
-#define MOE_MID_BM 128
-#define MOE_MID_BN 256
-#define MOE_MID_REST 64, 512, 2, 3, 1   // 2 x 4 waves of 64 x 64, 3 stages
-#define MOE_MID_RING_BYTES (3 * (128 + 256) * 128)
-#endif
-#ifndef MOE_BIG_BM
-#define MOE_BIG_BM 256
-#define MOE_BIG_BN 256
-#define MOE_BIG_REST 64, 512, 4, 2, 1   // 4 x 2 waves of 64 x 128, 2 stages
-#endif
-#define MOE_RING_MID MOE_MID_BM, MOE_MID_BN, MOE_MID_REST
-#define MOE_RING_BIG MOE_BIG_BM, MOE_BIG_BN, MOE_BIG_REST
-constexpr size_t kMidRingBytes = MOE_MID_RING_BYTES;  // static LDS of the mid ring
-#ifndef MOE_BIG_ROWS
-#define MOE_BIG_ROWS 256  // segments of at least this many rows take the big tiles
 #endif
 #ifndef MOE_DECODE_ROWS
 #define MOE_DECODE_ROWS 16  // mean rows per segment up to which the decode tiles are used
@@ -657,11 +709,11 @@ int persistent_grid(Kern kernel, size_t dyn_lds, int fallback, int threads = 256
   return g > 8 ? g : 8;
 }
 
-template <int MODE, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES, int OCC>
+template <int MODE, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
 void launch_ring(const GemmArgs& g, hipStream_t s) {
   const size_t lds_tiles = (size_t)(g.n_seg_total + 1) * sizeof(int);
-  auto k = gemm_ring_kernel<MODE, BM, BN, BK, NTHR, WAVES_M, STAGES, OCC>;
-  k<<<persistent_grid(k, lds_tiles, OCC, NTHR), NTHR, lds_tiles, s>>>(g);
+  auto k = gemm_ring_kernel<MODE, BM, BN, BK, NTHR, WAVES_M, STAGES, 1>;
+  k<<<persistent_grid(k, lds_tiles, 1, NTHR), NTHR, lds_tiles, s>>>(g);
 }
 
 }  // namespace
@@ -743,13 +795,12 @@ void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_prob
   }
   // Segments of MOE_BIG_ROWS rows or more take 256 x 256 tiles (half the
   // weight re-reads of their many row tiles), the rest 128 x 256 tiles; each
-  // shape walks its own device-built tile table, one launch per shape.
-  const bool deep_mid = lds_tiles + kMidRingBytes <= kMaxLdsBytes;
+  // shape has its own device-built tile table.
   TilePlans tp{};
-  tp.t[0] = TilePlan{0, MOE_MID_BM, MOE_MID_BN / 2, 1, MOE_BIG_ROWS, t[0]};
-  tp.t[1] = TilePlan{1, MOE_MID_BM, MOE_MID_BN, 1, MOE_BIG_ROWS, t[1]};
-  tp.t[2] = TilePlan{0, MOE_BIG_BM, MOE_BIG_BN / 2, MOE_BIG_ROWS, kAll, t[2]};
-  tp.t[3] = TilePlan{1, MOE_BIG_BM, MOE_BIG_BN, MOE_BIG_ROWS, kAll, t[3]};
+  tp.t[0] = TilePlan{0, Mid1Cfg::kBM, Mid1Cfg::kBN / 2, 1, MOE_BIG_ROWS, t[0]};
+  tp.t[1] = TilePlan{1, Mid2Cfg::kBM, Mid2Cfg::kBN, 1, MOE_BIG_ROWS, t[1]};
+  tp.t[2] = TilePlan{0, BigCfg::kBM, BigCfg::kBN / 2, MOE_BIG_ROWS, kAll, t[2]};
+  tp.t[3] = TilePlan{1, BigCfg::kBM, BigCfg::kBN, MOE_BIG_ROWS, kAll, t[3]};
   tp.n = 4;
   tile_plan_kernel<<<1, 1024, 0, s>>>(g1, g2, tp);
   MOE_DBG("tile plan");
@@ -758,16 +809,22 @@ void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_prob
   m2.tiles = t[1];
   b1.tiles = t[2];
   b2.tiles = t[3];
-  // a segment holds at most one row per token of its problem
+  // One launch per shape; the mid ring is cut to 2 stages if the 3-stage one
+  // leaves no room for its table.  A segment holds at most one row per token
+  // of its problem, so the big launch may be skipped.
+  const bool deep1 = lds_tiles + Mid1Cfg::kRingBytes <= kMaxLdsBytes;
+  const bool deep2 = lds_tiles + Mid2Cfg::kRingBytes <= kMaxLdsBytes;
   int longest = 0;
   for (int p = 0; p < n_probs; ++p) longest = probs[p].rows > longest ? probs[p].rows : longest;
   const bool any_big = longest >= MOE_BIG_ROWS && c.T >= MOE_BIG_ROWS;
-  if (deep_mid) launch_ring<0, MOE_RING_MID>(m1, s);
-  else launch_ring<0, MOE_MID_BM, MOE_MID_BN, 64, 512, 2, 2, 1>(m1, s);
-  if (any_big) launch_ring<0, MOE_RING_BIG>(b1, s);
-  if (deep_mid) launch_ring<1, MOE_RING_MID>(m2, s);
-  else launch_ring<1, MOE_MID_BM, MOE_MID_BN, 64, 512, 2, 2, 1>(m2, s);
-  if (any_big) launch_ring<1, MOE_RING_BIG>(b2, s);
+  using M1 = Mid1Cfg;
+  using M2 = Mid2Cfg;
+  if (deep1) launch_ring<0, MOE_MID1_TILE>(m1, s);
+  else launch_ring<0, M1::kBM, M1::kBN, M1::kBK, M1::kThreads, M1::kWM, 2>(m1, s);
+  if (any_big) launch_ring<0, MOE_BIG_TILE>(b1, s);
+  if (deep2) launch_ring<1, MOE_MID2_TILE>(m2, s);
+  else launch_ring<1, M2::kBM, M2::kBN, M2::kBK, M2::kThreads, M2::kWM, 2>(m2, s);
+  if (any_big) launch_ring<1, MOE_BIG_TILE>(b2, s);
   MOE_DBG("grouped gemms");
 }
 
