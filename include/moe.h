@@ -70,6 +70,10 @@ typedef struct moe_config {
   int32_t shared_I;         /* 0, or the shared expert's intermediate size */
   int32_t act_dtype;        /* moe_dtype of x, weights, x_perm, y_perm, out */
 } moe_config;
+/* Size limits (MOE_ERR_UNSUPPORTED beyond them): T*k <= 2^30; each of
+ * T*k*H, T*k*I, T*shared_I, 2*I*H and 2*shared_I*H below 2^31 elements (the
+ * kernels address every matrix with 32-bit byte offsets); bf16 needs H, I
+ * and shared_I to be multiples of 64, fp32 needs H % 4 == 0. */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* moe_status_string(moe_status s);

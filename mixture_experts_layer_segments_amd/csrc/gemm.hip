@@ -35,6 +35,7 @@ struct GemmProblem {
   const int32_t* seg_expert;   // nullable: expert 0
   const int32_t* a_rows;       // nullable: row r of the problem is row a_rows[r] of A
   int32_t n_seg, rows, N, K;
+  int32_t a_ld_rows;        // rows of the A allocation (bounds of the copy source)
   int32_t up_off;           // GEMM 1: row offset of W_up inside B
   int64_t b_stride;         // elements per expert in B
 };
@@ -181,6 +182,9 @@ __global__ __launch_bounds__(1024) void tile_plan_kernel(GemmArgs a1, GemmArgs a
 // once per fragment -- left to itself the compiler reloads one fragment at a
 // time to save registers (measured 3-6% faster on the large tiles).
 #define MOE_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+#ifndef MOE_COPY_WAVES
+#define MOE_COPY_WAVES 4
+#endif
 #ifndef MOE_SWZ8
 #define MOE_SWZ8(row) (((row) >> 1) & 7)
 #endif
@@ -214,15 +218,27 @@ __device__ __forceinline__ int swz(int row) {
   else return (row >> 2) & 3;
 }
 
-// Copy K stage kt of this wave's LPW 1 KiB blocks into its ring slot.
-template <int LPW, int NW, int STAGES, int STAGE_CH, int BK>
-__device__ __forceinline__ void ring_issue(const uint16_t* const* src, u32x4* ring, int kt,
-                                           int wv) {
+// Raw buffer resource over `bytes` bytes at `base` (word 3: the gfx9 raw
+// buffer format; loads past `bytes` return zero instead of touching memory).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Copy K stage kt of this wave's LPI 1 KiB blocks into its ring slot: block i
+// of wave w is block i * NI + w of the stage; the first A_IT of a wave's
+// blocks are A rows, the rest B rows.  `voff` holds each lane's byte offset
+// of its 16 bytes at k = 0; the stage's K offset goes in the scalar offset.
+template <int LPI, int NI, int STAGES, int STAGE_CH, int BK, int A_IT>
+__device__ __forceinline__ void ring_issue(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                           const uint32_t* voff, u32x4* ring, int kt, int wv) {
   u32x4* slot = ring + (kt % STAGES) * STAGE_CH;
+  const int koff = kt * BK * 2;
 #pragma unroll
-  for (int i = 0; i < LPW; ++i)
-    __builtin_amdgcn_global_load_lds(src[i] + kt * BK, MOE_LDS_PTR(slot + (i * NW + wv) * 64), 16,
-                                     0, 0);
+  for (int i = 0; i < LPI; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(i < A_IT ? ra : rb,
+                                             MOE_LDS_PTR(slot + (i * NI + wv) * 64), 16,
+                                             voff[i], koff, 0, 0);
 }
 
 // Ring-tile geometry shared by the per-tile body and the kernels that size
@@ -248,10 +264,16 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
   constexpr int TM = WM / 16, TN = WN / 16;
   constexpr int ROWS = BM + BN;         // A rows then B rows in one stage
   constexpr int STAGE_CH = ROWS * KCH;  // 16-byte chunks per stage
-  constexpr int LPW = ROWS / RPB / NW;  // 1 KiB copy instructions per wave per stage
+  // With 8 waves only one wave per SIMD (waves 0-3) issues the copies, so
+  // that its partner never stalls behind the copy issue and keeps the SIMD's
+  // matrix core fed.
+  constexpr int NI = (NW == 8 && MOE_COPY_WAVES == 4) ? 4 : NW;   // issuing waves
+  constexpr int LPI = ROWS / RPB / NI;  // 1 KiB copy instructions per issuing wave per stage
+  constexpr int A_IT = BM / RPB / NI;   // ... of which A rows
   static_assert(BK == 32 || BK == 64, "row piece of 64 or 128 bytes");
-  static_assert((ROWS / RPB) % NW == 0 && STAGES >= 2 && STAGES <= 6, "ring shape");
-  static_assert(LPW * (STAGES - 2) < 64, "vmcnt range");
+  static_assert((ROWS / RPB) % NI == 0 && (BM / RPB) % NI == 0, "copy blocks per wave");
+  static_assert(STAGES >= 2 && STAGES <= 6, "ring shape");
+  static_assert(LPI * (STAGES - 2) < 64, "vmcnt range");
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv / WAVES_N, wn = wv % WAVES_N;
@@ -290,26 +312,30 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
   const int K = P.K, N = P.N;
   const uint16_t* Bb = P.B + (size_t)e * P.b_stride;
 
-  // source of this lane's 16 bytes in each of the wave's copy instructions
-  const uint16_t* src[LPW];
+  // byte offset of this lane's 16 bytes at k = 0 in each of the wave's copies
+  const int wvs = __builtin_amdgcn_readfirstlane(wv);
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(P.A, (uint32_t)((size_t)P.a_ld_rows * K * 2));
+  const __amdgpu_buffer_rsrc_t rb =
+      buffer_rsrc(Bb, (uint32_t)((size_t)(MODE == 0 ? 2 * N : N) * K * 2));
+  uint32_t voff[LPI];
 #pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int row = (i * NW + wv) * RPB + lane / KCH;
+  for (int i = 0; i < LPI; ++i) {
+    const int row = (i * NI + wvs) * RPB + lane / KCH;
     const int kc = (lane % KCH) ^ swz<KCH>(row);
-    if ((i * NW + wv) * RPB < BM) {
+    int grow;   // row of A (i < A_IT) or of this expert's B
+    if (i < A_IT) {
       const int ar = r0 + min(m0 + row, len - 1);
-      src[i] = P.A + (size_t)(P.a_rows ? P.a_rows[ar] : ar) * K + kc * 8;
+      grow = P.a_rows ? P.a_rows[ar] : ar;
     } else {
       const int br = row - BM;
-      int brow;
       if (MODE == 0) {
         const int col = min(n0 + (br % (BN / 2)), N - 1);
-        brow = br < BN / 2 ? col : P.up_off + col;
+        grow = br < BN / 2 ? col : P.up_off + col;
       } else {
-        brow = min(n0 + br, N - 1);
+        grow = min(n0 + br, N - 1);
       }
-      src[i] = Bb + (size_t)brow * K + kc * 8;
     }
+    voff[i] = (uint32_t)grow * (uint32_t)(K * 2) + kc * 16;
   }
 
   f32x4 acc[TM][TN];
@@ -323,12 +349,15 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
   raw_barrier();     // every wave is done reading the ring
 #pragma unroll
   for (int st = 0; st < STAGES - 1; ++st)
-    if (st < KT) ring_issue<LPW, NW, STAGES, STAGE_CH, BK>(src, ring, st, wv);
+    if (st < KT && wvs < NI)
+      ring_issue<LPI, NI, STAGES, STAGE_CH, BK, A_IT>(ra, rb, voff, ring, st, wvs);
   for (int kt = 0; kt < KT; ++kt) {
     // stage kt has landed once only the copies of later stages remain
-    wait_stages<LPW, STAGES - 2>(min(STAGES - 2, KT - 1 - kt));
+    // (waves that issue no copies have none in flight: their wait is free)
+    wait_stages<LPI, STAGES - 2>(min(STAGES - 2, KT - 1 - kt));
     raw_barrier();
-    if (kt + STAGES - 1 < KT) ring_issue<LPW, NW, STAGES, STAGE_CH, BK>(src, ring, kt + STAGES - 1, wv);
+    if (kt + STAGES - 1 < KT && wvs < NI)
+      ring_issue<LPI, NI, STAGES, STAGE_CH, BK, A_IT>(ra, rb, voff, ring, kt + STAGES - 1, wvs);
     const u32x4* slot = ring + (kt % STAGES) * STAGE_CH;
     // Fragments of K step kk + 1 are read while the MFMAs of step kk run:
     // two register sets, and the scheduler is told to interleave the LDS
@@ -749,6 +778,7 @@ void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_prob
     a.a_rows = P.a_rows;
     a.n_seg = P.n_seg;
     a.rows = P.rows;
+    a.a_ld_rows = P.a_rows ? c.T : P.rows;   // gathered rows come from x
     a.N = P.Iw;
     a.K = H;
     a.up_off = P.Iw;
@@ -757,6 +787,7 @@ void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_prob
     b = a;
     b.A = (const uint16_t*)P.h;
     b.a_rows = nullptr;
+    b.a_ld_rows = P.rows;
     b.B = (const uint16_t*)P.w2;
     b.C = (uint16_t*)P.y;
     b.scale = P.row_scale;

@@ -84,10 +84,11 @@ moe_status check_config(const moe_config* c) {
   if (c->split_ways > kMaxWays) return MOE_ERR_UNSUPPORTED;
   if (c->shared_I < 0) return MOE_ERR_INVALID_ARG;
   if ((int64_t)c->T * c->k > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED;
-  // 32-bit element offsets inside the kernels
-  if ((int64_t)c->T * c->k * c->H >= (int64_t)1 << 32 ||
-      (int64_t)2 * c->I * c->H >= (int64_t)1 << 32 ||
-      (int64_t)2 * c->shared_I * c->H >= (int64_t)1 << 32)
+  // the kernels address each activation and weight matrix with 32-bit byte
+  // offsets: keep every one below 2^31 elements
+  const int64_t lim = (int64_t)1 << 31, A = (int64_t)c->T * c->k;
+  if (A * c->H >= lim || A * c->I >= lim || (int64_t)c->T * c->shared_I >= lim ||
+      (int64_t)2 * c->I * c->H >= lim || (int64_t)2 * c->shared_I * c->H >= lim)
     return MOE_ERR_UNSUPPORTED;
   if (c->act_dtype == MOE_DT_BF16) {
     if (c->H % 64 || c->I % 64 || c->shared_I % 64) return MOE_ERR_UNSUPPORTED;
