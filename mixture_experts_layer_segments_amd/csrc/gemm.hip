@@ -44,7 +44,9 @@ struct GemmArgs {
   GemmProblem p[2];
   int32_t n_probs;
   int32_t n_seg_total;
-  const int32_t* tiles;     // [n_seg_total + 1] exclusive prefix of tiles
+  // this launch's tiles: segments with min_len <= length < max_len, each cut
+  // into ceil(length / tile_bm) x ceil(N / tile_ncols) tiles
+  int32_t tile_bm, tile_ncols, min_len, max_len;
 };
 
 __device__ __forceinline__ void seg_range(const GemmProblem& P, int s, int& r0, int& len,
@@ -82,73 +84,55 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
 }
 
 // ---------------------------------------------------------------- tile tables
-// One table per (GEMM, tile shape): out[s] = exclusive prefix over all
-// segments of ceil(len/bm) * ceil(N/bn), counting only segments whose length
-// lies in [min_len, max_len) -- so that large segments can be tiled with one
-// shape and the rest with another.
-struct TilePlan {
-  int32_t gemm;              // 0: GEMM 1 problems, 1: GEMM 2 problems
-  int32_t bm, bn;            // rows per tile, output columns per tile
-  int32_t min_len, max_len;  // segment lengths this table covers
-  int32_t* out;              // [n_seg_total + 1]
-};
-constexpr int kMaxPlans = 4;
-struct TilePlans {
-  TilePlan t[kMaxPlans];
-  int32_t n;
-};
+// Every workgroup of a grouped-GEMM launch builds the launch's tile table in
+// its own LDS from the segment offsets at kernel start: tiles_l[g] = tiles of
+// the segments before g (an exclusive prefix), tiles_l[n] = the total.  The
+// lengths never leave the device, no separate planning launch runs, and the
+// cost is one read of the offsets (L2-resident after the first workgroup)
+// and a block scan.
+__device__ __forceinline__ int seg_tiles(const GemmArgs& a, int g) {
+  const int p = g < a.p[0].n_seg ? 0 : 1;
+  const GemmProblem& P = a.p[p];
+  const int s = g - (p ? a.p[0].n_seg : 0);
+  const int len = P.seg_offsets ? P.seg_offsets[s + 1] - P.seg_offsets[s] : P.rows;
+  if (len < a.min_len || len >= a.max_len) return 0;
+  return ((len + a.tile_bm - 1) / a.tile_bm) * ((P.N + a.tile_ncols - 1) / a.tile_ncols);
+}
 
-__global__ __launch_bounds__(1024) void tile_plan_kernel(GemmArgs a1, GemmArgs a2,
-                                                         TilePlans plans) {
-  __shared__ int v[kMaxSegments + 2];
-  __shared__ int wt[17];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int n = a1.n_seg_total;
-  for (int pl = 0; pl < plans.n; ++pl) {
-    const TilePlan& T = plans.t[pl];
-    const GemmArgs& A = T.gemm ? a2 : a1;
-    for (int g = tid; g < n; g += 1024) {
-      int p = 0, s = g;
-      if (s >= A.p[0].n_seg) {
-        p = 1;
-        s -= A.p[0].n_seg;
-      }
-      int r0, len, e;
-      seg_range(A.p[p], s, r0, len, e);
-      const bool mine = len >= T.min_len && len < T.max_len;
-      v[g] = mine ? ((len + T.bm - 1) / T.bm) * ((A.p[p].N + T.bn - 1) / T.bn) : 0;
-    }
-    __syncthreads();
-    const int per = (n + 1023) / 1024;
-    const int lo = min(n, tid * per), hi = min(n, lo + per);
-    int sum = 0;
-    for (int i = lo; i < hi; ++i) sum += v[i];
-    int incl = sum;
+// `wsum`: NTHR / 64 + 1 ints of LDS scratch.  Ends with a barrier.
+template <int NTHR>
+__device__ void build_tile_table(const GemmArgs& a, int* tiles_l, int* wsum) {
+  constexpr int NW = NTHR / 64;
+  const int n = a.n_seg_total, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int per = (n + NTHR - 1) / NTHR;
+  const int lo = min(n, tid * per), hi = min(n, lo + per);
+  int sum = 0;
+  for (int g = lo; g < hi; ++g) sum += seg_tiles(a, g);
+  int incl = sum;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(incl, off);
-      if (lane >= off) incl += o;
-    }
-    if (lane == 63) wt[wv] = incl;
-    __syncthreads();
-    if (tid == 0) {
-      int run = 0;
-      for (int w = 0; w < 16; ++w) {
-        const int t = wt[w];
-        wt[w] = run;
-        run += t;
-      }
-      wt[16] = run;
-    }
-    __syncthreads();
-    int run = wt[wv] + incl - sum;
-    for (int i = lo; i < hi; ++i) {
-      T.out[i] = run;
-      run += v[i];
-    }
-    if (tid == 0) T.out[n] = wt[16];
-    __syncthreads();
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
   }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int w = 0; w < NW; ++w) {
+      const int t = wsum[w];
+      wsum[w] = run;
+      run += t;
+    }
+    wsum[NW] = run;
+  }
+  __syncthreads();
+  int run = wsum[wv] + incl - sum;
+  for (int g = lo; g < hi; ++g) {
+    tiles_l[g] = run;
+    run += seg_tiles(a, g);
+  }
+  if (tid == 0) tiles_l[n] = wsum[NW];
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------- bf16 MFMA tiles
@@ -436,12 +420,15 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
 // Static schedule: workgroup l (XCD-remapped) takes tiles l, l + G, l + 2G...
 template <int MODE, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES, int OCC>
 __global__ __launch_bounds__(NTHR, OCC) void gemm_ring_kernel(GemmArgs args) {
-  __shared__ u32x4 ring[RingShape<BM, BN, BK, STAGES>::RING_CH];
+  // The ring and the tile table are this kernel's only LDS objects: with a
+  // third one the compiler can no longer tell the operand reads from the
+  // in-flight ring copies and waits for every copy before each stage's first
+  // read (measured 15-30% slower).  The table build's scan scratch therefore
+  // borrows the ring, which is idle until the first tile.
+  __shared__ __attribute__((aligned(1024))) u32x4 ring[RingShape<BM, BN, BK, STAGES>::RING_CH];
   extern __shared__ int tiles_l[];
-  const int nst = args.n_seg_total;
-  for (int i = threadIdx.x; i <= nst; i += NTHR) tiles_l[i] = args.tiles[i];
-  __syncthreads();
-  const int total = tiles_l[nst];
+  build_tile_table<NTHR>(args, tiles_l, reinterpret_cast<int*>(ring));
+  const int total = tiles_l[args.n_seg_total];
   const int G = gridDim.x;
   for (int tile = xcd_logical(blockIdx.x, G); tile < total; tile += G)
     ring_tile<MODE, BM, BN, BK, NTHR, WAVES_M, STAGES>(args, tiles_l, tile, ring);
@@ -550,15 +537,15 @@ void gemm_decode_kernel(GemmArgs args) {
   constexpr int KPW = BK / 32 / 4;               // MFMA K steps per wave per stage
   constexpr int TN = BN / 16;                    // n subtiles
   static_assert(KPW >= 1 && B_CH >= 1, "tile shape");
-  __shared__ u32x4 Bs[BN * KCH];
+  __shared__ __attribute__((aligned(1024))) u32x4 Bs[BN * KCH];   // swizzled rows: keep banks
   extern __shared__ int tiles_l[];
   f32x4 (*red)[TN][64] = reinterpret_cast<f32x4 (*)[TN][64]>(&Bs[0]);  // after the K loop
   static_assert(sizeof(f32x4) * 4 * TN * 64 <= sizeof(u32x4) * BN * KCH, "reduction fits");
 
+  __shared__ int wsum[256 / 64 + 1];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nst = args.n_seg_total;
-  for (int i = tid; i <= nst; i += 256) tiles_l[i] = args.tiles[i];
-  __syncthreads();
+  build_tile_table<256>(args, tiles_l, wsum);
   const int total = tiles_l[nst];
   const int G = gridDim.x;
   const int logical = xcd_logical(blockIdx.x, G);
@@ -748,7 +735,7 @@ void launch_ring(const GemmArgs& g, hipStream_t s) {
 }  // namespace
 
 void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_probs,
-                        int32_t* tiles, hipStream_t s) {
+                        hipStream_t s) {
   const int H = c.H;
   if (c.act_dtype == MOE_DT_F32) {
     for (int p = 0; p < n_probs; ++p) {
@@ -799,8 +786,6 @@ void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_prob
   }
   g1.n_probs = g2.n_probs = n_probs;
   g1.n_seg_total = g2.n_seg_total = nst;
-  int32_t* const t[kMaxPlans] = {tiles, tiles + (nst + 1), tiles + 2 * (nst + 1),
-                                 tiles + 3 * (nst + 1)};
   int max_rows = 0;
   bool k_ok = H % DBK1 == 0;
   for (int p = 0; p < n_probs; ++p) {
@@ -809,47 +794,40 @@ void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_prob
   }
   const size_t lds_tiles = (size_t)(nst + 1) * sizeof(int);
   constexpr int kAll = 0x7fffffff;
+  auto cover = [](GemmArgs g, int bm, int ncols, int min_len, int max_len) {
+    g.tile_bm = bm;
+    g.tile_ncols = ncols;
+    g.min_len = min_len;
+    g.max_len = max_len;
+    return g;
+  };
   // Few rows per segment on average: weight streaming with 16-row tiles.
   if (k_ok && (int64_t)max_rows <= (int64_t)MOE_DECODE_ROWS * nst) {
-    TilePlans tp{};
-    tp.t[0] = TilePlan{0, 16, DBN1 / 2, 1, kAll, t[0]};
-    tp.t[1] = TilePlan{1, 16, DBN2, 1, kAll, t[1]};
-    tp.n = 2;
-    tile_plan_kernel<<<1, 1024, 0, s>>>(g1, g2, tp);
-    g1.tiles = t[0];
-    g2.tiles = t[1];
     auto k1 = gemm_decode_kernel<0, DBN1, DBK1, 1, MOE_DWAVES>;
     auto k2 = gemm_decode_kernel<1, DBN2, DBK2, 1, MOE_DWAVES>;
-    k1<<<persistent_grid(k1, lds_tiles, 4), 256, lds_tiles, s>>>(g1);
-    k2<<<persistent_grid(k2, lds_tiles, 4), 256, lds_tiles, s>>>(g2);
+    k1<<<persistent_grid(k1, lds_tiles, 4), 256, lds_tiles, s>>>(cover(g1, 16, DBN1 / 2, 1, kAll));
+    k2<<<persistent_grid(k2, lds_tiles, 4), 256, lds_tiles, s>>>(cover(g2, 16, DBN2, 1, kAll));
+    MOE_DBG("grouped gemms");
     return;
   }
   // Segments of MOE_BIG_ROWS rows or more take 256 x 256 tiles (half the
-  // weight re-reads of their many row tiles), the rest 128 x 256 tiles; each
-  // shape has its own device-built tile table.
-  TilePlans tp{};
-  tp.t[0] = TilePlan{0, Mid1Cfg::kBM, Mid1Cfg::kBN / 2, 1, MOE_BIG_ROWS, t[0]};
-  tp.t[1] = TilePlan{1, Mid2Cfg::kBM, Mid2Cfg::kBN, 1, MOE_BIG_ROWS, t[1]};
-  tp.t[2] = TilePlan{0, BigCfg::kBM, BigCfg::kBN / 2, MOE_BIG_ROWS, kAll, t[2]};
-  tp.t[3] = TilePlan{1, BigCfg::kBM, BigCfg::kBN, MOE_BIG_ROWS, kAll, t[3]};
-  tp.n = 4;
-  tile_plan_kernel<<<1, 1024, 0, s>>>(g1, g2, tp);
-  MOE_DBG("tile plan");
-  GemmArgs m1 = g1, m2 = g2, b1 = g1, b2 = g2;
-  m1.tiles = t[0];
-  m2.tiles = t[1];
-  b1.tiles = t[2];
-  b2.tiles = t[3];
-  // One launch per shape; the mid ring is cut to 2 stages if the 3-stage one
-  // leaves no room for its table.  A segment holds at most one row per token
-  // of its problem, so the big launch may be skipped.
-  const bool deep1 = lds_tiles + Mid1Cfg::kRingBytes <= kMaxLdsBytes;
-  const bool deep2 = lds_tiles + Mid2Cfg::kRingBytes <= kMaxLdsBytes;
+  // weight re-reads of their many row tiles), the rest 128 x 256 tiles: one
+  // launch per shape, each covering its own segments.  The mid ring is cut
+  // to 2 stages if the 3-stage one leaves no room for the tile table.  A
+  // segment holds at most one row per token of its problem, so the big
+  // launches may be skipped.
+  using M1 = Mid1Cfg;
+  using M2 = Mid2Cfg;
+  const GemmArgs m1 = cover(g1, M1::kBM, M1::kBN / 2, 1, MOE_BIG_ROWS);
+  const GemmArgs m2 = cover(g2, M2::kBM, M2::kBN, 1, MOE_BIG_ROWS);
+  const GemmArgs b1 = cover(g1, BigCfg::kBM, BigCfg::kBN / 2, MOE_BIG_ROWS, kAll);
+  const GemmArgs b2 = cover(g2, BigCfg::kBM, BigCfg::kBN, MOE_BIG_ROWS, kAll);
+  constexpr size_t kStaticExtra = 64;   // the kernel's other static LDS (scan scratch)
+  const bool deep1 = lds_tiles + M1::kRingBytes + kStaticExtra <= kMaxLdsBytes;
+  const bool deep2 = lds_tiles + M2::kRingBytes + kStaticExtra <= kMaxLdsBytes;
   int longest = 0;
   for (int p = 0; p < n_probs; ++p) longest = probs[p].rows > longest ? probs[p].rows : longest;
   const bool any_big = longest >= MOE_BIG_ROWS && c.T >= MOE_BIG_ROWS;
-  using M1 = Mid1Cfg;
-  using M2 = Mid2Cfg;
   if (deep1) launch_ring<0, MOE_MID1_TILE>(m1, s);
   else launch_ring<0, M1::kBM, M1::kBN, M1::kBK, M1::kThreads, M1::kWM, 2>(m1, s);
   if (any_big) launch_ring<0, MOE_BIG_TILE>(b1, s);

@@ -32,7 +32,6 @@ Layout make_layout(const moe_config& c) {
   L.blk_off = take(S * nb * 4);
   L.seg_of_bin = take(nbins * 4);
   L.p_end = o;
-  L.tiles = take(4 * (S + 2) * 4);
   L.h = take(A * c.I * eb);
   L.shared_h = take((size_t)c.T * c.shared_I * eb);
   L.g_end = o;
@@ -197,7 +196,7 @@ moe_status moe_grouped_ffn(const moe_config* cfg, const void* x_perm,
   p.n_seg = num_segments(*cfg);
   p.rows = cfg->T * cfg->k;
   p.Iw = cfg->I;
-  launch_grouped_ffn(*cfg, &p, 1, (int32_t*)(ws + L.tiles), (hipStream_t)stream);
+  launch_grouped_ffn(*cfg, &p, 1, (hipStream_t)stream);
   return launch_status();
 }
 
@@ -279,7 +278,7 @@ moe_status moe_layer_forward(const moe_config* cfg, const float* logits, const v
     p[1].rows = cfg->T;
     p[1].Iw = cfg->shared_I;
   }
-  launch_grouped_ffn(*cfg, p, shared ? 2 : 1, (int32_t*)(ws + L.tiles), s);
+  launch_grouped_ffn(*cfg, p, shared ? 2 : 1, s);
   launch_combine(*cfg, ws + L.y_perm, a2r, nullptr, shared ? ws + L.shared_y : nullptr, out,
                  s);
   return launch_status();

@@ -46,10 +46,10 @@ inline int chunk_len(int64_t A) {
 inline int num_chunks(int64_t A) { return (int)((A + chunk_len(A) - 1) / chunk_len(A)); }
 
 // Offsets of the workspace regions (bytes).  P: permutation scratch;
-// G: grouped-FFN scratch (tile tables, h); L: layer intermediates.
+// G: grouped-FFN scratch (h); L: layer intermediates.
 struct Layout {
   size_t cnt_bin, blk_off, seg_of_bin, p_end;                 // region P
-  size_t tiles, h, shared_h, g_end;                           // region G
+  size_t h, shared_h, g_end;                                  // region G
   size_t y_perm, shared_y, seg_offsets, seg_expert,           // region L
       assign_to_row, row_to_token, row_w, l_end;
 };
@@ -88,9 +88,8 @@ struct FfnProblem {
   int32_t rows;           // max rows (A rows)
   int32_t Iw;             // intermediate size of this problem
 };
-// `tiles`: 4 * (total segments + 1) int32 of scratch for the tile tables.
 void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_probs,
-                        int32_t* tiles, hipStream_t s);
+                        hipStream_t s);
 void launch_combine(const moe_config& c, const void* y_perm, const int32_t* a2r,
                     const float* w, const void* shared_y, void* out, hipStream_t s);
 
