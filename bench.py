@@ -35,10 +35,10 @@ GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_segments_amd", "csrc", "gem
 # what it reads for a plain 1 GiB device copy), keyed by workload.  An entry
 # only applies while gemm.hip still has the hash it was measured with.
 MEASURED_TRAFFIC = {
-    "decode_bf16": {"gemm_src_sha256_16": "c6a263b8612806d1", "bytes": 5550795800},
-    "prefill_skew_bf16": {"gemm_src_sha256_16": "c6a263b8612806d1", "bytes": 8073820945},
-    "deepseek_v3_bf16": {"gemm_src_sha256_16": "c6a263b8612806d1", "bytes": 22972953148},
-    "ragged_stress_bf16": {"gemm_src_sha256_16": "c6a263b8612806d1", "bytes": 12891357114},
+    "decode_bf16": {"gemm_src_sha256_16": "18134e07b35f156e", "bytes": 5550901955},
+    "prefill_skew_bf16": {"gemm_src_sha256_16": "18134e07b35f156e", "bytes": 8287440312},
+    "deepseek_v3_bf16": {"gemm_src_sha256_16": "18134e07b35f156e", "bytes": 22980500232},
+    "ragged_stress_bf16": {"gemm_src_sha256_16": "18134e07b35f156e", "bytes": 13910302057},
 }
 
 
