@@ -182,6 +182,53 @@ moe_status moe_layer_forward(const moe_config* cfg, const float* logits, const v
                              float* topk_w, int32_t* counts, float* balancedness,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * FP8 expert weights (the MoE inference blog, "Communication pressure", its
+ * optimized MoE kernels: a low-precision GEMM kernel uses FP8 to cut memory
+ * and compute cost).  Format of one expert matrix W [R, C] (W13[e]: R = 2I,
+ * C = H; W2[e]: R = H, C = I):
+ *   q     [R, C] uint8, OCP E4M3 codes (OFP8: bias 7, subnormals m * 2^-9,
+ *         no infinity, largest finite 448);
+ *   scale [R/128, C/128] fp32, one power of two per 128 x 128 block;
+ *   W[r][c] = E4M3(q[r][c]) * scale[r/128][c/128].
+ * The layer then computes exactly as with bf16 weights equal to these values
+ * (they are exact in bf16); activations, h, y_perm and out stay bf16.  The
+ * FP8 calls need act_dtype bf16 and H, I, shared_I multiples of 128.
+ * ------------------------------------------------------------------------ */
+
+/* Quantize n_mat bf16 matrices [n_mat, rows, cols] (rows, cols multiples of
+ * 128) to the format above: per 128 x 128 block, scale = 2^s with s the
+ * smallest integer such that max|block| <= 448 * 2^s (s = 0 for an all-zero
+ * block), q = round-to-nearest-even E4M3 of w / 2^s (sign kept, so -0 -> 0x80).
+ *   src [n_mat, rows, cols] bf16; q [n_mat, rows, cols] out; scale
+ *   [n_mat, rows/128, cols/128] out.  16-byte aligned pointers.
+ * MOE_ERR_INVALID_ARG for bad sizes or pointers; asynchronous on `stream`. */
+moe_status moe_quantize_fp8(int32_t n_mat, int32_t rows, int32_t cols, const void* src,
+                            uint8_t* q, float* scale, void* stream);
+
+/* moe_grouped_ffn with FP8 expert weights: w13_q [E, 2I, H] + w13_scale
+ * [E, 2I/128, H/128]; w2_q [E, H, I] + w2_scale [E, H/128, I/128].  Other
+ * arguments, outputs and errors as moe_grouped_ffn. */
+moe_status moe_grouped_ffn_fp8w(const moe_config* cfg, const void* x_perm,
+                                const int32_t* seg_offsets, const int32_t* seg_expert,
+                                const uint8_t* w13_q, const float* w13_scale,
+                                const uint8_t* w2_q, const float* w2_scale,
+                                const float* row_scale, void* y_perm, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* moe_layer_forward with FP8 expert weights (routed as in
+ * moe_grouped_ffn_fp8w; shared_w13_q [2*shared_I, H] + shared_w13_scale
+ * [2*shared_I/128, H/128], shared_w2_q [H, shared_I] + shared_w2_scale
+ * [H/128, shared_I/128], all NULL when shared_I == 0). */
+moe_status moe_layer_forward_fp8w(const moe_config* cfg, const float* logits, const void* x,
+                                  const uint8_t* w13_q, const float* w13_scale,
+                                  const uint8_t* w2_q, const float* w2_scale,
+                                  const uint8_t* shared_w13_q, const float* shared_w13_scale,
+                                  const uint8_t* shared_w2_q, const float* shared_w2_scale,
+                                  void* out, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                                  float* balancedness, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,120 @@
+// FP8 expert weights: block quantization to OCP E4M3 (the MoE inference
+// blog, "Communication pressure": a low-precision GEMM kernel uses FP8 to cut
+// memory and compute cost; element format from the OCP 8-bit floating point
+// specification, E4M3: bias 7, subnormals m * 2^-9, no infinity, max 448).
+//
+// One workgroup per 128 x 128 block: the block maximum picks the power-of-two
+// scale 2^s (the smallest s with max <= 448 * 2^s), then every element is
+// rounded to the nearest E4M3 value of w / 2^s, ties to even.  All of it is
+// exact integer work on the fp32 bits (a bf16 value and a power-of-two
+// division are exact in fp32), so the codes are a pure function of the input.
+#include <math.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// E4M3 code of y (exact fp32), round to nearest even, saturating at 448.
+__device__ __forceinline__ uint32_t e4m3_rne(float y) {
+  const uint32_t b = __float_as_uint(y);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const uint32_t a = b & 0x7fffffffu;
+  const float af = __uint_as_float(a);
+  if (!(af < 448.0f)) return sign | 0x7Eu;   // 448 itself, and beyond (saturate)
+  if (af < 0.015625f) {                      // below 2^-6: quantum 2^-9
+    // af * 512 is exact and below 8; v_rndne rounds halves to even
+    return sign | (uint32_t)__builtin_rintf(af * 512.0f);
+  }
+  int E = (int)(a >> 23) - 127;              // -6 .. 8
+  uint32_t m3 = (a >> 20) & 7u;
+  const uint32_t rem = a & 0xfffffu;
+  m3 += (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) ? 1u : 0u;
+  if (m3 == 8u) {
+    m3 = 0u;
+    ++E;
+  }
+  if (E > 8 || (E == 8 && m3 == 7u)) return sign | 0x7Eu;
+  return sign | ((uint32_t)(E + 7) << 3) | m3;
+}
+
+// Smallest s with amax <= 448 * 2^s (amax finite, >= 0); 0 for amax == 0.
+// amax = (1 + m / 2^23) * 2^E and 448 = 1.75 * 2^8, so s = E - 8 when the
+// mantissa is at most 0.75 (m <= 0x600000), else E - 7.
+__device__ __forceinline__ int block_exponent(float amax) {
+  if (amax == 0.0f) return 0;
+  int adj = 0;
+  if (amax < 1.17549435e-38f) {              // fp32 subnormal: normalise exactly
+    amax *= 18446744073709551616.0f;         // 2^64
+    adj = -64;
+  }
+  const uint32_t b = __float_as_uint(amax);
+  const int E = (int)(b >> 23) - 127;
+  return E - 8 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0) + adj;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Thread t of the block's 256 handles row t / 2, columns (t % 2) * 64 .. +64.
+__global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t* __restrict__ src,
+                                                           uint8_t* __restrict__ q,
+                                                           float* __restrict__ scale, int rows,
+                                                           int cols) {
+  __shared__ float wmax[4];
+  const int bc = cols / 128, br = rows / 128;
+  const int blk = blockIdx.x;
+  const int mat = blk / (br * bc), rem = blk % (br * bc), bi = rem / bc, bj = rem % bc;
+  const int t = threadIdx.x;
+  const int row = bi * 128 + t / 2, col0 = bj * 128 + (t % 2) * 64;
+  const size_t base = ((size_t)mat * rows + row) * cols + col0;
+
+  u32x4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const u32x4*>(src + base + i * 8);
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[i][j])), fabsf(bf16_hi(v[i][j]))));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if ((t & 63) == 0) wmax[t >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const int s = block_exponent(amax);
+  if (t == 0) scale[((size_t)mat * br + bi) * bc + bj] = ldexpf(1.0f, s);
+
+  // 64 codes -> 16 words -> 4 x 16-byte stores (byte j of a word = column 4w + j)
+  uint32_t out[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; j += 2) {
+      const uint32_t c0 = e4m3_rne(ldexpf(bf16_lo(v[i][j]), -s));
+      const uint32_t c1 = e4m3_rne(ldexpf(bf16_hi(v[i][j]), -s));
+      const uint32_t c2 = e4m3_rne(ldexpf(bf16_lo(v[i][j + 1]), -s));
+      const uint32_t c3 = e4m3_rne(ldexpf(bf16_hi(v[i][j + 1]), -s));
+      out[i * 2 + j / 2] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<u32x4*>(q + base + i * 16) =
+        u32x4{out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]};
+}
+
+}  // namespace
+
+void launch_quantize_fp8(int n_mat, int rows, int cols, const void* src, uint8_t* q,
+                         float* scale, hipStream_t s) {
+  const int64_t blocks = (int64_t)n_mat * (rows / 128) * (cols / 128);
+  if (blocks == 0) return;
+  quantize_fp8_kernel<<<(unsigned)blocks, 256, 0, s>>>((const uint16_t*)src, q, scale, rows,
+                                                       cols);
+}
+
+}  // namespace moe

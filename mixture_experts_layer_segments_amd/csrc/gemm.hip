@@ -38,6 +38,8 @@ struct GemmProblem {
   int32_t a_ld_rows;        // rows of the A allocation (bounds of the copy source)
   int32_t up_off;           // GEMM 1: row offset of W_up inside B
   int64_t b_stride;         // elements per expert in B
+  const float* b_scale;     // FP8 weights: [n_w][NB/128][K/128] block scales (else unused)
+  int64_t s_stride;         // floats per expert in b_scale
 };
 
 struct GemmArgs {
@@ -81,6 +83,20 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 __device__ __forceinline__ uint16_t to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// 16 E4M3 weights (byte j of word w = element 4w + j) times their block's
+// power-of-two scale, as 16 bf16 in two 16-byte chunks (exact: an E4M3 value
+// times a power of two is a bf16 value).
+template <bool UPPER>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16(uint32_t w, float sc) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, sc, UPPER));
+}
+__device__ __forceinline__ void fp8x16_to_bf16(u32x4 src, float sc, u32x4& lo, u32x4& hi) {
+  lo = u32x4{fp8x2_to_bf16<false>(src.x, sc), fp8x2_to_bf16<true>(src.x, sc),
+             fp8x2_to_bf16<false>(src.y, sc), fp8x2_to_bf16<true>(src.y, sc)};
+  hi = u32x4{fp8x2_to_bf16<false>(src.z, sc), fp8x2_to_bf16<true>(src.z, sc),
+             fp8x2_to_bf16<false>(src.w, sc), fp8x2_to_bf16<true>(src.w, sc)};
 }
 
 // ---------------------------------------------------------------- tile tables
@@ -234,10 +250,42 @@ struct RingShape {
   static constexpr int RING_CH = STAGES * STAGE_CH;       // 16-byte chunks of the ring
 };
 
+// WF weight path: load one stage's codes (16-byte buffer loads, range-checked
+// by the expert matrix) and their block scales; dequantize them into a ring
+// slot as bf16 chunks 2*kc8 and 2*kc8 + 1 of each row.
+template <int NB8, int BK>
+__device__ __forceinline__ void load_b8(__amdgpu_buffer_rsrc_t rb, const float* Sb,
+                                        const uint32_t* off, const int* sc, int kc8, int kt,
+                                        u32x4* b8, float* s8) {
+#pragma unroll
+  for (int i = 0; i < NB8; ++i) {
+    b8[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, off[i], kt * BK, 0));
+    s8[i] = Sb[sc[i] + (kt * BK + kc8 * 16) / 128];
+  }
+}
+template <int NB8, int KCH, int STAGES, int STAGE_CH>
+__device__ __forceinline__ void store_b8(u32x4* ring, const int* dst, int kc8, int kt,
+                                         const u32x4* b8, const float* s8) {
+  u32x4* slot = ring + (kt % STAGES) * STAGE_CH;
+#pragma unroll
+  for (int i = 0; i < NB8; ++i) {
+    const int row = dst[i] / KCH;
+    u32x4 lo, hi;
+    fp8x16_to_bf16(b8[i], s8[i], lo, hi);
+    slot[dst[i] + ((2 * kc8) ^ swz<KCH>(row))] = lo;
+    slot[dst[i] + ((2 * kc8 + 1) ^ swz<KCH>(row))] = hi;
+  }
+}
+
 // One output tile (`tile` in the numbering of the tile table `tiles_l`, which
 // holds args.n_seg_total + 1 prefix entries) through the LDS ring `ring`.
 // Every thread of the workgroup calls it with the same tile.
-template <int MODE, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
+// WF = 1: the weights are E4M3 codes with 128 x 128 block scales.  Their rows
+// then skip the DMA: every thread loads its share of the next stage's weight
+// rows into registers at the start of a stage (16 codes per 16-byte load),
+// and at its end dequantizes them to bf16 (exact) into the ring, so the ring
+// and the MFMA fragments look exactly as with bf16 weights.
+template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
 __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles_l, int tile,
                                           u32x4* ring) {
   constexpr int KCH = BK / 8;           // 16-byte chunks per row piece
@@ -252,8 +300,11 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
   // that its partner never stalls behind the copy issue and keeps the SIMD's
   // matrix core fed.
   constexpr int NI = (NW == 8 && MOE_COPY_WAVES == 4) ? 4 : NW;   // issuing waves
-  constexpr int LPI = ROWS / RPB / NI;  // 1 KiB copy instructions per issuing wave per stage
+  constexpr int LPI = (WF ? BM : ROWS) / RPB / NI;  // 1 KiB copies per issuing wave per stage
   constexpr int A_IT = BM / RPB / NI;   // ... of which A rows
+  constexpr int KC8 = BK / 16;          // WF: 16-byte chunks of codes per weight row per stage
+  constexpr int NB8 = WF ? BN * KC8 / NTHR : 1;   // ... per thread
+  static_assert(!WF || (BN * KC8) % NTHR == 0, "weight chunks per thread");
   static_assert(BK == 32 || BK == 64, "row piece of 64 or 128 bytes");
   static_assert((ROWS / RPB) % NI == 0 && (BM / RPB) % NI == 0, "copy blocks per wave");
   static_assert(STAGES >= 2 && STAGES <= 6, "ring shape");
@@ -294,13 +345,14 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
   const int m0 = (first_m + lg % gm) * BM;
   const int n0 = (lg / gm) * ncols;
   const int K = P.K, N = P.N;
-  const uint16_t* Bb = P.B + (size_t)e * P.b_stride;
+  constexpr int WB = WF ? 1 : 2;        // bytes per weight
+  const uint8_t* Bb = reinterpret_cast<const uint8_t*>(P.B) + (size_t)e * P.b_stride * WB;
 
   // byte offset of this lane's 16 bytes at k = 0 in each of the wave's copies
   const int wvs = __builtin_amdgcn_readfirstlane(wv);
   const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(P.A, (uint32_t)((size_t)P.a_ld_rows * K * 2));
   const __amdgpu_buffer_rsrc_t rb =
-      buffer_rsrc(Bb, (uint32_t)((size_t)(MODE == 0 ? 2 * N : N) * K * 2));
+      buffer_rsrc(Bb, (uint32_t)((size_t)(MODE == 0 ? 2 * N : N) * K * WB));
   uint32_t voff[LPI];
 #pragma unroll
   for (int i = 0; i < LPI; ++i) {
@@ -321,6 +373,30 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
     }
     voff[i] = (uint32_t)grow * (uint32_t)(K * 2) + kc * 16;
   }
+  // WF: this thread's weight chunks -- byte offset at k = 0, block-scale
+  // index at k = 0, and the ring chunk (of two) the bf16 values go to
+  uint32_t b8off[NB8];
+  int b8sc[NB8], b8dst[NB8];
+  const float* Sb = WF ? P.b_scale + (size_t)e * P.s_stride : nullptr;
+  const int kc8 = tid % KC8;
+  if (WF) {
+#pragma unroll
+    for (int i = 0; i < NB8; ++i) {
+      const int br = (tid + NTHR * i) / KC8;
+      int grow;
+      if (MODE == 0) {
+        const int col = min(n0 + (br % (BN / 2)), N - 1);
+        grow = br < BN / 2 ? col : P.up_off + col;
+      } else {
+        grow = min(n0 + br, N - 1);
+      }
+      b8off[i] = (uint32_t)grow * (uint32_t)K + kc8 * 16;
+      b8sc[i] = (grow / 128) * (K / 128);
+      b8dst[i] = (BM + br) * KCH;
+    }
+  }
+  u32x4 b8[NB8];
+  float s8[NB8];
 
   f32x4 acc[TM][TN];
 #pragma unroll
@@ -331,16 +407,26 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
   const int KT = K / BK;
   wait_vmcnt<0>();   // this wave's earlier stores and copies are done
   raw_barrier();     // every wave is done reading the ring
+  if (WF) load_b8<NB8, BK>(rb, Sb, b8off, b8sc, kc8, 0, b8, s8);
 #pragma unroll
   for (int st = 0; st < STAGES - 1; ++st)
     if (st < KT && wvs < NI)
       ring_issue<LPI, NI, STAGES, STAGE_CH, BK, A_IT>(ra, rb, voff, ring, st, wvs);
+  if (WF) {
+    wait_vmcnt<0>();
+    store_b8<NB8, KCH, STAGES, STAGE_CH>(ring, b8dst, kc8, 0, b8, s8);
+  }
   for (int kt = 0; kt < KT; ++kt) {
     // stage kt has landed once only the copies of later stages remain
     // (waves that issue no copies have none in flight: their wait is free)
     wait_stages<LPI, STAGES - 2>(min(STAGES - 2, KT - 1 - kt));
+    if (WF) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // dequantized rows written
     raw_barrier();
-    if (kt + STAGES - 1 < KT && wvs < NI)
+    // WF: next stage's weight codes, issued before the A copies so that
+    // waiting for them leaves those copies in flight
+    if (WF && kt + 1 < KT) load_b8<NB8, BK>(rb, Sb, b8off, b8sc, kc8, kt + 1, b8, s8);
+    const bool copies = kt + STAGES - 1 < KT && wvs < NI;
+    if (copies)
       ring_issue<LPI, NI, STAGES, STAGE_CH, BK, A_IT>(ra, rb, voff, ring, kt + STAGES - 1, wvs);
     const u32x4* slot = ring + (kt % STAGES) * STAGE_CH;
     // Fragments of K step kk + 1 are read while the MFMAs of step kk run:
@@ -387,6 +473,12 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
         __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
       }
     }
+    if (WF && kt + 1 < KT) {
+      // the codes were issued before this stage's copies: wait for them only
+      if (copies) wait_vmcnt<LPI>();
+      else wait_vmcnt<0>();
+      store_b8<NB8, KCH, STAGES, STAGE_CH>(ring, b8dst, kc8, kt + 1, b8, s8);
+    }
   }
 
   uint16_t* Cb = P.C + (size_t)r0 * N;
@@ -418,7 +510,7 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
 }
 
 // Static schedule: workgroup l (XCD-remapped) takes tiles l, l + G, l + 2G...
-template <int MODE, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES, int OCC>
+template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES, int OCC>
 __global__ __launch_bounds__(NTHR, OCC) void gemm_ring_kernel(GemmArgs args) {
   // The ring and the tile table are this kernel's only LDS objects: with a
   // third one the compiler can no longer tell the operand reads from the
@@ -431,7 +523,7 @@ __global__ __launch_bounds__(NTHR, OCC) void gemm_ring_kernel(GemmArgs args) {
   const int total = tiles_l[args.n_seg_total];
   const int G = gridDim.x;
   for (int tile = xcd_logical(blockIdx.x, G); tile < total; tile += G)
-    ring_tile<MODE, BM, BN, BK, NTHR, WAVES_M, STAGES>(args, tiles_l, tile, ring);
+    ring_tile<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(args, tiles_l, tile, ring);
 }
 
 
@@ -528,12 +620,16 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 #ifndef MOE_DECODE_ROWS
 #define MOE_DECODE_ROWS 16  // mean rows per segment up to which the decode tiles are used
 #endif
-template <int MODE, int BN, int BK, int MT, int WAVES>
+// WF = 1: E4M3 weights with 128 x 128 block scales, loaded as 16-byte chunks
+// of 16 codes and dequantized (exactly) to bf16 on their way into LDS.
+template <int MODE, int WF, int BN, int BK, int MT, int WAVES>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES)))
 void gemm_decode_kernel(GemmArgs args) {
   constexpr int BM = 16 * MT;                    // rows per tile (MT subtiles of 16)
-  constexpr int KCH = BK / 8;                    // 16-byte chunks per row
-  constexpr int B_CH = BN * KCH / 256;           // chunks per thread per stage
+  constexpr int KCH = BK / 8;                    // 16-byte bf16 chunks per row
+  constexpr int LCH = WF ? BK / 16 : KCH;        // 16-byte chunks per row as loaded
+  constexpr int B_CH = BN * LCH / 256;           // loaded chunks per thread per stage
+  constexpr int WB = WF ? 1 : 2;                 // bytes per weight
   constexpr int KPW = BK / 32 / 4;               // MFMA K steps per wave per stage
   constexpr int TN = BN / 16;                    // n subtiles
   static_assert(KPW >= 1 && B_CH >= 1, "tile shape");
@@ -568,13 +664,16 @@ void gemm_decode_kernel(GemmArgs args) {
     const int m0 = (local % mt) * BM;
     const int n0 = (local / mt) * (MODE == 0 ? BN / 2 : BN);
     const int K = P.K, N = P.N;
-    const uint16_t* Bb = P.B + (size_t)e * P.b_stride;
+    const uint8_t* Bb = reinterpret_cast<const uint8_t*>(P.B) + (size_t)e * P.b_stride * WB;
+    const float* Sb = WF ? P.b_scale + (size_t)e * P.s_stride : nullptr;
 
-    // element offsets (within this expert's matrix) of this thread's chunks
+    // byte offsets (within this expert's matrix) of this thread's chunks,
+    // and (WF) the index of their block scale at k = 0
     uint32_t b_off[B_CH];
+    int b_sc[B_CH];
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
-      const int c = tid + 256 * i, row = c / KCH, kc = c % KCH;
+      const int c = tid + 256 * i, row = c / LCH, kc = c % LCH;
       int brow;
       if (MODE == 0) {
         const int col = min(n0 + (row % (BN / 2)), N - 1);
@@ -582,7 +681,8 @@ void gemm_decode_kernel(GemmArgs args) {
       } else {
         brow = min(n0 + row, N - 1);
       }
-      b_off[i] = (uint32_t)brow * (uint32_t)K + kc * 8;
+      b_off[i] = ((uint32_t)brow * (uint32_t)K + kc * (16 / WB)) * WB;
+      if (WF) b_sc[i] = (brow / 128) * (K / 128) + (kc * 16) / 128;
     }
     // this lane's activation row and its K offsets inside a stage
     bool a_ok[MT];
@@ -601,8 +701,12 @@ void gemm_decode_kernel(GemmArgs args) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[mi][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     u32x4 rb[B_CH], ra[MT][KPW];
+    float rs[B_CH];
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4*>(Bb + b_off[i]);
+    for (int i = 0; i < B_CH; ++i) {
+      rb[i] = *reinterpret_cast<const u32x4*>(Bb + b_off[i]);
+      if (WF) rs[i] = Sb[b_sc[i]];
+    }
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
@@ -614,8 +718,15 @@ void gemm_decode_kernel(GemmArgs args) {
       __syncthreads();  // everyone done with the previous stage (or tile)
 #pragma unroll
       for (int i = 0; i < B_CH; ++i) {
-        const int c = tid + 256 * i, row = c / KCH, kc = c % KCH;
-        Bs[row * KCH + (kc ^ (row & 7))] = rb[i];
+        const int c = tid + 256 * i, row = c / LCH, kc = c % LCH;
+        if (WF) {
+          u32x4 lo, hi;
+          fp8x16_to_bf16(rb[i], rs[i], lo, hi);
+          Bs[row * KCH + ((2 * kc) ^ (row & 7))] = lo;
+          Bs[row * KCH + ((2 * kc + 1) ^ (row & 7))] = hi;
+        } else {
+          Bs[row * KCH + (kc ^ (row & 7))] = rb[i];
+        }
       }
       __syncthreads();
       u32x4 ac[MT][KPW];
@@ -626,7 +737,10 @@ void gemm_decode_kernel(GemmArgs args) {
       if (kt + 1 < KT) {
         const int koff = (kt + 1) * BK;
 #pragma unroll
-        for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4*>(Bb + b_off[i] + koff);
+        for (int i = 0; i < B_CH; ++i) {
+          rb[i] = *reinterpret_cast<const u32x4*>(Bb + b_off[i] + koff * WB);
+          if (WF) rs[i] = Sb[b_sc[i] + koff / 128];
+        }
 #pragma unroll
         for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
@@ -725,11 +839,74 @@ int persistent_grid(Kern kernel, size_t dyn_lds, int fallback, int threads = 256
   return g > 8 ? g : 8;
 }
 
-template <int MODE, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
+template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
 void launch_ring(const GemmArgs& g, hipStream_t s) {
   const size_t lds_tiles = (size_t)(g.n_seg_total + 1) * sizeof(int);
-  auto k = gemm_ring_kernel<MODE, BM, BN, BK, NTHR, WAVES_M, STAGES, 1>;
+  auto k = gemm_ring_kernel<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES, 1>;
   k<<<persistent_grid(k, lds_tiles, 1, NTHR), NTHR, lds_tiles, s>>>(g);
+}
+
+}  // namespace
+
+namespace {
+
+constexpr int kAll = 0x7fffffff;
+
+GemmArgs cover(GemmArgs g, int bm, int ncols, int min_len, int max_len) {
+  g.tile_bm = bm;
+  g.tile_ncols = ncols;
+  g.min_len = min_len;
+  g.max_len = max_len;
+  return g;
+}
+
+// The bf16-activation GEMM pair for weight format WF (0: bf16, 1: E4M3 with
+// block scales).
+template <int WF>
+void launch_mfma_pair(const moe_config& c, const FfnProblem* probs, int n_probs,
+                      const GemmArgs& g1, const GemmArgs& g2, hipStream_t s) {
+  const int H = c.H, nst = g1.n_seg_total;
+  int max_rows = 0;
+  bool k_ok = H % DBK1 == 0;
+  for (int p = 0; p < n_probs; ++p) {
+    max_rows += probs[p].rows;
+    k_ok = k_ok && probs[p].Iw % DBK2 == 0;
+  }
+  const size_t lds_tiles = (size_t)(nst + 1) * sizeof(int);
+  // Few rows per segment on average: weight streaming with 16-row tiles.
+  if (k_ok && (int64_t)max_rows <= (int64_t)MOE_DECODE_ROWS * nst) {
+    auto k1 = gemm_decode_kernel<0, WF, DBN1, DBK1, 1, MOE_DWAVES>;
+    auto k2 = gemm_decode_kernel<1, WF, DBN2, DBK2, 1, MOE_DWAVES>;
+    k1<<<persistent_grid(k1, lds_tiles, 4), 256, lds_tiles, s>>>(cover(g1, 16, DBN1 / 2, 1, kAll));
+    k2<<<persistent_grid(k2, lds_tiles, 4), 256, lds_tiles, s>>>(cover(g2, 16, DBN2, 1, kAll));
+    MOE_DBG("grouped gemms");
+    return;
+  }
+  // Segments of MOE_BIG_ROWS rows or more take 256 x 256 tiles (half the
+  // weight re-reads of their many row tiles), the rest 128 x 256 tiles: one
+  // launch per shape, each covering its own segments.  The mid ring is cut
+  // to 2 stages if the 3-stage one leaves no room for the tile table.  A
+  // segment holds at most one row per token of its problem, so the big
+  // launches may be skipped.
+  using M1 = Mid1Cfg;
+  using M2 = Mid2Cfg;
+  const GemmArgs m1 = cover(g1, M1::kBM, M1::kBN / 2, 1, MOE_BIG_ROWS);
+  const GemmArgs m2 = cover(g2, M2::kBM, M2::kBN, 1, MOE_BIG_ROWS);
+  const GemmArgs b1 = cover(g1, BigCfg::kBM, BigCfg::kBN / 2, MOE_BIG_ROWS, kAll);
+  const GemmArgs b2 = cover(g2, BigCfg::kBM, BigCfg::kBN, MOE_BIG_ROWS, kAll);
+  constexpr size_t kMargin = 64;
+  const bool deep1 = lds_tiles + M1::kRingBytes + kMargin <= kMaxLdsBytes;
+  const bool deep2 = lds_tiles + M2::kRingBytes + kMargin <= kMaxLdsBytes;
+  int longest = 0;
+  for (int p = 0; p < n_probs; ++p) longest = probs[p].rows > longest ? probs[p].rows : longest;
+  const bool any_big = longest >= MOE_BIG_ROWS && c.T >= MOE_BIG_ROWS;
+  if (deep1) launch_ring<0, WF, MOE_MID1_TILE>(m1, s);
+  else launch_ring<0, WF, M1::kBM, M1::kBN, M1::kBK, M1::kThreads, M1::kWM, 2>(m1, s);
+  if (any_big) launch_ring<0, WF, MOE_BIG_TILE>(b1, s);
+  if (deep2) launch_ring<1, WF, MOE_MID2_TILE>(m2, s);
+  else launch_ring<1, WF, M2::kBM, M2::kBN, M2::kBK, M2::kThreads, M2::kWM, 2>(m2, s);
+  if (any_big) launch_ring<1, WF, MOE_BIG_TILE>(b2, s);
+  MOE_DBG("grouped gemms");
 }
 
 }  // namespace
@@ -770,6 +947,8 @@ void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_prob
     a.K = H;
     a.up_off = P.Iw;
     a.b_stride = (int64_t)2 * P.Iw * H;
+    a.b_scale = P.w13_scale;
+    a.s_stride = (int64_t)(2 * P.Iw / 128) * (H / 128);
     GemmProblem& b = g2.p[p];
     b = a;
     b.A = (const uint16_t*)P.h;
@@ -782,59 +961,14 @@ void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_prob
     b.K = P.Iw;
     b.up_off = 0;
     b.b_stride = (int64_t)H * P.Iw;
+    b.b_scale = P.w2_scale;
+    b.s_stride = (int64_t)(H / 128) * (P.Iw / 128);
     nst += P.n_seg;
   }
   g1.n_probs = g2.n_probs = n_probs;
   g1.n_seg_total = g2.n_seg_total = nst;
-  int max_rows = 0;
-  bool k_ok = H % DBK1 == 0;
-  for (int p = 0; p < n_probs; ++p) {
-    max_rows += probs[p].rows;
-    k_ok = k_ok && probs[p].Iw % DBK2 == 0;
-  }
-  const size_t lds_tiles = (size_t)(nst + 1) * sizeof(int);
-  constexpr int kAll = 0x7fffffff;
-  auto cover = [](GemmArgs g, int bm, int ncols, int min_len, int max_len) {
-    g.tile_bm = bm;
-    g.tile_ncols = ncols;
-    g.min_len = min_len;
-    g.max_len = max_len;
-    return g;
-  };
-  // Few rows per segment on average: weight streaming with 16-row tiles.
-  if (k_ok && (int64_t)max_rows <= (int64_t)MOE_DECODE_ROWS * nst) {
-    auto k1 = gemm_decode_kernel<0, DBN1, DBK1, 1, MOE_DWAVES>;
-    auto k2 = gemm_decode_kernel<1, DBN2, DBK2, 1, MOE_DWAVES>;
-    k1<<<persistent_grid(k1, lds_tiles, 4), 256, lds_tiles, s>>>(cover(g1, 16, DBN1 / 2, 1, kAll));
-    k2<<<persistent_grid(k2, lds_tiles, 4), 256, lds_tiles, s>>>(cover(g2, 16, DBN2, 1, kAll));
-    MOE_DBG("grouped gemms");
-    return;
-  }
-  // Segments of MOE_BIG_ROWS rows or more take 256 x 256 tiles (half the
-  // weight re-reads of their many row tiles), the rest 128 x 256 tiles: one
-  // launch per shape, each covering its own segments.  The mid ring is cut
-  // to 2 stages if the 3-stage one leaves no room for the tile table.  A
-  // segment holds at most one row per token of its problem, so the big
-  // launches may be skipped.
-  using M1 = Mid1Cfg;
-  using M2 = Mid2Cfg;
-  const GemmArgs m1 = cover(g1, M1::kBM, M1::kBN / 2, 1, MOE_BIG_ROWS);
-  const GemmArgs m2 = cover(g2, M2::kBM, M2::kBN, 1, MOE_BIG_ROWS);
-  const GemmArgs b1 = cover(g1, BigCfg::kBM, BigCfg::kBN / 2, MOE_BIG_ROWS, kAll);
-  const GemmArgs b2 = cover(g2, BigCfg::kBM, BigCfg::kBN, MOE_BIG_ROWS, kAll);
-  constexpr size_t kStaticExtra = 64;   // the kernel's other static LDS (scan scratch)
-  const bool deep1 = lds_tiles + M1::kRingBytes + kStaticExtra <= kMaxLdsBytes;
-  const bool deep2 = lds_tiles + M2::kRingBytes + kStaticExtra <= kMaxLdsBytes;
-  int longest = 0;
-  for (int p = 0; p < n_probs; ++p) longest = probs[p].rows > longest ? probs[p].rows : longest;
-  const bool any_big = longest >= MOE_BIG_ROWS && c.T >= MOE_BIG_ROWS;
-  if (deep1) launch_ring<0, MOE_MID1_TILE>(m1, s);
-  else launch_ring<0, M1::kBM, M1::kBN, M1::kBK, M1::kThreads, M1::kWM, 2>(m1, s);
-  if (any_big) launch_ring<0, MOE_BIG_TILE>(b1, s);
-  if (deep2) launch_ring<1, MOE_MID2_TILE>(m2, s);
-  else launch_ring<1, M2::kBM, M2::kBN, M2::kBK, M2::kThreads, M2::kWM, 2>(m2, s);
-  if (any_big) launch_ring<1, MOE_BIG_TILE>(b2, s);
-  MOE_DBG("grouped gemms");
+  if (probs[0].w_fp8) launch_mfma_pair<1>(c, probs, n_probs, g1, g2, s);
+  else launch_mfma_pair<0>(c, probs, n_probs, g1, g2, s);
 }
 
 }  // namespace moe

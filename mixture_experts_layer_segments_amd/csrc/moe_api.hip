@@ -108,6 +108,143 @@ moe_status launch_status() {
 
 using namespace moe;
 
+namespace {
+
+// Expert weights of one call: bf16 (scales NULL), or E4M3 codes with 128 x 128
+// block scales.
+struct Weights {
+  const void* w13;
+  const void* w2;
+  const float* w13_scale;
+  const float* w2_scale;
+  bool fp8;
+};
+
+// Extra requirements of FP8 weights: bf16 activations, 128-multiples, scales.
+moe_status check_fp8(const moe_config* cfg, const Weights& w) {
+  if (!w.fp8) return MOE_OK;
+  if (cfg->act_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
+  if (cfg->H % 128 || cfg->I % 128 || cfg->shared_I % 128) return MOE_ERR_UNSUPPORTED;
+  if (!w.w13_scale || !w.w2_scale) return MOE_ERR_INVALID_ARG;
+  if (!aligned(w.w13_scale, 4) || !aligned(w.w2_scale, 4)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+moe_status grouped_ffn(const moe_config* cfg, const void* x_perm, const int32_t* seg_offsets,
+                       const int32_t* seg_expert, const Weights& w, const float* row_scale,
+                       void* y_perm, void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!w.w13 || !w.w2) return MOE_ERR_INVALID_ARG;
+  if ((st = check_fp8(cfg, w)) != MOE_OK) return st;
+  if (cfg->T == 0) return MOE_OK;
+  if (!x_perm || !seg_offsets || !seg_expert || !y_perm || !workspace)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(x_perm, 16) || !aligned(w.w13, 16) || !aligned(w.w2, 16) ||
+      !aligned(y_perm, 16) || !aligned(workspace, kAlign) || !aligned(seg_offsets, 4) ||
+      !aligned(seg_expert, 4) || (row_scale && !aligned(row_scale, 4)))
+    return MOE_ERR_INVALID_ARG;
+  const Layout L = make_layout(*cfg);
+  if (workspace_bytes < L.g_end) return MOE_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  FfnProblem p{};
+  p.A = x_perm;
+  p.w13 = w.w13;
+  p.w2 = w.w2;
+  p.w_fp8 = w.fp8;
+  p.w13_scale = w.w13_scale;
+  p.w2_scale = w.w2_scale;
+  p.h = ws + L.h;
+  p.y = y_perm;
+  p.row_scale = row_scale;
+  p.seg_offsets = seg_offsets;
+  p.seg_expert = seg_expert;
+  p.n_seg = num_segments(*cfg);
+  p.rows = cfg->T * cfg->k;
+  p.Iw = cfg->I;
+  launch_grouped_ffn(*cfg, &p, 1, (hipStream_t)stream);
+  return launch_status();
+}
+
+moe_status layer_forward(const moe_config* cfg, const float* logits, const void* x,
+                         const Weights& w, const Weights& sw, void* out, int32_t* topk_ids,
+                         float* topk_w, int32_t* counts, float* balancedness, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  const bool shared = cfg->shared_I > 0;
+  if (!w.w13 || !w.w2 || (shared && (!sw.w13 || !sw.w2))) return MOE_ERR_INVALID_ARG;
+  if ((st = check_fp8(cfg, w)) != MOE_OK) return st;
+  if (shared && (st = check_fp8(cfg, sw)) != MOE_OK) return st;
+  if (cfg->T == 0) return MOE_OK;
+  if (!logits || !x || !out || !topk_ids || !topk_w || !counts || !balancedness || !workspace)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w.w13, 16) || !aligned(w.w2, 16) || !aligned(out, 16) ||
+      (shared && (!aligned(sw.w13, 16) || !aligned(sw.w2, 16))) ||
+      !aligned(workspace, kAlign) || !aligned(logits, 4) || !aligned(topk_ids, 4) ||
+      !aligned(topk_w, 4) || !aligned(counts, 4) || !aligned(balancedness, 4))
+    return MOE_ERR_INVALID_ARG;
+  const Layout L = make_layout(*cfg);
+  if (workspace_bytes < L.l_end) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  int32_t* seg_offsets = (int32_t*)(ws + L.seg_offsets);
+  int32_t* seg_expert = (int32_t*)(ws + L.seg_expert);
+  int32_t* a2r = (int32_t*)(ws + L.assign_to_row);
+  int32_t* r2t = (int32_t*)(ws + L.row_to_token);
+  float* row_w = (float*)(ws + L.row_w);
+
+  MOE_DBG("layer entry");
+  // no x_perm: GEMM 1 gathers its rows from x through row_to_token
+  if (cfg->T * cfg->k <= kSmallA) {
+    launch_route_permute_small(*cfg, logits, topk_ids, topk_w, counts, seg_offsets, seg_expert,
+                               a2r, r2t, row_w, balancedness, s);
+  } else {
+    launch_route(*cfg, logits, topk_ids, topk_w, s);
+    launch_permute(*cfg, x, topk_ids, nullptr, seg_offsets, seg_expert, a2r, r2t, counts,
+                   balancedness, topk_w, row_w, ws, L, s);
+  }
+  MOE_DBG("route + permute");
+  FfnProblem p[2]{};
+  p[0].A = x;
+  p[0].a_rows = r2t;
+  p[0].w13 = w.w13;
+  p[0].w2 = w.w2;
+  p[0].w_fp8 = w.fp8;
+  p[0].w13_scale = w.w13_scale;
+  p[0].w2_scale = w.w2_scale;
+  p[0].h = ws + L.h;
+  p[0].y = ws + L.y_perm;
+  p[0].row_scale = row_w;
+  p[0].seg_offsets = seg_offsets;
+  p[0].seg_expert = seg_expert;
+  p[0].n_seg = num_segments(*cfg);
+  p[0].rows = cfg->T * cfg->k;
+  p[0].Iw = cfg->I;
+  if (shared) {
+    p[1].A = x;
+    p[1].w13 = sw.w13;
+    p[1].w2 = sw.w2;
+    p[1].w_fp8 = sw.fp8;
+    p[1].w13_scale = sw.w13_scale;
+    p[1].w2_scale = sw.w2_scale;
+    p[1].h = ws + L.shared_h;
+    p[1].y = ws + L.shared_y;
+    p[1].row_scale = nullptr;
+    p[1].seg_offsets = nullptr;
+    p[1].seg_expert = nullptr;
+    p[1].n_seg = 1;
+    p[1].rows = cfg->T;
+    p[1].Iw = cfg->shared_I;
+  }
+  launch_grouped_ffn(*cfg, p, shared ? 2 : 1, s);
+  launch_combine(*cfg, ws + L.y_perm, a2r, nullptr, shared ? ws + L.shared_y : nullptr, out,
+                 s);
+  return launch_status();
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* moe_status_string(moe_status s) {
@@ -167,37 +304,25 @@ moe_status moe_permute(const moe_config* cfg, const void* x, const int32_t* topk
   return launch_status();
 }
 
+
 moe_status moe_grouped_ffn(const moe_config* cfg, const void* x_perm,
                            const int32_t* seg_offsets, const int32_t* seg_expert,
                            const void* w13, const void* w2, const float* row_scale,
                            void* y_perm, void* workspace, size_t workspace_bytes,
                            void* stream) {
-  moe_status st = check_config(cfg);
-  if (st != MOE_OK) return st;
-  if (cfg->T == 0) return MOE_OK;
-  if (!x_perm || !seg_offsets || !seg_expert || !w13 || !w2 || !y_perm || !workspace)
-    return MOE_ERR_INVALID_ARG;
-  if (!aligned(x_perm, 16) || !aligned(w13, 16) || !aligned(w2, 16) || !aligned(y_perm, 16) ||
-      !aligned(workspace, kAlign) || !aligned(seg_offsets, 4) || !aligned(seg_expert, 4) ||
-      (row_scale && !aligned(row_scale, 4)))
-    return MOE_ERR_INVALID_ARG;
-  const Layout L = make_layout(*cfg);
-  if (workspace_bytes < L.g_end) return MOE_ERR_WORKSPACE;
-  char* ws = (char*)workspace;
-  FfnProblem p{};
-  p.A = x_perm;
-  p.w13 = w13;
-  p.w2 = w2;
-  p.h = ws + L.h;
-  p.y = y_perm;
-  p.row_scale = row_scale;
-  p.seg_offsets = seg_offsets;
-  p.seg_expert = seg_expert;
-  p.n_seg = num_segments(*cfg);
-  p.rows = cfg->T * cfg->k;
-  p.Iw = cfg->I;
-  launch_grouped_ffn(*cfg, &p, 1, (hipStream_t)stream);
-  return launch_status();
+  return grouped_ffn(cfg, x_perm, seg_offsets, seg_expert, Weights{w13, w2, nullptr, nullptr, false},
+                     row_scale, y_perm, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_grouped_ffn_fp8w(const moe_config* cfg, const void* x_perm,
+                                const int32_t* seg_offsets, const int32_t* seg_expert,
+                                const uint8_t* w13_q, const float* w13_scale,
+                                const uint8_t* w2_q, const float* w2_scale,
+                                const float* row_scale, void* y_perm, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return grouped_ffn(cfg, x_perm, seg_offsets, seg_expert,
+                     Weights{w13_q, w2_q, w13_scale, w2_scale, true}, row_scale, y_perm,
+                     workspace, workspace_bytes, stream);
 }
 
 moe_status moe_unpermute_combine(const moe_config* cfg, const void* y_perm,
@@ -219,68 +344,34 @@ moe_status moe_layer_forward(const moe_config* cfg, const float* logits, const v
                              const void* shared_w2, void* out, int32_t* topk_ids,
                              float* topk_w, int32_t* counts, float* balancedness,
                              void* workspace, size_t workspace_bytes, void* stream) {
-  moe_status st = check_config(cfg);
-  if (st != MOE_OK) return st;
-  if (cfg->T == 0) return MOE_OK;
-  const bool shared = cfg->shared_I > 0;
-  if (!logits || !x || !w13 || !w2 || !out || !topk_ids || !topk_w || !counts ||
-      !balancedness || !workspace || (shared && (!shared_w13 || !shared_w2)))
-    return MOE_ERR_INVALID_ARG;
-  if (!aligned(x, 16) || !aligned(w13, 16) || !aligned(w2, 16) || !aligned(out, 16) ||
-      (shared && (!aligned(shared_w13, 16) || !aligned(shared_w2, 16))) ||
-      !aligned(workspace, kAlign) || !aligned(logits, 4) || !aligned(topk_ids, 4) ||
-      !aligned(topk_w, 4) || !aligned(counts, 4) || !aligned(balancedness, 4))
-    return MOE_ERR_INVALID_ARG;
-  const Layout L = make_layout(*cfg);
-  if (workspace_bytes < L.l_end) return MOE_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  int32_t* seg_offsets = (int32_t*)(ws + L.seg_offsets);
-  int32_t* seg_expert = (int32_t*)(ws + L.seg_expert);
-  int32_t* a2r = (int32_t*)(ws + L.assign_to_row);
-  int32_t* r2t = (int32_t*)(ws + L.row_to_token);
-  float* row_w = (float*)(ws + L.row_w);
+  return layer_forward(cfg, logits, x, Weights{w13, w2, nullptr, nullptr, false},
+                       Weights{shared_w13, shared_w2, nullptr, nullptr, false}, out, topk_ids,
+                       topk_w, counts, balancedness, workspace, workspace_bytes, stream);
+}
 
-  MOE_DBG("layer entry");
-  // no x_perm: GEMM 1 gathers its rows from x through row_to_token
-  if (cfg->T * cfg->k <= kSmallA) {
-    launch_route_permute_small(*cfg, logits, topk_ids, topk_w, counts, seg_offsets, seg_expert,
-                               a2r, r2t, row_w, balancedness, s);
-  } else {
-    launch_route(*cfg, logits, topk_ids, topk_w, s);
-    launch_permute(*cfg, x, topk_ids, nullptr, seg_offsets, seg_expert, a2r, r2t, counts,
-                   balancedness, topk_w, row_w, ws, L, s);
-  }
-  MOE_DBG("route + permute");
-  FfnProblem p[2]{};
-  p[0].A = x;
-  p[0].a_rows = r2t;
-  p[0].w13 = w13;
-  p[0].w2 = w2;
-  p[0].h = ws + L.h;
-  p[0].y = ws + L.y_perm;
-  p[0].row_scale = row_w;
-  p[0].seg_offsets = seg_offsets;
-  p[0].seg_expert = seg_expert;
-  p[0].n_seg = num_segments(*cfg);
-  p[0].rows = cfg->T * cfg->k;
-  p[0].Iw = cfg->I;
-  if (shared) {
-    p[1].A = x;
-    p[1].w13 = shared_w13;
-    p[1].w2 = shared_w2;
-    p[1].h = ws + L.shared_h;
-    p[1].y = ws + L.shared_y;
-    p[1].row_scale = nullptr;
-    p[1].seg_offsets = nullptr;
-    p[1].seg_expert = nullptr;
-    p[1].n_seg = 1;
-    p[1].rows = cfg->T;
-    p[1].Iw = cfg->shared_I;
-  }
-  launch_grouped_ffn(*cfg, p, shared ? 2 : 1, s);
-  launch_combine(*cfg, ws + L.y_perm, a2r, nullptr, shared ? ws + L.shared_y : nullptr, out,
-                 s);
+moe_status moe_layer_forward_fp8w(const moe_config* cfg, const float* logits, const void* x,
+                                  const uint8_t* w13_q, const float* w13_scale,
+                                  const uint8_t* w2_q, const float* w2_scale,
+                                  const uint8_t* shared_w13_q, const float* shared_w13_scale,
+                                  const uint8_t* shared_w2_q, const float* shared_w2_scale,
+                                  void* out, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                                  float* balancedness, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  return layer_forward(cfg, logits, x, Weights{w13_q, w2_q, w13_scale, w2_scale, true},
+                       Weights{shared_w13_q, shared_w2_q, shared_w13_scale, shared_w2_scale, true},
+                       out, topk_ids, topk_w, counts, balancedness, workspace, workspace_bytes,
+                       stream);
+}
+
+moe_status moe_quantize_fp8(int32_t n_mat, int32_t rows, int32_t cols, const void* src,
+                            uint8_t* q, float* scale, void* stream) {
+  if (n_mat < 0 || rows <= 0 || cols <= 0 || rows % 128 || cols % 128)
+    return MOE_ERR_INVALID_ARG;
+  if ((int64_t)rows * cols >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  if (n_mat == 0) return MOE_OK;
+  if (!src || !q || !scale || !aligned(src, 16) || !aligned(q, 16) || !aligned(scale, 4))
+    return MOE_ERR_INVALID_ARG;
+  launch_quantize_fp8(n_mat, rows, cols, src, q, scale, (hipStream_t)stream);
   return launch_status();
 }
 

@@ -87,9 +87,15 @@ struct FfnProblem {
   int32_t n_seg;          // segments (1 for shared)
   int32_t rows;           // max rows (A rows)
   int32_t Iw;             // intermediate size of this problem
+  int32_t w_fp8;          // 1: w13 / w2 are E4M3 codes with the block scales below
+  const float* w13_scale; // [n_w, 2*Iw/128, K1/128] (w_fp8 only)
+  const float* w2_scale;  // [n_w, K1/128, Iw/128]
 };
 void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_probs,
                         hipStream_t s);
+// FP8 weights: block-quantize n_mat bf16 matrices [rows, cols] (multiples of 128).
+void launch_quantize_fp8(int n_mat, int rows, int cols, const void* src, uint8_t* q,
+                         float* scale, hipStream_t s);
 void launch_combine(const moe_config& c, const void* y_perm, const int32_t* a2r,
                     const float* w, const void* shared_y, void* out, hipStream_t s);
 

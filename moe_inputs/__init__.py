@@ -46,6 +46,8 @@ class MoEShape:
     k: int                      # experts per token
     I: int                      # expert intermediate size
     dtype: str = "bf16"         # "f32" or "bf16": x, weights and outputs
+    weights: str = "native"     # "native" (weights in dtype) or "fp8": the library
+                                # block-quantizes the drawn bf16 weights to E4M3
     score: str = "softmax"      # "softmax" (flat) or "sigmoid" (grouped)
     n_group: int = 1            # expert groups (contiguous blocks of E/n_group)
     topk_group: int = 1         # groups kept per token
@@ -90,6 +92,12 @@ WORKLOADS = {
     "ragged_stress_bf16": MoEShape("ragged_stress_bf16", T=16384, H=4096, E=128, k=8, I=1536,
                                    zipf_s=1.5, n_hot_split=8, split_ways=2, seed=105),
 }
+# The same layers with FP8 (E4M3, 128 x 128 block-scaled) expert weights: the
+# weights are drawn exactly as above and quantized by the code under test
+# (the library) or by the oracle, each on its own.
+for _n in ("decode", "prefill_skew", "deepseek_v3", "ragged_stress"):
+    _b = WORKLOADS[_n + "_bf16"]
+    WORKLOADS[_n + "_fp8w"] = dataclasses.replace(_b, name=_n + "_fp8w", weights="fp8")
 
 
 def _rng(cfg: MoEShape, tensor_id: int, expert_id: int = 0) -> np.random.Generator:

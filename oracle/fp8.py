@@ -84,22 +84,27 @@ def block_exponent(amax: float) -> int:
     return s
 
 
+def block_exponents(amax) -> np.ndarray:
+    """block_exponent of every element of amax (vectorised): with
+    amax = f * 2^E, f in [0.5, 1), 448 * 2^s >= amax first holds at
+    s = E - 9 when f <= 0.875 (448 = 0.875 * 2^9), else at s = E - 8."""
+    a = np.asarray(amax, dtype=np.float64)
+    f, E = np.frexp(a)
+    s = E.astype(np.int64) - 9 + (f > 0.875)
+    return np.where(a == 0.0, 0, s)
+
+
 def quantize_blocks(w, block: int = BLOCK):
     """Codes uint8 [R, K] and power-of-two scales float64 [R/block, K/block]
     of one matrix w [R, K] (R and K multiples of ``block``)."""
     w = np.asarray(w, dtype=np.float64)
     R, K = w.shape
     assert R % block == 0 and K % block == 0, (R, K)
-    codes = np.empty((R, K), dtype=np.uint8)
-    scales = np.empty((R // block, K // block), dtype=np.float64)
-    for bi in range(R // block):
-        for bj in range(K // block):
-            blk = w[bi * block:(bi + 1) * block, bj * block:(bj + 1) * block]
-            s = block_exponent(float(np.max(np.abs(blk))))
-            scales[bi, bj] = 2.0 ** s
-            codes[bi * block:(bi + 1) * block, bj * block:(bj + 1) * block] = \
-                e4m3_encode(blk / 2.0 ** s)
-    return codes, scales
+    blocks = w.reshape(R // block, block, K // block, block)
+    s = block_exponents(np.abs(blocks).max(axis=(1, 3)))            # [R/b, K/b]
+    scaled = np.ldexp(blocks, -s[:, None, :, None])                 # exact
+    codes = e4m3_encode(scaled).reshape(R, K)
+    return codes, np.ldexp(1.0, s).astype(np.float64)
 
 
 def dequantize_blocks(codes, scales, block: int = BLOCK) -> np.ndarray:

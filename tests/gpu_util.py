@@ -7,6 +7,7 @@ import numpy as np
 import torch
 
 import moe_inputs as mi
+from oracle import fp8 as ofp8
 from oracle import moe_oracle as orc
 
 BF16_REL = 1.5e-2   # max|gpu - oracle| <= BF16_REL * max|oracle|  (bf16 layers)
@@ -60,6 +61,21 @@ class SmallCase:
         f = lambda a: None if a is None else mi.values_f64(a, cfg.dtype)  # noqa: E731
         self.x64, self.w13_64, self.w2_64 = f(self.xb), f(self.w13b), f(self.w2b)
         self.sw13_64, self.sw2_64 = f(self.sw13b), f(self.sw2b)
+        if cfg.weights == "fp8":
+            # the oracle quantizes the same drawn weights itself and runs the
+            # layer on the dequantized values
+            self.q = {}
+            for name in ("w13", "w2", "sw13", "sw2"):
+                w = getattr(self, name + "_64")
+                if w is None:
+                    continue
+                mats = w if w.ndim == 3 else w[None]
+                qs = [ofp8.quantize_blocks(m) for m in mats]
+                codes = np.stack([c for c, _ in qs])
+                scales = np.stack([sc for _, sc in qs])
+                self.q[name] = (codes, scales)
+                deq = np.stack([ofp8.dequantize_blocks(c, sc) for c, sc in qs])
+                setattr(self, name + "_64", deq if w.ndim == 3 else deq[0])
         self.ref = orc.layer_forward(cfg, self.logits, self.x64, self.w13_64, self.w2_64,
                                      self.sw13_64, self.sw2_64)
 
@@ -74,14 +90,43 @@ class SmallCase:
         return d
 
 
+def quantize_fp8(moe, w):
+    """The library's block quantizer on a device bf16 tensor [.., R, C]:
+    (codes uint8, scales fp32)."""
+    if w is None:
+        return None, None
+    q = torch.empty(w.shape, dtype=torch.uint8, device=dev())
+    sc = torch.empty(w.shape[:-2] + (w.shape[-2] // 128, w.shape[-1] // 128),
+                     dtype=torch.float32, device=dev())
+    moe.moe_quantize_fp8(w, q, sc)
+    return q, sc
+
+
+def fp8_weights(moe, d):
+    """Device inputs d with bf16 weights -> the same with FP8 codes + scales."""
+    out = dict(d)
+    for name in ("w13", "w2", "sw13", "sw2"):
+        out[name], out[name + "_s"] = quantize_fp8(moe, d[name])
+    torch.cuda.synchronize()
+    return out
+
+
 def run_layer(moe, cfg, d):
-    """moe_layer_forward on device inputs d; returns its outputs."""
+    """moe_layer_forward (or, for FP8 weights, moe_layer_forward_fp8w with
+    the library's own quantization of d's weights) on device inputs d."""
     o = dict(out=empty((cfg.T, cfg.H), tdtype(cfg)), ids=empty((cfg.T, cfg.k), torch.int32),
              w=empty((cfg.T, cfg.k), torch.float32), counts=empty((cfg.E,), torch.int32),
              bal=empty((1,), torch.float32))
     ws = empty((moe.moe_workspace_size(cfg),), torch.uint8)
-    moe.moe_layer_forward(cfg, d["logits"], d["x"], d["w13"], d["w2"], d["sw13"], d["sw2"],
-                          o["out"], o["ids"], o["w"], o["counts"], o["bal"], ws)
+    if cfg.weights == "fp8":
+        q = fp8_weights(moe, d)
+        o["q"] = q
+        moe.moe_layer_forward_fp8w(cfg, d["logits"], d["x"], q["w13"], q["w13_s"], q["w2"],
+                                   q["w2_s"], q["sw13"], q["sw13_s"], q["sw2"], q["sw2_s"],
+                                   o["out"], o["ids"], o["w"], o["counts"], o["bal"], ws)
+    else:
+        moe.moe_layer_forward(cfg, d["logits"], d["x"], d["w13"], d["w2"], d["sw13"], d["sw2"],
+                              o["out"], o["ids"], o["w"], o["counts"], o["bal"], ws)
     torch.cuda.synchronize()
     return o
 

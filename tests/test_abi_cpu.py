@@ -22,7 +22,7 @@ def moe():
 def _declared():
     with open(os.path.join(ROOT, "include", "moe.h")) as f:
         text = f.read()
-    return sorted(set(re.findall(r"^\S.*?\b(moe_[a-z_]+)\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\S.*?\b(moe_[a-z0-9_]+)\(", text, flags=re.M)))
 
 
 def test_exports_every_declared_symbol(moe):
@@ -121,3 +121,30 @@ def test_config_struct_matches_header(moe):
     fields = re.findall(r"int32_t\s+([^;]+);", body)
     names = [n.strip() for grp in fields for n in grp.split(",")]
     assert names == [f for f, _ in moe.MoEConfig._fields_]
+
+
+def test_fp8_calls_validate_before_launching(moe):
+    """The FP8 entry points reject bad sizes and pointers on the host."""
+    bf = mi.WORKLOADS["decode_bf16"]
+    lib = moe.lib
+    c = moe.make_config(bf)
+    ws = moe.moe_workspace_size(c)
+    args = [FAKE] * 8 + [None] + [FAKE, FAKE, ws, None]
+    # quantizer: sizes must be positive multiples of 128
+    assert lib.moe_quantize_fp8(1, 100, 128, FAKE, FAKE, FAKE, None) == -1
+    assert lib.moe_quantize_fp8(1, 128, 0, FAKE, FAKE, FAKE, None) == -1
+    assert lib.moe_quantize_fp8(-1, 128, 128, FAKE, FAKE, FAKE, None) == -1
+    assert lib.moe_quantize_fp8(0, 128, 128, None, None, None, None) == 0
+    assert lib.moe_quantize_fp8(1, 128, 128, None, FAKE, FAKE, None) == -1
+    # grouped FFN: bf16 activations only, 128-multiples, scales required
+    f32 = moe.make_config(bf.replace(dtype="f32"))
+    assert lib.moe_grouped_ffn_fp8w(ctypes.byref(f32), *args[:3], FAKE, FAKE, FAKE, FAKE,
+                                    None, FAKE, FAKE, ws, None) == -2
+    odd = moe.make_config(bf.replace(I=192))
+    assert lib.moe_grouped_ffn_fp8w(ctypes.byref(odd), *args[:3], FAKE, FAKE, FAKE, FAKE,
+                                    None, FAKE, FAKE, ws, None) == -2
+    assert lib.moe_grouped_ffn_fp8w(ctypes.byref(c), *args[:3], FAKE, None, FAKE, FAKE,
+                                    None, FAKE, FAKE, ws, None) == -1
+    assert lib.moe_layer_forward_fp8w(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                      None, None, None, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      FAKE, ws, None) == -1

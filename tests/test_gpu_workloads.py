@@ -6,12 +6,17 @@ Routing ids, expert counts, balancedness and the whole permutation
 oracle bit for bit over the full batch.  The layer output and the grouped-FFN
 rows are compared on a sample of tokens (first, last, random, tokens of the
 hottest expert and of both replicas of a split expert), each computed by the
-oracle from the definition out[t] = sum_j w_tj SwiGLU_e(x_t) (+ shared)."""
+oracle from the definition out[t] = sum_j w_tj SwiGLU_e(x_t) (+ shared).
+The FP8-weight variants run the same layers through moe_layer_forward_fp8w
+with the library's own quantization of the drawn weights; the oracle
+quantizes the same weights itself (their codes are compared bit for bit for
+every expert the sample needs) and computes with the dequantized values."""
 import numpy as np
 import pytest
 import torch
 
 import moe_inputs as mi
+from oracle import fp8 as ofp8
 from oracle import moe_oracle as orc
 from tests import gpu_util as gu
 
@@ -20,7 +25,8 @@ pytestmark = pytest.mark.gpu
 
 def _sample_tokens(cfg, ids, rng):
     T = cfg.T
-    toks = {0, T - 1} | set(rng.choice(T, size=min(T, 10), replace=False).tolist())
+    n_rand = 10 if cfg.weights != "fp8" else 3     # FP8: the oracle quantizes each expert needed
+    toks = {0, T - 1} | set(rng.choice(T, size=min(T, n_rand), replace=False).tolist())
     counts = np.bincount(ids.ravel(), minlength=cfg.E)
     hot = int(np.argmax(counts))
     users = np.nonzero((ids == hot).any(axis=1))[0]
@@ -32,7 +38,8 @@ def _sample_tokens(cfg, ids, rng):
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["tiny_fp32", "decode_bf16", "prefill_skew_bf16",
-                                  "ragged_stress_bf16", "deepseek_v3_bf16"])
+                                  "ragged_stress_bf16", "deepseek_v3_bf16", "decode_fp8w",
+                                  "prefill_skew_fp8w", "ragged_stress_fp8w", "deepseek_v3_fp8w"])
 def test_workload_full_size(name):
     import mixture_experts_layer_segments_amd as moe
     cfg = mi.WORKLOADS[name]
@@ -54,13 +61,24 @@ def test_workload_full_size(name):
     w13_d = torch.empty((cfg.E, 2 * cfg.I, cfg.H), dtype=tdt, device=dev)
     w2_d = torch.empty((cfg.E, cfg.H, cfg.I), dtype=tdt, device=dev)
     y_ref = {}   # (i, j) -> oracle expert output row (unweighted)
+    codes_ref = {}   # FP8: expert -> oracle codes and scales of (w13, w2)
+
+    def weights64(a, b):
+        a64, b64 = mi.values_f64(a, cfg.dtype), mi.values_f64(b, cfg.dtype)
+        if cfg.weights != "fp8":
+            return a64, b64, None
+        qa, qb = ofp8.quantize_blocks(a64), ofp8.quantize_blocks(b64)
+        return ofp8.dequantize_blocks(*qa), ofp8.dequantize_blocks(*qb), (qa, qb)
 
     def put(e, a, b):
         w13_d[e].copy_(gu.to_dev(a, cfg.dtype))
         w2_d[e].copy_(gu.to_dev(b, cfg.dtype))
         if e in need:
             rows = [i for i, _ in need[e]]
-            y = orc.swiglu(x64_s[rows], mi.values_f64(a, cfg.dtype), mi.values_f64(b, cfg.dtype))
+            a64, b64, q = weights64(a, b)
+            if q is not None:
+                codes_ref[e] = q
+            y = orc.swiglu(x64_s[rows], a64, b64)
             for n, (i, j) in enumerate(need[e]):
                 y_ref[(i, j)] = y[n]
 
@@ -73,12 +91,21 @@ def test_workload_full_size(name):
              w2=w2_d, sw13=None, sw2=None)
     if cfg.shared_I:
         s13, s2 = mi.shared_w13(cfg), mi.shared_w2(cfg)
-        out_ref += orc.swiglu(x64_s, mi.values_f64(s13, cfg.dtype), mi.values_f64(s2, cfg.dtype))
+        a64, b64, _ = weights64(s13, s2)
+        out_ref += orc.swiglu(x64_s, a64, b64)
         d["sw13"], d["sw2"] = gu.to_dev(s13, cfg.dtype), gu.to_dev(s2, cfg.dtype)
     torch.cuda.synchronize()
 
     print(f"[workload] {name}: layer forward", flush=True)
     o = gu.run_layer(moe, cfg, d)
+    if cfg.weights == "fp8":
+        q = o["q"]
+        for e, (qa, qb) in codes_ref.items():
+            assert np.array_equal(q["w13"][e].cpu().numpy(), qa[0]), f"w13 codes of expert {e}"
+            assert np.array_equal(q["w13_s"][e].cpu().numpy().astype(np.float64), qa[1]), e
+            assert np.array_equal(q["w2"][e].cpu().numpy(), qb[0]), f"w2 codes of expert {e}"
+            assert np.array_equal(q["w2_s"][e].cpu().numpy().astype(np.float64), qb[1]), e
+        print(f"[workload] {name}: codes of {len(codes_ref)} experts match", flush=True)
     ids_g = o["ids"].cpu().numpy()
     mism = gu.check_routing(cfg, ids_g, o["w"].cpu().numpy(), ids_r, w_r, gap, logits)
     assert (o["counts"].cpu().numpy() == plan_r["counts"]).all()
@@ -104,8 +131,13 @@ def test_workload_full_size(name):
                            xs.view(torch.int16) if cfg.dtype == "bf16" else xs)
         y = torch.empty_like(g["x_perm"])
         ws = gu.empty((moe.moe_workspace_size(cfg),), torch.uint8)
-        moe.moe_grouped_ffn(cfg, g["x_perm"], g["seg_offsets"], g["seg_expert"], w13_d, w2_d,
-                            None, y, ws)
+        if cfg.weights == "fp8":
+            q = o["q"]
+            moe.moe_grouped_ffn_fp8w(cfg, g["x_perm"], g["seg_offsets"], g["seg_expert"],
+                                     q["w13"], q["w13_s"], q["w2"], q["w2_s"], None, y, ws)
+        else:
+            moe.moe_grouped_ffn(cfg, g["x_perm"], g["seg_offsets"], g["seg_expert"], w13_d,
+                                w2_d, None, y, ws)
         torch.cuda.synchronize()
         yg = gu.host_f64(y[rows]).reshape(len(toks), cfg.k, cfg.H)
         yr = np.stack([np.stack([y_ref[(i, j)] for j in range(cfg.k)]) for i in range(len(toks))])

@@ -101,6 +101,15 @@ def test_block_exponent_definition():
         assert fp8.block_exponent(float(a)) == _brute_exponent(float(a)), a
 
 
+def test_vectorised_exponents_follow_the_definition():
+    rng = np.random.default_rng(4)
+    a = np.concatenate([np.exp(rng.uniform(-60, 60, 2000)), 448.0 * 2.0 ** np.arange(-40, 40),
+                        np.nextafter(448.0 * 2.0 ** np.arange(-40, 40), np.inf),
+                        np.nextafter(448.0 * 2.0 ** np.arange(-40, 40), 0), [0.0]])
+    got = fp8.block_exponents(a)
+    assert all(int(g) == (0 if x == 0 else _brute_exponent(float(x))) for g, x in zip(got, a))
+
+
 def test_block_quantization_uses_the_range_and_bounds_the_error():
     rng = np.random.default_rng(11)
     w = rng.normal(0, 0.02, size=(256, 384))
@@ -141,12 +150,14 @@ def test_zero_block():
 # ------------------------------------------------------------ planted mistakes
 PINS = [test_finite_codes_are_distinct_monotone_and_round_trip, test_midpoints_round_to_even_codes,
         test_nearest_value_by_brute_force, test_saturation, test_block_exponent_definition,
+        test_vectorised_exponents_follow_the_definition,
         test_block_quantization_uses_the_range_and_bounds_the_error,
         test_exact_reconstruction_of_e4m3_matrices, test_zero_block,
         lambda: [test_ofp8_table_values(c, v) for c, v in
                  [(0x01, 2.0 ** -9), (0x08, 2.0 ** -6), (0x38, 1.0), (0x7E, 448.0), (0x77, 240.0)]]]
 
 _orig_encode, _orig_decode, _orig_exp = fp8.e4m3_encode, fp8.e4m3_decode, fp8.block_exponent
+_orig_exps = fp8.block_exponents
 
 
 def _ties_away(y):
@@ -166,6 +177,10 @@ def _bias8_decode(codes):
 
 def _floor_exponent(amax):
     return 0 if amax == 0 else math.floor(math.log2(amax / 448.0))
+
+
+def _exponents_off_by_one(amax):
+    return _orig_exps(amax) - 1
 
 
 def _truncate(y):
@@ -188,8 +203,10 @@ def _planted(name, fn):
 
 @pytest.mark.parametrize("name,fn", [("e4m3_encode", _ties_away), ("e4m3_decode", _bias8_decode),
                                      ("block_exponent", _floor_exponent),
-                                     ("e4m3_encode", _truncate)],
-                         ids=["ties_away", "bias8_decode", "floor_exponent", "truncate"])
+                                     ("e4m3_encode", _truncate),
+                                     ("block_exponents", _exponents_off_by_one)],
+                         ids=["ties_away", "bias8_decode", "floor_exponent", "truncate",
+                              "exponents_off_by_one"])
 def test_planted_mistake_is_caught(name, fn):
     failed = 0
     with _planted(name, fn):
