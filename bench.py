@@ -73,15 +73,24 @@ def ffn_flops(cfg) -> int:
     return 6 * cfg.H * cfg.I * cfg.A + 6 * cfg.H * cfg.shared_I * cfg.T
 
 
+def weight_bytes(cfg, n: int) -> int:
+    """Bytes of n expert matrices of n x H elements: 1 byte per E4M3 code
+    plus a 4-byte scale per 128 x 128 block for FP8 weights, else the
+    activation element size."""
+    if cfg.weights == "fp8":
+        return n * cfg.H + (n * cfg.H // (128 * 128)) * 4
+    return n * cfg.H * cfg.elem_bytes
+
+
 def ffn_bytes(cfg, active_experts: int) -> int:
     """Algorithmic HBM bytes of the grouped FFN: the weights of every active
     expert read once, x_perm read, h written and read, y_perm written (and the
     shared expert's weights and rows)."""
     eb = cfg.elem_bytes
-    w = active_experts * 3 * cfg.H * cfg.I * eb
+    w = active_experts * weight_bytes(cfg, 3 * cfg.I)
     act = cfg.A * (cfg.H * 2 + cfg.I * 2) * eb
     if cfg.shared_I:
-        w += 3 * cfg.H * cfg.shared_I * eb
+        w += weight_bytes(cfg, 3 * cfg.shared_I)
         act += cfg.T * (cfg.H * 2 + cfg.shared_I * 2) * eb
     return w + act
 
@@ -110,6 +119,23 @@ def device_inputs(cfg):
     if cfg.shared_I:
         d["sw13"] = up(mi.shared_w13(cfg)).to(dev)
         d["sw2"] = up(mi.shared_w2(cfg)).to(dev)
+    if cfg.weights == "fp8":
+        # the library's block quantizer, outside any timed region; the bf16
+        # weights are dropped afterwards
+        import mixture_experts_layer_segments_amd as moe
+        for name in ("w13", "w2", "sw13", "sw2"):
+            w = d[name]
+            d[name + "_s"] = None
+            if w is None:
+                continue
+            q = torch.empty(w.shape, dtype=torch.uint8, device=dev)
+            sc = torch.empty(w.shape[:-2] + (w.shape[-2] // 128, w.shape[-1] // 128),
+                             dtype=torch.float32, device=dev)
+            moe.moe_quantize_fp8(w, q, sc)
+            d[name], d[name + "_s"] = q, sc
+            del w
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     torch.cuda.synchronize()
     return d
 
@@ -124,6 +150,7 @@ def cpu_baseline(cfg, logits, budget_s=20.0):
     is scaled to all active experts."""
     from threadpoolctl import threadpool_limits
 
+    from oracle import fp8 as ofp8
     from oracle import moe_oracle as orc
     threads = max(1, min(16, os.cpu_count() or 1))
     with threadpool_limits(limits=threads):
@@ -144,6 +171,9 @@ def cpu_baseline(cfg, logits, budget_s=20.0):
             if t_ffn[0] > budget_s:
                 return
             w13, w2 = mi.values_f64(a, cfg.dtype), mi.values_f64(b, cfg.dtype)
+            if cfg.weights == "fp8":   # the oracle's own quantization, untimed like generation
+                w13 = ofp8.dequantize_blocks(*ofp8.quantize_blocks(w13))
+                w2 = ofp8.dequantize_blocks(*ofp8.quantize_blocks(w2))
             t1 = time.perf_counter()
             for s in np.nonzero(seg_exp == e)[0]:
                 r0, r1 = int(seg_off[s]), int(seg_off[s + 1])
@@ -165,7 +195,8 @@ def cpu_baseline(cfg, logits, budget_s=20.0):
              f"scaled by {n}/{len(done)}")
     return {"value": cfg.T / est, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": (f"{cfg.name}: float64 numpy oracle, routing + permutation + combine of all "
-                       f"{cfg.T} tokens and {scope}; {est:.2f} s per layer (weight generation "
+                       f"{cfg.T} tokens and {scope}; {est:.2f} s per layer (weight generation"
+                       f"{', FP8 quantization' if cfg.weights == 'fp8' else ''} "
                        f"and bf16->f64 conversion untimed)")}
 
 
@@ -220,9 +251,23 @@ def main(argv=None):
     bal = torch.empty((1,), dtype=torch.float32, device=dev)
     ws = torch.empty((moe.moe_workspace_size(cfg),), dtype=torch.uint8, device=dev)
 
+    fp8 = cfg.weights == "fp8"
+
     def step():
-        moe.moe_layer_forward(cfg, d["logits"], d["x"], d["w13"], d["w2"], d["sw13"], d["sw2"],
-                              out, ids, w, counts, bal, ws)
+        if fp8:
+            moe.moe_layer_forward_fp8w(cfg, d["logits"], d["x"], d["w13"], d["w13_s"], d["w2"],
+                                       d["w2_s"], d["sw13"], d["sw13_s"], d["sw2"], d["sw2_s"],
+                                       out, ids, w, counts, bal, ws)
+        else:
+            moe.moe_layer_forward(cfg, d["logits"], d["x"], d["w13"], d["w2"], d["sw13"],
+                                  d["sw2"], out, ids, w, counts, bal, ws)
+
+    def ffn():
+        if fp8:
+            moe.moe_grouped_ffn_fp8w(cfg, x_perm, so, se, d["w13"], d["w13_s"], d["w2"],
+                                     d["w2_s"], None, y_perm, ws)
+        else:
+            moe.moe_grouped_ffn(cfg, x_perm, so, se, d["w13"], d["w2"], None, y_perm, ws)
 
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -252,12 +297,12 @@ def main(argv=None):
     r2t = torch.empty((A,), dtype=torch.int32, device=dev)
     moe.moe_permute(cfg, d["x"], ids, x_perm, so, se, a2r, r2t, counts, bal, ws)
     for _ in range(2):
-        moe.moe_grouped_ffn(cfg, x_perm, so, se, d["w13"], d["w2"], None, y_perm, ws)
+        ffn()
     f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     f0.record(stream)
     for _ in range(args.steps):
-        moe.moe_grouped_ffn(cfg, x_perm, so, se, d["w13"], d["w2"], None, y_perm, ws)
+        ffn()
     f1.record(stream)
     torch.cuda.synchronize()
     ffn_ms = f0.elapsed_time(f1) / args.steps
@@ -276,8 +321,8 @@ def main(argv=None):
         roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic(cfg.name)}
-    roof["kernel"] = ("grouped FFN: the two grouped-GEMM launches of one moe_grouped_ffn call "
-                      "(gate/up + SwiGLU, then down + row scale)")
+    roof["kernel"] = ("grouped FFN: the two grouped-GEMM launches of one moe_grouped_ffn"
+                      + ("_fp8w" if fp8 else "") + " call (gate/up + SwiGLU, then down + row scale)")
     roof["ms_per_launch"] = round(ffn_ms, 4)
     roof["algorithmic_bytes"] = by
     roof["algorithmic_flops"] = fl
@@ -286,10 +331,13 @@ def main(argv=None):
         "metric": METRIC, "value": round(cfg.T / (ms * 1e-3), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded; random-init weights)",
+        "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded; random-init weights)",
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "experts": cfg.E,
                    "top_k": cfg.k, "intermediate": cfg.I, "shared_intermediate": cfg.shared_I,
                    "assignments": cfg.A, "active_experts": active,
+                   "weights": ("fp8 e4m3, 128x128 power-of-two block scales, dequantized to "
+                               "bf16 in the GEMMs") if fp8 else cfg.dtype,
                    "balancedness": float(bal.item())},
         "grouped_gemm_tflops": round(tflops, 2),
         "grouped_gemm_frac_mfma": round(tflops / BF16_PEAK_TFLOPS, 4),

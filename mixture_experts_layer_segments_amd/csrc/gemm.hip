@@ -25,6 +25,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct GemmProblem {
   const uint16_t* A;        // [rows, K] bf16 bits
@@ -225,88 +226,76 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
                                            0x00020000);
 }
 
-// Copy K stage kt of this wave's LPI 1 KiB blocks into its ring slot: block i
-// of wave w is block i * NI + w of the stage; the first A_IT of a wave's
-// blocks are A rows, the rest B rows.  `voff` holds each lane's byte offset
-// of its 16 bytes at k = 0; the stage's K offset goes in the scalar offset.
-template <int LPI, int NI, int STAGES, int STAGE_CH, int BK, int A_IT>
+// Copy K stage kt of this wave's LPI 1 KiB blocks into its ring slot: the
+// wave's first A_IT blocks are A blocks i * NI + w (RPB rows of 128-byte
+// pieces each), the rest B blocks (i - A_IT) * NI + w, starting at chunk A_CH
+// of the slot (bf16 weights: 128-byte row pieces; E4M3 codes: 64-byte
+// pieces, 16 rows per block).  `voff` holds each lane's byte offset of its
+// 16 bytes at k = 0; the stage's K offset goes in the scalar offset.
+template <int LPI, int NI, int STAGES, int STAGE_CH, int A_CH, int BK, int A_IT, int WB>
 __device__ __forceinline__ void ring_issue(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                            const uint32_t* voff, u32x4* ring, int kt, int wv) {
   u32x4* slot = ring + (kt % STAGES) * STAGE_CH;
-  const int koff = kt * BK * 2;
 #pragma unroll
-  for (int i = 0; i < LPI; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(i < A_IT ? ra : rb,
-                                             MOE_LDS_PTR(slot + (i * NI + wv) * 64), 16,
-                                             voff[i], koff, 0, 0);
+  for (int i = 0; i < LPI; ++i) {
+    if (i < A_IT)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MOE_LDS_PTR(slot + (i * NI + wv) * 64), 16,
+                                               voff[i], kt * BK * 2, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, MOE_LDS_PTR(slot + A_CH + ((i - A_IT) * NI + wv) * 64), 16, voff[i],
+          kt * BK * WB, 0, 0);
+  }
 }
 
 // Ring-tile geometry shared by the per-tile body and the kernels that size
-// the ring.
-template <int BM, int BN, int BK, int STAGES>
+// the ring (WF = 1: the weight rows of a stage hold 1-byte E4M3 codes).
+template <int WF, int BM, int BN, int BK, int STAGES>
 struct RingShape {
-  static constexpr int KCH = BK / 8;                      // 16-byte chunks per row piece
-  static constexpr int STAGE_CH = (BM + BN) * KCH;        // 16-byte chunks per stage
+  static constexpr int KCH = BK / 8;                      // A: 16-byte chunks per row piece
+  static constexpr int KCHB = WF ? BK / 16 : KCH;         // B: 16-byte chunks per row piece
+  static constexpr int A_CH = BM * KCH;                   // A chunks per stage
+  static constexpr int STAGE_CH = A_CH + BN * KCHB;       // 16-byte chunks per stage
   static constexpr int RING_CH = STAGES * STAGE_CH;       // 16-byte chunks of the ring
 };
 
-// WF weight path: load one stage's codes (16-byte buffer loads, range-checked
-// by the expert matrix) and their block scales; dequantize them into a ring
-// slot as bf16 chunks 2*kc8 and 2*kc8 + 1 of each row.
-template <int NB8, int BK>
-__device__ __forceinline__ void load_b8(__amdgpu_buffer_rsrc_t rb, const float* Sb,
-                                        const uint32_t* off, const int* sc, int kc8, int kt,
-                                        u32x4* b8, float* s8) {
-#pragma unroll
-  for (int i = 0; i < NB8; ++i) {
-    b8[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, off[i], kt * BK, 0));
-    s8[i] = Sb[sc[i] + (kt * BK + kc8 * 16) / 128];
-  }
-}
-template <int NB8, int KCH, int STAGES, int STAGE_CH>
-__device__ __forceinline__ void store_b8(u32x4* ring, const int* dst, int kc8, int kt,
-                                         const u32x4* b8, const float* s8) {
-  u32x4* slot = ring + (kt % STAGES) * STAGE_CH;
-#pragma unroll
-  for (int i = 0; i < NB8; ++i) {
-    const int row = dst[i] / KCH;
-    u32x4 lo, hi;
-    fp8x16_to_bf16(b8[i], s8[i], lo, hi);
-    slot[dst[i] + ((2 * kc8) ^ swz<KCH>(row))] = lo;
-    slot[dst[i] + ((2 * kc8 + 1) ^ swz<KCH>(row))] = hi;
-  }
+// 8 E4M3 codes (byte j of word w = element 4w + j) times their block's
+// power-of-two scale, as an MFMA operand of 8 bf16 (exact).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi, float sc) {
+  return __builtin_bit_cast(bf16x8, u32x4{fp8x2_to_bf16<false>(lo, sc), fp8x2_to_bf16<true>(lo, sc),
+                                          fp8x2_to_bf16<false>(hi, sc), fp8x2_to_bf16<true>(hi, sc)});
 }
 
 // One output tile (`tile` in the numbering of the tile table `tiles_l`, which
 // holds args.n_seg_total + 1 prefix entries) through the LDS ring `ring`.
 // Every thread of the workgroup calls it with the same tile.
-// WF = 1: the weights are E4M3 codes with 128 x 128 block scales.  Their rows
-// then skip the DMA: every thread loads its share of the next stage's weight
-// rows into registers at the start of a stage (16 codes per 16-byte load),
-// and at its end dequantizes them to bf16 (exact) into the ring, so the ring
-// and the MFMA fragments look exactly as with bf16 weights.
+// WF = 1: the weights are E4M3 codes with 128 x 128 block scales.  The codes
+// travel into the ring as they are (half the bytes of bf16, so the ring holds
+// more stages) and are dequantized when a wave reads its MFMA operand: an
+// 8-byte LDS read and four conversions with the block's scale.  The tile's
+// block scales (its two 128-row blocks of weights x K/128) are staged once
+// per tile into `scl`, LDS beside the tile table.
 template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
 __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles_l, int tile,
-                                          u32x4* ring) {
-  constexpr int KCH = BK / 8;           // 16-byte chunks per row piece
-  constexpr int RPB = 64 / KCH;         // row pieces per 1 KiB copy block
+                                          u32x4* ring, float* scl) {
+  using RS = RingShape<WF, BM, BN, BK, STAGES>;
+  constexpr int KCH = RS::KCH, KCHB = RS::KCHB, A_CH = RS::A_CH, STAGE_CH = RS::STAGE_CH;
+  constexpr int RPB = 64 / KCH;         // A rows per 1 KiB copy block
+  constexpr int RPBB = 64 / KCHB;       // B rows per 1 KiB copy block
   constexpr int NW = NTHR / 64;
   constexpr int WAVES_N = NW / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;   // wave tile
   constexpr int TM = WM / 16, TN = WN / 16;
-  constexpr int ROWS = BM + BN;         // A rows then B rows in one stage
-  constexpr int STAGE_CH = ROWS * KCH;  // 16-byte chunks per stage
+  constexpr int WB = WF ? 1 : 2;        // bytes per weight
   // With 8 waves only one wave per SIMD (waves 0-3) issues the copies, so
   // that its partner never stalls behind the copy issue and keeps the SIMD's
   // matrix core fed.
   constexpr int NI = (NW == 8 && MOE_COPY_WAVES == 4) ? 4 : NW;   // issuing waves
-  constexpr int LPI = (WF ? BM : ROWS) / RPB / NI;  // 1 KiB copies per issuing wave per stage
-  constexpr int A_IT = BM / RPB / NI;   // ... of which A rows
-  constexpr int KC8 = BK / 16;          // WF: 16-byte chunks of codes per weight row per stage
-  constexpr int NB8 = WF ? BN * KC8 / NTHR : 1;   // ... per thread
-  static_assert(!WF || (BN * KC8) % NTHR == 0, "weight chunks per thread");
+  constexpr int A_IT = BM / RPB / NI;   // A copies per issuing wave per stage
+  constexpr int LPI = A_IT + BN / RPBB / NI;   // all copies per issuing wave per stage
   static_assert(BK == 32 || BK == 64, "row piece of 64 or 128 bytes");
-  static_assert((ROWS / RPB) % NI == 0 && (BM / RPB) % NI == 0, "copy blocks per wave");
+  static_assert(!WF || BK == 64, "E4M3 weights: 64-byte row pieces");
+  static_assert((BM / RPB) % NI == 0 && (BN / RPBB) % NI == 0, "copy blocks per wave");
   static_assert(STAGES >= 2 && STAGES <= 6, "ring shape");
   static_assert(LPI * (STAGES - 2) < 64, "vmcnt range");
 
@@ -345,7 +334,6 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
   const int m0 = (first_m + lg % gm) * BM;
   const int n0 = (lg / gm) * ncols;
   const int K = P.K, N = P.N;
-  constexpr int WB = WF ? 1 : 2;        // bytes per weight
   const uint8_t* Bb = reinterpret_cast<const uint8_t*>(P.B) + (size_t)e * P.b_stride * WB;
 
   // byte offset of this lane's 16 bytes at k = 0 in each of the wave's copies
@@ -356,33 +344,15 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
   uint32_t voff[LPI];
 #pragma unroll
   for (int i = 0; i < LPI; ++i) {
-    const int row = (i * NI + wvs) * RPB + lane / KCH;
-    const int kc = (lane % KCH) ^ swz<KCH>(row);
-    int grow;   // row of A (i < A_IT) or of this expert's B
     if (i < A_IT) {
+      const int row = (i * NI + wvs) * RPB + lane / KCH;
+      const int kc = (lane % KCH) ^ swz<KCH>(row);
       const int ar = r0 + min(m0 + row, len - 1);
-      grow = P.a_rows ? P.a_rows[ar] : ar;
+      const int grow = P.a_rows ? P.a_rows[ar] : ar;
+      voff[i] = (uint32_t)grow * (uint32_t)(K * 2) + kc * 16;
     } else {
-      const int br = row - BM;
-      if (MODE == 0) {
-        const int col = min(n0 + (br % (BN / 2)), N - 1);
-        grow = br < BN / 2 ? col : P.up_off + col;
-      } else {
-        grow = min(n0 + br, N - 1);
-      }
-    }
-    voff[i] = (uint32_t)grow * (uint32_t)(K * 2) + kc * 16;
-  }
-  // WF: this thread's weight chunks -- byte offset at k = 0, block-scale
-  // index at k = 0, and the ring chunk (of two) the bf16 values go to
-  uint32_t b8off[NB8];
-  int b8sc[NB8], b8dst[NB8];
-  const float* Sb = WF ? P.b_scale + (size_t)e * P.s_stride : nullptr;
-  const int kc8 = tid % KC8;
-  if (WF) {
-#pragma unroll
-    for (int i = 0; i < NB8; ++i) {
-      const int br = (tid + NTHR * i) / KC8;
+      const int br = ((i - A_IT) * NI + wvs) * RPBB + lane / KCHB;   // row of the weight tile
+      const int kc = (lane % KCHB) ^ swz<KCHB>(BM + br);
       int grow;
       if (MODE == 0) {
         const int col = min(n0 + (br % (BN / 2)), N - 1);
@@ -390,13 +360,9 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
       } else {
         grow = min(n0 + br, N - 1);
       }
-      b8off[i] = (uint32_t)grow * (uint32_t)K + kc8 * 16;
-      b8sc[i] = (grow / 128) * (K / 128);
-      b8dst[i] = (BM + br) * KCH;
+      voff[i] = (uint32_t)grow * (uint32_t)(K * WB) + kc * 16;
     }
   }
-  u32x4 b8[NB8];
-  float s8[NB8];
 
   f32x4 acc[TM][TN];
 #pragma unroll
@@ -405,35 +371,50 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int KT = K / BK;
+  const int KB = K / 128;               // WF: K blocks of the scales
   wait_vmcnt<0>();   // this wave's earlier stores and copies are done
-  raw_barrier();     // every wave is done reading the ring
-  if (WF) load_b8<NB8, BK>(rb, Sb, b8off, b8sc, kc8, 0, b8, s8);
+  raw_barrier();     // every wave is done reading the ring (and the scales)
+  if (WF) {
+    // the tile's scales: group 0 / 1 = its first / second 128 weight rows
+    // (GEMM 1: the gate / up halves), x every K block
+    const float* Sb = P.b_scale + (size_t)e * P.s_stride;
+    const int nrb = (MODE == 0 ? 2 * N : N) / 128;
+    for (int i = tid; i < 2 * KB; i += NTHR) {
+      const int g = i / KB, kb = i % KB;
+      const int rb_ = MODE == 0 ? (g ? (P.up_off + n0) / 128 : n0 / 128) : min(n0 / 128 + g, nrb - 1);
+      scl[i] = Sb[rb_ * KB + kb];
+    }
+  }
 #pragma unroll
   for (int st = 0; st < STAGES - 1; ++st)
     if (st < KT && wvs < NI)
-      ring_issue<LPI, NI, STAGES, STAGE_CH, BK, A_IT>(ra, rb, voff, ring, st, wvs);
-  if (WF) {
-    wait_vmcnt<0>();
-    store_b8<NB8, KCH, STAGES, STAGE_CH>(ring, b8dst, kc8, 0, b8, s8);
-  }
+      ring_issue<LPI, NI, STAGES, STAGE_CH, A_CH, BK, A_IT, WB>(ra, rb, voff, ring, st, wvs);
+  // WF: the scale group of this wave's weight fragments (GEMM 1: gate
+  // fragments use group 0, up fragments group 1)
+  const int g_down = MODE == 1 ? (wn * WN) / 128 : 0;
   for (int kt = 0; kt < KT; ++kt) {
     // stage kt has landed once only the copies of later stages remain
     // (waves that issue no copies have none in flight: their wait is free)
     wait_stages<LPI, STAGES - 2>(min(STAGES - 2, KT - 1 - kt));
-    if (WF) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // dequantized rows written
+    if (WF) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the tile's scales are written
     raw_barrier();
-    // WF: next stage's weight codes, issued before the A copies so that
-    // waiting for them leaves those copies in flight
-    if (WF && kt + 1 < KT) load_b8<NB8, BK>(rb, Sb, b8off, b8sc, kc8, kt + 1, b8, s8);
-    const bool copies = kt + STAGES - 1 < KT && wvs < NI;
-    if (copies)
-      ring_issue<LPI, NI, STAGES, STAGE_CH, BK, A_IT>(ra, rb, voff, ring, kt + STAGES - 1, wvs);
+    if (kt + STAGES - 1 < KT && wvs < NI)
+      ring_issue<LPI, NI, STAGES, STAGE_CH, A_CH, BK, A_IT, WB>(ra, rb, voff, ring,
+                                                                kt + STAGES - 1, wvs);
     const u32x4* slot = ring + (kt % STAGES) * STAGE_CH;
+    float sc0 = 1.0f, sc1 = 1.0f;
+    if (WF) {
+      const int kb = kt * BK / 128;
+      sc0 = scl[(MODE == 0 ? 0 : g_down) * KB + kb];
+      sc1 = scl[KB + kb];
+    }
     // Fragments of K step kk + 1 are read while the MFMAs of step kk run:
     // two register sets, and the scheduler is told to interleave the LDS
-    // reads one by one among the MFMAs.
+    // reads one by one among the MFMAs.  (WF: the weight fragment is read as
+    // 8 codes and dequantized just before its MFMAs.)
     bf16x8 af[2][TM], bfr[2][TN];
-    auto load_frags = [&](int kk, bf16x8* a, bf16x8* b) {
+    uint32_t b8[2][TN][2];
+    auto load_frags = [&](int kk, bf16x8* a, bf16x8* b, uint32_t (*b8r)[2]) {
       const int ch = kk * 4 + (lane >> 4);
 #pragma unroll
       for (int mi = 0; mi < TM; ++mi) {
@@ -442,15 +423,31 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
       }
 #pragma unroll
       for (int ni = 0; ni < TN; ++ni) {
-        const int row = BM + brow_of[ni] + (lane & 15);
-        b[ni] = __builtin_bit_cast(bf16x8, slot[row * KCH + (ch ^ swz<KCH>(row))]);
+        const int br = brow_of[ni] + (lane & 15);
+        if (WF) {
+          // codes of K kk*32 + q*8 .. +8: chunk 2*kk + q/2 of the 64-byte piece, half q % 2
+          const int c = kk * 2 + ((lane >> 4) >> 1);
+          const u32x2 v = reinterpret_cast<const u32x2*>(
+              slot + A_CH + br * KCHB + (c ^ swz<KCHB>(BM + br)))[(lane >> 4) & 1];
+          b8r[ni][0] = v.x;
+          b8r[ni][1] = v.y;
+        } else {
+          const int row = BM + br;
+          b[ni] = __builtin_bit_cast(bf16x8, slot[row * KCH + (ch ^ swz<KCH>(row))]);
+        }
       }
     };
-    load_frags(0, af[0], bfr[0]);
+    load_frags(0, af[0], bfr[0], b8[0]);
 #pragma unroll
     for (int kk = 0; kk < BK / 32; ++kk) {
       const int cur = kk & 1;
-      if (kk + 1 < BK / 32) load_frags(kk + 1, af[cur ^ 1], bfr[cur ^ 1]);
+      if (kk + 1 < BK / 32) load_frags(kk + 1, af[cur ^ 1], bfr[cur ^ 1], b8[cur ^ 1]);
+      if (WF) {
+#pragma unroll
+        for (int ni = 0; ni < TN; ++ni)
+          bfr[cur][ni] = fp8x8_to_bf16(b8[cur][ni][0], b8[cur][ni][1],
+                                       (MODE == 0 && ni >= TN / 2) ? sc1 : sc0);
+      }
 #pragma unroll
       for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
@@ -472,12 +469,6 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
       } else {
         __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
       }
-    }
-    if (WF && kt + 1 < KT) {
-      // the codes were issued before this stage's copies: wait for them only
-      if (copies) wait_vmcnt<LPI>();
-      else wait_vmcnt<0>();
-      store_b8<NB8, KCH, STAGES, STAGE_CH>(ring, b8dst, kc8, kt + 1, b8, s8);
     }
   }
 
@@ -517,13 +508,15 @@ __global__ __launch_bounds__(NTHR, OCC) void gemm_ring_kernel(GemmArgs args) {
   // in-flight ring copies and waits for every copy before each stage's first
   // read (measured 15-30% slower).  The table build's scan scratch therefore
   // borrows the ring, which is idle until the first tile.
-  __shared__ __attribute__((aligned(1024))) u32x4 ring[RingShape<BM, BN, BK, STAGES>::RING_CH];
+  // (WF: the dynamic LDS also holds a tile's block scales, after the table.)
+  __shared__ __attribute__((aligned(1024))) u32x4 ring[RingShape<WF, BM, BN, BK, STAGES>::RING_CH];
   extern __shared__ int tiles_l[];
   build_tile_table<NTHR>(args, tiles_l, reinterpret_cast<int*>(ring));
   const int total = tiles_l[args.n_seg_total];
+  float* scl = reinterpret_cast<float*>(tiles_l + args.n_seg_total + 1);
   const int G = gridDim.x;
   for (int tile = xcd_logical(blockIdx.x, G); tile < total; tile += G)
-    ring_tile<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(args, tiles_l, tile, ring);
+    ring_tile<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(args, tiles_l, tile, ring, scl);
 }
 
 
@@ -535,14 +528,22 @@ __global__ __launch_bounds__(NTHR, OCC) void gemm_ring_kernel(GemmArgs args) {
 #ifndef MOE_BIG_TILE
 #define MOE_BIG_TILE 256, 256, 64, 512, 4, 2   // 4 x 2 waves of 64 x 128
 #endif
+// E4M3 weights: the weight rows of a stage take half the bytes, so the same
+// tiles hold one more stage.
+#ifndef MOE_MID_TILE_F8
+#define MOE_MID_TILE_F8 128, 256, 64, 512, 2, 4
+#endif
+#ifndef MOE_BIG_TILE_F8
+#define MOE_BIG_TILE_F8 256, 256, 64, 512, 4, 3
+#endif
 #ifndef MOE_BIG_ROWS
 #define MOE_BIG_ROWS 256
 #endif
-template <int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
+template <int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
 struct TileCfg {
-  static constexpr int kRingBytes = RingShape<BM, BN, BK, STAGES>::RING_CH * 16;
+  static constexpr int kRingBytes = RingShape<WF, BM, BN, BK, STAGES>::RING_CH * 16;
   static constexpr int kThreads = NTHR;
-  static constexpr int kBM = BM, kBN = BN, kBK = BK, kWM = WAVES_M;
+  static constexpr int kBM = BM, kBN = BN, kBK = BK, kWM = WAVES_M, kStages = STAGES;
 };
 #ifndef MOE_MID1_TILE
 #define MOE_MID1_TILE MOE_MID_TILE
@@ -550,9 +551,18 @@ struct TileCfg {
 #ifndef MOE_MID2_TILE
 #define MOE_MID2_TILE MOE_MID_TILE
 #endif
-using Mid1Cfg = TileCfg<MOE_MID1_TILE>;   // GEMM 1 and GEMM 2 may differ
-using Mid2Cfg = TileCfg<MOE_MID2_TILE>;
-using BigCfg = TileCfg<MOE_BIG_TILE>;
+// tile shapes per weight format: [0] bf16, [1] E4M3
+template <int WF> struct Tiles;
+template <> struct Tiles<0> {
+  using Mid1 = TileCfg<0, MOE_MID1_TILE>;   // GEMM 1 and GEMM 2 may differ
+  using Mid2 = TileCfg<0, MOE_MID2_TILE>;
+  using Big = TileCfg<0, MOE_BIG_TILE>;
+};
+template <> struct Tiles<1> {
+  using Mid1 = TileCfg<1, MOE_MID_TILE_F8>;
+  using Mid2 = TileCfg<1, MOE_MID_TILE_F8>;
+  using Big = TileCfg<1, MOE_BIG_TILE_F8>;
+};
 
 
 // ---------------------------------------------------------------- fp32 path
@@ -839,11 +849,19 @@ int persistent_grid(Kern kernel, size_t dyn_lds, int fallback, int threads = 256
   return g > 8 ? g : 8;
 }
 
+// Dynamic LDS of a ring launch: the tile table, and (E4M3 weights) a tile's
+// block scales: 2 groups x K/128 floats for the longest K of the problems.
+inline size_t ring_dyn_lds(const GemmArgs& g, int wf) {
+  int kmax = 0;
+  for (int p = 0; p < g.n_probs; ++p) kmax = g.p[p].K > kmax ? g.p[p].K : kmax;
+  return (size_t)(g.n_seg_total + 1) * sizeof(int) + (wf ? (size_t)2 * (kmax / 128) * 4 : 0);
+}
+
 template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
 void launch_ring(const GemmArgs& g, hipStream_t s) {
-  const size_t lds_tiles = (size_t)(g.n_seg_total + 1) * sizeof(int);
+  const size_t dyn = ring_dyn_lds(g, WF);
   auto k = gemm_ring_kernel<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES, 1>;
-  k<<<persistent_grid(k, lds_tiles, 1, NTHR), NTHR, lds_tiles, s>>>(g);
+  k<<<persistent_grid(k, dyn, 1, NTHR), NTHR, dyn, s>>>(g);
 }
 
 }  // namespace
@@ -888,24 +906,26 @@ void launch_mfma_pair(const moe_config& c, const FfnProblem* probs, int n_probs,
   // to 2 stages if the 3-stage one leaves no room for the tile table.  A
   // segment holds at most one row per token of its problem, so the big
   // launches may be skipped.
-  using M1 = Mid1Cfg;
-  using M2 = Mid2Cfg;
+  using M1 = typename Tiles<WF>::Mid1;
+  using M2 = typename Tiles<WF>::Mid2;
+  using BG = typename Tiles<WF>::Big;
   const GemmArgs m1 = cover(g1, M1::kBM, M1::kBN / 2, 1, MOE_BIG_ROWS);
   const GemmArgs m2 = cover(g2, M2::kBM, M2::kBN, 1, MOE_BIG_ROWS);
-  const GemmArgs b1 = cover(g1, BigCfg::kBM, BigCfg::kBN / 2, MOE_BIG_ROWS, kAll);
-  const GemmArgs b2 = cover(g2, BigCfg::kBM, BigCfg::kBN, MOE_BIG_ROWS, kAll);
+  const GemmArgs b1 = cover(g1, BG::kBM, BG::kBN / 2, MOE_BIG_ROWS, kAll);
+  const GemmArgs b2 = cover(g2, BG::kBM, BG::kBN, MOE_BIG_ROWS, kAll);
   constexpr size_t kMargin = 64;
-  const bool deep1 = lds_tiles + M1::kRingBytes + kMargin <= kMaxLdsBytes;
-  const bool deep2 = lds_tiles + M2::kRingBytes + kMargin <= kMaxLdsBytes;
+  const bool deep1 = ring_dyn_lds(g1, WF) + M1::kRingBytes + kMargin <= kMaxLdsBytes;
+  const bool deep2 = ring_dyn_lds(g2, WF) + M2::kRingBytes + kMargin <= kMaxLdsBytes;
   int longest = 0;
   for (int p = 0; p < n_probs; ++p) longest = probs[p].rows > longest ? probs[p].rows : longest;
   const bool any_big = longest >= MOE_BIG_ROWS && c.T >= MOE_BIG_ROWS;
-  if (deep1) launch_ring<0, WF, MOE_MID1_TILE>(m1, s);
+  // (a 2-stage ring of the mid shape always fits beside the largest table)
+  if (deep1) launch_ring<0, WF, M1::kBM, M1::kBN, M1::kBK, M1::kThreads, M1::kWM, M1::kStages>(m1, s);
   else launch_ring<0, WF, M1::kBM, M1::kBN, M1::kBK, M1::kThreads, M1::kWM, 2>(m1, s);
-  if (any_big) launch_ring<0, WF, MOE_BIG_TILE>(b1, s);
-  if (deep2) launch_ring<1, WF, MOE_MID2_TILE>(m2, s);
+  if (any_big) launch_ring<0, WF, BG::kBM, BG::kBN, BG::kBK, BG::kThreads, BG::kWM, BG::kStages>(b1, s);
+  if (deep2) launch_ring<1, WF, M2::kBM, M2::kBN, M2::kBK, M2::kThreads, M2::kWM, M2::kStages>(m2, s);
   else launch_ring<1, WF, M2::kBM, M2::kBN, M2::kBK, M2::kThreads, M2::kWM, 2>(m2, s);
-  if (any_big) launch_ring<1, WF, MOE_BIG_TILE>(b2, s);
+  if (any_big) launch_ring<1, WF, BG::kBM, BG::kBN, BG::kBK, BG::kThreads, BG::kWM, BG::kStages>(b2, s);
   MOE_DBG("grouped gemms");
 }
 
