@@ -819,6 +819,13 @@ void gemm_decode_kernel(GemmArgs args) {
 #define MOE_DBK2 256
 #endif
 constexpr int DBN1 = MOE_DBN1, DBK1 = MOE_DBK1, DBN2 = MOE_DBN2, DBK2 = MOE_DBK2;
+// E4M3 weights: twice the K per stage, so that a stage moves as many bytes
+// (and keeps as many in flight) as with bf16 weights
+#ifndef MOE_DBK_F8
+#define MOE_DBK_F8 512
+#endif
+template <int WF> constexpr int decode_bk1() { return WF ? MOE_DBK_F8 : DBK1; }
+template <int WF> constexpr int decode_bk2() { return WF ? MOE_DBK_F8 : DBK2; }
 
 // Persistent grid: as many workgroups as can be resident at once (a larger
 // grid would run its excess only after others finish), a multiple of 8 so
@@ -884,17 +891,18 @@ template <int WF>
 void launch_mfma_pair(const moe_config& c, const FfnProblem* probs, int n_probs,
                       const GemmArgs& g1, const GemmArgs& g2, hipStream_t s) {
   const int H = c.H, nst = g1.n_seg_total;
+  constexpr int BK1 = decode_bk1<WF>(), BK2 = decode_bk2<WF>();
   int max_rows = 0;
-  bool k_ok = H % DBK1 == 0;
+  bool k_ok = H % BK1 == 0;
   for (int p = 0; p < n_probs; ++p) {
     max_rows += probs[p].rows;
-    k_ok = k_ok && probs[p].Iw % DBK2 == 0;
+    k_ok = k_ok && probs[p].Iw % BK2 == 0;
   }
   const size_t lds_tiles = (size_t)(nst + 1) * sizeof(int);
   // Few rows per segment on average: weight streaming with 16-row tiles.
   if (k_ok && (int64_t)max_rows <= (int64_t)MOE_DECODE_ROWS * nst) {
-    auto k1 = gemm_decode_kernel<0, WF, DBN1, DBK1, 1, MOE_DWAVES>;
-    auto k2 = gemm_decode_kernel<1, WF, DBN2, DBK2, 1, MOE_DWAVES>;
+    auto k1 = gemm_decode_kernel<0, WF, DBN1, BK1, 1, MOE_DWAVES>;
+    auto k2 = gemm_decode_kernel<1, WF, DBN2, BK2, 1, MOE_DWAVES>;
     k1<<<persistent_grid(k1, lds_tiles, 4), 256, lds_tiles, s>>>(cover(g1, 16, DBN1 / 2, 1, kAll));
     k2<<<persistent_grid(k2, lds_tiles, 4), 256, lds_tiles, s>>>(cover(g2, 16, DBN2, 1, kAll));
     MOE_DBG("grouped gemms");
