@@ -35,10 +35,14 @@ GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_segments_amd", "csrc", "gem
 # what it reads for a plain 1 GiB device copy), keyed by workload.  An entry
 # only applies while gemm.hip still has the hash it was measured with.
 MEASURED_TRAFFIC = {
-    "decode_bf16": {"gemm_src_sha256_16": "18134e07b35f156e", "bytes": 5550901955},
-    "prefill_skew_bf16": {"gemm_src_sha256_16": "18134e07b35f156e", "bytes": 8287440312},
-    "deepseek_v3_bf16": {"gemm_src_sha256_16": "18134e07b35f156e", "bytes": 22980500232},
-    "ragged_stress_bf16": {"gemm_src_sha256_16": "18134e07b35f156e", "bytes": 13910302057},
+    "decode_bf16": {"gemm_src_sha256_16": "49faeb91d41e53b5", "bytes": 5555619606},
+    "prefill_skew_bf16": {"gemm_src_sha256_16": "49faeb91d41e53b5", "bytes": 8296622205},
+    "deepseek_v3_bf16": {"gemm_src_sha256_16": "49faeb91d41e53b5", "bytes": 23007011565},
+    "ragged_stress_bf16": {"gemm_src_sha256_16": "49faeb91d41e53b5", "bytes": 14069722682},
+    "decode_fp8w": {"gemm_src_sha256_16": "49faeb91d41e53b5", "bytes": 2779700052},
+    "prefill_skew_fp8w": {"gemm_src_sha256_16": "49faeb91d41e53b5", "bytes": 4075577945},
+    "deepseek_v3_fp8w": {"gemm_src_sha256_16": "49faeb91d41e53b5", "bytes": 13126936196},
+    "ragged_stress_fp8w": {"gemm_src_sha256_16": "49faeb91d41e53b5", "bytes": 10773917313},
 }
 
 
