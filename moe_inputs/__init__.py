@@ -54,7 +54,10 @@ class MoEShape:
     group_score_topn: int = 2   # group score = sum of its top-n member scores
     renormalize: int = 1        # weights renormalised over the k winners
     n_hot_split: int = 0        # hottest experts given replica segments
-    split_ways: int = 1         # replicas per hot expert (token index mod ways)
+    split_ways: int = 1         # replicas per hot expert
+    split_mode: str = "parity"  # "parity": replica = token index mod ways;
+                                # "bounded": consecutive runs, water-filled loads
+    split_c_permille: int = 0   # relaxation ratio C of the bounded split, in 1/1000
     shared_I: int = 0           # shared expert intermediate (0 = none)
     x_std: float = 1.0
     w_std: float = 0.02

@@ -31,14 +31,22 @@ decision in), keeps the best groups (ties to the lower group id) and then the
 k largest logits inside them; the shared expert is added with weight 1;
 SwiGLU is silu(x W_gate) * (x W_up) then W_down, no biases; rows inside a
 segment are in increasing assignment index a = t*k + j; hot experts are the
-n largest logical counts (ties to the lower id) and replica p of a hot expert
-holds the assignments whose token index t has t mod ways == p.
+n largest logical counts (ties to the lower id); in the parity split, replica
+p of a hot expert holds the assignments whose token index t has
+t mod ways == p; in the load-bounded split (Zepp section 4.1, Eq. 1 and
+section 5, "Routing", restricted to one GPU) the replicas take consecutive
+runs of the expert's assignments in increasing a, with loads chosen by
+greedy water-filling in replica order under the integer-rounded bounds
+floor(q(1-C)) <= load <= ceil(q(1+C)), q = d / ways.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` to facts that
 do not come from this file (printed numbers, closed forms, brute force,
 special cases that reduce to a dense MLP).
 """
 from __future__ import annotations
+
+from fractions import Fraction
+import math
 
 import numpy as np
 
@@ -158,19 +166,62 @@ def segment_list(counts: np.ndarray, n_hot: int, ways: int):
     return np.array(seg_expert, dtype=np.int32), np.array(seg_replica, dtype=np.int32)
 
 
-def segment_of_assignments(ids: np.ndarray, seg_expert, seg_replica, ways: int) -> np.ndarray:
-    """Segment of each assignment a = t*k + j."""
+def replica_loads(d: int, ways: int, c_permille: int) -> list:
+    """Per-replica loads of one hot expert with d assignments under the
+    relaxed balance constraint of Zepp section 4.1, Eq. 1, on one GPU.
+
+    The balanced reference load is q = d / ways for every replica, and
+    C = c_permille / 1000 is the relaxation ratio.  Section 5 ("Routing")
+    rounds the bounds to integers, floor(q(1-C)) <= load <= ceil(q(1+C)),
+    and fills replicas greedily: each takes as much as its upper bound
+    allows while leaving enough unassigned demand for the lower bounds of
+    the replicas still to come.  All replicas live on the one GPU, so the
+    source-GPU-first order of the pages is plain replica order.  Exact
+    rational arithmetic."""
+    q = Fraction(d, ways)
+    C = Fraction(c_permille, 1000)
+    lb = max(0, math.floor(q * (1 - C)))
+    ub = math.ceil(q * (1 + C))
+    loads, left = [], d
+    for p in range(ways):
+        later = ways - 1 - p
+        n = min(ub, left - later * lb)
+        loads.append(n)
+        left -= n
+    assert left == 0 and all(lb <= n <= ub for n in loads)
+    return loads
+
+
+def segment_of_assignments(ids: np.ndarray, seg_expert, seg_replica, ways: int,
+                           loads=None) -> np.ndarray:
+    """Segment of each assignment a = t*k + j.
+
+    ``loads`` is None for the parity split (replica t mod ways), else a dict
+    expert -> per-replica loads: replica p of that expert takes the
+    assignments of rank loads[0] + .. + loads[p-1] up to (excluding)
+    loads[0] + .. + loads[p] among the expert's assignments in increasing a.
+    """
     T, k = ids.shape
     lookup = {}
     for s, (e, p) in enumerate(zip(seg_expert.tolist(), seg_replica.tolist())):
         lookup[(e, p)] = s
+    seen = {}
     out = np.empty(T * k, dtype=np.int64)
     for t in range(T):
         for j in range(k):
             e = int(ids[t, j])
             s = lookup.get((e, -1))
             if s is None:
-                s = lookup[(e, t % ways)]
+                if loads is None:
+                    s = lookup[(e, t % ways)]
+                else:
+                    r = seen.get(e, 0)
+                    seen[e] = r + 1
+                    p, end = 0, loads[e][0]
+                    while r >= end:
+                        p += 1
+                        end += loads[e][p]
+                    s = lookup[(e, p)]
             out[t * k + j] = s
     return out
 
@@ -255,7 +306,11 @@ def plan(cfg, ids):
     """Histogram, segments, permutation and balancedness for routed ids."""
     counts = expert_counts(ids, cfg.E)
     seg_expert, seg_replica = segment_list(counts, cfg.n_hot_split, cfg.split_ways)
-    seg_of_a = segment_of_assignments(ids, seg_expert, seg_replica, cfg.split_ways)
+    loads = None
+    if getattr(cfg, "split_mode", "parity") == "bounded":
+        loads = {int(e): replica_loads(int(counts[e]), cfg.split_ways, cfg.split_c_permille)
+                 for e in set(seg_expert[seg_replica >= 0].tolist())}
+    seg_of_a = segment_of_assignments(ids, seg_expert, seg_replica, cfg.split_ways, loads)
     seg_offsets, row_to_assign, assign_to_row, row_to_token = permutation(
         seg_of_a, len(seg_expert), cfg.k)
     return dict(counts=counts, seg_expert=seg_expert, seg_replica=seg_replica,

@@ -128,6 +128,43 @@ def coldest_are_hot(counts, n_hot):
     return sorted(range(len(counts)), key=lambda e: (int(counts[e]), e))[:n_hot]
 
 
+orig_soa = o.segment_of_assignments
+orig_replica_loads = o.replica_loads
+
+
+def no_reservation(d, ways, c_permille):
+    """Fills each replica to its upper bound without keeping back the later
+    replicas' lower bounds."""
+    q = o.Fraction(d, ways)
+    ub = o.math.ceil(q * (1 + o.Fraction(c_permille, 1000)))
+    loads, left = [], d
+    for _ in range(ways):
+        n = min(ub, left)
+        loads.append(n)
+        left -= n
+    return loads
+
+
+def floor_upper_bound(d, ways, c_permille):
+    q = o.Fraction(d, ways)
+    C = o.Fraction(c_permille, 1000)
+    lb, ub = max(0, o.math.floor(q * (1 - C))), o.math.floor(q * (1 + C))
+    loads, left = [], d
+    for p in range(ways):
+        n = left if p == ways - 1 else min(ub, left - (ways - 1 - p) * lb)
+        loads.append(n)
+        left -= n
+    return loads
+
+
+def last_replica_first(d, ways, c_permille):
+    return orig_replica_loads(d, ways, c_permille)[::-1]
+
+
+def parity_for_bounded(ids, seg_expert, seg_replica, ways, loads=None):
+    return orig_soa(ids, seg_expert, seg_replica, ways, None)
+
+
 MISTAKES = [
     ("route_flat", ascending_route),
     ("route_flat", never_renormalised),
@@ -142,6 +179,10 @@ MISTAKES = [
     ("balancedness", inverted_balancedness),
     ("balancedness", active_only_balancedness),
     ("hot_experts", coldest_are_hot),
+    ("replica_loads", no_reservation),
+    ("replica_loads", floor_upper_bound),
+    ("replica_loads", last_replica_first),
+    ("segment_of_assignments", parity_for_bounded),
 ]
 
 

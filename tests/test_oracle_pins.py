@@ -233,6 +233,80 @@ def test_hot_experts_are_the_largest_counts():
     assert sr.tolist() == [-1, 0, 1, 0, 1, -1, -1, -1, -1, -1]
 
 
+# ------------------------------------------------- load-bounded replica split
+def _feasible(d, ways, c_permille):
+    """Every integer load vector of the rounded relaxed-balance bounds of
+    Zepp section 4.1, Eq. 1 (with the integer rounding of section 5,
+    "Routing"), by brute force, in lexicographic order."""
+    q_num, q_den = d * (1000 - c_permille), 1000 * ways         # q(1-C) as a fraction
+    lb = max(0, q_num // q_den) if c_permille <= 1000 else 0
+    ub = -((-d * (1000 + c_permille)) // q_den)                 # ceil(q(1+C))
+    out = []
+    for n in itertools.product(range(d + 1), repeat=ways):
+        if sum(n) == d and all(lb <= v <= ub for v in n):
+            out.append(list(n))
+    return out, lb, ub
+
+
+@pytest.mark.parametrize("ways,c", [(2, 0), (2, 250), (3, 0), (3, 500), (3, 1500), (4, 100)])
+def test_water_filling_is_the_greediest_feasible_split(ways, c):
+    """Brute force over all load vectors: the bounds admit at least one, the
+    oracle's loads are one of them, and greedy filling in replica order
+    (each replica as full as the others' lower bounds allow) is the
+    lexicographically largest feasible vector."""
+    for d in range(0, 19):
+        feas, lb, ub = _feasible(d, ways, c)
+        got = o.replica_loads(d, ways, c)
+        assert feas, (d, ways, c)
+        assert got in feas, (d, ways, c, got, lb, ub)
+        assert got == max(feas), (d, ways, c, got, max(feas))
+
+
+def test_water_filling_closed_forms():
+    """C = 0: the near-equal split of d into ways parts, larger parts first
+    (numpy's array_split sizes); C >= ways - 1: the upper bound reaches d and
+    the lower bound is 0, so replica 0 takes all; integer q with C = 0: every
+    replica gets exactly q."""
+    for d in range(0, 40):
+        for ways in (2, 3, 4):
+            sizes = [len(part) for part in np.array_split(np.arange(d), ways)]
+            assert o.replica_loads(d, ways, 0) == sizes
+            assert o.replica_loads(d, ways, 1000 * (ways - 1)) == [d] + [0] * (ways - 1)
+    assert o.replica_loads(12, 3, 0) == [4, 4, 4]
+    assert o.replica_loads(10, 3, 500) == [5, 4, 1]     # q = 10/3: bounds 1 .. 5
+    assert o.replica_loads(100, 2, 250) == [63, 37]     # q = 50: bounds 37 .. 63
+
+
+@pytest.mark.parametrize("c", [0, 300, 1000])
+def test_bounded_split_only_moves_segment_boundaries(c):
+    """The bounded split cuts each hot expert's rows, in increasing a, into
+    consecutive runs: the row order equals the unsplit permutation's, the
+    runs have the water-filled lengths, every row belongs to its segment's
+    expert, and the layer output is bit for bit the unsplit one (replicas
+    keep the logical selection and weights, Zepp section 4.1)."""
+    cfg, lg, x, w13, w2 = _tiny(T=47, E=6, k=3, n_hot_split=2, split_ways=3,
+                                split_mode="bounded", split_c_permille=c)
+    a = o.layer_forward(cfg, lg, x, w13, w2)
+    b = o.layer_forward(cfg.replace(n_hot_split=0, split_ways=1, split_mode="parity"), lg, x,
+                        w13, w2)
+    assert (a["row_to_assign"] == b["row_to_assign"]).all()
+    assert (a["out"] == b["out"]).all()
+    counts = np.bincount(a["ids"].ravel(), minlength=cfg.E)
+    hot = sorted(range(cfg.E), key=lambda e: (-counts[e], e))[:2]
+    lens = np.diff(a["seg_offsets"])
+    for e in range(cfg.E):
+        mine = np.nonzero(a["seg_expert"] == e)[0]
+        if e in hot:
+            d = int(counts[e])
+            assert len(mine) == 3
+            # the brute-force greediest feasible vector, independent of the oracle
+            assert lens[mine].tolist() == max(_feasible(d, 3, c)[0])
+        else:
+            assert lens[mine].tolist() == [counts[e]]
+        rows = a["row_to_assign"][a["seg_offsets"][mine[0]]:a["seg_offsets"][mine[-1] + 1]]
+        assert (a["ids"].ravel()[rows] == e).all() and (np.diff(rows) > 0).all()
+
+
 # ---------------------------------------------------------------- expert MLP
 def test_swiglu_hand_example():
     """x = [1, 2]; W_gate column [0.5, 0.25] -> g = 1; W_up column [1, -1]
