@@ -53,6 +53,25 @@ typedef enum {
   MOE_SCORE_SIGMOID = 1  /* group-limited top-k on sigmoid scores */
 } moe_score;
 
+/* Replica split of the hot experts.
+ *  MOE_SPLIT_PARITY:  replica p holds the assignments of tokens t with
+ *                     t mod split_ways == p.
+ *  MOE_SPLIT_BOUNDED: the relaxed balance constraint of the Zepp paper
+ *                     (section 4.1, Eq. 1) on one GPU, with the integer
+ *                     rounding and greedy water-filling of its section 5
+ *                     ("Routing"): for an expert with d assignments,
+ *                     q = d / split_ways and C = split_c_permille / 1000,
+ *                     every replica load lies in
+ *                     [floor(q (1 - C)), ceil(q (1 + C))]; replicas are
+ *                     filled in order, each as far as the upper bound allows
+ *                     while the later replicas can still reach their lower
+ *                     bound, and replica p takes the next consecutive run of
+ *                     the expert's assignments in increasing a.  With C = 0
+ *                     the loads differ by at most one, larger ones first.
+ *                     All replicas share the one GPU, so the pages' cost
+ *                     term is the same for every feasible split. */
+typedef enum { MOE_SPLIT_PARITY = 0, MOE_SPLIT_BOUNDED = 1 } moe_split_mode;
+
 /* Layer description, a host struct read by every call (never retained). */
 typedef struct moe_config {
   int32_t T;  /* tokens in the batch (>= 0) */
@@ -66,9 +85,14 @@ typedef struct moe_config {
   int32_t group_score_topn; /* a group's score = sum of its best n member scores */
   int32_t renormalize;      /* 1: the k weights are renormalised to sum to 1 */
   int32_t n_hot_split;      /* hottest experts given replica segments (0 = none) */
-  int32_t split_ways;       /* replicas per hot expert: token index mod ways (1..4) */
+  int32_t split_ways;       /* replicas per hot expert (1..4) */
   int32_t shared_I;         /* 0, or the shared expert's intermediate size */
   int32_t act_dtype;        /* moe_dtype of x, weights, x_perm, y_perm, out */
+  int32_t split_mode;       /* moe_split_mode: how a hot expert's assignments
+                             * are spread over its replicas */
+  int32_t split_c_permille; /* MOE_SPLIT_BOUNDED: relaxation ratio C of the
+                             * load bounds in 1/1000 (0..100000); ignored
+                             * otherwise */
 } moe_config;
 /* Size limits (MOE_ERR_UNSUPPORTED beyond them): T*k <= 2^30; each of
  * T*k*H, T*k*I, T*shared_I, 2*I*H and 2*shared_I*H below 2^31 elements (the
@@ -117,10 +141,10 @@ moe_status moe_route_topk(const moe_config* cfg, const float* logits,
  *   seg_expert    [S]     out: logical expert of each segment.  Segments are
  *                          in ascending expert order; a hot expert (one of the
  *                          n_hot_split largest counts, lower id on a tie) has
- *                          split_ways adjacent replica segments, replica p
- *                          holding its assignments with t mod split_ways == p
- *                          (replicas keep the logical selection and weights,
- *                          Zepp section 4.1).  Empty segments stay listed.
+ *                          split_ways adjacent replica segments, filled as
+ *                          split_mode says (replicas keep the logical
+ *                          selection and weights, Zepp section 4.1).  Empty
+ *                          segments stay listed.
  *   assign_to_row [T*k]   out: row of each assignment (-1 if dropped).
  *   row_to_token  [T*k]   out: token of each row (rows < seg_offsets[S]).
  *   counts        [E]     out: assignments per logical expert.
@@ -181,6 +205,15 @@ moe_status moe_layer_forward(const moe_config* cfg, const float* logits, const v
                              const void* shared_w2, void* out, int32_t* topk_ids,
                              float* topk_w, int32_t* counts, float* balancedness,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Where moe_layer_forward (and moe_layer_forward_fp8w) leave the
+ * permutation they built inside their workspace, as byte offsets from its
+ * start: offsets[0] seg_offsets [S+1], offsets[1] seg_expert [S],
+ * offsets[2] assign_to_row [T*k], offsets[3] row_to_token [T*k] (int32, the
+ * contents and meaning of the moe_permute outputs of the same names).  They
+ * hold the last call's values once it has completed, until the workspace is
+ * used again.  MOE_ERR_INVALID_ARG for an invalid cfg or a NULL offsets. */
+moe_status moe_layer_plan_offsets(const moe_config* cfg, size_t offsets[4]);
 
 /* ------------------------------------------------------------------------
  * FP8 expert weights (the MoE inference blog, "Communication pressure", its

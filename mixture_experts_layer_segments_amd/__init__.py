@@ -15,9 +15,11 @@ import ctypes
 import os
 
 from ._lib import (  # noqa: F401
-    LIB_PATH, MOE_DT_BF16, MOE_DT_F32, MOE_SCORE_SIGMOID, MOE_SCORE_SOFTMAX, MoEConfig,
+    LIB_PATH, MOE_DT_BF16, MOE_DT_F32, MOE_SCORE_SIGMOID, MOE_SCORE_SOFTMAX, MOE_SPLIT_BOUNDED,
+    MOE_SPLIT_PARITY, MoEConfig,
     MoEError, lib, make_config, moe_grouped_ffn, moe_layer_forward, moe_num_segments,
     moe_permute, moe_route_topk, moe_status_string, moe_unpermute_combine,
     moe_workspace_size, moe_quantize_fp8, moe_grouped_ffn_fp8w, moe_layer_forward_fp8w,
+    moe_layer_plan_offsets,
     EXPORTED_SYMBOLS,
 )

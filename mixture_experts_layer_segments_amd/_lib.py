@@ -14,11 +14,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_DT_F32, MOE_DT_BF16 = 0, 1
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+MOE_SPLIT_PARITY, MOE_SPLIT_BOUNDED = 0, 1
 
 EXPORTED_SYMBOLS = (
     "moe_status_string", "moe_num_segments", "moe_workspace_size", "moe_route_topk",
     "moe_permute", "moe_grouped_ffn", "moe_unpermute_combine", "moe_layer_forward",
     "moe_quantize_fp8", "moe_grouped_ffn_fp8w", "moe_layer_forward_fp8w",
+    "moe_layer_plan_offsets",
 )
 
 
@@ -26,7 +28,8 @@ class MoEConfig(ctypes.Structure):
     """Mirror of ``moe_config`` in include/moe.h."""
     _fields_ = [(n, ctypes.c_int32) for n in (
         "T", "H", "E", "k", "I", "score", "n_group", "topk_group", "group_score_topn",
-        "renormalize", "n_hot_split", "split_ways", "shared_I", "act_dtype")]
+        "renormalize", "n_hot_split", "split_ways", "shared_I", "act_dtype", "split_mode",
+        "split_c_permille")]
 
 
 class MoEError(RuntimeError):
@@ -50,6 +53,8 @@ lib.moe_num_segments.restype = ctypes.c_int32
 lib.moe_num_segments.argtypes = [_cfgp]
 lib.moe_workspace_size.restype = ctypes.c_size_t
 lib.moe_workspace_size.argtypes = [_cfgp]
+lib.moe_layer_plan_offsets.restype = ctypes.c_int
+lib.moe_layer_plan_offsets.argtypes = [_cfgp, ctypes.POINTER(ctypes.c_size_t)]
 lib.moe_route_topk.restype = ctypes.c_int
 lib.moe_route_topk.argtypes = [_cfgp, _p, _p, _p, _p]
 lib.moe_permute.restype = ctypes.c_int
@@ -71,7 +76,8 @@ lib.moe_layer_forward_fp8w.argtypes = [_cfgp] + [_p] * 16 + [ctypes.c_size_t, _p
 def make_config(shape) -> MoEConfig:
     """MoEConfig from any object with the layer's fields (T, H, E, k, I,
     dtype 'f32'|'bf16', score 'softmax'|'sigmoid', n_group, topk_group,
-    group_score_topn, renormalize, n_hot_split, split_ways, shared_I)."""
+    group_score_topn, renormalize, n_hot_split, split_ways, split_mode
+    'parity'|'bounded', split_c_permille, shared_I)."""
     g = lambda n, d: getattr(shape, n, d)  # noqa: E731
     return MoEConfig(
         T=shape.T, H=shape.H, E=shape.E, k=shape.k, I=shape.I,
@@ -80,7 +86,9 @@ def make_config(shape) -> MoEConfig:
         group_score_topn=g("group_score_topn", 2), renormalize=int(g("renormalize", 1)),
         n_hot_split=g("n_hot_split", 0), split_ways=g("split_ways", 1),
         shared_I=g("shared_I", 0),
-        act_dtype=MOE_DT_F32 if g("dtype", "bf16") == "f32" else MOE_DT_BF16)
+        act_dtype=MOE_DT_F32 if g("dtype", "bf16") == "f32" else MOE_DT_BF16,
+        split_mode=MOE_SPLIT_BOUNDED if g("split_mode", "parity") == "bounded" else MOE_SPLIT_PARITY,
+        split_c_permille=g("split_c_permille", 0))
 
 
 def moe_status_string(status: int) -> str:
@@ -97,6 +105,14 @@ def moe_num_segments(cfg) -> int:
 
 def moe_workspace_size(cfg) -> int:
     return int(lib.moe_workspace_size(ctypes.byref(_cfg(cfg))))
+
+
+def moe_layer_plan_offsets(cfg) -> dict:
+    """Byte offsets of seg_offsets, seg_expert, assign_to_row and
+    row_to_token inside the layer call's workspace."""
+    off = (ctypes.c_size_t * 4)()
+    _check(lib.moe_layer_plan_offsets(ctypes.byref(_cfg(cfg)), off), "moe_layer_plan_offsets")
+    return dict(zip(("seg_offsets", "seg_expert", "assign_to_row", "row_to_token"), off))
 
 
 def _ptr(t):

@@ -18,8 +18,7 @@ Layout make_layout(const moe_config& c) {
   Layout L{};
   const size_t A = (size_t)c.T * c.k;
   const size_t eb = c.act_dtype == MOE_DT_F32 ? 4 : 2;
-  const int ways = c.n_hot_split > 0 ? c.split_ways : 1;
-  const size_t nbins = (size_t)c.E * ways;
+  const size_t nbins = (size_t)c.E * bin_ways(c);
   const size_t nb = (size_t)num_chunks((int64_t)A);
   const size_t S = (size_t)num_segments(c);
   size_t o = 0;
@@ -81,6 +80,9 @@ moe_status check_config(const moe_config* c) {
   }
   if (c->n_hot_split < 0 || c->split_ways < 1) return MOE_ERR_INVALID_ARG;
   if (c->split_ways > kMaxWays) return MOE_ERR_UNSUPPORTED;
+  if (c->split_mode != MOE_SPLIT_PARITY && c->split_mode != MOE_SPLIT_BOUNDED)
+    return MOE_ERR_INVALID_ARG;
+  if (c->split_c_permille < 0 || c->split_c_permille > 100000) return MOE_ERR_INVALID_ARG;
   if (c->shared_I < 0) return MOE_ERR_INVALID_ARG;
   if ((int64_t)c->T * c->k > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED;
   // the kernels address each activation and weight matrix with 32-bit byte
@@ -266,6 +268,18 @@ int32_t moe_num_segments(const moe_config* cfg) {
 size_t moe_workspace_size(const moe_config* cfg) {
   if (check_config(cfg) != MOE_OK) return 0;
   return make_layout(*cfg).l_end;
+}
+
+moe_status moe_layer_plan_offsets(const moe_config* cfg, size_t offsets[4]) {
+  const moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!offsets) return MOE_ERR_INVALID_ARG;
+  const Layout L = make_layout(*cfg);
+  offsets[0] = L.seg_offsets;
+  offsets[1] = L.seg_expert;
+  offsets[2] = L.assign_to_row;
+  offsets[3] = L.row_to_token;
+  return MOE_OK;
 }
 
 moe_status moe_route_topk(const moe_config* cfg, const float* logits, int32_t* topk_ids,

@@ -35,6 +35,13 @@ constexpr int kSmallA = 1024;  // assignments up to which one workgroup routes a
 
 inline size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
 
+// Replicas per hot expert (1 when nothing is split) and the histogram bins
+// per expert: a replica is its own bin only in the parity split.
+inline int split_ways(const moe_config& c) { return c.n_hot_split > 0 ? c.split_ways : 1; }
+inline int bin_ways(const moe_config& c) {
+  return c.split_mode == MOE_SPLIT_PARITY ? split_ways(c) : 1;
+}
+
 // Assignment chunk of one histogram / rank block: a multiple of 64, at least
 // 256, grown so that there are at most ~256 chunks.
 inline int chunk_len(int64_t A) {

@@ -5,7 +5,9 @@
 //
 // Four kernels, no global atomics, deterministic output:
 //  1. hist:   one block per chunk of assignments counts them per bin
-//             (expert, t mod ways) in LDS -> cnt_bin[bin][chunk].
+//             (expert, t mod bin_ways) in LDS -> cnt_bin[bin][chunk]; a bin
+//             is a replica in the parity split (bin_ways = split_ways), the
+//             whole expert otherwise (bin_ways = 1).
 //  2. plan:   one block: expert counts, the hot experts, the segment list,
 //             seg_offsets (exclusive scan), per-(segment, chunk) bases
 //             blk_off[s][b] = seg_offsets[s] + rows of s in chunks < b, and
@@ -39,13 +41,13 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
 }
 
 __global__ __launch_bounds__(1024) void plan_kernel(
-    const int32_t* __restrict__ cnt_bin, int nb, int E, int ways, int n_hot,
-    int32_t* __restrict__ counts, int32_t* __restrict__ seg_offsets,
+    const int32_t* __restrict__ cnt_bin, int nb, int E, int bin_ways, int ways, int n_hot,
+    int c, int32_t* __restrict__ counts, int32_t* __restrict__ seg_offsets,
     int32_t* __restrict__ seg_expert, int32_t* __restrict__ seg_of_bin,
     int32_t* __restrict__ blk_off, float* __restrict__ bal) {
   __shared__ plan_dev::PlanLds L;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int nbins = E * ways;
+  const int nbins = E * bin_ways;
 
   // bin totals: one wave per bin, coalesced over chunks
   for (int bin = wv; bin < nbins; bin += 16) {
@@ -56,23 +58,26 @@ __global__ __launch_bounds__(1024) void plan_kernel(
     if (lane == 0) L.tot[bin] = s;
   }
   __syncthreads();
-  const int S = plan_dev::plan_segments(L, E, ways, n_hot, counts, seg_offsets, seg_expert,
-                                        seg_of_bin, bal);
+  const int S = plan_dev::plan_segments(L, E, bin_ways, ways, n_hot, c, counts, seg_offsets,
+                                        seg_expert, seg_of_bin, bal);
 
-  // per-(segment, chunk) bases: one wave per segment scans over chunks
+  // per-(segment, chunk) bases: one wave per segment scans over chunks.  In
+  // the load-bounded split only the first segment of a hot expert is ever
+  // looked up (its rows run on through the later ones); the later replica
+  // segments get bases too, which nothing reads.
   for (int s = wv; s < S; s += 16) {
     const int e = L.seg_exp[s];
     const int f = L.seg_first[e];
-    const bool hot = L.seg_first[e + 1] - f > 1;
+    const bool per_replica = L.seg_first[e + 1] - f > 1 && bin_ways > 1;
     int carry = L.seg_off[s];
     for (int b0 = 0; b0 < nb; b0 += 64) {
       const int b = b0 + lane;
       int v = 0;
       if (b < nb) {
-        if (hot) {
-          v = cnt_bin[(size_t)(e * ways + (s - f)) * nb + b];
+        if (per_replica) {
+          v = cnt_bin[(size_t)(e * bin_ways + (s - f)) * nb + b];
         } else {
-          for (int p = 0; p < ways; ++p) v += cnt_bin[(size_t)(e * ways + p) * nb + b];
+          for (int p = 0; p < bin_ways; ++p) v += cnt_bin[(size_t)(e * bin_ways + p) * nb + b];
         }
       }
       const int incl = plan_dev::wave_incl_scan(v, lane);
@@ -134,7 +139,8 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ id
 template <int VPL>
 __global__ __launch_bounds__(1024) void route_permute_small_kernel(
     const float* __restrict__ logits, int T, int E, int k, int score, int n_group,
-    int topk_group, int topn, int renorm, int ways, int n_hot, int32_t* __restrict__ ids,
+    int topk_group, int topn, int renorm, int bin_ways, int ways, int n_hot, int c,
+    int32_t* __restrict__ ids,
     float* __restrict__ w, int32_t* __restrict__ counts, int32_t* __restrict__ seg_offsets,
     int32_t* __restrict__ seg_expert, int32_t* __restrict__ a2r, int32_t* __restrict__ r2t,
     float* __restrict__ row_w, float* __restrict__ bal) {
@@ -144,7 +150,7 @@ __global__ __launch_bounds__(1024) void route_permute_small_kernel(
   __shared__ float w_a[kSmallA];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int A = T * k;
-  for (int i = tid; i < E * ways; i += 1024) L.tot[i] = 0;
+  for (int i = tid; i < E * bin_ways; i += 1024) L.tot[i] = 0;
   __syncthreads();
   for (int t = wv; t < T; t += 16) {
     int my_id;
@@ -157,12 +163,14 @@ __global__ __launch_bounds__(1024) void route_permute_small_kernel(
       w[a] = my_w;
       id_a[a] = my_id;
       w_a[a] = my_w;
-      atomicAdd(&L.tot[my_id * ways + t % ways], 1);
+      atomicAdd(&L.tot[my_id * bin_ways + t % bin_ways], 1);
     }
   }
   __syncthreads();
-  plan_dev::plan_segments(L, E, ways, n_hot, counts, seg_offsets, seg_expert, seg_of_bin, bal);
-  for (int a = tid; a < A; a += 1024) id_a[a] = seg_of_bin[id_a[a] * ways + (a / k) % ways];
+  plan_dev::plan_segments(L, E, bin_ways, ways, n_hot, c, counts, seg_offsets, seg_expert,
+                          seg_of_bin, bal);
+  for (int a = tid; a < A; a += 1024)
+    id_a[a] = seg_of_bin[id_a[a] * bin_ways + (a / k) % bin_ways];
   __syncthreads();
   for (int a = tid; a < A; a += 1024) {
     const int sa = id_a[a];
@@ -202,10 +210,9 @@ template <int VPL>
 void launch_small_vpl(const moe_config& c, const float* logits, int32_t* ids, float* w,
                       int32_t* counts, int32_t* seg_offsets, int32_t* seg_expert, int32_t* a2r,
                       int32_t* r2t, float* row_w, float* bal, hipStream_t s) {
-  const int ways = c.n_hot_split > 0 ? c.split_ways : 1;
   route_permute_small_kernel<VPL><<<1, 1024, 0, s>>>(
       logits, c.T, c.E, c.k, c.score, c.n_group, c.topk_group, c.group_score_topn,
-      c.renormalize, ways, c.n_hot_split, ids, w, counts, seg_offsets, seg_expert, a2r, r2t,
+      c.renormalize, bin_ways(c), split_ways(c), c.n_hot_split, c.split_c_permille, ids, w, counts, seg_offsets, seg_expert, a2r, r2t,
       row_w, bal);
 }
 
@@ -233,17 +240,18 @@ void launch_permute(const moe_config& c, const void* x, const int32_t* ids, void
                     int32_t* counts, float* bal, const float* w, float* row_w, char* ws,
                     const Layout& L, hipStream_t s) {
   const int A = c.T * c.k;
-  const int ways = c.n_hot_split > 0 ? c.split_ways : 1;
+  const int bw = bin_ways(c);
   const int chunk = chunk_len(A);
   const int nb = num_chunks(A);
   const int S = num_segments(c);
   int32_t* cnt_bin = reinterpret_cast<int32_t*>(ws + L.cnt_bin);
   int32_t* blk_off = reinterpret_cast<int32_t*>(ws + L.blk_off);
   int32_t* seg_of_bin = reinterpret_cast<int32_t*>(ws + L.seg_of_bin);
-  hist_kernel<<<nb, 256, 0, s>>>(ids, A, c.k, c.E, ways, chunk, nb, cnt_bin);
-  plan_kernel<<<1, 1024, 0, s>>>(cnt_bin, nb, c.E, ways, c.n_hot_split, counts, seg_offsets,
-                                 seg_expert, seg_of_bin, blk_off, bal);
-  rank_kernel<<<nb, 64, S * sizeof(int), s>>>(ids, A, c.k, c.E, ways, chunk, nb, S,
+  hist_kernel<<<nb, 256, 0, s>>>(ids, A, c.k, c.E, bw, chunk, nb, cnt_bin);
+  plan_kernel<<<1, 1024, 0, s>>>(cnt_bin, nb, c.E, bw, split_ways(c), c.n_hot_split,
+                                 c.split_c_permille, counts, seg_offsets, seg_expert, seg_of_bin,
+                                 blk_off, bal);
+  rank_kernel<<<nb, 64, S * sizeof(int), s>>>(ids, A, c.k, c.E, bw, chunk, nb, S,
                                               seg_of_bin, blk_off, a2r, r2t, w, row_w);
   if (!x_perm) return;  // the caller reads rows of x through row_to_token
   const int eb = c.act_dtype == MOE_DT_F32 ? 4 : 2;

@@ -50,7 +50,7 @@ __device__ inline int block_exclusive_scan(int* data, int n, int* wave_tot) {
 
 // LDS scratch of plan_segments, declared by the calling kernel.
 struct PlanLds {
-  int tot[kMaxBins];            // in: assignments per bin (expert, t mod ways)
+  int tot[kMaxBins];            // in: assignments per bin (expert, t mod bin_ways)
   int cnt_e[kMaxE];             // assignments per logical expert
   int seg_first[kMaxE + 1];     // first segment of each expert; [E] = S
   int seg_off[kMaxSegments + 1];  // out: exclusive offsets of the segments
@@ -59,12 +59,34 @@ struct PlanLds {
   int red[2][16];
 };
 
+// Load of replica p of a hot expert with d assignments in the load-bounded
+// split (Zepp paper, section 4.1, Eq. 1 with the integer-rounded bounds and
+// the greedy water-filling of section 5, "Routing"): with q = d / ways and
+// C = c / 1000 every load lies in [floor(q (1 - C)), ceil(q (1 + C))];
+// replicas are filled in order, each up to the upper bound but leaving the
+// later replicas their lower bounds.  Exact integer arithmetic.
+__device__ inline void bounded_loads(int d, int ways, int c, int* out) {
+  const int64_t den = 1000ll * ways;
+  const int64_t lb = c >= 1000 ? 0 : (int64_t)d * (1000 - c) / den;
+  const int64_t ub = ((int64_t)d * (1000 + c) + den - 1) / den;
+  int64_t left = d;
+  for (int p = 0; p < ways; ++p) {
+    const int64_t n = min(ub, left - (int64_t)(ways - 1 - p) * lb);
+    out[p] = (int)n;
+    left -= n;
+  }
+}
+
 // From bin totals to expert counts, the hot experts (the n_hot largest
 // counts, lower id on a tie) with `ways` replica segments each, segment
 // offsets, the bin -> segment map and balancedness = (sum/E) / max by one fp64
-// division of exact integers.  Writes counts[E], seg_offsets[S+1],
-// seg_expert[S], seg_of_bin[E*ways] and bal[0]; returns S.
-__device__ inline int plan_segments(PlanLds& L, int E, int ways, int n_hot,
+// division of exact integers.  Bins are (expert, t mod bin_ways): bin_ways =
+// ways for the parity split (a replica is one bin), 1 otherwise (c >= 0 is
+// then the relaxation of the load-bounded split, and every bin maps to the
+// expert's first segment: its rows run on through the replica segments).
+// Writes counts[E], seg_offsets[S+1], seg_expert[S], seg_of_bin[E*bin_ways]
+// and bal[0]; returns S.
+__device__ inline int plan_segments(PlanLds& L, int E, int bin_ways, int ways, int n_hot, int c,
                                     int32_t* __restrict__ counts,
                                     int32_t* __restrict__ seg_offsets,
                                     int32_t* __restrict__ seg_expert, int32_t* seg_of_bin,
@@ -72,7 +94,7 @@ __device__ inline int plan_segments(PlanLds& L, int E, int ways, int n_hot,
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   for (int e = tid; e < E; e += 1024) {
     int s = 0;
-    for (int p = 0; p < ways; ++p) s += L.tot[e * ways + p];
+    for (int p = 0; p < bin_ways; ++p) s += L.tot[e * bin_ways + p];
     L.cnt_e[e] = s;
     counts[e] = s;
   }
@@ -103,9 +125,17 @@ __device__ inline int plan_segments(PlanLds& L, int E, int ways, int n_hot,
     for (int p = 0; p < nseg; ++p) {
       L.seg_exp[f + p] = e;
       seg_expert[f + p] = e;
-      L.seg_off[f + p] = nseg > 1 ? L.tot[e * ways + p] : L.cnt_e[e];
     }
-    for (int p = 0; p < ways; ++p) seg_of_bin[e * ways + p] = nseg > 1 ? f + p : f;
+    if (nseg == 1) {
+      L.seg_off[f] = L.cnt_e[e];
+    } else if (bin_ways > 1) {
+      for (int p = 0; p < nseg; ++p) L.seg_off[f + p] = L.tot[e * bin_ways + p];
+    } else {
+      int loads[kMaxWays];
+      bounded_loads(L.cnt_e[e], nseg, c, loads);
+      for (int p = 0; p < nseg; ++p) L.seg_off[f + p] = loads[p];
+    }
+    for (int p = 0; p < bin_ways; ++p) seg_of_bin[e * bin_ways + p] = nseg > 1 ? f + p : f;
   }
   __syncthreads();
 

@@ -101,6 +101,11 @@ WORKLOADS = {
 for _n in ("decode", "prefill_skew", "deepseek_v3", "ragged_stress"):
     _b = WORKLOADS[_n + "_bf16"]
     WORKLOADS[_n + "_fp8w"] = dataclasses.replace(_b, name=_n + "_fp8w", weights="fp8")
+# The ragged layer with its hot experts split by load bounds (C = 0.1) instead
+# of token parity.
+WORKLOADS["ragged_stress_bounded_bf16"] = dataclasses.replace(
+    WORKLOADS["ragged_stress_bf16"], name="ragged_stress_bounded_bf16", split_mode="bounded",
+    split_c_permille=100)
 
 
 def _rng(cfg: MoEShape, tensor_id: int, expert_id: int = 0) -> np.random.Generator:

@@ -128,6 +128,12 @@ def run_layer(moe, cfg, d):
         moe.moe_layer_forward(cfg, d["logits"], d["x"], d["w13"], d["w2"], d["sw13"], d["sw2"],
                               o["out"], o["ids"], o["w"], o["counts"], o["bal"], ws)
     torch.cuda.synchronize()
+    # the permutation the layer built, from where it leaves it in the workspace
+    off = moe.moe_layer_plan_offsets(cfg)
+    S, A = moe.moe_num_segments(cfg), cfg.T * cfg.k
+    for key, name, n in (("seg_offsets", "seg_offsets", S + 1), ("seg_expert", "seg_expert", S),
+                         ("a2r", "assign_to_row", A), ("r2t", "row_to_token", A)):
+        o[key] = ws[off[name]:off[name] + 4 * n].view(torch.int32).clone()
     return o
 
 

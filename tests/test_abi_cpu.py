@@ -70,7 +70,8 @@ def _layer(moe, cfg, ws_bytes=None, **override):
     ("E", 0, -1), ("k", 0, -1), ("H", -8, -1), ("I", 0, -1), ("T", -1, -1),
     ("k", 65, -2), ("E", 2048, -2), ("act_dtype", 7, -1), ("score", 3, -1),
     ("n_group", 3, -1), ("split_ways", 9, -2), ("H", 100, -2), ("I", 96, -2),
-    ("shared_I", 32, -2), ("renormalize", 2, -1),
+    ("shared_I", 32, -2), ("renormalize", 2, -1), ("split_mode", 2, -1),
+    ("split_c_permille", -1, -1), ("split_c_permille", 100001, -1),
     ("H", 1 << 24, -2),   # T*k*H reaches 2^31 elements: beyond 32-bit byte offsets
 ])
 def test_bad_config_is_rejected(moe, field, value, status):

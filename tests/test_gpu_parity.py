@@ -1,7 +1,8 @@
 """GPU parity of every C-ABI call against the CPU oracle on small layers that
 the whole oracle finishes in seconds, spanning several tiles with ragged
 tails, plus the degenerate cases (one expert, k = E, one hot expert taking
-every token, replica splits, dropped ids, an empty batch)."""
+every token, parity and load-bounded replica splits, dropped ids, an empty
+batch)."""
 import numpy as np
 import pytest
 import torch
@@ -37,6 +38,22 @@ SHAPES = {
     # many rows per segment (256 x 256 tiles), N and K tails in both GEMMs
     "bf16_big_tiles": mi.MoEShape("t12", T=1100, H=320, E=3, k=1, I=192, zipf_s=1.0,
                                   seed=25),
+    # load-bounded replica splits: balanced (C = 0), relaxed, and C large enough
+    # that replica 0 takes everything; both the one-workgroup path (T*k <= 1024)
+    # and the four-kernel permutation
+    "bf16_bounded_split": mi.MoEShape("t13", T=300, H=576, E=16, k=4, I=320, zipf_s=1.2,
+                                      n_hot_split=3, split_ways=2, split_mode="bounded",
+                                      seed=26),
+    "bf16_bounded_three_way": mi.MoEShape("t14", T=257, H=128, E=12, k=3, I=64, zipf_s=1.5,
+                                          n_hot_split=2, split_ways=3, split_mode="bounded",
+                                          split_c_permille=500, seed=27),
+    "bf16_bounded_decode": mi.MoEShape("t15", T=40, H=1024, E=32, k=2, I=512, zipf_s=1.0,
+                                       n_hot_split=4, split_ways=4, split_mode="bounded",
+                                       split_c_permille=250, seed=28),
+    "f32_bounded_all_to_first": mi.MoEShape("t16", T=50, H=132, E=10, k=3, I=70, dtype="f32",
+                                            zipf_s=1.0, n_hot_split=2, split_ways=4,
+                                            split_mode="bounded", split_c_permille=3000,
+                                            seed=29),
 }
 
 
@@ -128,8 +145,9 @@ def test_layer_forward(moe, case):
     r = case.ref
     gu.check_routing(c, o["ids"].cpu().numpy(), o["w"].cpu().numpy(), r["ids"], r["w"],
                      r["group_gap"], case.logits)
-    assert (o["counts"].cpu().numpy() == r["counts"]).all()
-    assert o["bal"].cpu().numpy()[0] == r["balancedness"]
+    # the layer's own permutation (one workgroup for T*k <= 1024, else the
+    # four-kernel path), bit for bit
+    gu.check_plan(o, r)
     err = gu.rel_err(gu.host_f64(o["out"]), r["out"])
     print(f"  layer rel err {err:.3e}")
     assert err <= gu.rel_tol(c), err
@@ -153,9 +171,11 @@ def test_one_hot_expert_takes_every_token(moe):
     assert gu.rel_err(gu.host_f64(o["out"]), case.ref["out"]) <= gu.BF16_REL
 
 
-def test_dropped_ids(moe):
+@pytest.mark.parametrize("split_mode", ["parity", "bounded"])
+def test_dropped_ids(moe, split_mode):
     """Ids outside [0, E) join no segment and get assign_to_row = -1."""
-    cfg = mi.MoEShape("drop", T=40, H=128, E=6, k=3, I=64, n_hot_split=1, split_ways=2, seed=22)
+    cfg = mi.MoEShape("drop", T=40, H=128, E=6, k=3, I=64, n_hot_split=1, split_ways=2,
+                      split_mode=split_mode, split_c_permille=200, seed=22)
     rng = np.random.default_rng(0)
     ids = rng.integers(0, cfg.E, size=(cfg.T, cfg.k)).astype(np.int32)
     bad = rng.random((cfg.T, cfg.k)) < 0.2
@@ -165,7 +185,15 @@ def test_dropped_ids(moe):
     valid = ~bad.ravel()
     counts = np.bincount(ids.ravel()[valid], minlength=cfg.E)
     se, sr = orc.segment_list(counts, cfg.n_hot_split, cfg.split_ways)
-    seg = orc.segment_of_assignments(np.where(bad, 0, ids), se, sr, cfg.split_ways)
+    if split_mode == "parity":
+        seg = orc.segment_of_assignments(np.where(bad, 0, ids), se, sr, cfg.split_ways)
+    else:
+        # the valid assignments alone, in increasing a, as one column
+        loads = {int(e): orc.replica_loads(int(counts[e]), cfg.split_ways, cfg.split_c_permille)
+                 for e in set(se[sr >= 0].tolist())}
+        seg = np.zeros(ids.size, dtype=np.int64)
+        seg[valid] = orc.segment_of_assignments(ids.ravel()[valid][:, None], se, sr,
+                                                cfg.split_ways, loads)
     seg = np.where(valid, seg, len(se))   # dropped -> a sentinel past the end
     so, r2a, a2r, r2t = orc.permutation(seg, len(se) + 1, cfg.k)
     a2r = np.where(valid, a2r, -1)

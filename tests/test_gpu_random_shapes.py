@@ -31,6 +31,8 @@ def _random_shape(rng, i):
         kw["group_score_topn"] = int(rng.integers(1, min(per, 3) + 1))
     if rng.random() < 0.4 and E >= 2:
         kw.update(n_hot_split=int(rng.integers(1, min(E, 4) + 1)), split_ways=int(rng.integers(2, 4)))
+        if rng.random() < 0.5:
+            kw.update(split_mode="bounded", split_c_permille=int(rng.choice([0, 100, 700, 2500])))
     if dtype == "bf16" and rng.random() < 0.2:
         kw["shared_I"] = int(rng.choice([64, 128, 256]))
     if rng.random() < 0.2:

@@ -33,13 +33,15 @@ def _sample_tokens(cfg, ids, rng):
     for parity in (0, 1):
         sel = users[users % 2 == parity]
         toks |= set(sel[:2].tolist())
+    toks |= set(users[-2:].tolist())   # the last replica of a load-bounded split
     return np.array(sorted(toks))
 
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["tiny_fp32", "decode_bf16", "prefill_skew_bf16",
                                   "ragged_stress_bf16", "deepseek_v3_bf16", "decode_fp8w",
-                                  "prefill_skew_fp8w", "ragged_stress_fp8w", "deepseek_v3_fp8w"])
+                                  "prefill_skew_fp8w", "ragged_stress_fp8w", "deepseek_v3_fp8w",
+                                  "ragged_stress_bounded_bf16"])
 def test_workload_full_size(name):
     import mixture_experts_layer_segments_amd as moe
     cfg = mi.WORKLOADS[name]
@@ -108,6 +110,8 @@ def test_workload_full_size(name):
         print(f"[workload] {name}: codes of {len(codes_ref)} experts match", flush=True)
     ids_g = o["ids"].cpu().numpy()
     mism = gu.check_routing(cfg, ids_g, o["w"].cpu().numpy(), ids_r, w_r, gap, logits)
+    if mism.size == 0:
+        gu.check_plan(o, plan_r)      # the permutation the layer built, bit for bit
     assert (o["counts"].cpu().numpy() == plan_r["counts"]).all()
     assert o["bal"].cpu().numpy()[0] == plan_r["balancedness"]
     got = gu.host_f64(o["out"][torch.from_numpy(toks).to(dev)])
