@@ -58,6 +58,8 @@ class MoEShape:
     split_mode: str = "parity"  # "parity": replica = token index mod ways;
                                 # "bounded": consecutive runs, water-filled loads
     split_c_permille: int = 0   # relaxation ratio C of the bounded split, in 1/1000
+    capacity_factor_permille: int = 0   # > 0: fixed slots per expert = ceil(f * mean),
+                                        # overflow dropped (masked layout)
     shared_I: int = 0           # shared expert intermediate (0 = none)
     x_std: float = 1.0
     w_std: float = 0.02

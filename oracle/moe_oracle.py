@@ -37,7 +37,11 @@ t mod ways == p; in the load-bounded split (Zepp section 4.1, Eq. 1 and
 section 5, "Routing", restricted to one GPU) the replicas take consecutive
 runs of the expert's assignments in increasing a, with loads chosen by
 greedy water-filling in replica order under the integer-rounded bounds
-floor(q(1-C)) <= load <= ceil(q(1+C)), q = d / ways.
+floor(q(1-C)) <= load <= ceil(q(1+C)), q = d / ways.  With a capacity
+factor f (the book's "Capacity, padding, and the drop decision"), each expert
+gets ceil(f * mean) fixed slots, the assignments beyond them (in increasing
+a) are dropped and contribute zero, and the rows follow the fixed-size masked
+layout of the MoE inference blog ("Prefill and decode kernel layouts").
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` to facts that
 do not come from this file (printed numbers, closed forms, brute force,
@@ -243,6 +247,55 @@ def permutation(seg_of_a: np.ndarray, S: int, k: int):
             assign_to_row.astype(np.int32), (row_to_assign // k).astype(np.int32))
 
 
+def capacity(A: int, E: int, factor_permille: int) -> int:
+    """Slots per expert of the fixed-capacity layout ("Capacity, padding, and
+    the drop decision"): a multiple of the mean load A / E, here
+    factor = factor_permille / 1000, rounded up so that the slots hold at
+    least factor x mean assignments.  Exact integer arithmetic."""
+    return -(-A * factor_permille // (1000 * E))
+
+
+def capacity_plan(ids: np.ndarray, E: int, cap: int):
+    """The fixed-size masked layout of the MoE inference blog ("Prefill and
+    decode kernel layouts") with the drop rule of the book's "Capacity,
+    padding, and the drop decision": expert e owns rows [e*cap, (e+1)*cap);
+    its assignments, in increasing a = t*k + j, take those rows in order, and
+    the ones that find them full are dropped (assign_to_row = -1).
+
+    Segments: 2E of them, segment 2e = expert e's kept rows, segment 2e+1 =
+    its unused slots (expert -1: padding, computed by nobody).  Rows of the
+    padding have row_to_token = -1.
+    """
+    T, k = ids.shape
+    A = T * k
+    used = np.zeros(E, dtype=np.int64)
+    a2r = np.full(A, -1, dtype=np.int64)
+    for a in range(A):
+        e = int(ids[a // k, a % k])
+        if not 0 <= e < E:
+            continue
+        if used[e] < cap:
+            a2r[a] = e * cap + used[e]
+        used[e] += 1
+    kept = np.minimum(used, cap)
+    seg_offsets = np.zeros(2 * E + 1, dtype=np.int64)
+    seg_expert = np.empty(2 * E, dtype=np.int64)
+    for e in range(E):
+        seg_offsets[2 * e] = e * cap
+        seg_offsets[2 * e + 1] = e * cap + kept[e]
+        seg_expert[2 * e] = e
+        seg_expert[2 * e + 1] = -1
+    seg_offsets[2 * E] = E * cap
+    r2a = np.full(E * cap, -1, dtype=np.int64)
+    r2a[a2r[a2r >= 0]] = np.nonzero(a2r >= 0)[0]
+    r2t = np.where(r2a >= 0, r2a // k, -1)
+    return dict(seg_offsets=seg_offsets.astype(np.int32), seg_expert=seg_expert.astype(np.int32),
+                seg_replica=np.full(2 * E, -1, dtype=np.int32),
+                assign_to_row=a2r.astype(np.int32), row_to_assign=r2a.astype(np.int32),
+                row_to_token=r2t.astype(np.int32), overflow=(used - kept).astype(np.int32),
+                capacity=cap)
+
+
 def balancedness(loads) -> np.float32:
     """mean(loads) / max(loads) ("The slowest expert sets the pace"), in
     float64, rounded once to fp32.  Zero loads count in the mean."""
@@ -268,24 +321,31 @@ def swiglu(x_rows: np.ndarray, w13_e: np.ndarray, w2_e: np.ndarray) -> np.ndarra
 
 def grouped_ffn(x_perm: np.ndarray, seg_offsets, seg_expert, w13: np.ndarray, w2: np.ndarray):
     """Every segment through its expert ("Follow one token through an MoE
-    layer", step 3): y_perm rows in the permuted order, float64."""
+    layer", step 3): y_perm rows in the permuted order, float64.  A segment
+    whose expert lies outside [0, E) is padding: nothing is computed for it
+    (its rows stay zero here)."""
+    E = w13.shape[0]
     y = np.zeros((x_perm.shape[0], w2.shape[1]), dtype=np.float64)
     for s in range(len(seg_expert)):
         r0, r1 = int(seg_offsets[s]), int(seg_offsets[s + 1])
-        if r1 > r0:
-            e = int(seg_expert[s])
+        e = int(seg_expert[s])
+        if r1 > r0 and 0 <= e < E:
             y[r0:r1] = swiglu(x_perm[r0:r1], w13[e], w2[e])
     return y
 
 
 def combine(y_perm: np.ndarray, assign_to_row, w: np.ndarray, shared_y=None):
     """Inverse permutation and router-weighted sum ("Follow one token through
-    an MoE layer", step 4), plus the shared expert with weight 1."""
+    an MoE layer", step 4), plus the shared expert with weight 1.  A dropped
+    assignment (row -1) contributes nothing: its output for the layer is zero
+    ("Capacity, padding, and the drop decision")."""
     T, k = w.shape
     out = np.zeros((T, y_perm.shape[1]), dtype=np.float64)
     for t in range(T):
         for j in range(k):
-            out[t] += w[t, j] * y_perm[assign_to_row[t * k + j]]
+            r = int(assign_to_row[t * k + j])
+            if r >= 0:
+                out[t] += w[t, j] * y_perm[r]
     if shared_y is not None:
         out += shared_y
     return out
@@ -305,6 +365,11 @@ def route(cfg, logits):
 def plan(cfg, ids):
     """Histogram, segments, permutation and balancedness for routed ids."""
     counts = expert_counts(ids, cfg.E)
+    cf = getattr(cfg, "capacity_factor_permille", 0)
+    if cf > 0:
+        p = capacity_plan(ids, cfg.E, capacity(ids.size, cfg.E, cf))
+        p.update(counts=counts, balancedness=balancedness(counts))
+        return p
     seg_expert, seg_replica = segment_list(counts, cfg.n_hot_split, cfg.split_ways)
     loads = None
     if getattr(cfg, "split_mode", "parity") == "bounded":
@@ -324,7 +389,8 @@ def layer_forward(cfg, logits, x64, w13_64, w2_64, sw13_64=None, sw2_64=None):
     path, keyed by name."""
     ids, w, gap = route(cfg, logits)
     p = plan(cfg, ids)
-    x_perm = x64[p["row_to_token"]]
+    r2t = p["row_to_token"]
+    x_perm = np.where((r2t >= 0)[:, None], x64[np.maximum(r2t, 0)], 0.0)
     y_perm = grouped_ffn(x_perm, p["seg_offsets"], p["seg_expert"], w13_64, w2_64)
     shared_y = swiglu(x64, sw13_64, sw2_64) if sw13_64 is not None else None
     out = combine(y_perm, p["assign_to_row"], w, shared_y)

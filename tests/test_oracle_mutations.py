@@ -165,6 +165,37 @@ def parity_for_bounded(ids, seg_expert, seg_replica, ways, loads=None):
     return orig_soa(ids, seg_expert, seg_replica, ways, None)
 
 
+orig_capacity_plan = o.capacity_plan
+
+
+def capacity_rounded_down(A, E, factor_permille):
+    return A * factor_permille // (1000 * E)
+
+
+def keeps_the_latest(ids, E, cap):
+    """Drops the earliest assignments of a full expert instead of the latest."""
+    rev = ids.ravel()[::-1].reshape(ids.shape[0] * ids.shape[1], 1)
+    p = orig_capacity_plan(rev, E, cap)
+    k = ids.shape[1]
+    a2r = p["assign_to_row"][::-1].copy()
+    r2a = np.full(E * cap, -1)
+    r2a[a2r[a2r >= 0]] = np.nonzero(a2r >= 0)[0]
+    p.update(assign_to_row=a2r, row_to_assign=r2a, row_to_token=np.where(r2a >= 0, r2a // k, -1))
+    return p
+
+
+def never_drops(ids, E, cap):
+    return orig_capacity_plan(ids, E, max(cap, int(np.bincount(ids.ravel(), minlength=E).max())))
+
+
+def dropped_rows_wrap_around(y_perm, assign_to_row, w, shared_y=None):
+    T, k = w.shape
+    out = np.zeros((T, y_perm.shape[1]))
+    for a in range(T * k):
+        out[a // k] += w[a // k, a % k] * y_perm[assign_to_row[a]]   # row -1: the last row
+    return out if shared_y is None else out + shared_y
+
+
 MISTAKES = [
     ("route_flat", ascending_route),
     ("route_flat", never_renormalised),
@@ -183,6 +214,10 @@ MISTAKES = [
     ("replica_loads", floor_upper_bound),
     ("replica_loads", last_replica_first),
     ("segment_of_assignments", parity_for_bounded),
+    ("capacity", capacity_rounded_down),
+    ("capacity_plan", keeps_the_latest),
+    ("capacity_plan", never_drops),
+    ("combine", dropped_rows_wrap_around),
 ]
 
 

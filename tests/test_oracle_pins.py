@@ -307,6 +307,95 @@ def test_bounded_split_only_moves_segment_boundaries(c):
         assert (a["ids"].ravel()[rows] == e).all() and (np.diff(rows) > 0).all()
 
 
+# ------------------------------------------------- capacity and drop
+def _ids_with_counts(counts, k):
+    """[T, k] ids with the given per-expert counts and distinct experts per
+    token: the assignments sorted by expert, slot j of token t taking item
+    j*T + t (T >= the largest count keeps a token's experts distinct)."""
+    items = np.repeat(np.arange(len(counts)), counts)
+    T = len(items) // k
+    assert T >= max(counts)
+    ids = items.reshape(k, T).T.copy()
+    assert all(len(set(r.tolist())) == k for r in ids)
+    return ids
+
+
+def test_capacity_worked_example():
+    """1.25 x the mean of 8 gives 10 slots per expert, 80 slots for 64
+    assignments, and expert 0 (22 assignments) overflows by 12; sizing every
+    expert for the busiest gives 22 x 8 = 176 slots, about two thirds of them
+    padding ("Capacity, padding, and the drop decision")."""
+    g = _gold("serving_moe_capacity.json")
+    counts = g["expert_counts"]
+    E, A = len(counts), g["assignments"]
+    assert A == sum(counts) and A / E == g["mean_per_expert"]
+    cap = o.capacity(A, E, round(g["capacity_factor"] * 1000))
+    assert cap == g["slots_per_expert"] and E * cap == g["total_slots"]
+    ids = _ids_with_counts(counts, 2)
+    p = o.capacity_plan(ids, E, cap)
+    assert p["overflow"][0] == g["expert0_overflow"]
+    assert p["overflow"].tolist() == [max(0, c - cap) for c in counts]
+    # padding to the maximum: the factor max / mean drops nothing
+    cap_max = o.capacity(A, E, 2750)             # factor 22 / 8 = 2.75
+    assert cap_max == g["pad_to_max_slots_per_expert"]
+    assert E * cap_max == g["pad_to_max_total_slots"]
+    assert abs((E * cap_max - A) / (E * cap_max) - g["pad_to_max_padding_fraction_approx"]) < 0.04
+    assert not o.capacity_plan(ids, E, cap_max)["overflow"].any()
+
+
+def test_capacity_rounds_up_to_hold_factor_times_mean():
+    assert o.capacity(63, 8, 1250) == 10        # 9.84 slots needed -> 10
+    assert o.capacity(64, 8, 1000) == 8
+    assert o.capacity(65, 8, 1000) == 9
+    assert o.capacity(1, 64, 1) == 1
+
+
+@pytest.mark.parametrize("cap", [1, 3, 10])
+def test_masked_layout_and_drop_rule_by_brute_force(cap):
+    """Expert e owns rows [e*cap, (e+1)*cap); its first cap assignments in
+    increasing a fill them in order, the rest are dropped (row -1); the
+    segments are [kept rows of e, padding of e] for every e."""
+    counts = [22, 14, 7, 6, 5, 4, 3, 3]
+    ids = _ids_with_counts(counts, 2)
+    E, k = len(counts), 2
+    p = o.capacity_plan(ids, E, cap)
+    flat = ids.ravel()
+    for e in range(E):
+        mine = [a for a in range(flat.size) if flat[a] == e]
+        for n, a in enumerate(mine):
+            assert p["assign_to_row"][a] == (e * cap + n if n < cap else -1)
+        kept = min(len(mine), cap)
+        assert p["seg_offsets"][2 * e] == e * cap and p["seg_offsets"][2 * e + 1] == e * cap + kept
+        assert p["seg_expert"][2 * e] == e and p["seg_expert"][2 * e + 1] == -1
+        assert (p["row_to_token"][e * cap + kept:(e + 1) * cap] == -1).all()
+    assert p["seg_offsets"][-1] == E * cap
+
+
+def test_capacity_layer_drops_exactly_the_overflow():
+    """The layer with a capacity equals the definition with the dropped
+    slots' terms removed (their outputs become zeros); a capacity that holds
+    every assignment gives the dropless layer."""
+    cfg, lg, x, w13, w2 = _tiny(T=40, E=6, k=3, zipf_s=1.2)
+    free = o.layer_forward(cfg, lg, x, w13, w2)
+    roomy = o.layer_forward(cfg.replace(capacity_factor_permille=2000), lg, x, w13, w2)
+    assert roomy["capacity"] == 40 and (roomy["assign_to_row"] >= 0).all()   # 2 x mean 20
+    np.testing.assert_allclose(roomy["out"], free["out"], rtol=1e-12, atol=1e-13)
+    tight = o.layer_forward(cfg.replace(capacity_factor_permille=900), lg, x, w13, w2)
+    cap = tight["capacity"]
+    assert cap == -(-40 * 3 * 900 // (1000 * 6))
+    ids, w = free["ids"], free["w"]
+    seen, keep = {}, np.zeros(ids.shape, dtype=bool)
+    for t in range(ids.shape[0]):
+        for j in range(ids.shape[1]):
+            e = int(ids[t, j])
+            keep[t, j] = seen.get(e, 0) < cap
+            seen[e] = seen.get(e, 0) + 1
+    assert not keep.all()
+    want = o.token_outputs(list(range(40)), x, ids, np.where(keep, w, 0.0),
+                           lambda e: (w13[e], w2[e]))
+    np.testing.assert_allclose(tight["out"], want, rtol=1e-12, atol=1e-13)
+
+
 # ---------------------------------------------------------------- expert MLP
 def test_swiglu_hand_example():
     """x = [1, 2]; W_gate column [0.5, 0.25] -> g = 1; W_up column [1, -1]
