@@ -71,10 +71,12 @@ def dispatch_bytes(cfg, assignments: int | None = None) -> int:
     return A * cfg.H * cfg.elem_bytes
 
 
-def ffn_flops(cfg) -> int:
-    """Algorithmic flops of the expert MLPs: 6*H*I per assignment (gate, up
-    and down projections), plus 6*H*shared_I per token for a shared expert."""
-    return 6 * cfg.H * cfg.I * cfg.A + 6 * cfg.H * cfg.shared_I * cfg.T
+def ffn_flops(cfg, rows: int | None = None) -> int:
+    """Algorithmic flops of the expert MLPs: 6*H*I per computed assignment
+    (gate, up and down projections; all T*k of them unless a fixed capacity
+    drops some), plus 6*H*shared_I per token for a shared expert."""
+    rows = cfg.A if rows is None else rows
+    return 6 * cfg.H * cfg.I * rows + 6 * cfg.H * cfg.shared_I * cfg.T
 
 
 def weight_bytes(cfg, n: int) -> int:
@@ -86,13 +88,14 @@ def weight_bytes(cfg, n: int) -> int:
     return n * cfg.H * cfg.elem_bytes
 
 
-def ffn_bytes(cfg, active_experts: int) -> int:
+def ffn_bytes(cfg, active_experts: int, rows: int | None = None) -> int:
     """Algorithmic HBM bytes of the grouped FFN: the weights of every active
-    expert read once, x_perm read, h written and read, y_perm written (and the
-    shared expert's weights and rows)."""
+    expert read once, x_perm read, h written and read, y_perm written, for
+    every computed row (and the shared expert's weights and rows)."""
     eb = cfg.elem_bytes
+    rows = cfg.A if rows is None else rows
     w = active_experts * weight_bytes(cfg, 3 * cfg.I)
-    act = cfg.A * (cfg.H * 2 + cfg.I * 2) * eb
+    act = rows * (cfg.H * 2 + cfg.I * 2) * eb
     if cfg.shared_I:
         w += weight_bytes(cfg, 3 * cfg.shared_I)
         act += cfg.T * (cfg.H * 2 + cfg.shared_I * 2) * eb
@@ -169,7 +172,7 @@ def cpu_baseline(cfg, logits, budget_s=20.0):
         n = len(active_experts)
         order = [active_experts[(i * 37) % n] for i in range(n)] if n % 37 else list(active_experts)
         t_ffn, done = [0.0], []
-        y = np.zeros((cfg.A, cfg.H))
+        y = np.zeros((len(p["row_to_token"]), cfg.H))
 
         def run(e, a, b):
             if t_ffn[0] > budget_s:
@@ -288,17 +291,20 @@ def main(argv=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / args.steps
-    active = int((counts.cpu() > 0).sum())   # experts whose weights the step must read
+    counts_h = counts.cpu().numpy()
+    active = int((counts_h > 0).sum())   # experts whose weights the step must read
+    cap = moe.moe_num_rows(cfg) // cfg.E if cfg.capacity_factor_permille else cfg.A
+    computed = int(np.minimum(counts_h, cap).sum())   # rows the FFN computes (drops excluded)
 
     # dominant kernels: the grouped FFN on the permuted rows of this batch
-    S = moe.moe_num_segments(cfg)
+    S, R = moe.moe_num_segments(cfg), moe.moe_num_rows(cfg)
     A = cfg.A
-    x_perm = torch.empty((A, cfg.H), dtype=tdt, device=dev)
-    y_perm = torch.empty((A, cfg.H), dtype=tdt, device=dev)
+    x_perm = torch.empty((R, cfg.H), dtype=tdt, device=dev)
+    y_perm = torch.empty((R, cfg.H), dtype=tdt, device=dev)
     so = torch.empty((S + 1,), dtype=torch.int32, device=dev)
     se = torch.empty((S,), dtype=torch.int32, device=dev)
     a2r = torch.empty((A,), dtype=torch.int32, device=dev)
-    r2t = torch.empty((A,), dtype=torch.int32, device=dev)
+    r2t = torch.empty((R,), dtype=torch.int32, device=dev)
     moe.moe_permute(cfg, d["x"], ids, x_perm, so, se, a2r, r2t, counts, bal, ws)
     for _ in range(2):
         ffn()
@@ -312,8 +318,8 @@ def main(argv=None):
     ffn_ms = f0.elapsed_time(f1) / args.steps
 
     routed = cfg.replace(shared_I=0)
-    fl = ffn_flops(routed)
-    by = ffn_bytes(routed, active)
+    fl = ffn_flops(routed, computed)
+    by = ffn_bytes(routed, active, computed)
     gbs = by / (ffn_ms * 1e-3) / 1e9
     tflops = fl / (ffn_ms * 1e-3) / 1e12
     hbm_bound = fl / (BF16_PEAK_TFLOPS * 1e12) < by / (HBM_PEAK_GBS * 1e9)
@@ -342,7 +348,12 @@ def main(argv=None):
                    "assignments": cfg.A, "active_experts": active,
                    "weights": ("fp8 e4m3, 128x128 power-of-two block scales, dequantized to "
                                "bf16 in the GEMMs") if fp8 else cfg.dtype,
-                   "balancedness": float(bal.item())},
+                   "balancedness": float(bal.item()),
+                   **({"capacity_factor": cfg.capacity_factor_permille / 1000,
+                       "slots_per_expert": cap, "computed_assignments": computed}
+                      if cfg.capacity_factor_permille else {}),
+                   **({"split": cfg.split_mode, "split_c": cfg.split_c_permille / 1000}
+                      if cfg.n_hot_split else {})},
         "grouped_gemm_tflops": round(tflops, 2),
         "grouped_gemm_frac_mfma": round(tflops / BF16_PEAK_TFLOPS, 4),
         "grouped_gemm_frac_hbm": round(gbs / HBM_PEAK_GBS, 4),

@@ -93,7 +93,22 @@ typedef struct moe_config {
   int32_t split_c_permille; /* MOE_SPLIT_BOUNDED: relaxation ratio C of the
                              * load bounds in 1/1000 (0..100000); ignored
                              * otherwise */
+  int32_t capacity_factor_permille; /* 0: dropless, packed segments.  > 0
+                             * (up to 1000000): the fixed-capacity layout
+                             * below, factor f = value / 1000; needs
+                             * n_hot_split = 0 */
 } moe_config;
+/* Fixed-capacity layout (the book's "Capacity, padding, and the drop
+ * decision"; the fixed-size masked layout of the MoE inference blog's
+ * "Prefill and decode kernel layouts"): every expert gets
+ * cap = ceil(f * T*k / E) slots, expert e owning rows [e*cap, (e+1)*cap) of
+ * x_perm / y_perm.  Its assignments, in increasing a = t*k + j, fill those
+ * rows in order; the ones that find them full are dropped (assign_to_row =
+ * -1, no contribution to out: their output for the layer is zero).  There
+ * are S = 2E segments: segment 2e holds expert e's kept rows, segment 2e+1
+ * the rest of its slots, with seg_expert = -1 (padding: no expert computes
+ * it, row_to_token = -1 there).  Routing counts and balancedness are those
+ * of the routed ids, before any drop. */
 /* Size limits (MOE_ERR_UNSUPPORTED beyond them): T*k <= 2^30; each of
  * T*k*H, T*k*I, T*shared_I, 2*I*H and 2*shared_I*H below 2^31 elements (the
  * kernels address every matrix with 32-bit byte offsets); bf16 needs H, I
@@ -103,8 +118,13 @@ typedef struct moe_config {
 const char* moe_status_string(moe_status s);
 
 /* Number of segments S = E + min(n_hot_split, E) * (split_ways - 1)
- * (split_ways > 1 only); -1 if cfg is NULL or invalid. */
+ * (split_ways > 1 only), or 2E in the fixed-capacity layout; -1 if cfg is
+ * NULL or invalid. */
 int32_t moe_num_segments(const moe_config* cfg);
+
+/* Rows R of x_perm, y_perm and row_to_token: T*k, or E * cap in the
+ * fixed-capacity layout; -1 if cfg is NULL or invalid. */
+int32_t moe_num_rows(const moe_config* cfg);
 
 /* Bytes of device workspace that suffices for every call below with this
  * configuration (moe_layer_forward needs all of it; moe_permute and
@@ -131,12 +151,15 @@ moe_status moe_route_topk(const moe_config* cfg, const float* logits,
                           int32_t* topk_ids, float* topk_w, void* stream);
 
 /* Step 2 -- histogram / prefix-sum permutation into contiguous per-expert
- * segments ("Follow one token through an MoE layer", step 1).
+ * segments ("Follow one token through an MoE layer", step 1), or into the
+ * fixed-capacity layout when capacity_factor_permille > 0.  R =
+ * moe_num_rows(cfg).
  *   x             [T, H]  act_dtype.
  *   topk_ids      [T, k]  ids in [0, E); an id outside is dropped (its
  *                          assign_to_row is -1 and it joins no segment).
- *   x_perm        [T*k, H] out: x_perm[r] = x[row_to_token[r]] byte for byte,
- *                          for r < seg_offsets[S]; later rows untouched.
+ *   x_perm        [R, H]  out: x_perm[r] = x[row_to_token[r]] byte for byte,
+ *                          for r < seg_offsets[S] with row_to_token[r] >= 0;
+ *                          other rows untouched.
  *   seg_offsets   [S+1]   out: exclusive prefix sum of segment lengths.
  *   seg_expert    [S]     out: logical expert of each segment.  Segments are
  *                          in ascending expert order; a hot expert (one of the
@@ -146,7 +169,8 @@ moe_status moe_route_topk(const moe_config* cfg, const float* logits,
  *                          selection and weights, Zepp section 4.1).  Empty
  *                          segments stay listed.
  *   assign_to_row [T*k]   out: row of each assignment (-1 if dropped).
- *   row_to_token  [T*k]   out: token of each row (rows < seg_offsets[S]).
+ *   row_to_token  [R]     out: token of each row (rows < seg_offsets[S];
+ *                          -1 on padding rows).
  *   counts        [E]     out: assignments per logical expert.
  *   balancedness  [1]     out, fp32: (sum(counts) / E) / max(counts), from
  *                          exact integers by one fp64 division ("The slowest
@@ -166,14 +190,16 @@ moe_status moe_permute(const moe_config* cfg, const void* x, const int32_t* topk
  * with different token counts).  Per row r of segment s, e = seg_expert[s]:
  *   h = silu(x_perm[r] . W_gate[e]) * (x_perm[r] . W_up[e])   (fp32, rounded
  *       to act_dtype), y_perm[r] = row_scale[r] * (h . W_down[e]).
- *   x_perm      [T*k, H]  rows as produced by moe_permute.
+ * A segment whose seg_expert lies outside [0, E) is skipped (its rows of
+ * y_perm are left untouched): the padding of the fixed-capacity layout.
+ *   x_perm      [R, H]  rows as produced by moe_permute (R = moe_num_rows).
  *   seg_offsets [S+1], seg_expert [S] as produced by moe_permute (read on the
  *               device; the host never needs the counts).
  *   w13         [E, 2I, H] act_dtype, K-contiguous: rows 0..I-1 of expert e
  *               are W_gate[e]^T, rows I..2I-1 are W_up[e]^T.
  *   w2          [E, H, I]  act_dtype, W_down[e]^T.
- *   row_scale   [T*k] fp32 indexed by row, or NULL for 1.0.
- *   y_perm      [T*k, H] out (rows < seg_offsets[S]).
+ *   row_scale   [R] fp32 indexed by row, or NULL for 1.0.
+ *   y_perm      [R, H] out (rows of computed segments).
  * bf16 needs H and I multiples of 64; all pointers 16-byte aligned. */
 moe_status moe_grouped_ffn(const moe_config* cfg, const void* x_perm,
                            const int32_t* seg_offsets, const int32_t* seg_expert,

@@ -20,7 +20,7 @@ EXPORTED_SYMBOLS = (
     "moe_status_string", "moe_num_segments", "moe_workspace_size", "moe_route_topk",
     "moe_permute", "moe_grouped_ffn", "moe_unpermute_combine", "moe_layer_forward",
     "moe_quantize_fp8", "moe_grouped_ffn_fp8w", "moe_layer_forward_fp8w",
-    "moe_layer_plan_offsets",
+    "moe_layer_plan_offsets", "moe_num_rows",
 )
 
 
@@ -29,7 +29,7 @@ class MoEConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "T", "H", "E", "k", "I", "score", "n_group", "topk_group", "group_score_topn",
         "renormalize", "n_hot_split", "split_ways", "shared_I", "act_dtype", "split_mode",
-        "split_c_permille")]
+        "split_c_permille", "capacity_factor_permille")]
 
 
 class MoEError(RuntimeError):
@@ -53,6 +53,8 @@ lib.moe_num_segments.restype = ctypes.c_int32
 lib.moe_num_segments.argtypes = [_cfgp]
 lib.moe_workspace_size.restype = ctypes.c_size_t
 lib.moe_workspace_size.argtypes = [_cfgp]
+lib.moe_num_rows.restype = ctypes.c_int32
+lib.moe_num_rows.argtypes = [_cfgp]
 lib.moe_layer_plan_offsets.restype = ctypes.c_int
 lib.moe_layer_plan_offsets.argtypes = [_cfgp, ctypes.POINTER(ctypes.c_size_t)]
 lib.moe_route_topk.restype = ctypes.c_int
@@ -77,7 +79,7 @@ def make_config(shape) -> MoEConfig:
     """MoEConfig from any object with the layer's fields (T, H, E, k, I,
     dtype 'f32'|'bf16', score 'softmax'|'sigmoid', n_group, topk_group,
     group_score_topn, renormalize, n_hot_split, split_ways, split_mode
-    'parity'|'bounded', split_c_permille, shared_I)."""
+    'parity'|'bounded', split_c_permille, shared_I, capacity_factor_permille)."""
     g = lambda n, d: getattr(shape, n, d)  # noqa: E731
     return MoEConfig(
         T=shape.T, H=shape.H, E=shape.E, k=shape.k, I=shape.I,
@@ -88,7 +90,8 @@ def make_config(shape) -> MoEConfig:
         shared_I=g("shared_I", 0),
         act_dtype=MOE_DT_F32 if g("dtype", "bf16") == "f32" else MOE_DT_BF16,
         split_mode=MOE_SPLIT_BOUNDED if g("split_mode", "parity") == "bounded" else MOE_SPLIT_PARITY,
-        split_c_permille=g("split_c_permille", 0))
+        split_c_permille=g("split_c_permille", 0),
+        capacity_factor_permille=g("capacity_factor_permille", 0))
 
 
 def moe_status_string(status: int) -> str:
@@ -101,6 +104,10 @@ def _cfg(cfg) -> MoEConfig:
 
 def moe_num_segments(cfg) -> int:
     return int(lib.moe_num_segments(ctypes.byref(_cfg(cfg))))
+
+
+def moe_num_rows(cfg) -> int:
+    return int(lib.moe_num_rows(ctypes.byref(_cfg(cfg))))
 
 
 def moe_workspace_size(cfg) -> int:

@@ -36,6 +36,7 @@ struct GemmProblem {
   const int32_t* seg_expert;   // nullable: expert 0
   const int32_t* a_rows;       // nullable: row r of the problem is row a_rows[r] of A
   int32_t n_seg, rows, N, K;
+  int32_t n_w;              // experts in B: a segment of another expert (padding) is skipped
   int32_t a_ld_rows;        // rows of the A allocation (bounds of the copy source)
   int32_t up_off;           // GEMM 1: row offset of W_up inside B
   int64_t b_stride;         // elements per expert in B
@@ -113,6 +114,7 @@ __device__ __forceinline__ int seg_tiles(const GemmArgs& a, int g) {
   const int s = g - (p ? a.p[0].n_seg : 0);
   const int len = P.seg_offsets ? P.seg_offsets[s + 1] - P.seg_offsets[s] : P.rows;
   if (len < a.min_len || len >= a.max_len) return 0;
+  if (P.seg_offsets && (unsigned)P.seg_expert[s] >= (unsigned)P.n_w) return 0;
   return ((len + a.tile_bm - 1) / a.tile_bm) * ((P.N + a.tile_ncols - 1) / a.tile_ncols);
 }
 
@@ -585,7 +587,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
                                                        const int32_t* __restrict__ seg_expert,
                                                        const int32_t* __restrict__ a_rows,
                                                        int n_seg, int rows, int N, int K,
-                                                       int up_off, int64_t b_stride) {
+                                                       int up_off, int64_t b_stride, int n_w) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int row = (int)(idx / N), col = (int)(idx % N);
   if (row >= rows) return;
@@ -593,6 +595,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
   if (seg_offsets) {
     if (row >= seg_offsets[n_seg]) return;
     e = seg_expert[find_segment(seg_offsets, n_seg, row)];
+    if ((unsigned)e >= (unsigned)n_w) return;   // padding segment
   }
   const float* a = A + (size_t)(a_rows ? a_rows[row] : row) * K;
   const float* b = B + (size_t)e * b_stride;
@@ -949,10 +952,10 @@ void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_prob
       int64_t n1 = (int64_t)P.rows * Iw, n2 = (int64_t)P.rows * H;
       gemm_f32_kernel<0><<<(unsigned)((n1 + 255) / 256), 256, 0, s>>>(
           (const float*)P.A, (const float*)P.w13, (float*)P.h, nullptr, P.seg_offsets,
-          P.seg_expert, P.a_rows, P.n_seg, P.rows, Iw, H, Iw, (int64_t)2 * Iw * H);
+          P.seg_expert, P.a_rows, P.n_seg, P.rows, Iw, H, Iw, (int64_t)2 * Iw * H, P.n_w);
       gemm_f32_kernel<1><<<(unsigned)((n2 + 255) / 256), 256, 0, s>>>(
           (const float*)P.h, (const float*)P.w2, (float*)P.y, P.row_scale, P.seg_offsets,
-          P.seg_expert, nullptr, P.n_seg, P.rows, H, Iw, 0, (int64_t)H * Iw);
+          P.seg_expert, nullptr, P.n_seg, P.rows, H, Iw, 0, (int64_t)H * Iw, P.n_w);
     }
     return;
   }
@@ -970,6 +973,7 @@ void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_prob
     a.a_rows = P.a_rows;
     a.n_seg = P.n_seg;
     a.rows = P.rows;
+    a.n_w = P.n_w;
     a.a_ld_rows = P.a_rows ? c.T : P.rows;   // gathered rows come from x
     a.N = P.Iw;
     a.K = H;

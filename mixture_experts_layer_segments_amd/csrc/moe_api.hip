@@ -9,6 +9,7 @@
 namespace moe {
 
 int32_t num_segments(const moe_config& c) {
+  if (c.capacity_factor_permille > 0) return 2 * c.E;
   if (c.n_hot_split > 0 && c.split_ways > 1)
     return c.E + (c.n_hot_split < c.E ? c.n_hot_split : c.E) * (c.split_ways - 1);
   return c.E;
@@ -17,6 +18,7 @@ int32_t num_segments(const moe_config& c) {
 Layout make_layout(const moe_config& c) {
   Layout L{};
   const size_t A = (size_t)c.T * c.k;
+  const size_t R = (size_t)num_rows(c);
   const size_t eb = c.act_dtype == MOE_DT_F32 ? 4 : 2;
   const size_t nbins = (size_t)c.E * bin_ways(c);
   const size_t nb = (size_t)num_chunks((int64_t)A);
@@ -31,16 +33,16 @@ Layout make_layout(const moe_config& c) {
   L.blk_off = take(S * nb * 4);
   L.seg_of_bin = take(nbins * 4);
   L.p_end = o;
-  L.h = take(A * c.I * eb);
+  L.h = take(R * c.I * eb);
   L.shared_h = take((size_t)c.T * c.shared_I * eb);
   L.g_end = o;
-  L.y_perm = take(A * c.H * eb);
+  L.y_perm = take(R * c.H * eb);
   L.shared_y = take(c.shared_I > 0 ? (size_t)c.T * c.H * eb : 0);
   L.seg_offsets = take((S + 1) * 4);
   L.seg_expert = take(S * 4);
   L.assign_to_row = take(A * 4);
-  L.row_to_token = take(A * 4);
-  L.row_w = take(A * 4);
+  L.row_to_token = take(R * 4);
+  L.row_w = take(R * 4);
   L.l_end = o;
   return L;
 }
@@ -83,12 +85,18 @@ moe_status check_config(const moe_config* c) {
   if (c->split_mode != MOE_SPLIT_PARITY && c->split_mode != MOE_SPLIT_BOUNDED)
     return MOE_ERR_INVALID_ARG;
   if (c->split_c_permille < 0 || c->split_c_permille > 100000) return MOE_ERR_INVALID_ARG;
+  if (c->capacity_factor_permille < 0 || c->capacity_factor_permille > 1000000)
+    return MOE_ERR_INVALID_ARG;
+  if (c->capacity_factor_permille > 0 && c->n_hot_split > 0 && c->split_ways > 1)
+    return MOE_ERR_UNSUPPORTED;
   if (c->shared_I < 0) return MOE_ERR_INVALID_ARG;
   if ((int64_t)c->T * c->k > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED;
   // the kernels address each activation and weight matrix with 32-bit byte
   // offsets: keep every one below 2^31 elements
-  const int64_t lim = (int64_t)1 << 31, A = (int64_t)c->T * c->k;
+  const int64_t lim = (int64_t)1 << 31, A = (int64_t)c->T * c->k, R = num_rows(*c);
+  if (R > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED;
   if (A * c->H >= lim || A * c->I >= lim || (int64_t)c->T * c->shared_I >= lim ||
+      R * c->H >= lim || R * c->I >= lim ||
       (int64_t)2 * c->I * c->H >= lim || (int64_t)2 * c->shared_I * c->H >= lim)
     return MOE_ERR_UNSUPPORTED;
   if (c->act_dtype == MOE_DT_BF16) {
@@ -162,7 +170,8 @@ moe_status grouped_ffn(const moe_config* cfg, const void* x_perm, const int32_t*
   p.seg_offsets = seg_offsets;
   p.seg_expert = seg_expert;
   p.n_seg = num_segments(*cfg);
-  p.rows = cfg->T * cfg->k;
+  p.rows = (int32_t)num_rows(*cfg);
+  p.n_w = cfg->E;
   p.Iw = cfg->I;
   launch_grouped_ffn(*cfg, &p, 1, (hipStream_t)stream);
   return launch_status();
@@ -221,7 +230,8 @@ moe_status layer_forward(const moe_config* cfg, const float* logits, const void*
   p[0].seg_offsets = seg_offsets;
   p[0].seg_expert = seg_expert;
   p[0].n_seg = num_segments(*cfg);
-  p[0].rows = cfg->T * cfg->k;
+  p[0].rows = (int32_t)num_rows(*cfg);
+  p[0].n_w = cfg->E;
   p[0].Iw = cfg->I;
   if (shared) {
     p[1].A = x;
@@ -237,6 +247,7 @@ moe_status layer_forward(const moe_config* cfg, const float* logits, const void*
     p[1].seg_expert = nullptr;
     p[1].n_seg = 1;
     p[1].rows = cfg->T;
+    p[1].n_w = 1;
     p[1].Iw = cfg->shared_I;
   }
   launch_grouped_ffn(*cfg, p, shared ? 2 : 1, s);
@@ -263,6 +274,11 @@ const char* moe_status_string(moe_status s) {
 int32_t moe_num_segments(const moe_config* cfg) {
   if (check_config(cfg) != MOE_OK) return -1;
   return num_segments(*cfg);
+}
+
+int32_t moe_num_rows(const moe_config* cfg) {
+  if (check_config(cfg) != MOE_OK) return -1;
+  return (int32_t)num_rows(*cfg);
 }
 
 size_t moe_workspace_size(const moe_config* cfg) {

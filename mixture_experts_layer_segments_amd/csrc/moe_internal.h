@@ -42,6 +42,18 @@ inline int bin_ways(const moe_config& c) {
   return c.split_mode == MOE_SPLIT_PARITY ? split_ways(c) : 1;
 }
 
+// Slots per expert of the fixed-capacity layout, ceil(f * T*k / E) with
+// f = capacity_factor_permille / 1000; 0 for the dropless layout.
+inline int64_t capacity(const moe_config& c) {
+  if (c.capacity_factor_permille <= 0) return 0;
+  const int64_t num = (int64_t)c.T * c.k * c.capacity_factor_permille, den = 1000ll * c.E;
+  return (num + den - 1) / den;
+}
+// Rows of x_perm / h / y_perm / row_to_token.
+inline int64_t num_rows(const moe_config& c) {
+  return c.capacity_factor_permille > 0 ? c.E * capacity(c) : (int64_t)c.T * c.k;
+}
+
 // Assignment chunk of one histogram / rank block: a multiple of 64, at least
 // 256, grown so that there are at most ~256 chunks.
 inline int chunk_len(int64_t A) {
@@ -92,7 +104,8 @@ struct FfnProblem {
   const int32_t* seg_expert;
   const int32_t* a_rows;  // nullable: GEMM 1 reads row a_rows[r] of A for row r
   int32_t n_seg;          // segments (1 for shared)
-  int32_t rows;           // max rows (A rows)
+  int32_t rows;           // rows of h / y (and of A unless a_rows gathers)
+  int32_t n_w;            // experts in w13 / w2; segments of other experts are skipped
   int32_t Iw;             // intermediate size of this problem
   int32_t w_fp8;          // 1: w13 / w2 are E4M3 codes with the block scales below
   const float* w13_scale; // [n_w, 2*Iw/128, K1/128] (w_fp8 only)

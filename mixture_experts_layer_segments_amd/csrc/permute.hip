@@ -42,9 +42,9 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
 
 __global__ __launch_bounds__(1024) void plan_kernel(
     const int32_t* __restrict__ cnt_bin, int nb, int E, int bin_ways, int ways, int n_hot,
-    int c, int32_t* __restrict__ counts, int32_t* __restrict__ seg_offsets,
+    int c, int cap, int32_t* __restrict__ counts, int32_t* __restrict__ seg_offsets,
     int32_t* __restrict__ seg_expert, int32_t* __restrict__ seg_of_bin,
-    int32_t* __restrict__ blk_off, float* __restrict__ bal) {
+    int32_t* __restrict__ blk_off, int32_t* __restrict__ r2t, float* __restrict__ bal) {
   __shared__ plan_dev::PlanLds L;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nbins = E * bin_ways;
@@ -58,15 +58,19 @@ __global__ __launch_bounds__(1024) void plan_kernel(
     if (lane == 0) L.tot[bin] = s;
   }
   __syncthreads();
-  const int S = plan_dev::plan_segments(L, E, bin_ways, ways, n_hot, c, counts, seg_offsets,
-                                        seg_expert, seg_of_bin, bal);
+  const int S = cap > 0 ? plan_dev::plan_capacity(L, E, cap, counts, seg_offsets, seg_expert,
+                                                  seg_of_bin, r2t, bal)
+                        : plan_dev::plan_segments(L, E, bin_ways, ways, n_hot, c, counts,
+                                                  seg_offsets, seg_expert, seg_of_bin, bal);
 
   // per-(segment, chunk) bases: one wave per segment scans over chunks.  In
   // the load-bounded split only the first segment of a hot expert is ever
   // looked up (its rows run on through the later ones); the later replica
-  // segments get bases too, which nothing reads.
+  // segments get bases too, which nothing reads.  Padding segments of the
+  // fixed-capacity layout (expert -1) get none.
   for (int s = wv; s < S; s += 16) {
     const int e = L.seg_exp[s];
+    if (e < 0) continue;
     const int f = L.seg_first[e];
     const bool per_replica = L.seg_first[e + 1] - f > 1 && bin_ways > 1;
     int carry = L.seg_off[s];
@@ -89,6 +93,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(
 
 __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ ids, int A, int k,
                                                   int E, int ways, int chunk, int nb, int S,
+                                                  int cap,
                                                   const int32_t* __restrict__ seg_of_bin,
                                                   const int32_t* __restrict__ blk_off,
                                                   int32_t* __restrict__ a2r,
@@ -104,9 +109,9 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ id
   const int a_end = min(A, (b + 1) * chunk);
   for (int a0 = b * chunk; a0 < a_end; a0 += 64) {
     const int a = a0 + lane;
-    int seg = -1;
+    int seg = -1, e = -1;
     if (a < a_end) {
-      const int e = ids[a];
+      e = ids[a];
       if (e >= 0 && e < E) seg = seg_of_bin[e * ways + (a / k) % ways];
     }
     int row = -1;
@@ -120,6 +125,8 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ id
       if (lane == leader) run[sl] = base + __popcll(m);
       pending &= ~m;
     }
+    // fixed capacity: an assignment past its expert's last slot is dropped
+    if (cap > 0 && row >= (e + 1) * cap) row = -1;
     if (a < a_end) {
       a2r[a] = row;
       if (row >= 0) {
@@ -139,7 +146,7 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ id
 template <int VPL>
 __global__ __launch_bounds__(1024) void route_permute_small_kernel(
     const float* __restrict__ logits, int T, int E, int k, int score, int n_group,
-    int topk_group, int topn, int renorm, int bin_ways, int ways, int n_hot, int c,
+    int topk_group, int topn, int renorm, int bin_ways, int ways, int n_hot, int c, int cap,
     int32_t* __restrict__ ids,
     float* __restrict__ w, int32_t* __restrict__ counts, int32_t* __restrict__ seg_offsets,
     int32_t* __restrict__ seg_expert, int32_t* __restrict__ a2r, int32_t* __restrict__ r2t,
@@ -167,8 +174,11 @@ __global__ __launch_bounds__(1024) void route_permute_small_kernel(
     }
   }
   __syncthreads();
-  plan_dev::plan_segments(L, E, bin_ways, ways, n_hot, c, counts, seg_offsets, seg_expert,
-                          seg_of_bin, bal);
+  if (cap > 0)
+    plan_dev::plan_capacity(L, E, cap, counts, seg_offsets, seg_expert, seg_of_bin, r2t, bal);
+  else
+    plan_dev::plan_segments(L, E, bin_ways, ways, n_hot, c, counts, seg_offsets, seg_expert,
+                            seg_of_bin, bal);
   for (int a = tid; a < A; a += 1024)
     id_a[a] = seg_of_bin[id_a[a] * bin_ways + (a / k) % bin_ways];
   __syncthreads();
@@ -176,6 +186,10 @@ __global__ __launch_bounds__(1024) void route_permute_small_kernel(
     const int sa = id_a[a];
     int before = 0;
     for (int b = 0; b < a; ++b) before += id_a[b] == sa;
+    if (cap > 0 && before >= cap) {   // fixed capacity: the expert's slots are full
+      a2r[a] = -1;
+      continue;
+    }
     const int row = L.seg_off[sa] + before;
     a2r[a] = row;
     r2t[row] = a / k;
@@ -193,6 +207,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows_max || r >= *total_rows) return;
   const int t = r2t[r];
+  if (t < 0) return;   // a padding row of the fixed-capacity layout
   const uint4* src = x + (size_t)t * row_chunks;
   uint4* dst = x_perm + (size_t)r * row_chunks;
   int c = lane;
@@ -212,7 +227,8 @@ void launch_small_vpl(const moe_config& c, const float* logits, int32_t* ids, fl
                       int32_t* r2t, float* row_w, float* bal, hipStream_t s) {
   route_permute_small_kernel<VPL><<<1, 1024, 0, s>>>(
       logits, c.T, c.E, c.k, c.score, c.n_group, c.topk_group, c.group_score_topn,
-      c.renormalize, bin_ways(c), split_ways(c), c.n_hot_split, c.split_c_permille, ids, w, counts, seg_offsets, seg_expert, a2r, r2t,
+      c.renormalize, bin_ways(c), split_ways(c), c.n_hot_split, c.split_c_permille,
+      (int)capacity(c), ids, w, counts, seg_offsets, seg_expert, a2r, r2t,
       row_w, bal);
 }
 
@@ -248,16 +264,18 @@ void launch_permute(const moe_config& c, const void* x, const int32_t* ids, void
   int32_t* blk_off = reinterpret_cast<int32_t*>(ws + L.blk_off);
   int32_t* seg_of_bin = reinterpret_cast<int32_t*>(ws + L.seg_of_bin);
   hist_kernel<<<nb, 256, 0, s>>>(ids, A, c.k, c.E, bw, chunk, nb, cnt_bin);
+  const int cap = (int)capacity(c);
   plan_kernel<<<1, 1024, 0, s>>>(cnt_bin, nb, c.E, bw, split_ways(c), c.n_hot_split,
-                                 c.split_c_permille, counts, seg_offsets, seg_expert, seg_of_bin,
-                                 blk_off, bal);
-  rank_kernel<<<nb, 64, S * sizeof(int), s>>>(ids, A, c.k, c.E, bw, chunk, nb, S,
+                                 c.split_c_permille, cap, counts, seg_offsets, seg_expert,
+                                 seg_of_bin, blk_off, r2t, bal);
+  rank_kernel<<<nb, 64, S * sizeof(int), s>>>(ids, A, c.k, c.E, bw, chunk, nb, S, cap,
                                               seg_of_bin, blk_off, a2r, r2t, w, row_w);
   if (!x_perm) return;  // the caller reads rows of x through row_to_token
   const int eb = c.act_dtype == MOE_DT_F32 ? 4 : 2;
   const int row_chunks = c.H * eb / 16;
-  gather_kernel<<<(A + 3) / 4, 256, 0, s>>>(reinterpret_cast<const uint4*>(x), r2t,
-                                            seg_offsets + S, A, row_chunks,
+  const int R = (int)num_rows(c);
+  gather_kernel<<<(R + 3) / 4, 256, 0, s>>>(reinterpret_cast<const uint4*>(x), r2t,
+                                            seg_offsets + S, R, row_chunks,
                                             reinterpret_cast<uint4*>(x_perm));
 }
 

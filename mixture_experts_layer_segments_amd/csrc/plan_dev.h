@@ -77,6 +77,37 @@ __device__ inline void bounded_loads(int d, int ways, int c, int* out) {
   }
 }
 
+// balancedness = (sum/E) / max of the expert counts in L.cnt_e, by one fp64
+// division of exact integers ("The slowest expert sets the pace").  Ends with
+// a barrier.
+__device__ inline void balancedness(PlanLds& L, int E, float* __restrict__ bal) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int mx = 0, sm = 0;
+  for (int e = tid; e < E; e += 1024) {
+    mx = max(mx, L.cnt_e[e]);
+    sm += L.cnt_e[e];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    mx = max(mx, __shfl_xor(mx, off));
+    sm += __shfl_xor(sm, off);
+  }
+  if (lane == 0) {
+    L.red[0][wv] = mx;
+    L.red[1][wv] = sm;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int m = 0, su = 0;
+    for (int i = 0; i < 16; ++i) {
+      m = max(m, L.red[0][i]);
+      su += L.red[1][i];
+    }
+    bal[0] = m > 0 ? (float)(((double)su / (double)E) / (double)m) : 0.0f;
+  }
+  __syncthreads();
+}
+
 // From bin totals to expert counts, the hot experts (the n_hot largest
 // counts, lower id on a tie) with `ways` replica segments each, segment
 // offsets, the bin -> segment map and balancedness = (sum/E) / max by one fp64
@@ -91,7 +122,7 @@ __device__ inline int plan_segments(PlanLds& L, int E, int bin_ways, int ways, i
                                     int32_t* __restrict__ seg_offsets,
                                     int32_t* __restrict__ seg_expert, int32_t* seg_of_bin,
                                     float* __restrict__ bal) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x;
   for (int e = tid; e < E; e += 1024) {
     int s = 0;
     for (int p = 0; p < bin_ways; ++p) s += L.tot[e * bin_ways + p];
@@ -146,31 +177,51 @@ __device__ inline int plan_segments(PlanLds& L, int E, int bin_ways, int ways, i
     L.seg_off[S] = total;
   }
 
-  int mx = 0, sm = 0;
-  for (int e = tid; e < E; e += 1024) {
-    mx = max(mx, L.cnt_e[e]);
-    sm += L.cnt_e[e];
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    mx = max(mx, __shfl_xor(mx, off));
-    sm += __shfl_xor(sm, off);
-  }
-  if (lane == 0) {
-    L.red[0][wv] = mx;
-    L.red[1][wv] = sm;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int m = 0, su = 0;
-    for (int i = 0; i < 16; ++i) {
-      m = max(m, L.red[0][i]);
-      su += L.red[1][i];
-    }
-    bal[0] = m > 0 ? (float)(((double)su / (double)E) / (double)m) : 0.0f;
-  }
-  __syncthreads();
+  balancedness(L, E, bal);
   return S;
+}
+
+// Fixed-capacity layout (the book's "Capacity, padding, and the drop
+// decision"; the MoE inference blog's masked decode layout): expert e owns
+// rows [e*cap, (e+1)*cap); segment 2e holds its kept rows (the first
+// min(count, cap) of its assignments), segment 2e+1 the unused slots, marked
+// with expert -1.  One bin per expert.  Writes counts[E], seg_offsets[2E+1],
+// seg_expert[2E], seg_of_bin[E] (-> 2e) and bal[0]; row_to_token = -1 on the
+// padding rows; returns S = 2E.  L.seg_first[e] = 2e for the callers.
+__device__ inline int plan_capacity(PlanLds& L, int E, int cap, int32_t* __restrict__ counts,
+                                    int32_t* __restrict__ seg_offsets,
+                                    int32_t* __restrict__ seg_expert, int32_t* seg_of_bin,
+                                    int32_t* __restrict__ r2t, float* __restrict__ bal) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 1024) {
+    const int c = L.tot[e];
+    const int kept = min(c, cap);
+    L.cnt_e[e] = c;
+    counts[e] = c;
+    L.seg_first[e] = 2 * e;
+    L.seg_exp[2 * e] = e;
+    L.seg_exp[2 * e + 1] = -1;
+    L.seg_off[2 * e] = e * cap;
+    L.seg_off[2 * e + 1] = e * cap + kept;
+    seg_expert[2 * e] = e;
+    seg_expert[2 * e + 1] = -1;
+    seg_offsets[2 * e] = e * cap;
+    seg_offsets[2 * e + 1] = e * cap + kept;
+    seg_of_bin[e] = 2 * e;
+  }
+  if (tid == 0) {
+    L.seg_first[E] = 2 * E;
+    L.seg_off[2 * E] = E * cap;
+    seg_offsets[2 * E] = E * cap;
+  }
+  __syncthreads();
+  const int R = E * cap;
+  for (int r = tid; r < R; r += 1024) {
+    const int e = r / cap;
+    if (r >= L.seg_off[2 * e + 1]) r2t[r] = -1;
+  }
+  balancedness(L, E, bal);
+  return 2 * E;
 }
 
 }  // namespace plan_dev

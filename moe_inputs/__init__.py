@@ -74,7 +74,10 @@ class MoEShape:
 
     @property
     def S(self) -> int:
-        """Segments: one per expert plus the extra replica segments."""
+        """Segments: one per expert plus the extra replica segments, or kept
+        rows and padding of every expert in the fixed-capacity layout."""
+        if self.capacity_factor_permille > 0:
+            return 2 * self.E
         return self.E + self.n_hot_split * (self.split_ways - 1)
 
     @property
@@ -103,6 +106,10 @@ WORKLOADS = {
 for _n in ("decode", "prefill_skew", "deepseek_v3", "ragged_stress"):
     _b = WORKLOADS[_n + "_bf16"]
     WORKLOADS[_n + "_fp8w"] = dataclasses.replace(_b, name=_n + "_fp8w", weights="fp8")
+# The decode layer in the fixed-capacity (masked) layout at 1.25 x the mean
+# load, overflow dropped.
+WORKLOADS["decode_capacity_bf16"] = dataclasses.replace(
+    WORKLOADS["decode_bf16"], name="decode_capacity_bf16", capacity_factor_permille=1250)
 # The ragged layer with its hot experts split by load bounds (C = 0.1) instead
 # of token parity.
 WORKLOADS["ragged_stress_bounded_bf16"] = dataclasses.replace(

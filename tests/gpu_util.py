@@ -90,6 +90,24 @@ class SmallCase:
         return d
 
 
+def x_perm_of(case):
+    """The oracle's permuted rows on the device ([R, H]; padding rows of the
+    fixed-capacity layout hold token 0, which no kernel reads) and the mask of
+    live rows among the first seg_offsets[S]."""
+    r = case.ref
+    r2t = r["row_to_token"]
+    R = int(r["seg_offsets"][-1])
+    return to_dev(case.xb[np.maximum(r2t, 0)], case.cfg.dtype), r2t[:R] >= 0
+
+
+def row_weights(case):
+    """Router weight of every row (0 on padding rows), fp32."""
+    r = case.ref
+    r2a = r["row_to_assign"]
+    w = r["w"].reshape(-1)[np.maximum(r2a, 0)]
+    return np.where(r2a >= 0, w, 0.0).astype(np.float32)
+
+
 def quantize_fp8(moe, w):
     """The library's block quantizer on a device bf16 tensor [.., R, C]:
     (codes uint8, scales fp32)."""
@@ -130,19 +148,19 @@ def run_layer(moe, cfg, d):
     torch.cuda.synchronize()
     # the permutation the layer built, from where it leaves it in the workspace
     off = moe.moe_layer_plan_offsets(cfg)
-    S, A = moe.moe_num_segments(cfg), cfg.T * cfg.k
+    S, A, R = moe.moe_num_segments(cfg), cfg.T * cfg.k, moe.moe_num_rows(cfg)
     for key, name, n in (("seg_offsets", "seg_offsets", S + 1), ("seg_expert", "seg_expert", S),
-                         ("a2r", "assign_to_row", A), ("r2t", "row_to_token", A)):
+                         ("a2r", "assign_to_row", A), ("r2t", "row_to_token", R)):
         o[key] = ws[off[name]:off[name] + 4 * n].view(torch.int32).clone()
     return o
 
 
 def run_permute(moe, cfg, x_d, ids_d):
-    S = moe.moe_num_segments(cfg)
+    S, R = moe.moe_num_segments(cfg), moe.moe_num_rows(cfg)
     A = cfg.T * cfg.k
-    o = dict(x_perm=empty((A, cfg.H), tdtype(cfg)), seg_offsets=empty((S + 1,), torch.int32),
+    o = dict(x_perm=empty((R, cfg.H), tdtype(cfg)), seg_offsets=empty((S + 1,), torch.int32),
              seg_expert=empty((S,), torch.int32), a2r=empty((A,), torch.int32),
-             r2t=empty((A,), torch.int32), counts=empty((cfg.E,), torch.int32),
+             r2t=empty((R,), torch.int32), counts=empty((cfg.E,), torch.int32),
              bal=empty((1,), torch.float32))
     ws = empty((moe.moe_workspace_size(cfg),), torch.uint8)
     moe.moe_permute(cfg, x_d, ids_d, o["x_perm"], o["seg_offsets"], o["seg_expert"], o["a2r"],

@@ -51,6 +51,25 @@ def test_segments_and_workspace_of_the_workloads(moe):
         assert ws >= cfg.A * (cfg.H + cfg.I) * eb
 
 
+def test_capacity_rows_follow_the_book(moe):
+    """The library's slot arithmetic on the book's example ("Capacity,
+    padding, and the drop decision"): 64 assignments over 8 experts at
+    1.25 x the mean give 80 slots; sizing for the busiest expert (22, factor
+    2.75) gives 176; S = 2E segments (kept rows and padding per expert)."""
+    book = mi.MoEShape("book", T=32, H=64, E=8, k=2, I=64, capacity_factor_permille=1250)
+    assert moe.moe_num_rows(book) == 80 and moe.moe_num_segments(book) == 16 == book.S
+    assert moe.moe_num_rows(book.replace(capacity_factor_permille=2750)) == 176
+    assert moe.moe_num_rows(book.replace(capacity_factor_permille=0)) == 64
+    dec = mi.WORKLOADS["decode_capacity_bf16"]
+    assert moe.moe_num_rows(dec) == 64 * 3          # ceil(1.25 * 128 / 64) = 3 slots
+    assert moe.moe_workspace_size(dec) >= 192 * (dec.H + dec.I) * 2
+    # a fixed capacity with replica segments is not supported
+    rag = moe.make_config(mi.WORKLOADS["ragged_stress_bf16"])
+    rag.capacity_factor_permille = 1250
+    assert moe.lib.moe_num_rows(ctypes.byref(rag)) == -1
+    assert moe.lib.moe_route_topk(ctypes.byref(rag), FAKE, FAKE, FAKE, None) == -2
+
+
 FAKE = 1 << 20          # 256-byte aligned non-null address, never dereferenced
 
 
@@ -72,6 +91,7 @@ def _layer(moe, cfg, ws_bytes=None, **override):
     ("n_group", 3, -1), ("split_ways", 9, -2), ("H", 100, -2), ("I", 96, -2),
     ("shared_I", 32, -2), ("renormalize", 2, -1), ("split_mode", 2, -1),
     ("split_c_permille", -1, -1), ("split_c_permille", 100001, -1),
+    ("capacity_factor_permille", -1, -1), ("capacity_factor_permille", 1000001, -1),
     ("H", 1 << 24, -2),   # T*k*H reaches 2^31 elements: beyond 32-bit byte offsets
 ])
 def test_bad_config_is_rejected(moe, field, value, status):

@@ -54,6 +54,17 @@ SHAPES = {
                                             zipf_s=1.0, n_hot_split=2, split_ways=4,
                                             split_mode="bounded", split_c_permille=3000,
                                             seed=29),
+    # fixed-capacity layout with drops: weight-streaming tiles through the
+    # one-workgroup planner, ring tiles through the four-kernel one, fp32, and
+    # a capacity that holds every assignment (more slots than assignments)
+    "bf16_capacity_decode": mi.MoEShape("t17", T=40, H=1024, E=32, k=2, I=512, zipf_s=1.0,
+                                        capacity_factor_permille=1250, seed=30),
+    "bf16_capacity_rings": mi.MoEShape("t18", T=300, H=576, E=16, k=4, I=320, zipf_s=1.2,
+                                       capacity_factor_permille=1000, seed=31),
+    "f32_capacity": mi.MoEShape("t19", T=50, H=132, E=10, k=3, I=70, dtype="f32", zipf_s=1.0,
+                                capacity_factor_permille=800, seed=32),
+    "bf16_capacity_roomy": mi.MoEShape("t20", T=120, H=256, E=8, k=2, I=128, zipf_s=1.0,
+                                       capacity_factor_permille=4000, seed=33),
 }
 
 
@@ -86,8 +97,9 @@ def test_permute(moe, case):
     g = gu.run_permute(moe, c, d["x"], ids_d)
     gu.check_plan(g, case.ref)
     R = int(case.ref["seg_offsets"][-1])
-    xp = g["x_perm"][:R].cpu()
-    expect = d["x"].cpu()[torch.from_numpy(case.ref["row_to_token"][:R]).long()]
+    live = torch.from_numpy(case.ref["row_to_token"][:R] >= 0)   # not padding
+    xp = g["x_perm"][:R].cpu()[live]
+    expect = d["x"].cpu()[torch.from_numpy(case.ref["row_to_token"][:R]).long()[live]]
     assert torch.equal(xp.view(torch.int16) if c.dtype == "bf16" else xp.view(torch.int32),
                        expect.view(torch.int16) if c.dtype == "bf16" else expect.view(torch.int32))
 
@@ -96,22 +108,22 @@ def test_grouped_ffn(moe, case):
     c, d = case.cfg, case.device_inputs()
     r = case.ref
     R = int(r["seg_offsets"][-1])
-    x_perm = gu.to_dev(case.xb[r["row_to_token"]], c.dtype)
+    x_perm, live = gu.x_perm_of(case)
     so = torch.from_numpy(r["seg_offsets"]).to(gu.dev())
     se = torch.from_numpy(r["seg_expert"]).to(gu.dev())
-    y = gu.empty((c.T * c.k, c.H), gu.tdtype(c))
+    y = gu.empty((moe.moe_num_rows(c), c.H), gu.tdtype(c))
     ws = gu.empty((moe.moe_workspace_size(c),), torch.uint8)
     moe.moe_grouped_ffn(c, x_perm, so, se, d["w13"], d["w2"], None, y, ws)
     torch.cuda.synchronize()
-    err = gu.rel_err(gu.host_f64(y[:R]), r["y_perm"][:R])
+    err = gu.rel_err(gu.host_f64(y[:R])[live], r["y_perm"][:R][live])
     assert err <= gu.rel_tol(c), err
     # router weight applied in the epilogue
-    row_w = r["w"].reshape(-1)[r["row_to_assign"]].astype(np.float32)
+    row_w = gu.row_weights(case)
     moe.moe_grouped_ffn(c, x_perm, so, se, d["w13"], d["w2"],
                         torch.from_numpy(row_w).to(gu.dev()), y, ws)
     torch.cuda.synchronize()
     ref_s = r["y_perm"][:R] * row_w[:R, None].astype(np.float64)
-    err = gu.rel_err(gu.host_f64(y[:R]), ref_s)
+    err = gu.rel_err(gu.host_f64(y[:R])[live], ref_s[live])
     assert err <= gu.rel_tol(c), err
 
 
@@ -171,11 +183,15 @@ def test_one_hot_expert_takes_every_token(moe):
     assert gu.rel_err(gu.host_f64(o["out"]), case.ref["out"]) <= gu.BF16_REL
 
 
-@pytest.mark.parametrize("split_mode", ["parity", "bounded"])
+@pytest.mark.parametrize("split_mode", ["parity", "bounded", "capacity"])
 def test_dropped_ids(moe, split_mode):
     """Ids outside [0, E) join no segment and get assign_to_row = -1."""
-    cfg = mi.MoEShape("drop", T=40, H=128, E=6, k=3, I=64, n_hot_split=1, split_ways=2,
-                      split_mode=split_mode, split_c_permille=200, seed=22)
+    if split_mode == "capacity":
+        cfg = mi.MoEShape("drop", T=40, H=128, E=6, k=3, I=64, capacity_factor_permille=900,
+                          seed=22)
+    else:
+        cfg = mi.MoEShape("drop", T=40, H=128, E=6, k=3, I=64, n_hot_split=1, split_ways=2,
+                          split_mode=split_mode, split_c_permille=200, seed=22)
     rng = np.random.default_rng(0)
     ids = rng.integers(0, cfg.E, size=(cfg.T, cfg.k)).astype(np.int32)
     bad = rng.random((cfg.T, cfg.k)) < 0.2
@@ -184,6 +200,11 @@ def test_dropped_ids(moe, split_mode):
     g = gu.run_permute(moe, cfg, gu.to_dev(x, cfg.dtype), torch.from_numpy(ids).to(gu.dev()))
     valid = ~bad.ravel()
     counts = np.bincount(ids.ravel()[valid], minlength=cfg.E)
+    if split_mode == "capacity":
+        p = orc.capacity_plan(ids, cfg.E, orc.capacity(ids.size, cfg.E, 900))
+        p.update(counts=counts, balancedness=orc.balancedness(counts))
+        gu.check_plan(g, p)
+        return
     se, sr = orc.segment_list(counts, cfg.n_hot_split, cfg.split_ways)
     if split_mode == "parity":
         seg = orc.segment_of_assignments(np.where(bad, 0, ids), se, sr, cfg.split_ways)
