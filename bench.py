@@ -231,6 +231,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_bf16", choices=sorted(mi.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--launch", choices=("eager", "graph"), default="eager",
+                    help="run the timed steps as eager calls, or as replays of one HIP graph "
+                         "captured from a step (the other mode is timed too and reported)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args(argv)
@@ -281,16 +284,37 @@ def main(argv=None):
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
+    # One step captured into a HIP graph: every grid depends only on the
+    # configuration (segment lengths stay on the device), so replays serve
+    # any routing.
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
         step()
-    e1.record(stream)
+    stream.wait_stream(side)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+
+    def timed(run):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(args.steps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps, time.perf_counter() - t0
+
+    ms_eager, wall_eager = timed(step)
+    ms_graph, wall_graph = timed(graph.replay)
+    ms, wall = (ms_graph, wall_graph) if args.launch == "graph" else (ms_eager, wall_eager)
     counts_h = counts.cpu().numpy()
     active = int((counts_h > 0).sum())   # experts whose weights the step must read
     cap = moe.moe_num_rows(cfg) // cfg.E if cfg.capacity_factor_permille else cfg.A
@@ -358,6 +382,9 @@ def main(argv=None):
         "grouped_gemm_frac_mfma": round(tflops / BF16_PEAK_TFLOPS, 4),
         "grouped_gemm_frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
         "wall_s_timed": round(wall, 3),
+        "launch": args.launch,
+        "ms_per_step_eager": round(ms_eager, 4),
+        "ms_per_step_graph_replay": round(ms_graph, 4),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
