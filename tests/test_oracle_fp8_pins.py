@@ -1,11 +1,13 @@
-"""Pins of the FP8 weight oracle (CPU only).
+"""Pins of the FP8 oracle, weights and activations (CPU only).
 
 Every pin rests on something other than the oracle itself: the encodings
 the OCP 8-bit floating point specification (OFP8) tabulates for E4M3,
 brute force over the 254 finite codes, the definition of the block scale
-checked by linear search, and exact reconstruction of matrices built from
-E4M3 values.  The last test plants plausible mistakes in the oracle and
-checks that some pin fails for each.
+checked by linear search, exact reconstruction of matrices built from
+E4M3 values, torch's bf16 rounding, a hand-worked one-expert layer and a
+layer whose every value sits on the E4M3 grid (where the FP8 layer must
+equal the plain one).  The last test plants plausible mistakes in the oracle
+and checks that some pin fails for each.
 """
 import contextlib
 import math
@@ -147,8 +149,118 @@ def test_zero_block():
     assert s[0, 0] == 1.0 and not c.any()
 
 
+# ------------------------------------------------------------ activations
+def test_row_blocks_are_weight_blocks_of_one_row():
+    """A 1 x 128 piece of a row is quantized exactly as a 128 x 128 weight
+    block whose other rows are zero (the zeros do not change the maximum)."""
+    rng = np.random.default_rng(12)
+    x = rng.normal(0, 1.0, size=(5, 384)) * 2.0 ** rng.integers(-20, 20, size=(5, 1))
+    x[2, 128:256] = 0.0
+    codes, scales = fp8.quantize_rows(x)
+    assert codes.shape == (5, 384) and scales.shape == (5, 3)
+    for r in range(5):
+        pad = np.zeros((128, 384))
+        pad[0] = x[r]
+        c_ref, s_ref = fp8.quantize_blocks(pad)
+        assert np.array_equal(codes[r], c_ref[0]) and np.array_equal(scales[r], s_ref[0])
+    assert np.array_equal(fp8.dequantize_rows(codes, scales),
+                          fp8.e4m3_decode(codes) * np.repeat(scales, 128, 1))
+
+
+def test_scale_exponents_stay_in_the_e8m0_range():
+    """amax = 448 * 2^-128 would want s = -128; the E8M0 scale stops at
+    -127, so the block keeps 2^-127 and values below half its smallest
+    subnormal step (2^-137) become zero."""
+    assert fp8.block_exponent(448.0 * 2.0 ** -128) == -128
+    assert fp8.scale_exponents(np.array([448.0 * 2.0 ** -128, 448.0 * 2.0 ** -127, 1.0])).tolist() \
+        == [-127, -127, -8]
+    x = np.zeros((1, 128))
+    x[0, :3] = [2.0 ** -130, 2.0 ** -138, -2.0 ** -129]
+    codes, scales = fp8.quantize_rows(x)
+    assert scales[0, 0] == 2.0 ** -127
+    assert fp8.dequantize_rows(codes, scales)[0, :3].tolist() == [2.0 ** -130, 0.0, -2.0 ** -129]
+    w = np.zeros((128, 128))
+    w[0, 0] = 2.0 ** -131
+    c, sc = fp8.quantize_blocks(w)
+    assert sc[0, 0] == 2.0 ** -127 and fp8.dequantize_blocks(c, sc)[0, 0] == 2.0 ** -131
+
+
+def test_bf16_round_matches_torch():
+    import torch
+    rng = np.random.default_rng(13)
+    a = np.concatenate([rng.normal(0, 1, 5000) * 2.0 ** rng.integers(-30, 30, 5000),
+                        (1 + np.arange(256) / 256.0 + 2.0 ** -9), [0.0, -0.0, 1.0]])
+    want = torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(fp8.bf16_round(a), want)
+
+
+def _one_expert_case():
+    """T = 1, E = k = 1, H = I = 128: x = 1.1875 e_0; W_gate[:, 0] = 80,
+    W_up[:, 0] = 1.75 * 2^-6, other weights of W13 zero; W2 from E4M3 values.
+    Quantized x: 1.1875 * 256 = 304 lies halfway between the E4M3 values 288
+    and 320, and the even one is 320, so x -> 1.25; g = 1.25 * 80 = 100
+    (silu(100) = 100 in float64) and u = 1.25 * 1.75 * 2^-6, so
+    h = 3.41796875 for every i, 3.421875 in bf16; the row's scale is 2^-7
+    (3.421875 <= 448 * 2^-7 = 3.5), 3.421875 * 128 = 438 and the nearest
+    E4M3 value is 448, so h -> 3.5.  out = 3.5 * sum_i W2[:, i].  (Unquantized
+    x would give h -> 3.0, an unquantized h 3.421875.)"""
+    import moe_inputs as mi
+    cfg = mi.MoEShape("w8a8", T=1, H=128, E=1, k=1, I=128, weights="fp8")
+    x = np.zeros((1, 128))
+    x[0, 0] = 1.1875
+    w13 = np.zeros((1, 256, 128))
+    w13[0, :128, 0] = 80.0
+    w13[0, 128:, 0] = 1.75 * 2.0 ** -6
+    codes = np.array([0x38, 0x40, 0xB8, 0x30, 0x44, 0xC2])          # 1, 2, -1, 0.5, 2.5, -2.25
+    rng = np.random.default_rng(14)
+    w2 = fp8.e4m3_decode(rng.choice(codes, size=(1, 128, 128))) * 2.0 ** -4
+    w2[0, 0, 0] = 2.5 * 2.0 ** -4                                    # keeps the block scale 2^-9
+    return cfg, x, w13, w2
+
+
+def test_w8a8_layer_hand_example():
+    cfg, x, w13, w2 = _one_expert_case()
+    w13d = fp8.dequantize_blocks(*fp8.quantize_blocks(w13[0]))[None]
+    w2d = fp8.dequantize_blocks(*fp8.quantize_blocks(w2[0]))[None]
+    assert np.array_equal(w13d, w13) and np.array_equal(w2d, w2)      # exact weights
+    r = fp8.layer_forward_w8a8(cfg, np.zeros((1, 1), np.float32), x, w13d, w2d)
+    assert r["w"][0, 0] == 1.0
+    np.testing.assert_allclose(r["out"][0], 3.5 * w2[0].sum(axis=1), rtol=1e-15, atol=0)
+    # with a shared expert of the same weights, its output adds once more
+    r2 = fp8.layer_forward_w8a8(cfg, np.zeros((1, 1), np.float32), x, w13d, w2d, w13d[0], w2d[0])
+    np.testing.assert_allclose(r2["out"][0], 7.0 * w2[0].sum(axis=1), rtol=1e-15, atol=0)
+
+
+def test_w8a8_layer_equals_the_bf16_layer_when_every_value_is_on_the_grid():
+    """One-hot rows times powers of two, gate weights in [48, 96] (silu is the
+    identity there in float64), up weights powers of two: x, the weights and
+    h all sit on the E4M3 grid of their blocks, so every quantization is
+    exact and the FP8 layer must equal the plain layer on the same values."""
+    import moe_inputs as mi
+    from oracle import moe_oracle as orc
+    T, H, E, k, I = 24, 128, 4, 2, 128
+    cfg = mi.MoEShape("grid", T=T, H=H, E=E, k=k, I=I, weights="fp8", shared_I=128)
+    rng = np.random.default_rng(15)
+    x = np.zeros((T, H))
+    x[np.arange(T), rng.integers(0, H, T)] = rng.choice([1.0, 2.0], T)
+    gate = rng.choice([48.0, 56.0, 64.0, 80.0, 96.0], size=(E + 1, I, H))
+    up = rng.choice([1.0, -1.0, 0.5, -0.5], size=(E + 1, I, H)) * 2.0 ** -4
+    w13 = np.concatenate([gate, up], axis=1)
+    w2 = rng.choice([1.0, -1.25, 1.5, -1.75], size=(E + 1, H, I)) * 2.0 ** -6
+    for m in list(w13) + list(w2):
+        assert np.array_equal(fp8.dequantize_blocks(*fp8.quantize_blocks(m)), m)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    a = fp8.layer_forward_w8a8(cfg, lg, x, w13[:E], w2[:E], w13[E], w2[E])
+    b = orc.layer_forward(cfg, lg, x, w13[:E], w2[:E], w13[E], w2[E])
+    np.testing.assert_allclose(a["out"], b["out"], rtol=1e-13, atol=1e-13)
+    assert np.abs(b["out"]).max() > 1.0
+
+
 # ------------------------------------------------------------ planted mistakes
-PINS = [test_finite_codes_are_distinct_monotone_and_round_trip, test_midpoints_round_to_even_codes,
+PINS = [test_row_blocks_are_weight_blocks_of_one_row, test_scale_exponents_stay_in_the_e8m0_range,
+        test_bf16_round_matches_torch, test_w8a8_layer_hand_example,
+        test_w8a8_layer_equals_the_bf16_layer_when_every_value_is_on_the_grid,
+        test_finite_codes_are_distinct_monotone_and_round_trip, test_midpoints_round_to_even_codes,
         test_nearest_value_by_brute_force, test_saturation, test_block_exponent_definition,
         test_vectorised_exponents_follow_the_definition,
         test_block_quantization_uses_the_range_and_bounds_the_error,
@@ -201,12 +313,37 @@ def _planted(name, fn):
         setattr(fp8, name, orig)
 
 
+_orig_expert, _orig_qrows = fp8.expert_w8a8, fp8.quantize_rows
+
+
+def _h_not_quantized(xq_rows, w13_e, w2_e):
+    return fp8.bf16_round(fp8.swiglu_hidden(xq_rows, w13_e)) @ w2_e.T
+
+
+def _columns_as_blocks(x, block=128):
+    codes, scales = _orig_qrows(np.asarray(x).T, block)   # 128 x 1 pieces: wrong axis
+    return codes.T, np.repeat(scales.T, 1, 0)
+
+
+def _no_clamp(amax):
+    return fp8.block_exponents(amax)
+
+
+def _no_activation_quantization(x, block=128):
+    return np.asarray(x, dtype=np.float64)
+
+
 @pytest.mark.parametrize("name,fn", [("e4m3_encode", _ties_away), ("e4m3_decode", _bias8_decode),
                                      ("block_exponent", _floor_exponent),
                                      ("e4m3_encode", _truncate),
-                                     ("block_exponents", _exponents_off_by_one)],
+                                     ("block_exponents", _exponents_off_by_one),
+                                     ("expert_w8a8", _h_not_quantized),
+                                     ("quantize_rows", _columns_as_blocks),
+                                     ("scale_exponents", _no_clamp),
+                                     ("fake_quant_rows", _no_activation_quantization)],
                          ids=["ties_away", "bias8_decode", "floor_exponent", "truncate",
-                              "exponents_off_by_one"])
+                              "exponents_off_by_one", "h_not_quantized", "columns_as_blocks",
+                              "no_clamp", "no_activation_quantization"])
 def test_planted_mistake_is_caught(name, fn):
     failed = 0
     with _planted(name, fn):
