@@ -59,6 +59,7 @@ def measured_traffic(workload: str):
     return m["bytes"]
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, published
 FP32_PEAK_TFLOPS = 157.3
 
 
@@ -95,6 +96,13 @@ def ffn_bytes(cfg, active_experts: int, rows: int | None = None) -> int:
     eb = cfg.elem_bytes
     rows = cfg.A if rows is None else rows
     w = active_experts * weight_bytes(cfg, 3 * cfg.I)
+    if cfg.acts == "fp8":
+        # E4M3 x and h (1 byte + a 4-byte scale per 128), bf16 y_perm
+        act = rows * (cfg.H + 2 * cfg.I + 2 * cfg.H + 4 * (cfg.H + 2 * cfg.I) // 128)
+        if cfg.shared_I:
+            w += weight_bytes(cfg, 3 * cfg.shared_I)
+            act += cfg.T * (cfg.H + 2 * cfg.shared_I + 2 * cfg.H + 4 * (cfg.H + 2 * cfg.shared_I) // 128)
+        return w + act
     act = rows * (cfg.H * 2 + cfg.I * 2) * eb
     if cfg.shared_I:
         w += weight_bytes(cfg, 3 * cfg.shared_I)
@@ -165,7 +173,10 @@ def cpu_baseline(cfg, logits, budget_s=20.0):
         t0 = time.perf_counter()
         ids, w, _ = orc.route(cfg, logits)
         p = orc.plan(cfg, ids)
+        if cfg.acts == "fp8":          # FP8 activations: x quantized before dispatch
+            x64 = ofp8.fake_quant_rows(x64)
         x_perm = x64[p["row_to_token"]]
+        expert = ofp8.expert_w8a8 if cfg.acts == "fp8" else orc.swiglu
         t_route = time.perf_counter() - t0
         seg_off, seg_exp = p["seg_offsets"], p["seg_expert"]
         active_experts = np.nonzero(p["counts"] > 0)[0].tolist()
@@ -185,7 +196,7 @@ def cpu_baseline(cfg, logits, budget_s=20.0):
             for s in np.nonzero(seg_exp == e)[0]:
                 r0, r1 = int(seg_off[s]), int(seg_off[s + 1])
                 if r1 > r0:
-                    y[r0:r1] = orc.swiglu(x_perm[r0:r1], w13, w2)
+                    y[r0:r1] = expert(x_perm[r0:r1], w13, w2)
             t_ffn[0] += time.perf_counter() - t1
             done.append(e)
 
@@ -262,9 +273,15 @@ def main(argv=None):
     ws = torch.empty((moe.moe_workspace_size(cfg),), dtype=torch.uint8, device=dev)
 
     fp8 = cfg.weights == "fp8"
+    w8a8 = cfg.acts == "fp8"
+    xq = xs = None          # W8A8: x_perm quantized for the FFN leg (outside its timing)
 
     def step():
-        if fp8:
+        if w8a8:
+            moe.moe_layer_forward_w8a8(cfg, d["logits"], d["x"], d["w13"], d["w13_s"], d["w2"],
+                                       d["w2_s"], d["sw13"], d["sw13_s"], d["sw2"], d["sw2_s"],
+                                       out, ids, w, counts, bal, ws)
+        elif fp8:
             moe.moe_layer_forward_fp8w(cfg, d["logits"], d["x"], d["w13"], d["w13_s"], d["w2"],
                                        d["w2_s"], d["sw13"], d["sw13_s"], d["sw2"], d["sw2_s"],
                                        out, ids, w, counts, bal, ws)
@@ -273,7 +290,10 @@ def main(argv=None):
                                   d["sw2"], out, ids, w, counts, bal, ws)
 
     def ffn():
-        if fp8:
+        if w8a8:
+            moe.moe_grouped_ffn_w8a8(cfg, xq, xs, so, se, d["w13"], d["w13_s"], d["w2"],
+                                     d["w2_s"], None, y_perm, ws)
+        elif fp8:
             moe.moe_grouped_ffn_fp8w(cfg, x_perm, so, se, d["w13"], d["w13_s"], d["w2"],
                                      d["w2_s"], None, y_perm, ws)
         else:
@@ -330,6 +350,10 @@ def main(argv=None):
     a2r = torch.empty((A,), dtype=torch.int32, device=dev)
     r2t = torch.empty((R,), dtype=torch.int32, device=dev)
     moe.moe_permute(cfg, d["x"], ids, x_perm, so, se, a2r, r2t, counts, bal, ws)
+    if w8a8:
+        xq = torch.empty((R, cfg.H), dtype=torch.uint8, device=dev)
+        xs = torch.empty((R, cfg.H // 128), dtype=torch.float32, device=dev)
+        moe.moe_quantize_act_fp8(x_perm, xq, xs)
     for _ in range(2):
         ffn()
     f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -346,17 +370,19 @@ def main(argv=None):
     by = ffn_bytes(routed, active, computed)
     gbs = by / (ffn_ms * 1e-3) / 1e9
     tflops = fl / (ffn_ms * 1e-3) / 1e12
-    hbm_bound = fl / (BF16_PEAK_TFLOPS * 1e12) < by / (HBM_PEAK_GBS * 1e9)
+    mfma_peak = FP8_PEAK_TFLOPS if w8a8 else BF16_PEAK_TFLOPS   # the contraction's own dtype
+    hbm_bound = fl / (mfma_peak * 1e12) < by / (HBM_PEAK_GBS * 1e9)
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(cfg.name)}
     else:
-        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": mfma_peak,
+                "unit": "TFLOP/s", "frac": round(tflops / mfma_peak, 4),
                 "traffic": measured_traffic(cfg.name)}
     roof["kernel"] = ("grouped FFN: the two grouped-GEMM launches of one moe_grouped_ffn"
-                      + ("_fp8w" if fp8 else "") + " call (gate/up + SwiGLU, then down + row scale)")
+                      + ("_w8a8" if w8a8 else "_fp8w" if fp8 else "")
+                      + " call (gate/up + SwiGLU, then down + row scale)")
     roof["ms_per_launch"] = round(ffn_ms, 4)
     roof["algorithmic_bytes"] = by
     roof["algorithmic_flops"] = fl
@@ -365,13 +391,16 @@ def main(argv=None):
         "metric": METRIC, "value": round(cfg.T / (ms * 1e-3), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": cfg.dtype,
+        "vs_baseline": None, "dtype": "fp8e4m3" if w8a8 else cfg.dtype,
         "data": "synthetic (seeded; random-init weights)",
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "experts": cfg.E,
                    "top_k": cfg.k, "intermediate": cfg.I, "shared_intermediate": cfg.shared_I,
                    "assignments": cfg.A, "active_experts": active,
-                   "weights": ("fp8 e4m3, 128x128 power-of-two block scales, dequantized to "
-                               "bf16 in the GEMMs") if fp8 else cfg.dtype,
+                   "weights": ("fp8 e4m3, 128x128 power-of-two block scales" +
+                               ("" if w8a8 else ", dequantized to bf16 in the GEMMs"))
+                   if fp8 else cfg.dtype,
+                   **({"activations": "fp8 e4m3, 1x128 power-of-two scales (x before dispatch, "
+                                      "h between the GEMMs); fp8 x fp8 MFMAs"} if w8a8 else {}),
                    "balancedness": float(bal.item()),
                    **({"capacity_factor": cfg.capacity_factor_permille / 1000,
                        "slots_per_expert": cap, "computed_assignments": computed}
@@ -379,7 +408,7 @@ def main(argv=None):
                    **({"split": cfg.split_mode, "split_c": cfg.split_c_permille / 1000}
                       if cfg.n_hot_split else {})},
         "grouped_gemm_tflops": round(tflops, 2),
-        "grouped_gemm_frac_mfma": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "grouped_gemm_frac_mfma": round(tflops / mfma_peak, 4),
         "grouped_gemm_frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
         "wall_s_timed": round(wall, 3),
         "launch": args.launch,

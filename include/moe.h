@@ -232,10 +232,10 @@ moe_status moe_layer_forward(const moe_config* cfg, const float* logits, const v
                              float* topk_w, int32_t* counts, float* balancedness,
                              void* workspace, size_t workspace_bytes, void* stream);
 
-/* Where moe_layer_forward (and moe_layer_forward_fp8w) leave the
+/* Where moe_layer_forward (and its _fp8w and _w8a8 forms) leave the
  * permutation they built inside their workspace, as byte offsets from its
  * start: offsets[0] seg_offsets [S+1], offsets[1] seg_expert [S],
- * offsets[2] assign_to_row [T*k], offsets[3] row_to_token [T*k] (int32, the
+ * offsets[2] assign_to_row [T*k], offsets[3] row_to_token [R] (int32, the
  * contents and meaning of the moe_permute outputs of the same names).  They
  * hold the last call's values once it has completed, until the workspace is
  * used again.  MOE_ERR_INVALID_ARG for an invalid cfg or a NULL offsets. */
@@ -280,6 +280,52 @@ moe_status moe_grouped_ffn_fp8w(const moe_config* cfg, const void* x_perm,
  * [2*shared_I/128, H/128], shared_w2_q [H, shared_I] + shared_w2_scale
  * [H/128, shared_I/128], all NULL when shared_I == 0). */
 moe_status moe_layer_forward_fp8w(const moe_config* cfg, const float* logits, const void* x,
+                                  const uint8_t* w13_q, const float* w13_scale,
+                                  const uint8_t* w2_q, const float* w2_scale,
+                                  const uint8_t* shared_w13_q, const float* shared_w13_scale,
+                                  const uint8_t* shared_w2_q, const float* shared_w2_scale,
+                                  void* out, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                                  float* balancedness, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/* ------------------------------------------------------------------------
+ * FP8 activations as well (W8A8; the MoE inference blog, "Communication
+ * pressure": token activations may be quantized to FP8 before dispatch, and
+ * the low-precision expert GEMM).  An activation matrix X [R, C] (C a
+ * multiple of 128) is held as
+ *   q     [R, C] uint8 E4M3 codes;
+ *   scale [R, C/128] fp32, one power of two per 1 x 128 piece of a row;
+ *   X[r][c] = E4M3(q[r][c]) * scale[r][c/128].
+ * Scales follow the weights' rule (the smallest s with max|piece| <= 448 * 2^s,
+ * 0 for an all-zero piece), with s kept in [-127, 127] -- the range of the
+ * 8-bit power-of-two scales of the FP8 matrix instructions -- in the weights'
+ * quantizer too.  In the layer, x is quantized before dispatch; GEMM 1
+ * multiplies E4M3 x and weights with fp32 accumulation, h = silu(g) * u is
+ * rounded to bf16 and quantized the same way, and GEMM 2 multiplies E4M3 h
+ * and W2; y_perm and out stay bf16.
+ * ------------------------------------------------------------------------ */
+
+/* Quantize bf16 rows src [rows, cols] (cols a multiple of 128; 16-byte
+ * aligned src and q) into q [rows, cols] and scale [rows, cols/128] as
+ * above.  MOE_ERR_INVALID_ARG for bad sizes or pointers; asynchronous. */
+moe_status moe_quantize_act_fp8(int32_t rows, int32_t cols, const void* src, uint8_t* q,
+                                float* scale, void* stream);
+
+/* moe_grouped_ffn_fp8w with FP8 activations: x_perm_q [R, H] codes and
+ * x_perm_scale [R, H/128] (the rows of moe_permute's x_perm, quantized with
+ * moe_quantize_act_fp8).  Other arguments, outputs and errors as
+ * moe_grouped_ffn_fp8w. */
+moe_status moe_grouped_ffn_w8a8(const moe_config* cfg, const uint8_t* x_perm_q,
+                                const float* x_perm_scale, const int32_t* seg_offsets,
+                                const int32_t* seg_expert, const uint8_t* w13_q,
+                                const float* w13_scale, const uint8_t* w2_q,
+                                const float* w2_scale, const float* row_scale, void* y_perm,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* moe_layer_forward_fp8w with FP8 activations: x [T, H] bf16 is quantized
+ * inside the call (into the workspace) before dispatch.  Arguments, outputs
+ * and errors as moe_layer_forward_fp8w. */
+moe_status moe_layer_forward_w8a8(const moe_config* cfg, const float* logits, const void* x,
                                   const uint8_t* w13_q, const float* w13_scale,
                                   const uint8_t* w2_q, const float* w2_scale,
                                   const uint8_t* shared_w13_q, const float* shared_w13_scale,

@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     MoEError, lib, make_config, moe_grouped_ffn, moe_layer_forward, moe_num_segments,
     moe_permute, moe_route_topk, moe_status_string, moe_unpermute_combine,
     moe_workspace_size, moe_quantize_fp8, moe_grouped_ffn_fp8w, moe_layer_forward_fp8w,
-    moe_layer_plan_offsets, moe_num_rows,
+    moe_layer_plan_offsets, moe_num_rows, moe_quantize_act_fp8, moe_grouped_ffn_w8a8,
+    moe_layer_forward_w8a8,
     EXPORTED_SYMBOLS,
 )

@@ -20,7 +20,8 @@ EXPORTED_SYMBOLS = (
     "moe_status_string", "moe_num_segments", "moe_workspace_size", "moe_route_topk",
     "moe_permute", "moe_grouped_ffn", "moe_unpermute_combine", "moe_layer_forward",
     "moe_quantize_fp8", "moe_grouped_ffn_fp8w", "moe_layer_forward_fp8w",
-    "moe_layer_plan_offsets", "moe_num_rows",
+    "moe_layer_plan_offsets", "moe_num_rows", "moe_quantize_act_fp8", "moe_grouped_ffn_w8a8",
+    "moe_layer_forward_w8a8",
 )
 
 
@@ -73,6 +74,12 @@ lib.moe_grouped_ffn_fp8w.restype = ctypes.c_int
 lib.moe_grouped_ffn_fp8w.argtypes = [_cfgp] + [_p] * 10 + [ctypes.c_size_t, _p]
 lib.moe_layer_forward_fp8w.restype = ctypes.c_int
 lib.moe_layer_forward_fp8w.argtypes = [_cfgp] + [_p] * 16 + [ctypes.c_size_t, _p]
+lib.moe_quantize_act_fp8.restype = ctypes.c_int
+lib.moe_quantize_act_fp8.argtypes = [ctypes.c_int32] * 2 + [_p] * 4
+lib.moe_grouped_ffn_w8a8.restype = ctypes.c_int
+lib.moe_grouped_ffn_w8a8.argtypes = [_cfgp] + [_p] * 11 + [ctypes.c_size_t, _p]
+lib.moe_layer_forward_w8a8.restype = ctypes.c_int
+lib.moe_layer_forward_w8a8.argtypes = [_cfgp] + [_p] * 16 + [ctypes.c_size_t, _p]
 
 
 def make_config(shape) -> MoEConfig:
@@ -216,3 +223,31 @@ def moe_layer_forward_fp8w(cfg, logits, x, w13_q, w13_scale, w2_q, w2_scale, sha
         _ptr(shared_w2_scale), _ptr(out), _ptr(topk_ids), _ptr(topk_w), _ptr(counts),
         _ptr(balancedness), _ptr(workspace), _nbytes(workspace), _stream(stream)),
         "moe_layer_forward_fp8w")
+
+
+def moe_quantize_act_fp8(src, q, scale, stream=None):
+    """src [rows, cols] bf16 -> q uint8 [rows, cols], scale fp32 [rows, cols/128]."""
+    rows, cols = tuple(src.shape)
+    _check(lib.moe_quantize_act_fp8(rows, cols, _ptr(src), _ptr(q), _ptr(scale), _stream(stream)),
+           "moe_quantize_act_fp8")
+
+
+def moe_grouped_ffn_w8a8(cfg, x_perm_q, x_perm_scale, seg_offsets, seg_expert, w13_q, w13_scale,
+                         w2_q, w2_scale, row_scale, y_perm, workspace, stream=None):
+    _check(lib.moe_grouped_ffn_w8a8(ctypes.byref(_cfg(cfg)), _ptr(x_perm_q), _ptr(x_perm_scale),
+                                    _ptr(seg_offsets), _ptr(seg_expert), _ptr(w13_q),
+                                    _ptr(w13_scale), _ptr(w2_q), _ptr(w2_scale), _ptr(row_scale),
+                                    _ptr(y_perm), _ptr(workspace), _nbytes(workspace),
+                                    _stream(stream)),
+           "moe_grouped_ffn_w8a8")
+
+
+def moe_layer_forward_w8a8(cfg, logits, x, w13_q, w13_scale, w2_q, w2_scale, shared_w13_q,
+                           shared_w13_scale, shared_w2_q, shared_w2_scale, out, topk_ids, topk_w,
+                           counts, balancedness, workspace, stream=None):
+    _check(lib.moe_layer_forward_w8a8(
+        ctypes.byref(_cfg(cfg)), _ptr(logits), _ptr(x), _ptr(w13_q), _ptr(w13_scale), _ptr(w2_q),
+        _ptr(w2_scale), _ptr(shared_w13_q), _ptr(shared_w13_scale), _ptr(shared_w2_q),
+        _ptr(shared_w2_scale), _ptr(out), _ptr(topk_ids), _ptr(topk_w), _ptr(counts),
+        _ptr(balancedness), _ptr(workspace), _nbytes(workspace), _stream(stream)),
+        "moe_layer_forward_w8a8")

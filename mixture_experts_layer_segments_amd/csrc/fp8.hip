@@ -16,6 +16,7 @@ namespace moe {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // E4M3 code of y (exact fp32), round to nearest even, saturating at 448.
 __device__ __forceinline__ uint32_t e4m3_rne(float y) {
@@ -40,9 +41,11 @@ __device__ __forceinline__ uint32_t e4m3_rne(float y) {
   return sign | ((uint32_t)(E + 7) << 3) | m3;
 }
 
-// Smallest s with amax <= 448 * 2^s (amax finite, >= 0); 0 for amax == 0.
-// amax = (1 + m / 2^23) * 2^E and 448 = 1.75 * 2^8, so s = E - 8 when the
-// mantissa is at most 0.75 (m <= 0x600000), else E - 7.
+// Smallest s with amax <= 448 * 2^s (amax finite, >= 0); 0 for amax == 0;
+// kept in [-127, 127], the range of the 8-bit power-of-two (E8M0) scales the
+// FP8 matrix instructions take.  amax = (1 + m / 2^23) * 2^E and
+// 448 = 1.75 * 2^8, so s = E - 8 when the mantissa is at most 0.75
+// (m <= 0x600000), else E - 7.
 __device__ __forceinline__ int block_exponent(float amax) {
   if (amax == 0.0f) return 0;
   int adj = 0;
@@ -52,7 +55,13 @@ __device__ __forceinline__ int block_exponent(float amax) {
   }
   const uint32_t b = __float_as_uint(amax);
   const int E = (int)(b >> 23) - 127;
-  return E - 8 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0) + adj;
+  const int s = E - 8 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0) + adj;
+  return max(-127, min(127, s));
+}
+
+// 2^s for s in [-127, 127], exactly (ldexpf of 1 would do; this states it).
+__device__ __forceinline__ float pow2(int s) {
+  return s >= -126 ? __uint_as_float((uint32_t)(s + 127) << 23) : __uint_as_float(0x00400000u);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -86,7 +95,7 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t* __res
   __syncthreads();
   amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   const int s = block_exponent(amax);
-  if (t == 0) scale[((size_t)mat * br + bi) * bc + bj] = ldexpf(1.0f, s);
+  if (t == 0) scale[((size_t)mat * br + bi) * bc + bj] = pow2(s);
 
   // 64 codes -> 16 words -> 4 x 16-byte stores (byte j of a word = column 4w + j)
   uint32_t out[16];
@@ -107,7 +116,50 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t* __res
         u32x4{out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]};
 }
 
+// Activations: one power-of-two scale per 1 x 128 piece of a row.  A group
+// of 16 lanes takes one piece (8 elements a lane, one 16-byte load), so a
+// 256-thread block quantizes 16 pieces; the piece maximum is reduced over
+// the group with lane shuffles.
+__global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(const uint16_t* __restrict__ src,
+                                                                uint8_t* __restrict__ q,
+                                                                float* __restrict__ scale,
+                                                                int64_t pieces, int cols) {
+  const int64_t piece = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (piece >= pieces) return;                      // whole groups of 16 leave together
+  const int sub = threadIdx.x & 15;
+  const int pr = cols / 128;
+  const int64_t row = piece / pr;
+  const int col = (int)(piece % pr) * 128 + sub * 8;
+  const size_t at = (size_t)row * cols + col;
+  const u32x4 v = *reinterpret_cast<const u32x4*>(src + at);
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[j])), fabsf(bf16_hi(v[j]))));
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+  const int s = block_exponent(amax);
+  if (sub == 0) scale[piece] = pow2(s);
+  uint32_t w[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t c0 = e4m3_rne(ldexpf(bf16_lo(v[2 * j]), -s));
+    const uint32_t c1 = e4m3_rne(ldexpf(bf16_hi(v[2 * j]), -s));
+    const uint32_t c2 = e4m3_rne(ldexpf(bf16_lo(v[2 * j + 1]), -s));
+    const uint32_t c3 = e4m3_rne(ldexpf(bf16_hi(v[2 * j + 1]), -s));
+    w[j] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+  }
+  *reinterpret_cast<u32x2*>(q + at) = u32x2{w[0], w[1]};
+}
+
 }  // namespace
+
+void launch_quantize_rows_fp8(int64_t rows, int cols, const void* src, uint8_t* q, float* scale,
+                              hipStream_t s) {
+  const int64_t pieces = rows * (cols / 128);
+  if (pieces == 0) return;
+  quantize_rows_fp8_kernel<<<(unsigned)((pieces + 15) / 16), 256, 0, s>>>(
+      (const uint16_t*)src, q, scale, pieces, cols);
+}
 
 void launch_quantize_fp8(int n_mat, int rows, int cols, const void* src, uint8_t* q,
                          float* scale, hipStream_t s) {

@@ -26,6 +26,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 struct GemmProblem {
   const uint16_t* A;        // [rows, K] bf16 bits
@@ -42,6 +44,7 @@ struct GemmProblem {
   int64_t b_stride;         // elements per expert in B
   const float* b_scale;     // FP8 weights: [n_w][NB/128][K/128] block scales (else unused)
   int64_t s_stride;         // floats per expert in b_scale
+  const float* a_scale;     // FP8 activations: [A rows][K/128] scales of the A codes
 };
 
 struct GemmArgs {
@@ -234,7 +237,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 // of the slot (bf16 weights: 128-byte row pieces; E4M3 codes: 64-byte
 // pieces, 16 rows per block).  `voff` holds each lane's byte offset of its
 // 16 bytes at k = 0; the stage's K offset goes in the scalar offset.
-template <int LPI, int NI, int STAGES, int STAGE_CH, int A_CH, int BK, int A_IT, int WB>
+template <int LPI, int NI, int STAGES, int STAGE_CH, int A_CH, int BK, int A_IT, int WB, int AB>
 __device__ __forceinline__ void ring_issue(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                            const uint32_t* voff, u32x4* ring, int kt, int wv) {
   u32x4* slot = ring + (kt % STAGES) * STAGE_CH;
@@ -242,7 +245,7 @@ __device__ __forceinline__ void ring_issue(__amdgpu_buffer_rsrc_t ra, __amdgpu_b
   for (int i = 0; i < LPI; ++i) {
     if (i < A_IT)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MOE_LDS_PTR(slot + (i * NI + wv) * 64), 16,
-                                               voff[i], kt * BK * 2, 0, 0);
+                                               voff[i], kt * BK * AB, 0, 0);
     else
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rb, MOE_LDS_PTR(slot + A_CH + ((i - A_IT) * NI + wv) * 64), 16, voff[i],
@@ -251,11 +254,13 @@ __device__ __forceinline__ void ring_issue(__amdgpu_buffer_rsrc_t ra, __amdgpu_b
 }
 
 // Ring-tile geometry shared by the per-tile body and the kernels that size
-// the ring (WF = 1: the weight rows of a stage hold 1-byte E4M3 codes).
+// the ring (WF = 1: the weight rows of a stage hold 1-byte E4M3 codes; WF = 2:
+// the activation rows too).
 template <int WF, int BM, int BN, int BK, int STAGES>
 struct RingShape {
-  static constexpr int KCH = BK / 8;                      // A: 16-byte chunks per row piece
-  static constexpr int KCHB = WF ? BK / 16 : KCH;         // B: 16-byte chunks per row piece
+  static constexpr int AB = WF == 2 ? 1 : 2;              // bytes per activation element
+  static constexpr int KCH = BK * AB / 16;                // A: 16-byte chunks per row piece
+  static constexpr int KCHB = WF ? BK / 16 : BK / 8;      // B: 16-byte chunks per row piece
   static constexpr int A_CH = BM * KCH;                   // A chunks per stage
   static constexpr int STAGE_CH = A_CH + BN * KCHB;       // 16-byte chunks per stage
   static constexpr int RING_CH = STAGES * STAGE_CH;       // 16-byte chunks of the ring
@@ -282,6 +287,7 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
                                           u32x4* ring, float* scl) {
   using RS = RingShape<WF, BM, BN, BK, STAGES>;
   constexpr int KCH = RS::KCH, KCHB = RS::KCHB, A_CH = RS::A_CH, STAGE_CH = RS::STAGE_CH;
+  constexpr int AB = RS::AB;            // bytes per activation element
   constexpr int RPB = 64 / KCH;         // A rows per 1 KiB copy block
   constexpr int RPBB = 64 / KCHB;       // B rows per 1 KiB copy block
   constexpr int NW = NTHR / 64;
@@ -295,8 +301,8 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
   constexpr int NI = (NW == 8 && MOE_COPY_WAVES == 4) ? 4 : NW;   // issuing waves
   constexpr int A_IT = BM / RPB / NI;   // A copies per issuing wave per stage
   constexpr int LPI = A_IT + BN / RPBB / NI;   // all copies per issuing wave per stage
-  static_assert(BK == 32 || BK == 64, "row piece of 64 or 128 bytes");
-  static_assert(!WF || BK == 64, "E4M3 weights: 64-byte row pieces");
+  static_assert(WF == 2 ? BK == 128 : (BK == 32 || BK == 64), "row piece of 64 or 128 bytes");
+  static_assert(WF != 1 || BK == 64, "E4M3 weights: 64-byte row pieces");
   static_assert((BM / RPB) % NI == 0 && (BN / RPBB) % NI == 0, "copy blocks per wave");
   static_assert(STAGES >= 2 && STAGES <= 6, "ring shape");
   static_assert(LPI * (STAGES - 2) < 64, "vmcnt range");
@@ -340,7 +346,7 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
 
   // byte offset of this lane's 16 bytes at k = 0 in each of the wave's copies
   const int wvs = __builtin_amdgcn_readfirstlane(wv);
-  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(P.A, (uint32_t)((size_t)P.a_ld_rows * K * 2));
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(P.A, (uint32_t)((size_t)P.a_ld_rows * K * AB));
   const __amdgpu_buffer_rsrc_t rb =
       buffer_rsrc(Bb, (uint32_t)((size_t)(MODE == 0 ? 2 * N : N) * K * WB));
   uint32_t voff[LPI];
@@ -351,7 +357,7 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
       const int kc = (lane % KCH) ^ swz<KCH>(row);
       const int ar = r0 + min(m0 + row, len - 1);
       const int grow = P.a_rows ? P.a_rows[ar] : ar;
-      voff[i] = (uint32_t)grow * (uint32_t)(K * 2) + kc * 16;
+      voff[i] = (uint32_t)grow * (uint32_t)(K * AB) + kc * 16;
     } else {
       const int br = ((i - A_IT) * NI + wvs) * RPBB + lane / KCHB;   // row of the weight tile
       const int kc = (lane % KCHB) ^ swz<KCHB>(BM + br);
@@ -386,11 +392,21 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
       const int rb_ = MODE == 0 ? (g ? (P.up_off + n0) / 128 : n0 / 128) : min(n0 / 128 + g, nrb - 1);
       scl[i] = Sb[rb_ * KB + kb];
     }
+    if (WF == 2) {
+      // and the E8M0 exponents of its activation rows' scales, a byte each
+      uint8_t* ascl = reinterpret_cast<uint8_t*>(scl + 2 * KB);
+      for (int i = tid; i < BM * KB; i += NTHR) {
+        const int row = i / KB, kb = i % KB;
+        const int ar = r0 + min(m0 + row, len - 1);
+        const int grow = P.a_rows ? P.a_rows[ar] : ar;
+        ascl[i] = (uint8_t)(__float_as_uint(P.a_scale[(size_t)grow * KB + kb]) >> 23);
+      }
+    }
   }
 #pragma unroll
   for (int st = 0; st < STAGES - 1; ++st)
     if (st < KT && wvs < NI)
-      ring_issue<LPI, NI, STAGES, STAGE_CH, A_CH, BK, A_IT, WB>(ra, rb, voff, ring, st, wvs);
+      ring_issue<LPI, NI, STAGES, STAGE_CH, A_CH, BK, A_IT, WB, AB>(ra, rb, voff, ring, st, wvs);
   // WF: the scale group of this wave's weight fragments (GEMM 1: gate
   // fragments use group 0, up fragments group 1)
   const int g_down = MODE == 1 ? (wn * WN) / 128 : 0;
@@ -401,9 +417,46 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
     if (WF) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the tile's scales are written
     raw_barrier();
     if (kt + STAGES - 1 < KT && wvs < NI)
-      ring_issue<LPI, NI, STAGES, STAGE_CH, A_CH, BK, A_IT, WB>(ra, rb, voff, ring,
-                                                                kt + STAGES - 1, wvs);
+      ring_issue<LPI, NI, STAGES, STAGE_CH, A_CH, BK, A_IT, WB, AB>(ra, rb, voff, ring,
+                                                                    kt + STAGES - 1, wvs);
     const u32x4* slot = ring + (kt % STAGES) * STAGE_CH;
+    if constexpr (WF == 2) {
+      // E4M3 x E4M3: one 128-deep MFMA K step per stage.  Lane l supplies row
+      // (or weight row) l % 16, chunks g and 4 + g (g = l / 16) of the 128-byte
+      // piece, and its row's E8M0 scale (every lane of a row the same one: a
+      // scale covers the whole 128-deep step).
+      const uint8_t* ascl = reinterpret_cast<const uint8_t*>(scl + 2 * KB);
+      const int g = lane >> 4;
+      int sa[TM], sb[TN];
+#pragma unroll
+      for (int mi = 0; mi < TM; ++mi) sa[mi] = ascl[(wm * WM + mi * 16 + (lane & 15)) * KB + kt];
+      const int e0 = (int)(__float_as_uint(scl[(MODE == 0 ? 0 : g_down) * KB + kt]) >> 23);
+      const int e1 = (int)(__float_as_uint(scl[KB + kt]) >> 23);
+#pragma unroll
+      for (int ni = 0; ni < TN; ++ni) sb[ni] = (MODE == 0 && ni >= TN / 2) ? e1 : e0;
+      i32x8 af[TM], bq[TN];
+#pragma unroll
+      for (int mi = 0; mi < TM; ++mi) {
+        const int row = wm * WM + mi * 16 + (lane & 15);
+        const u32x4 lo = slot[row * KCH + (g ^ swz<KCH>(row))];
+        const u32x4 hi = slot[row * KCH + ((4 + g) ^ swz<KCH>(row))];
+        af[mi] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int ni = 0; ni < TN; ++ni) {
+        const int br = brow_of[ni] + (lane & 15);
+        const u32x4* brow = slot + A_CH + br * KCHB;
+        const u32x4 lo = brow[g ^ swz<KCHB>(BM + br)];
+        const u32x4 hi = brow[(4 + g) ^ swz<KCHB>(BM + br)];
+        bq[ni] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int mi = 0; mi < TM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < TN; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              af[mi], bq[ni], acc[mi][ni], 0, 0, 0, sa[mi], 0, sb[ni]);
+    } else {
     float sc0 = 1.0f, sc1 = 1.0f;
     if (WF) {
       const int kb = kt * BK / 128;
@@ -471,6 +524,7 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
       } else {
         __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
       }
+    }
     }
   }
 
@@ -541,6 +595,7 @@ __global__ __launch_bounds__(NTHR, OCC) void gemm_ring_kernel(GemmArgs args) {
 #ifndef MOE_BIG_ROWS
 #define MOE_BIG_ROWS 256
 #endif
+
 template <int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
 struct TileCfg {
   static constexpr int kRingBytes = RingShape<WF, BM, BN, BK, STAGES>::RING_CH * 16;
@@ -564,6 +619,19 @@ template <> struct Tiles<1> {
   using Mid1 = TileCfg<1, MOE_MID_TILE_F8>;
   using Mid2 = TileCfg<1, MOE_MID_TILE_F8>;
   using Big = TileCfg<1, MOE_BIG_TILE_F8>;
+};
+// E4M3 activations and weights: 128-deep stages (128-byte row pieces, as the
+// bf16 tiles' 64-deep ones), one scaled FP8 MFMA K step each.
+#ifndef MOE_MID_TILE_W8A8
+#define MOE_MID_TILE_W8A8 128, 256, 128, 512, 2, 3
+#endif
+#ifndef MOE_BIG_TILE_W8A8
+#define MOE_BIG_TILE_W8A8 256, 256, 128, 512, 4, 2
+#endif
+template <> struct Tiles<2> {
+  using Mid1 = TileCfg<2, MOE_MID_TILE_W8A8>;
+  using Mid2 = TileCfg<2, MOE_MID_TILE_W8A8>;
+  using Big = TileCfg<2, MOE_BIG_TILE_W8A8>;
 };
 
 
@@ -633,8 +701,25 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 #ifndef MOE_DECODE_ROWS
 #define MOE_DECODE_ROWS 16  // mean rows per segment up to which the decode tiles are used
 #endif
+// One activation fragment of the decode tiles, 8 consecutive K elements of
+// row `arow` starting at element offset `off` (K index k): bf16 as stored,
+// or (WF = 2) 8 E4M3 codes times their 1 x 128 scale, exactly, as bf16.
+template <int WF>
+__device__ __forceinline__ u32x4 decode_a_frag(const GemmProblem& P, bool ok, uint32_t off,
+                                               int arow, int k) {
+  if (!ok) return u32x4{0u, 0u, 0u, 0u};
+  if constexpr (WF == 2) {
+    const u32x2 c = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(P.A) + off);
+    const float sc = P.a_scale[(size_t)arow * (P.K / 128) + k / 128];
+    return __builtin_bit_cast(u32x4, fp8x8_to_bf16(c.x, c.y, sc));
+  } else {
+    return *reinterpret_cast<const u32x4*>(P.A + off);
+  }
+}
+
 // WF = 1: E4M3 weights with 128 x 128 block scales, loaded as 16-byte chunks
 // of 16 codes and dequantized (exactly) to bf16 on their way into LDS.
+// WF = 2: E4M3 activations too (see decode_a_frag).
 template <int MODE, int WF, int BN, int BK, int MT, int WAVES>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES)))
 void gemm_decode_kernel(GemmArgs args) {
@@ -643,6 +728,7 @@ void gemm_decode_kernel(GemmArgs args) {
   constexpr int LCH = WF ? BK / 16 : KCH;        // 16-byte chunks per row as loaded
   constexpr int B_CH = BN * LCH / 256;           // loaded chunks per thread per stage
   constexpr int WB = WF ? 1 : 2;                 // bytes per weight
+  constexpr int AB = WF == 2 ? 1 : 2;            // bytes per activation element
   constexpr int KPW = BK / 32 / 4;               // MFMA K steps per wave per stage
   constexpr int TN = BN / 16;                    // n subtiles
   static_assert(KPW >= 1 && B_CH >= 1, "tile shape");
@@ -697,16 +783,19 @@ void gemm_decode_kernel(GemmArgs args) {
       b_off[i] = ((uint32_t)brow * (uint32_t)K + kc * (16 / WB)) * WB;
       if (WF) b_sc[i] = (brow / 128) * (K / 128) + (kc * 16) / 128;
     }
-    // this lane's activation row and its K offsets inside a stage
+    // this lane's activation row and its K offsets inside a stage (WF = 2:
+    // E4M3 codes, dequantized with their 1 x 128 scale on the way to the MFMA)
     bool a_ok[MT];
     uint32_t a_off[MT];
+    int a_row[MT];
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) {
       a_ok[mi] = m0 + mi * 16 + r < len;
       const int ar = r0 + min(m0 + mi * 16 + r, len - 1);
-      a_off[mi] = (uint32_t)(P.a_rows ? P.a_rows[ar] : ar) * (uint32_t)K +
-                  (wv * KPW * 32 + q * 8);
+      a_row[mi] = P.a_rows ? P.a_rows[ar] : ar;
+      a_off[mi] = (uint32_t)a_row[mi] * (uint32_t)K + (wv * KPW * 32 + q * 8);
     }
+    (void)AB;
 
     f32x4 acc[MT][TN];
 #pragma unroll
@@ -724,7 +813,8 @@ void gemm_decode_kernel(GemmArgs args) {
     for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
       for (int jj = 0; jj < KPW; ++jj)
-        ra[mi][jj] = a_ok[mi] ? *reinterpret_cast<const u32x4*>(P.A + a_off[mi] + jj * 32) : zero;
+        ra[mi][jj] = decode_a_frag<WF>(P, a_ok[mi], a_off[mi] + jj * 32, a_row[mi],
+                                       wv * KPW * 32 + jj * 32);
 
     const int KT = K / BK;
     for (int kt = 0; kt < KT; ++kt) {
@@ -758,8 +848,8 @@ void gemm_decode_kernel(GemmArgs args) {
         for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
           for (int jj = 0; jj < KPW; ++jj)
-            ra[mi][jj] =
-                a_ok[mi] ? *reinterpret_cast<const u32x4*>(P.A + a_off[mi] + koff + jj * 32) : zero;
+            ra[mi][jj] = decode_a_frag<WF>(P, a_ok[mi], a_off[mi] + koff + jj * 32, a_row[mi],
+                                           koff + wv * KPW * 32 + jj * 32);
       }
 #pragma unroll
       for (int jj = 0; jj < KPW; ++jj) {
@@ -861,15 +951,20 @@ int persistent_grid(Kern kernel, size_t dyn_lds, int fallback, int threads = 256
 
 // Dynamic LDS of a ring launch: the tile table, and (E4M3 weights) a tile's
 // block scales: 2 groups x K/128 floats for the longest K of the problems.
-inline size_t ring_dyn_lds(const GemmArgs& g, int wf) {
+// Dynamic LDS of a ring launch: the tile table, then (FP8 weights) a tile's
+// two groups of weight block scales, then (FP8 activations) the E8M0 bytes
+// of its BM rows' scales.
+inline size_t ring_dyn_lds(const GemmArgs& g, int wf, int bm) {
   int kmax = 0;
   for (int p = 0; p < g.n_probs; ++p) kmax = g.p[p].K > kmax ? g.p[p].K : kmax;
-  return (size_t)(g.n_seg_total + 1) * sizeof(int) + (wf ? (size_t)2 * (kmax / 128) * 4 : 0);
+  const size_t kb = (size_t)(kmax / 128);
+  return (size_t)(g.n_seg_total + 1) * sizeof(int) + (wf ? 2 * kb * 4 : 0) +
+         (wf == 2 ? (size_t)bm * kb : 0);
 }
 
 template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
 void launch_ring(const GemmArgs& g, hipStream_t s) {
-  const size_t dyn = ring_dyn_lds(g, WF);
+  const size_t dyn = ring_dyn_lds(g, WF, BM);
   auto k = gemm_ring_kernel<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES, 1>;
   k<<<persistent_grid(k, dyn, 1, NTHR), NTHR, dyn, s>>>(g);
 }
@@ -888,8 +983,19 @@ GemmArgs cover(GemmArgs g, int bm, int ncols, int min_len, int max_len) {
   return g;
 }
 
-// The bf16-activation GEMM pair for weight format WF (0: bf16, 1: E4M3 with
-// block scales).
+// Between the two GEMMs of an FP8-activation pair: h of every problem, as
+// GEMM 1 wrote it in bf16, quantized in 1 x 128 pieces for GEMM 2.
+template <int WF>
+void quantize_h(const FfnProblem* probs, int n_probs, hipStream_t s) {
+  if constexpr (WF == 2) {
+    for (int p = 0; p < n_probs; ++p)
+      launch_quantize_rows_fp8(probs[p].rows, probs[p].Iw, probs[p].h, probs[p].h_q,
+                               probs[p].h_scale, s);
+  }
+}
+
+// The GEMM pair for operand format WF (0: bf16; 1: E4M3 weights with block
+// scales, bf16 activations; 2: E4M3 weights and activations).
 template <int WF>
 void launch_mfma_pair(const moe_config& c, const FfnProblem* probs, int n_probs,
                       const GemmArgs& g1, const GemmArgs& g2, hipStream_t s) {
@@ -907,6 +1013,7 @@ void launch_mfma_pair(const moe_config& c, const FfnProblem* probs, int n_probs,
     auto k1 = gemm_decode_kernel<0, WF, DBN1, BK1, 1, MOE_DWAVES>;
     auto k2 = gemm_decode_kernel<1, WF, DBN2, BK2, 1, MOE_DWAVES>;
     k1<<<persistent_grid(k1, lds_tiles, 4), 256, lds_tiles, s>>>(cover(g1, 16, DBN1 / 2, 1, kAll));
+    quantize_h<WF>(probs, n_probs, s);
     k2<<<persistent_grid(k2, lds_tiles, 4), 256, lds_tiles, s>>>(cover(g2, 16, DBN2, 1, kAll));
     MOE_DBG("grouped gemms");
     return;
@@ -914,26 +1021,31 @@ void launch_mfma_pair(const moe_config& c, const FfnProblem* probs, int n_probs,
   // Segments of MOE_BIG_ROWS rows or more take 256 x 256 tiles (half the
   // weight re-reads of their many row tiles), the rest 128 x 256 tiles: one
   // launch per shape, each covering its own segments.  The mid ring is cut
-  // to 2 stages if the 3-stage one leaves no room for the tile table.  A
-  // segment holds at most one row per token of its problem, so the big
-  // launches may be skipped.
+  // to 2 stages if the 3-stage one leaves no room for the tile table (and
+  // the scales), and the mid tiles take the long segments too if the big
+  // ring does not fit beside them.  A segment holds at most one row per
+  // token of its problem, so the big launches may be skipped.
   using M1 = typename Tiles<WF>::Mid1;
   using M2 = typename Tiles<WF>::Mid2;
   using BG = typename Tiles<WF>::Big;
-  const GemmArgs m1 = cover(g1, M1::kBM, M1::kBN / 2, 1, MOE_BIG_ROWS);
-  const GemmArgs m2 = cover(g2, M2::kBM, M2::kBN, 1, MOE_BIG_ROWS);
+  constexpr size_t kMargin = 64;
+  const bool big_fits = ring_dyn_lds(g1, WF, BG::kBM) + BG::kRingBytes + kMargin <= kMaxLdsBytes &&
+                        ring_dyn_lds(g2, WF, BG::kBM) + BG::kRingBytes + kMargin <= kMaxLdsBytes;
+  const int mid_hi = big_fits ? MOE_BIG_ROWS : kAll;
+  const GemmArgs m1 = cover(g1, M1::kBM, M1::kBN / 2, 1, mid_hi);
+  const GemmArgs m2 = cover(g2, M2::kBM, M2::kBN, 1, mid_hi);
   const GemmArgs b1 = cover(g1, BG::kBM, BG::kBN / 2, MOE_BIG_ROWS, kAll);
   const GemmArgs b2 = cover(g2, BG::kBM, BG::kBN, MOE_BIG_ROWS, kAll);
-  constexpr size_t kMargin = 64;
-  const bool deep1 = ring_dyn_lds(g1, WF) + M1::kRingBytes + kMargin <= kMaxLdsBytes;
-  const bool deep2 = ring_dyn_lds(g2, WF) + M2::kRingBytes + kMargin <= kMaxLdsBytes;
+  const bool deep1 = ring_dyn_lds(g1, WF, M1::kBM) + M1::kRingBytes + kMargin <= kMaxLdsBytes;
+  const bool deep2 = ring_dyn_lds(g2, WF, M2::kBM) + M2::kRingBytes + kMargin <= kMaxLdsBytes;
   int longest = 0;
   for (int p = 0; p < n_probs; ++p) longest = probs[p].rows > longest ? probs[p].rows : longest;
-  const bool any_big = longest >= MOE_BIG_ROWS && c.T >= MOE_BIG_ROWS;
+  const bool any_big = big_fits && longest >= MOE_BIG_ROWS && c.T >= MOE_BIG_ROWS;
   // (a 2-stage ring of the mid shape always fits beside the largest table)
   if (deep1) launch_ring<0, WF, M1::kBM, M1::kBN, M1::kBK, M1::kThreads, M1::kWM, M1::kStages>(m1, s);
   else launch_ring<0, WF, M1::kBM, M1::kBN, M1::kBK, M1::kThreads, M1::kWM, 2>(m1, s);
   if (any_big) launch_ring<0, WF, BG::kBM, BG::kBN, BG::kBK, BG::kThreads, BG::kWM, BG::kStages>(b1, s);
+  quantize_h<WF>(probs, n_probs, s);
   if (deep2) launch_ring<1, WF, M2::kBM, M2::kBN, M2::kBK, M2::kThreads, M2::kWM, M2::kStages>(m2, s);
   else launch_ring<1, WF, M2::kBM, M2::kBN, M2::kBK, M2::kThreads, M2::kWM, 2>(m2, s);
   if (any_big) launch_ring<1, WF, BG::kBM, BG::kBN, BG::kBK, BG::kThreads, BG::kWM, BG::kStages>(b2, s);
@@ -981,9 +1093,11 @@ void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_prob
     a.b_stride = (int64_t)2 * P.Iw * H;
     a.b_scale = P.w13_scale;
     a.s_stride = (int64_t)(2 * P.Iw / 128) * (H / 128);
+    a.a_scale = P.a_scale;
     GemmProblem& b = g2.p[p];
     b = a;
-    b.A = (const uint16_t*)P.h;
+    b.A = (const uint16_t*)(P.a_fp8 ? (const void*)P.h_q : P.h);
+    b.a_scale = P.h_scale;
     b.a_rows = nullptr;
     b.a_ld_rows = P.rows;
     b.B = (const uint16_t*)P.w2;
@@ -999,7 +1113,8 @@ void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_prob
   }
   g1.n_probs = g2.n_probs = n_probs;
   g1.n_seg_total = g2.n_seg_total = nst;
-  if (probs[0].w_fp8) launch_mfma_pair<1>(c, probs, n_probs, g1, g2, s);
+  if (probs[0].a_fp8) launch_mfma_pair<2>(c, probs, n_probs, g1, g2, s);
+  else if (probs[0].w_fp8) launch_mfma_pair<1>(c, probs, n_probs, g1, g2, s);
   else launch_mfma_pair<0>(c, probs, n_probs, g1, g2, s);
 }
 

@@ -35,6 +35,11 @@ Layout make_layout(const moe_config& c) {
   L.p_end = o;
   L.h = take(R * c.I * eb);
   L.shared_h = take((size_t)c.T * c.shared_I * eb);
+  const size_t ib = ((size_t)c.I + 127) / 128, sb = ((size_t)c.shared_I + 127) / 128;
+  L.h_q = take(R * c.I);
+  L.h_s = take(R * ib * 4);
+  L.shared_hq = take((size_t)c.T * c.shared_I);
+  L.shared_hs = take((size_t)c.T * sb * 4);
   L.g_end = o;
   L.y_perm = take(R * c.H * eb);
   L.shared_y = take(c.shared_I > 0 ? (size_t)c.T * c.H * eb : 0);
@@ -43,6 +48,8 @@ Layout make_layout(const moe_config& c) {
   L.assign_to_row = take(A * 4);
   L.row_to_token = take(R * 4);
   L.row_w = take(R * 4);
+  L.x_q = take((size_t)c.T * c.H);
+  L.x_s = take((size_t)c.T * (((size_t)c.H + 127) / 128) * 4);
   L.l_end = o;
   return L;
 }
@@ -128,6 +135,7 @@ struct Weights {
   const float* w13_scale;
   const float* w2_scale;
   bool fp8;
+  bool acts_fp8 = false;   // with fp8: E4M3 activations too (W8A8)
 };
 
 // Extra requirements of FP8 weights: bf16 activations, 128-multiples, scales.
@@ -140,9 +148,10 @@ moe_status check_fp8(const moe_config* cfg, const Weights& w) {
   return MOE_OK;
 }
 
-moe_status grouped_ffn(const moe_config* cfg, const void* x_perm, const int32_t* seg_offsets,
-                       const int32_t* seg_expert, const Weights& w, const float* row_scale,
-                       void* y_perm, void* workspace, size_t workspace_bytes, void* stream) {
+moe_status grouped_ffn(const moe_config* cfg, const void* x_perm, const float* x_perm_scale,
+                       const int32_t* seg_offsets, const int32_t* seg_expert, const Weights& w,
+                       const float* row_scale, void* y_perm, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
   if (!w.w13 || !w.w2) return MOE_ERR_INVALID_ARG;
@@ -150,6 +159,7 @@ moe_status grouped_ffn(const moe_config* cfg, const void* x_perm, const int32_t*
   if (cfg->T == 0) return MOE_OK;
   if (!x_perm || !seg_offsets || !seg_expert || !y_perm || !workspace)
     return MOE_ERR_INVALID_ARG;
+  if (w.acts_fp8 && (!x_perm_scale || !aligned(x_perm_scale, 4))) return MOE_ERR_INVALID_ARG;
   if (!aligned(x_perm, 16) || !aligned(w.w13, 16) || !aligned(w.w2, 16) ||
       !aligned(y_perm, 16) || !aligned(workspace, kAlign) || !aligned(seg_offsets, 4) ||
       !aligned(seg_expert, 4) || (row_scale && !aligned(row_scale, 4)))
@@ -173,6 +183,10 @@ moe_status grouped_ffn(const moe_config* cfg, const void* x_perm, const int32_t*
   p.rows = (int32_t)num_rows(*cfg);
   p.n_w = cfg->E;
   p.Iw = cfg->I;
+  p.a_fp8 = w.acts_fp8;
+  p.a_scale = x_perm_scale;
+  p.h_q = (uint8_t*)(ws + L.h_q);
+  p.h_scale = (float*)(ws + L.h_s);
   launch_grouped_ffn(*cfg, &p, 1, (hipStream_t)stream);
   return launch_status();
 }
@@ -206,6 +220,14 @@ moe_status layer_forward(const moe_config* cfg, const float* logits, const void*
   float* row_w = (float*)(ws + L.row_w);
 
   MOE_DBG("layer entry");
+  // FP8 activations: x is quantized before dispatch (1 x 128 pieces)
+  const void* xa = x;
+  const float* xs = nullptr;
+  if (w.acts_fp8) {
+    launch_quantize_rows_fp8(cfg->T, cfg->H, x, (uint8_t*)(ws + L.x_q), (float*)(ws + L.x_s), s);
+    xa = ws + L.x_q;
+    xs = (const float*)(ws + L.x_s);
+  }
   // no x_perm: GEMM 1 gathers its rows from x through row_to_token
   if (cfg->T * cfg->k <= kSmallA) {
     launch_route_permute_small(*cfg, logits, topk_ids, topk_w, counts, seg_offsets, seg_expert,
@@ -217,7 +239,11 @@ moe_status layer_forward(const moe_config* cfg, const float* logits, const void*
   }
   MOE_DBG("route + permute");
   FfnProblem p[2]{};
-  p[0].A = x;
+  p[0].A = xa;
+  p[0].a_fp8 = w.acts_fp8;
+  p[0].a_scale = xs;
+  p[0].h_q = (uint8_t*)(ws + L.h_q);
+  p[0].h_scale = (float*)(ws + L.h_s);
   p[0].a_rows = r2t;
   p[0].w13 = w.w13;
   p[0].w2 = w.w2;
@@ -234,7 +260,11 @@ moe_status layer_forward(const moe_config* cfg, const float* logits, const void*
   p[0].n_w = cfg->E;
   p[0].Iw = cfg->I;
   if (shared) {
-    p[1].A = x;
+    p[1].A = xa;
+    p[1].a_fp8 = w.acts_fp8;
+    p[1].a_scale = xs;
+    p[1].h_q = (uint8_t*)(ws + L.shared_hq);
+    p[1].h_scale = (float*)(ws + L.shared_hs);
     p[1].w13 = sw.w13;
     p[1].w2 = sw.w2;
     p[1].w_fp8 = sw.fp8;
@@ -340,8 +370,9 @@ moe_status moe_grouped_ffn(const moe_config* cfg, const void* x_perm,
                            const void* w13, const void* w2, const float* row_scale,
                            void* y_perm, void* workspace, size_t workspace_bytes,
                            void* stream) {
-  return grouped_ffn(cfg, x_perm, seg_offsets, seg_expert, Weights{w13, w2, nullptr, nullptr, false},
-                     row_scale, y_perm, workspace, workspace_bytes, stream);
+  return grouped_ffn(cfg, x_perm, nullptr, seg_offsets, seg_expert,
+                     Weights{w13, w2, nullptr, nullptr, false}, row_scale, y_perm, workspace,
+                     workspace_bytes, stream);
 }
 
 moe_status moe_grouped_ffn_fp8w(const moe_config* cfg, const void* x_perm,
@@ -350,8 +381,19 @@ moe_status moe_grouped_ffn_fp8w(const moe_config* cfg, const void* x_perm,
                                 const uint8_t* w2_q, const float* w2_scale,
                                 const float* row_scale, void* y_perm, void* workspace,
                                 size_t workspace_bytes, void* stream) {
-  return grouped_ffn(cfg, x_perm, seg_offsets, seg_expert,
+  return grouped_ffn(cfg, x_perm, nullptr, seg_offsets, seg_expert,
                      Weights{w13_q, w2_q, w13_scale, w2_scale, true}, row_scale, y_perm,
+                     workspace, workspace_bytes, stream);
+}
+
+moe_status moe_grouped_ffn_w8a8(const moe_config* cfg, const uint8_t* x_perm_q,
+                                const float* x_perm_scale, const int32_t* seg_offsets,
+                                const int32_t* seg_expert, const uint8_t* w13_q,
+                                const float* w13_scale, const uint8_t* w2_q,
+                                const float* w2_scale, const float* row_scale, void* y_perm,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return grouped_ffn(cfg, x_perm_q, x_perm_scale, seg_offsets, seg_expert,
+                     Weights{w13_q, w2_q, w13_scale, w2_scale, true, true}, row_scale, y_perm,
                      workspace, workspace_bytes, stream);
 }
 
@@ -391,6 +433,31 @@ moe_status moe_layer_forward_fp8w(const moe_config* cfg, const float* logits, co
                        Weights{shared_w13_q, shared_w2_q, shared_w13_scale, shared_w2_scale, true},
                        out, topk_ids, topk_w, counts, balancedness, workspace, workspace_bytes,
                        stream);
+}
+
+moe_status moe_layer_forward_w8a8(const moe_config* cfg, const float* logits, const void* x,
+                                  const uint8_t* w13_q, const float* w13_scale,
+                                  const uint8_t* w2_q, const float* w2_scale,
+                                  const uint8_t* shared_w13_q, const float* shared_w13_scale,
+                                  const uint8_t* shared_w2_q, const float* shared_w2_scale,
+                                  void* out, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                                  float* balancedness, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  return layer_forward(
+      cfg, logits, x, Weights{w13_q, w2_q, w13_scale, w2_scale, true, true},
+      Weights{shared_w13_q, shared_w2_q, shared_w13_scale, shared_w2_scale, true, true}, out,
+      topk_ids, topk_w, counts, balancedness, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_quantize_act_fp8(int32_t rows, int32_t cols, const void* src, uint8_t* q,
+                                float* scale, void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 128) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)rows * cols >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!src || !q || !scale || !aligned(src, 16) || !aligned(q, 16) || !aligned(scale, 4))
+    return MOE_ERR_INVALID_ARG;
+  launch_quantize_rows_fp8(rows, cols, src, q, scale, (hipStream_t)stream);
+  return launch_status();
 }
 
 moe_status moe_quantize_fp8(int32_t n_mat, int32_t rows, int32_t cols, const void* src,

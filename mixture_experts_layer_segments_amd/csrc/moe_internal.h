@@ -68,9 +68,11 @@ inline int num_chunks(int64_t A) { return (int)((A + chunk_len(A) - 1) / chunk_l
 // G: grouped-FFN scratch (h); L: layer intermediates.
 struct Layout {
   size_t cnt_bin, blk_off, seg_of_bin, p_end;                 // region P
-  size_t h, shared_h, g_end;                                  // region G
+  size_t h, shared_h,                                         // region G
+      h_q, h_s, shared_hq, shared_hs, g_end;                  //   (FP8 activations: h quantized)
   size_t y_perm, shared_y, seg_offsets, seg_expert,           // region L
-      assign_to_row, row_to_token, row_w, l_end;
+      assign_to_row, row_to_token, row_w,
+      x_q, x_s, l_end;                                        //   (FP8 activations: x quantized)
 };
 Layout make_layout(const moe_config& c);
 int32_t num_segments(const moe_config& c);
@@ -110,12 +112,23 @@ struct FfnProblem {
   int32_t w_fp8;          // 1: w13 / w2 are E4M3 codes with the block scales below
   const float* w13_scale; // [n_w, 2*Iw/128, K1/128] (w_fp8 only)
   const float* w2_scale;  // [n_w, K1/128, Iw/128]
+  // FP8 activations (w_fp8 too): A holds E4M3 codes with a_scale [A rows,
+  // K1/128]; h is quantized into h_q [rows, Iw] / h_scale [rows, Iw/128]
+  // between the two GEMMs
+  int32_t a_fp8;
+  const float* a_scale;
+  uint8_t* h_q;
+  float* h_scale;
 };
 void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_probs,
                         hipStream_t s);
 // FP8 weights: block-quantize n_mat bf16 matrices [rows, cols] (multiples of 128).
 void launch_quantize_fp8(int n_mat, int rows, int cols, const void* src, uint8_t* q,
                          float* scale, hipStream_t s);
+// FP8 activations: quantize bf16 rows [rows, cols] (cols a multiple of 128) in
+// 1 x 128 pieces: codes [rows, cols] and scales [rows, cols / 128].
+void launch_quantize_rows_fp8(int64_t rows, int cols, const void* src, uint8_t* q,
+                              float* scale, hipStream_t s);
 void launch_combine(const moe_config& c, const void* y_perm, const int32_t* a2r,
                     const float* w, const void* shared_y, void* out, hipStream_t s);
 

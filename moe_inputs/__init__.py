@@ -48,6 +48,8 @@ class MoEShape:
     dtype: str = "bf16"         # "f32" or "bf16": x, weights and outputs
     weights: str = "native"     # "native" (weights in dtype) or "fp8": the library
                                 # block-quantizes the drawn bf16 weights to E4M3
+    acts: str = "native"        # "fp8" (with fp8 weights): activations quantized to
+                                # E4M3 in 1 x 128 pieces inside the layer (W8A8)
     score: str = "softmax"      # "softmax" (flat) or "sigmoid" (grouped)
     n_group: int = 1            # expert groups (contiguous blocks of E/n_group)
     topk_group: int = 1         # groups kept per token
@@ -106,6 +108,8 @@ WORKLOADS = {
 for _n in ("decode", "prefill_skew", "deepseek_v3", "ragged_stress"):
     _b = WORKLOADS[_n + "_bf16"]
     WORKLOADS[_n + "_fp8w"] = dataclasses.replace(_b, name=_n + "_fp8w", weights="fp8")
+    WORKLOADS[_n + "_w8a8"] = dataclasses.replace(_b, name=_n + "_w8a8", weights="fp8",
+                                                  acts="fp8")
 # The decode layer in the fixed-capacity (masked) layout at 1.25 x the mean
 # load, overflow dropped.
 WORKLOADS["decode_capacity_bf16"] = dataclasses.replace(

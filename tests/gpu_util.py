@@ -76,8 +76,12 @@ class SmallCase:
                 self.q[name] = (codes, scales)
                 deq = np.stack([ofp8.dequantize_blocks(c, sc) for c, sc in qs])
                 setattr(self, name + "_64", deq if w.ndim == 3 else deq[0])
-        self.ref = orc.layer_forward(cfg, self.logits, self.x64, self.w13_64, self.w2_64,
-                                     self.sw13_64, self.sw2_64)
+        if cfg.acts == "fp8":
+            self.ref = ofp8.layer_forward_w8a8(cfg, self.logits, self.x64, self.w13_64,
+                                               self.w2_64, self.sw13_64, self.sw2_64)
+        else:
+            self.ref = orc.layer_forward(cfg, self.logits, self.x64, self.w13_64, self.w2_64,
+                                         self.sw13_64, self.sw2_64)
 
     def device_inputs(self):
         c = self.cfg
@@ -88,6 +92,82 @@ class SmallCase:
             d["sw13"] = to_dev(self.sw13b, c.dtype)
             d["sw2"] = to_dev(self.sw2b, c.dtype)
         return d
+
+
+def h_code_slack(xq_rows, w13_e, w2_e) -> np.ndarray:
+    """W8A8: how far an expert's output rows [n, H] may move because the GPU
+    decides h's E4M3 codes on its own fp32 sums.  The GPU's h may differ from
+    the oracle's float64 h by about the rounding of a K-term fp32 sum; the
+    band used is 2^-20 sqrt(K) times the root-sum-square of the terms, 16 x
+    the usual size of that error, plus 2^-20 |h|.  Where the band around an
+    element holds two codes (after the bf16 rounding, at the oracle's piece
+    scale), or the band around a piece's maximum holds two scales, that
+    element's dequantized h may differ by one E4M3 step; the slack of an
+    output element is the sum of those steps times |W2|."""
+    I = w13_e.shape[0] // 2
+    K = xq_rows.shape[1]
+    wg, wu = w13_e[:I], w13_e[I:]
+    g, u = xq_rows @ wg.T, xq_rows @ wu.T
+    g2 = np.sqrt((xq_rows ** 2) @ (wg ** 2).T)
+    u2 = np.sqrt((xq_rows ** 2) @ (wu ** 2).T)
+    with np.errstate(over="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-g))
+    silu = g * sig
+    dsilu = np.abs(sig * (1.0 + g * (1.0 - sig)))
+    h = silu * u
+    dh = 2.0 ** -20 * np.sqrt(K) * (dsilu * np.abs(u) * g2 + np.abs(silu) * u2) + \
+        2.0 ** -20 * np.abs(h)
+    hb = ofp8.bf16_round(h)
+    n = h.shape[0]
+    _, sc = ofp8.quantize_rows(hb)
+    s_rep = np.repeat(sc, 128, axis=1)
+    two_codes = (ofp8.e4m3_encode(ofp8.bf16_round(h - dh) / s_rep) !=
+                 ofp8.e4m3_encode(ofp8.bf16_round(h + dh) / s_rep))
+    amax_lo = np.maximum(np.abs(h) - dh, 0.0).reshape(n, -1, 128).max(axis=2)
+    amax_hi = (np.abs(h) + dh).reshape(n, -1, 128).max(axis=2)
+    s_lo = ofp8.scale_exponents(ofp8.bf16_round(amax_lo))
+    s_hi = ofp8.scale_exponents(ofp8.bf16_round(amax_hi))
+    two_scales = np.repeat(s_lo != s_hi, 128, axis=1)
+    step = 2.0 ** -3 * np.abs(hb) + 2.0 ** -9 * np.repeat(2.0 ** s_hi, 128, axis=1)
+    return np.where(two_codes | two_scales, step, 0.0) @ np.abs(w2_e).T
+
+
+def w8a8_slack(case) -> np.ndarray:
+    """h_code_slack of every token of a SmallCase, summed over its routed
+    slots with their router weights (and the shared expert)."""
+    c, r = case.cfg, case.ref
+    xq = ofp8.fake_quant_rows(case.x64)
+    out = np.zeros((c.T, c.H))
+    kept = r["assign_to_row"].reshape(c.T, c.k) >= 0
+    for e in range(c.E):
+        t, j = np.nonzero((r["ids"] == e) & kept)
+        if t.size:
+            out[t] += r["w"][t, j][:, None] * h_code_slack(xq[t], case.w13_64[e], case.w2_64[e])
+    if c.shared_I:
+        out += h_code_slack(xq, case.sw13_64, case.sw2_64)
+    return out
+
+
+def check_w8a8_out(got, ref, slack, name=""):
+    """|got - ref| within the bf16 layer tolerance plus the per-element
+    h-code slack; returns the largest error beyond the slack, relative."""
+    m = np.abs(ref).max()
+    excess = (np.abs(got - ref) - slack) / m
+    worst = float(excess.max())
+    flagged = int((slack > 0).any(axis=1).sum())
+    print(f"  {name}: error beyond the h-code slack {worst:.3e} (raw "
+          f"{np.abs(got - ref).max() / m:.3e}; {flagged} of {len(ref)} rows with slack)", flush=True)
+    assert worst <= BF16_REL, worst
+    return worst
+
+
+def quantize_act(moe, x):
+    """The library's activation quantizer on a device bf16 tensor [R, C]:
+    (codes uint8 [R, C], scales fp32 [R, C / 128])."""
+    q = torch.empty(x.shape, dtype=torch.uint8, device=dev())
+    sc = torch.empty((x.shape[0], x.shape[1] // 128), dtype=torch.float32, device=dev())
+    moe.moe_quantize_act_fp8(x, q, sc)
+    return q, sc
 
 
 def x_perm_of(case):
@@ -139,9 +219,10 @@ def run_layer(moe, cfg, d):
     if cfg.weights == "fp8":
         q = fp8_weights(moe, d)
         o["q"] = q
-        moe.moe_layer_forward_fp8w(cfg, d["logits"], d["x"], q["w13"], q["w13_s"], q["w2"],
-                                   q["w2_s"], q["sw13"], q["sw13_s"], q["sw2"], q["sw2_s"],
-                                   o["out"], o["ids"], o["w"], o["counts"], o["bal"], ws)
+        call = moe.moe_layer_forward_w8a8 if cfg.acts == "fp8" else moe.moe_layer_forward_fp8w
+        call(cfg, d["logits"], d["x"], q["w13"], q["w13_s"], q["w2"], q["w2_s"], q["sw13"],
+             q["sw13_s"], q["sw2"], q["sw2_s"], o["out"], o["ids"], o["w"], o["counts"], o["bal"],
+             ws)
     else:
         moe.moe_layer_forward(cfg, d["logits"], d["x"], d["w13"], d["w2"], d["sw13"], d["sw2"],
                               o["out"], o["ids"], o["w"], o["counts"], o["bal"], ws)

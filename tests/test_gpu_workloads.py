@@ -41,7 +41,9 @@ def _sample_tokens(cfg, ids, rng):
 @pytest.mark.parametrize("name", ["tiny_fp32", "decode_bf16", "prefill_skew_bf16",
                                   "ragged_stress_bf16", "deepseek_v3_bf16", "decode_fp8w",
                                   "prefill_skew_fp8w", "ragged_stress_fp8w", "deepseek_v3_fp8w",
-                                  "ragged_stress_bounded_bf16", "decode_capacity_bf16"])
+                                  "ragged_stress_bounded_bf16", "decode_capacity_bf16",
+                                  "decode_w8a8", "prefill_skew_w8a8", "ragged_stress_w8a8",
+                                  "deepseek_v3_w8a8"])
 def test_workload_full_size(name):
     import mixture_experts_layer_segments_amd as moe
     cfg = mi.WORKLOADS[name]
@@ -63,6 +65,7 @@ def test_workload_full_size(name):
     w13_d = torch.empty((cfg.E, 2 * cfg.I, cfg.H), dtype=tdt, device=dev)
     w2_d = torch.empty((cfg.E, cfg.H, cfg.I), dtype=tdt, device=dev)
     y_ref = {}   # (i, j) -> oracle expert output row (unweighted)
+    slack_ref = {}   # W8A8: (i, j) -> h-code slack of that row (unweighted)
     codes_ref = {}   # FP8: expert -> oracle codes and scales of (w13, w2)
 
     def weights64(a, b):
@@ -72,6 +75,11 @@ def test_workload_full_size(name):
         qa, qb = ofp8.quantize_blocks(a64), ofp8.quantize_blocks(b64)
         return ofp8.dequantize_blocks(*qa), ofp8.dequantize_blocks(*qb), (qa, qb)
 
+    def expert(x_rows, a64, b64):
+        if cfg.acts == "fp8":      # x quantized in 1 x 128 pieces, h too (W8A8)
+            return ofp8.expert_w8a8(ofp8.fake_quant_rows(x_rows), a64, b64)
+        return orc.swiglu(x_rows, a64, b64)
+
     def put(e, a, b):
         w13_d[e].copy_(gu.to_dev(a, cfg.dtype))
         w2_d[e].copy_(gu.to_dev(b, cfg.dtype))
@@ -80,23 +88,30 @@ def test_workload_full_size(name):
             a64, b64, q = weights64(a, b)
             if q is not None:
                 codes_ref[e] = q
-            y = orc.swiglu(x64_s[rows], a64, b64)
+            y = expert(x64_s[rows], a64, b64)
+            sl = (gu.h_code_slack(ofp8.fake_quant_rows(x64_s[rows]), a64, b64)
+                  if cfg.acts == "fp8" else np.zeros_like(y))
             for n, (i, j) in enumerate(need[e]):
                 y_ref[(i, j)] = y[n]
+                slack_ref[(i, j)] = sl[n]
 
     print(f"[workload] {name}: generating {cfg.E} experts", flush=True)
     mi.for_each_expert(cfg, put)
     out_ref = np.zeros((len(toks), cfg.H))
+    out_slack = np.zeros((len(toks), cfg.H))
     kept = plan_r["assign_to_row"] >= 0          # the fixed-capacity layout drops some
     for (i, j), y in y_ref.items():
         if kept[toks[i] * cfg.k + j]:
             out_ref[i] += w_r[toks[i], j] * y
+            out_slack[i] += w_r[toks[i], j] * slack_ref[(i, j)]
     d = dict(logits=torch.from_numpy(logits).to(dev), x=gu.to_dev(xb, cfg.dtype), w13=w13_d,
              w2=w2_d, sw13=None, sw2=None)
     if cfg.shared_I:
         s13, s2 = mi.shared_w13(cfg), mi.shared_w2(cfg)
         a64, b64, _ = weights64(s13, s2)
-        out_ref += orc.swiglu(x64_s, a64, b64)
+        out_ref += expert(x64_s, a64, b64)
+        if cfg.acts == "fp8":
+            out_slack += gu.h_code_slack(ofp8.fake_quant_rows(x64_s), a64, b64)
         d["sw13"], d["sw2"] = gu.to_dev(s13, cfg.dtype), gu.to_dev(s2, cfg.dtype)
     torch.cuda.synchronize()
 
@@ -121,7 +136,10 @@ def test_workload_full_size(name):
     err = gu.rel_err(got[ok], out_ref[ok])
     print(f"[workload] {name}: sampled {ok.sum()} tokens, rel err {err:.3e}, "
           f"balancedness {o['bal'].item():.4f}", flush=True)
-    assert err <= gu.rel_tol(cfg), err
+    if cfg.acts == "fp8":
+        gu.check_w8a8_out(got[ok], out_ref[ok], out_slack[ok], name + " layer")
+    else:
+        assert err <= gu.rel_tol(cfg), err
 
     if mism.size == 0:
         print(f"[workload] {name}: permutation + grouped FFN steps", flush=True)
@@ -137,7 +155,12 @@ def test_workload_full_size(name):
                            xs.view(torch.int16) if cfg.dtype == "bf16" else xs)
         y = torch.empty_like(g["x_perm"])
         ws = gu.empty((moe.moe_workspace_size(cfg),), torch.uint8)
-        if cfg.weights == "fp8":
+        if cfg.acts == "fp8":
+            q = o["q"]
+            xq, xs = gu.quantize_act(moe, g["x_perm"])
+            moe.moe_grouped_ffn_w8a8(cfg, xq, xs, g["seg_offsets"], g["seg_expert"], q["w13"],
+                                     q["w13_s"], q["w2"], q["w2_s"], None, y, ws)
+        elif cfg.weights == "fp8":
             q = o["q"]
             moe.moe_grouped_ffn_fp8w(cfg, g["x_perm"], g["seg_offsets"], g["seg_expert"],
                                      q["w13"], q["w13_s"], q["w2"], q["w2_s"], None, y, ws)
@@ -149,4 +172,7 @@ def test_workload_full_size(name):
         yr = np.stack([y_ref[p] for p in pairs])
         err = gu.rel_err(yg, yr)
         print(f"[workload] {name}: grouped FFN sampled rows rel err {err:.3e}", flush=True)
-        assert err <= gu.rel_tol(cfg), err
+        if cfg.acts == "fp8":
+            gu.check_w8a8_out(yg, yr, np.stack([slack_ref[p] for p in pairs]), name + " FFN")
+        else:
+            assert err <= gu.rel_tol(cfg), err
