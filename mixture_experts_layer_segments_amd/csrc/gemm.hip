@@ -89,6 +89,9 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 __device__ __forceinline__ uint16_t to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)to_bf16(lo) | ((uint32_t)to_bf16(hi) << 16);
+}
 
 // 16 E4M3 weights (byte j of word w = element 4w + j) times their block's
 // power-of-two scale, as 16 bf16 in two 16-byte chunks (exact: an E4M3 value
@@ -273,44 +276,175 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi, float 
                                           fp8x2_to_bf16<false>(hi, sc), fp8x2_to_bf16<true>(hi, sc)});
 }
 
-// One output tile (`tile` in the numbering of the tile table `tiles_l`, which
-// holds args.n_seg_total + 1 prefix entries) through the LDS ring `ring`.
-// Every thread of the workgroup calls it with the same tile.
+// Ring tiles.  A workgroup of the persistent grid takes tiles l, l + G,
+// l + 2G, ...; each tile is set up (ring_setup), its block scales staged
+// (ring_scales), its first stages issued (ring_prologue), its K loop run over
+// the LDS ring (ring_kloop), and its output packed to bf16 (ring_pack) and
+// written through the then idle ring (ring_store): every wave stages its rows
+// there and writes them back as 16-byte row chunks, whole cache lines, instead
+// of 8-byte pieces 16 rows apart (measured: the output writes had been ~40% of
+// a 256 x 256 tile's time; the staged form is 5-10% faster overall).
+//
 // WF = 1: the weights are E4M3 codes with 128 x 128 block scales.  The codes
 // travel into the ring as they are (half the bytes of bf16, so the ring holds
 // more stages) and are dequantized when a wave reads its MFMA operand: an
 // 8-byte LDS read and four conversions with the block's scale.  The tile's
 // block scales (its two 128-row blocks of weights x K/128) are staged once
 // per tile into `scl`, LDS beside the tile table.
+// WF = 2: E4M3 activations too, one scaled FP8 MFMA K step per stage; the
+// E8M0 exponents of the tile's activation rows' scales follow `scl`.
 template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
-__device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles_l, int tile,
-                                          u32x4* ring, float* scl) {
+struct RingCfg {
   using RS = RingShape<WF, BM, BN, BK, STAGES>;
-  constexpr int KCH = RS::KCH, KCHB = RS::KCHB, A_CH = RS::A_CH, STAGE_CH = RS::STAGE_CH;
-  constexpr int AB = RS::AB;            // bytes per activation element
-  constexpr int RPB = 64 / KCH;         // A rows per 1 KiB copy block
-  constexpr int RPBB = 64 / KCHB;       // B rows per 1 KiB copy block
-  constexpr int NW = NTHR / 64;
-  constexpr int WAVES_N = NW / WAVES_M;
-  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;   // wave tile
-  constexpr int TM = WM / 16, TN = WN / 16;
-  constexpr int WB = WF ? 1 : 2;        // bytes per weight
+  static constexpr int KCH = RS::KCH, KCHB = RS::KCHB, A_CH = RS::A_CH, STAGE_CH = RS::STAGE_CH;
+  static constexpr int AB = RS::AB;            // bytes per activation element
+  static constexpr int RPB = 64 / KCH;         // A rows per 1 KiB copy block
+  static constexpr int RPBB = 64 / KCHB;       // B rows per 1 KiB copy block
+  static constexpr int NW = NTHR / 64;
+  static constexpr int WAVES_N = NW / WAVES_M;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;   // wave tile
+  static constexpr int TM = WM / 16, TN = WN / 16;
+  static constexpr int WB = WF ? 1 : 2;        // bytes per weight
   // With 8 waves only one wave per SIMD (waves 0-3) issues the copies, so
   // that its partner never stalls behind the copy issue and keeps the SIMD's
   // matrix core fed.
-  constexpr int NI = (NW == 8 && MOE_COPY_WAVES == 4) ? 4 : NW;   // issuing waves
-  constexpr int A_IT = BM / RPB / NI;   // A copies per issuing wave per stage
-  constexpr int LPI = A_IT + BN / RPBB / NI;   // all copies per issuing wave per stage
+  static constexpr int NI = (NW == 8 && MOE_COPY_WAVES == 4) ? 4 : NW;   // issuing waves
+  static constexpr int A_IT = BM / RPB / NI;   // A copies per issuing wave per stage
+  static constexpr int LPI = A_IT + BN / RPBB / NI;   // all copies per issuing wave per stage
   static_assert(WF == 2 ? BK == 128 : (BK == 32 || BK == 64), "row piece of 64 or 128 bytes");
   static_assert(WF != 1 || BK == 64, "E4M3 weights: 64-byte row pieces");
   static_assert((BM / RPB) % NI == 0 && (BN / RPBB) % NI == 0, "copy blocks per wave");
   static_assert(STAGES >= 2 && STAGES <= 6, "ring shape");
   static_assert(LPI * (STAGES - 2) < 64, "vmcnt range");
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv / WAVES_N, wn = wv % WAVES_N;
+// Where one tile sits: its segment's rows, expert, output corner and the
+// copy sources (voff: this lane's byte offset at k = 0 of each of the wave's
+// copies; only the issuing waves fill it).
+template <int LPI>
+struct RingTileState {
+  int r0, len, e, m0, n0;
+  const GemmProblem* P;
+  __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t voff[LPI];
+};
+
+template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
+__device__ __forceinline__ void ring_setup(const GemmArgs& args, const int* tiles_l, int tile,
+                                           RingTileState<RingCfg<MODE, WF, BM, BN, BK, NTHR,
+                                                                 WAVES_M, STAGES>::LPI>& t) {
+  using C = RingCfg<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>;
+  const int lane = threadIdx.x & 63;
+  const int wvs = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nst = args.n_seg_total;
+  int lo = 0, hi = nst - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (tiles_l[mid] <= tile) lo = mid; else hi = mid - 1;
+  }
+  const int gs = lo;
+  const int pi = gs < args.p[0].n_seg ? 0 : 1;
+  const GemmProblem& P = args.p[pi];
+  t.P = &args.p[pi];
+  seg_range(P, gs - (pi ? args.p[0].n_seg : 0), t.r0, t.len, t.e);
+  const int mt = (t.len + BM - 1) / BM;
+  const int ncols = MODE == 0 ? BN / 2 : BN;
+  const int nt = (P.N + ncols - 1) / ncols;
+  const int local = tile - tiles_l[gs];
+  const int grp = local / (kGroupM * nt);
+  const int first_m = grp * kGroupM;
+  const int gm = min(kGroupM, mt - first_m);
+  const int lg = local - grp * kGroupM * nt;
+  t.m0 = (first_m + lg % gm) * BM;
+  t.n0 = (lg / gm) * ncols;
+  const int K = P.K, N = P.N;
+  const uint8_t* Bb = reinterpret_cast<const uint8_t*>(P.B) + (size_t)t.e * P.b_stride * C::WB;
+  t.ra = buffer_rsrc(P.A, (uint32_t)((size_t)P.a_ld_rows * K * C::AB));
+  t.rb = buffer_rsrc(Bb, (uint32_t)((size_t)(MODE == 0 ? 2 * N : N) * K * C::WB));
+  if (wvs >= C::NI) return;
+#pragma unroll
+  for (int i = 0; i < C::LPI; ++i) {
+    if (i < C::A_IT) {
+      const int row = (i * C::NI + wvs) * C::RPB + lane / C::KCH;
+      const int kc = (lane % C::KCH) ^ swz<C::KCH>(row);
+      const int ar = t.r0 + min(t.m0 + row, t.len - 1);
+      const int grow = P.a_rows ? P.a_rows[ar] : ar;
+      t.voff[i] = (uint32_t)grow * (uint32_t)(K * C::AB) + kc * 16;
+    } else {
+      const int br = ((i - C::A_IT) * C::NI + wvs) * C::RPBB + lane / C::KCHB;  // weight-tile row
+      const int kc = (lane % C::KCHB) ^ swz<C::KCHB>(BM + br);
+      int grow;
+      if (MODE == 0) {
+        const int col = min(t.n0 + (br % (BN / 2)), N - 1);
+        grow = br < BN / 2 ? col : P.up_off + col;
+      } else {
+        grow = min(t.n0 + br, N - 1);
+      }
+      t.voff[i] = (uint32_t)grow * (uint32_t)(K * C::WB) + kc * 16;
+    }
+  }
+}
 
+// The tile's block scales into LDS (WF >= 1); the ring and `scl` must be free.
+template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
+__device__ __forceinline__ void ring_scales(
+    const RingTileState<RingCfg<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>::LPI>& t,
+    float* scl, int tid, int nthr) {
+  if constexpr (WF >= 1) {
+    const GemmProblem& P = *t.P;
+    const int K = P.K, N = P.N, KB = K / 128;
+    // group 0 / 1 = the tile's first / second 128 weight rows (GEMM 1: the
+    // gate / up halves), x every K block
+    const float* Sb = P.b_scale + (size_t)t.e * P.s_stride;
+    const int nrb = (MODE == 0 ? 2 * N : N) / 128;
+    for (int i = tid; i < 2 * KB; i += nthr) {
+      const int g = i / KB, kb = i % KB;
+      const int rb_ = MODE == 0 ? (g ? (P.up_off + t.n0) / 128 : t.n0 / 128)
+                                : min(t.n0 / 128 + g, nrb - 1);
+      scl[i] = Sb[rb_ * KB + kb];
+    }
+    if constexpr (WF == 2) {
+      // and the E8M0 exponents of its activation rows' scales, a byte each
+      uint8_t* ascl = reinterpret_cast<uint8_t*>(scl + 2 * KB);
+      for (int i = tid; i < BM * KB; i += nthr) {
+        const int row = i / KB, kb = i % KB;
+        const int ar = t.r0 + min(t.m0 + row, t.len - 1);
+        const int grow = P.a_rows ? P.a_rows[ar] : ar;
+        ascl[i] = (uint8_t)(__float_as_uint(P.a_scale[(size_t)grow * KB + kb]) >> 23);
+      }
+    }
+  }
+}
+
+// The first STAGES - 1 stages of a tile's ring (issuing waves).
+template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
+__device__ __forceinline__ void ring_prologue(
+    const RingTileState<RingCfg<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>::LPI>& t,
+    u32x4* ring) {
+  using C = RingCfg<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>;
+  const int wvs = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int KT = t.P->K / BK;
+  if (wvs >= C::NI) return;
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < KT)
+      ring_issue<C::LPI, C::NI, STAGES, C::STAGE_CH, C::A_CH, BK, C::A_IT, C::WB, C::AB>(
+          t.ra, t.rb, t.voff, ring, st, wvs);
+}
+
+// The K loop of one tile into `acc`.
+template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
+__device__ __forceinline__ void ring_kloop(
+    const RingTileState<RingCfg<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>::LPI>& t,
+    u32x4* ring, const float* scl,
+    f32x4 (&acc)[RingCfg<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>::TM]
+               [RingCfg<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>::TN]) {
+  using C = RingCfg<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>;
+  constexpr int KCH = C::KCH, KCHB = C::KCHB, A_CH = C::A_CH, STAGE_CH = C::STAGE_CH;
+  constexpr int TM = C::TM, TN = C::TN, WM = C::WM, WN = C::WN, LPI = C::LPI;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wvs = __builtin_amdgcn_readfirstlane(wv);
+  const int wm = wv / C::WAVES_N, wn = wv % C::WAVES_N;
   int brow_of[TN];
 #pragma unroll
   for (int ni = 0; ni < TN; ++ni) {
@@ -320,105 +454,26 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
     else
       brow_of[ni] = wn * WN + ni * 16;
   }
-
-  int lo = 0, hi = nst - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (tiles_l[mid] <= tile) lo = mid; else hi = mid - 1;
-  }
-  const int gs = lo;
-  const int pi = gs < args.p[0].n_seg ? 0 : 1;
-  const GemmProblem& P = args.p[pi];
-  int r0, len, e;
-  seg_range(P, gs - (pi ? args.p[0].n_seg : 0), r0, len, e);
-  const int mt = (len + BM - 1) / BM;
-  const int ncols = MODE == 0 ? BN / 2 : BN;
-  const int nt = (P.N + ncols - 1) / ncols;
-  const int local = tile - tiles_l[gs];
-  const int grp = local / (kGroupM * nt);
-  const int first_m = grp * kGroupM;
-  const int gm = min(kGroupM, mt - first_m);
-  const int lg = local - grp * kGroupM * nt;
-  const int m0 = (first_m + lg % gm) * BM;
-  const int n0 = (lg / gm) * ncols;
-  const int K = P.K, N = P.N;
-  const uint8_t* Bb = reinterpret_cast<const uint8_t*>(P.B) + (size_t)e * P.b_stride * WB;
-
-  // byte offset of this lane's 16 bytes at k = 0 in each of the wave's copies
-  const int wvs = __builtin_amdgcn_readfirstlane(wv);
-  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(P.A, (uint32_t)((size_t)P.a_ld_rows * K * AB));
-  const __amdgpu_buffer_rsrc_t rb =
-      buffer_rsrc(Bb, (uint32_t)((size_t)(MODE == 0 ? 2 * N : N) * K * WB));
-  uint32_t voff[LPI];
-#pragma unroll
-  for (int i = 0; i < LPI; ++i) {
-    if (i < A_IT) {
-      const int row = (i * NI + wvs) * RPB + lane / KCH;
-      const int kc = (lane % KCH) ^ swz<KCH>(row);
-      const int ar = r0 + min(m0 + row, len - 1);
-      const int grow = P.a_rows ? P.a_rows[ar] : ar;
-      voff[i] = (uint32_t)grow * (uint32_t)(K * AB) + kc * 16;
-    } else {
-      const int br = ((i - A_IT) * NI + wvs) * RPBB + lane / KCHB;   // row of the weight tile
-      const int kc = (lane % KCHB) ^ swz<KCHB>(BM + br);
-      int grow;
-      if (MODE == 0) {
-        const int col = min(n0 + (br % (BN / 2)), N - 1);
-        grow = br < BN / 2 ? col : P.up_off + col;
-      } else {
-        grow = min(n0 + br, N - 1);
-      }
-      voff[i] = (uint32_t)grow * (uint32_t)(K * WB) + kc * 16;
-    }
-  }
-
-  f32x4 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  const int K = t.P->K;
   const int KT = K / BK;
   const int KB = K / 128;               // WF: K blocks of the scales
-  wait_vmcnt<0>();   // this wave's earlier stores and copies are done
-  raw_barrier();     // every wave is done reading the ring (and the scales)
-  if (WF) {
-    // the tile's scales: group 0 / 1 = its first / second 128 weight rows
-    // (GEMM 1: the gate / up halves), x every K block
-    const float* Sb = P.b_scale + (size_t)e * P.s_stride;
-    const int nrb = (MODE == 0 ? 2 * N : N) / 128;
-    for (int i = tid; i < 2 * KB; i += NTHR) {
-      const int g = i / KB, kb = i % KB;
-      const int rb_ = MODE == 0 ? (g ? (P.up_off + n0) / 128 : n0 / 128) : min(n0 / 128 + g, nrb - 1);
-      scl[i] = Sb[rb_ * KB + kb];
-    }
-    if (WF == 2) {
-      // and the E8M0 exponents of its activation rows' scales, a byte each
-      uint8_t* ascl = reinterpret_cast<uint8_t*>(scl + 2 * KB);
-      for (int i = tid; i < BM * KB; i += NTHR) {
-        const int row = i / KB, kb = i % KB;
-        const int ar = r0 + min(m0 + row, len - 1);
-        const int grow = P.a_rows ? P.a_rows[ar] : ar;
-        ascl[i] = (uint8_t)(__float_as_uint(P.a_scale[(size_t)grow * KB + kb]) >> 23);
-      }
-    }
-  }
-#pragma unroll
-  for (int st = 0; st < STAGES - 1; ++st)
-    if (st < KT && wvs < NI)
-      ring_issue<LPI, NI, STAGES, STAGE_CH, A_CH, BK, A_IT, WB, AB>(ra, rb, voff, ring, st, wvs);
   // WF: the scale group of this wave's weight fragments (GEMM 1: gate
   // fragments use group 0, up fragments group 1)
   const int g_down = MODE == 1 ? (wn * WN) / 128 : 0;
   for (int kt = 0; kt < KT; ++kt) {
-    // stage kt has landed once only the copies of later stages remain
-    // (waves that issue no copies have none in flight: their wait is free)
-    wait_stages<LPI, STAGES - 2>(min(STAGES - 2, KT - 1 - kt));
+    // stage kt has landed once only the copies of later stages remain; the
+    // waves that issue no copies (and write the output) have nothing to wait for
+    if (wvs < C::NI) wait_stages<LPI, STAGES - 2>(min(STAGES - 2, KT - 1 - kt));
     if (WF) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the tile's scales are written
     raw_barrier();
-    if (kt + STAGES - 1 < KT && wvs < NI)
-      ring_issue<LPI, NI, STAGES, STAGE_CH, A_CH, BK, A_IT, WB, AB>(ra, rb, voff, ring,
-                                                                    kt + STAGES - 1, wvs);
+    if (kt + STAGES - 1 < KT && wvs < C::NI)
+      ring_issue<LPI, C::NI, STAGES, STAGE_CH, A_CH, BK, C::A_IT, C::WB, C::AB>(
+          t.ra, t.rb, t.voff, ring, kt + STAGES - 1, wvs);
     const u32x4* slot = ring + (kt % STAGES) * STAGE_CH;
     if constexpr (WF == 2) {
       // E4M3 x E4M3: one 128-deep MFMA K step per stage.  Lane l supplies row
@@ -450,113 +505,171 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
         const u32x4 hi = brow[(4 + g) ^ swz<KCHB>(BM + br)];
         bq[ni] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
+      // weights as the first operand: lane l gets output row l % 16 and
+      // columns 4 (l / 16) .. +3 of each 16 x 16 piece (row-wise stores)
 #pragma unroll
       for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
         for (int ni = 0; ni < TN; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              af[mi], bq[ni], acc[mi][ni], 0, 0, 0, sa[mi], 0, sb[ni]);
+              bq[ni], af[mi], acc[mi][ni], 0, 0, 0, sb[ni], 0, sa[mi]);
     } else {
-    float sc0 = 1.0f, sc1 = 1.0f;
-    if (WF) {
-      const int kb = kt * BK / 128;
-      sc0 = scl[(MODE == 0 ? 0 : g_down) * KB + kb];
-      sc1 = scl[KB + kb];
-    }
-    // Fragments of K step kk + 1 are read while the MFMAs of step kk run:
-    // two register sets, and the scheduler is told to interleave the LDS
-    // reads one by one among the MFMAs.  (WF: the weight fragment is read as
-    // 8 codes and dequantized just before its MFMAs.)
-    bf16x8 af[2][TM], bfr[2][TN];
-    uint32_t b8[2][TN][2];
-    auto load_frags = [&](int kk, bf16x8* a, bf16x8* b, uint32_t (*b8r)[2]) {
-      const int ch = kk * 4 + (lane >> 4);
-#pragma unroll
-      for (int mi = 0; mi < TM; ++mi) {
-        const int row = wm * WM + mi * 16 + (lane & 15);
-        a[mi] = __builtin_bit_cast(bf16x8, slot[row * KCH + (ch ^ swz<KCH>(row))]);
-      }
-#pragma unroll
-      for (int ni = 0; ni < TN; ++ni) {
-        const int br = brow_of[ni] + (lane & 15);
-        if (WF) {
-          // codes of K kk*32 + q*8 .. +8: chunk 2*kk + q/2 of the 64-byte piece, half q % 2
-          const int c = kk * 2 + ((lane >> 4) >> 1);
-          const u32x2 v = reinterpret_cast<const u32x2*>(
-              slot + A_CH + br * KCHB + (c ^ swz<KCHB>(BM + br)))[(lane >> 4) & 1];
-          b8r[ni][0] = v.x;
-          b8r[ni][1] = v.y;
-        } else {
-          const int row = BM + br;
-          b[ni] = __builtin_bit_cast(bf16x8, slot[row * KCH + (ch ^ swz<KCH>(row))]);
-        }
-      }
-    };
-    load_frags(0, af[0], bfr[0], b8[0]);
-#pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk) {
-      const int cur = kk & 1;
-      if (kk + 1 < BK / 32) load_frags(kk + 1, af[cur ^ 1], bfr[cur ^ 1], b8[cur ^ 1]);
+      float sc0 = 1.0f, sc1 = 1.0f;
       if (WF) {
-#pragma unroll
-        for (int ni = 0; ni < TN; ++ni)
-          bfr[cur][ni] = fp8x8_to_bf16(b8[cur][ni][0], b8[cur][ni][1],
-                                       (MODE == 0 && ni >= TN / 2) ? sc1 : sc0);
+        const int kb = kt * BK / 128;
+        sc0 = scl[(MODE == 0 ? 0 : g_down) * KB + kb];
+        sc1 = scl[KB + kb];
       }
+      // Fragments of K step kk + 1 are read while the MFMAs of step kk run:
+      // two register sets, and the scheduler is told to interleave the LDS
+      // reads one by one among the MFMAs.  (WF: the weight fragment is read as
+      // 8 codes and dequantized just before its MFMAs.)
+      bf16x8 af[2][TM], bfr[2][TN];
+      uint32_t b8[2][TN][2];
+      auto load_frags = [&](int kk, bf16x8* a, bf16x8* b, uint32_t (*b8r)[2]) {
+        const int ch = kk * 4 + (lane >> 4);
 #pragma unroll
-      for (int mi = 0; mi < TM; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < TN; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[cur][mi], bfr[cur][ni],
-                                                                acc[mi][ni], 0, 0, 0);
-      if (kk == 0) {
-        // first: this step's own fragment reads
-        __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
-      }
-      if (kk + 1 < BK / 32) {
-        constexpr int per = (TM * TN) / (TM + TN);
-#pragma unroll
-        for (int i = 0; i < TM + TN; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, per, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int mi = 0; mi < TM; ++mi) {
+          const int row = wm * WM + mi * 16 + (lane & 15);
+          a[mi] = __builtin_bit_cast(bf16x8, slot[row * KCH + (ch ^ swz<KCH>(row))]);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - per * (TM + TN), 0);
-      } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
-      }
-    }
-    }
-  }
-
-  uint16_t* Cb = P.C + (size_t)r0 * N;
-#pragma unroll
-  for (int mi = 0; mi < TM; ++mi) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = m0 + wm * WM + mi * 16 + (lane >> 4) * 4 + i;
-      if (row >= len) continue;
-      if (MODE == 0) {
-#pragma unroll
-        for (int ni = 0; ni < TN / 2; ++ni) {
-          const int col = n0 + wn * (WN / 2) + ni * 16 + (lane & 15);
-          if (col < N) {
-            const float g = acc[mi][ni][i], u = acc[mi][ni + TN / 2][i];
-            Cb[(size_t)row * N + col] = to_bf16(silu(g) * u);
-          }
-        }
-      } else {
-        const float sc = P.scale ? P.scale[r0 + row] : 1.0f;
 #pragma unroll
         for (int ni = 0; ni < TN; ++ni) {
-          const int col = n0 + wn * WN + ni * 16 + (lane & 15);
-          if (col < N) Cb[(size_t)row * N + col] = to_bf16(acc[mi][ni][i] * sc);
+          const int br = brow_of[ni] + (lane & 15);
+          if (WF) {
+            // codes of K kk*32 + q*8 .. +8: chunk 2*kk + q/2 of the 64-byte piece, half q % 2
+            const int c = kk * 2 + ((lane >> 4) >> 1);
+            const u32x2 v = reinterpret_cast<const u32x2*>(
+                slot + A_CH + br * KCHB + (c ^ swz<KCHB>(BM + br)))[(lane >> 4) & 1];
+            b8r[ni][0] = v.x;
+            b8r[ni][1] = v.y;
+          } else {
+            const int row = BM + br;
+            b[ni] = __builtin_bit_cast(bf16x8, slot[row * KCH + (ch ^ swz<KCH>(row))]);
+          }
+        }
+      };
+      load_frags(0, af[0], bfr[0], b8[0]);
+#pragma unroll
+      for (int kk = 0; kk < BK / 32; ++kk) {
+        const int cur = kk & 1;
+        if (kk + 1 < BK / 32) load_frags(kk + 1, af[cur ^ 1], bfr[cur ^ 1], b8[cur ^ 1]);
+        if (WF) {
+#pragma unroll
+          for (int ni = 0; ni < TN; ++ni)
+            bfr[cur][ni] = fp8x8_to_bf16(b8[cur][ni][0], b8[cur][ni][1],
+                                         (MODE == 0 && ni >= TN / 2) ? sc1 : sc0);
+        }
+#pragma unroll
+        for (int mi = 0; mi < TM; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < TN; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[cur][ni], af[cur][mi],
+                                                                  acc[mi][ni], 0, 0, 0);
+        if (kk == 0) {
+          // first: this step's own fragment reads
+          __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
+        }
+        if (kk + 1 < BK / 32) {
+          constexpr int per = (TM * TN) / (TM + TN);
+#pragma unroll
+          for (int i = 0; i < TM + TN; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, per, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - per * (TM + TN), 0);
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
         }
       }
     }
   }
 }
 
-// Static schedule: workgroup l (XCD-remapped) takes tiles l, l + G, l + 2G...
+// The tile's output: lane l holds row l % 16 of each 16 x 16 piece and its
+// columns 4 (l / 16) .. +3 (the weights are the MFMAs' first operand).
+// ring_pack turns them into bf16 pairs (SwiGLU for GEMM 1; the rows' output
+// scale `rsc` for GEMM 2) right after the K loop; ring_store stages each
+// wave's rows in its own part of the idle ring and writes them as 16-byte
+// row chunks, a row past the segment or columns past N getting an offset
+// past the store's range (the largest range, 2^31 - 64 elements of 2 bytes,
+// ends below it), so that they are dropped.
+template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
+__device__ __forceinline__ void ring_pack(
+    const f32x4 (&acc)[RingCfg<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>::TM]
+                     [RingCfg<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>::TN],
+    const float* rsc, u32x2* out) {
+  using C = RingCfg<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>;
+  constexpr int TM = C::TM, TN = C::TN, NPM = MODE == 0 ? TN / 2 : TN;
+#pragma unroll
+  for (int mi = 0; mi < TM; ++mi) {
+#pragma unroll
+    for (int ni = 0; ni < NPM; ++ni) {
+      if (MODE == 0) {
+        const f32x4 g = acc[mi][ni], u = acc[mi][ni + TN / 2];
+        out[mi * NPM + ni] = u32x2{pack_bf16x2(silu(g[0]) * u[0], silu(g[1]) * u[1]),
+                                   pack_bf16x2(silu(g[2]) * u[2], silu(g[3]) * u[3])};
+      } else {
+        const f32x4 y = acc[mi][ni];
+        const float sc = rsc[mi];
+        out[mi * NPM + ni] =
+            u32x2{pack_bf16x2(y[0] * sc, y[1] * sc), pack_bf16x2(y[2] * sc, y[3] * sc)};
+      }
+    }
+  }
+}
+
+template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
+__device__ __forceinline__ void ring_store(
+    const RingTileState<RingCfg<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>::LPI>& t,
+    const u32x2* out, u32x4* ring) {
+  using C = RingCfg<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>;
+  constexpr int TM = C::TM, WM = C::WM, WN = C::WN, NPM = MODE == 0 ? C::TN / 2 : C::TN;
+  constexpr int COUT = MODE == 0 ? WN / 2 : WN;   // output columns of a wave
+  constexpr int CPR = COUT / 8;                   // 16-byte chunks per output row
+  constexpr int LPR = CPR;                        // lanes reading one row
+  constexpr int RPI = 64 / LPR;                   // rows per store instruction
+  static_assert(CPR <= 16 && 64 % LPR == 0 && WM % RPI == 0, "output transpose shape");
+  // (the lane number is made opaque here, so that the compiler computes these
+  // lane-only addresses per tile instead of keeping them live through the K
+  // loop, where the registers are all taken)
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  const int wv = threadIdx.x >> 6;
+  const int wm = wv / C::WAVES_N, wn = wv % C::WAVES_N;
+  // this wave's region of the (idle) ring: WM rows of CPR chunks, chunk c of
+  // row r at c ^ (r % CPR), so that the 16 rows one write instruction
+  // touches and the chunks one read instruction touches hit distinct banks
+  u32x4* reg = ring + (size_t)wv * WM * CPR;
+#pragma unroll
+  for (int mi = 0; mi < TM; ++mi) {
+    const int r = mi * 16 + (lane & 15);
+#pragma unroll
+    for (int ni = 0; ni < NPM; ++ni) {
+      const int c = ni * 2 + ((lane >> 4) >> 1);        // 16-byte chunk of columns 4q..4q+3
+      reinterpret_cast<u32x2*>(reg + r * CPR + (c ^ (r % CPR)))[(lane >> 4) & 1] =
+          out[mi * NPM + ni];
+    }
+  }
+  const GemmProblem& P = *t.P;
+  const int N = P.N;
+  const __amdgpu_buffer_rsrc_t rc =
+      buffer_rsrc(P.C + (size_t)t.r0 * N, (uint32_t)((size_t)t.len * N * 2));
+  const int col0 = t.n0 + wn * COUT;
+#pragma unroll
+  for (int it = 0; it < WM / RPI; ++it) {
+    const int r = it * RPI + lane / LPR, c = lane % LPR;
+    const u32x4 v = reg[r * CPR + (c ^ (r % CPR))];
+    const int row = t.m0 + wm * WM + r, col = col0 + c * 8;
+    // N % 64 == 0 for these tiles: the 8 columns are in or out together
+    const uint32_t off = (row < t.len && col < N)
+                             ? ((uint32_t)row * (uint32_t)N + (uint32_t)col) * 2u
+                             : 0xFFFFFFF0u;
+    __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, 0);
+  }
+}
+
+// Persistent schedule: workgroup l (XCD-remapped) takes tiles l, l + G, ...
 template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES, int OCC>
 __global__ __launch_bounds__(NTHR, OCC) void gemm_ring_kernel(GemmArgs args) {
   // The ring and the tile table are this kernel's only LDS objects: with a
@@ -565,14 +678,41 @@ __global__ __launch_bounds__(NTHR, OCC) void gemm_ring_kernel(GemmArgs args) {
   // read (measured 15-30% slower).  The table build's scan scratch therefore
   // borrows the ring, which is idle until the first tile.
   // (WF: the dynamic LDS also holds a tile's block scales, after the table.)
+  using C = RingCfg<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>;
   __shared__ __attribute__((aligned(1024))) u32x4 ring[RingShape<WF, BM, BN, BK, STAGES>::RING_CH];
   extern __shared__ int tiles_l[];
   build_tile_table<NTHR>(args, tiles_l, reinterpret_cast<int*>(ring));
   const int total = tiles_l[args.n_seg_total];
   float* scl = reinterpret_cast<float*>(tiles_l + args.n_seg_total + 1);
   const int G = gridDim.x;
-  for (int tile = xcd_logical(blockIdx.x, G); tile < total; tile += G)
-    ring_tile<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(args, tiles_l, tile, ring, scl);
+  int tile = xcd_logical(blockIdx.x, G);
+  if (tile >= total) return;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int wm = wv / C::WAVES_N;
+  constexpr int NPM = MODE == 0 ? C::TN / 2 : C::TN;
+  RingTileState<C::LPI> cur;
+  for (; tile < total; tile += G) {
+    ring_setup<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(args, tiles_l, tile, cur);
+    raw_barrier();   // the ring and the scales are free (the previous tile's output is out)
+    ring_scales<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, scl, threadIdx.x, NTHR);
+    ring_prologue<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, ring);
+    u32x2 outv[C::TM * NPM];
+    {
+      f32x4 acc[C::TM][C::TN];
+      ring_kloop<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, ring, scl, acc);
+      // this tile's output scales (GEMM 2)
+      float rsc[C::TM];
+#pragma unroll
+      for (int mi = 0; mi < C::TM; ++mi) {
+        const int row = cur.m0 + wm * C::WM + mi * 16 + (lane & 15);
+        rsc[mi] =
+            (MODE == 1 && cur.P->scale) ? cur.P->scale[cur.r0 + min(row, cur.len - 1)] : 1.0f;
+      }
+      ring_pack<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(acc, rsc, outv);
+    }
+    raw_barrier();   // every wave is done reading the ring: it takes the output
+    ring_store<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, outv, ring);
+  }
 }
 
 
