@@ -35,14 +35,18 @@ GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_segments_amd", "csrc", "gem
 # what it reads for a plain 1 GiB device copy), keyed by workload.  An entry
 # only applies while gemm.hip still has the hash it was measured with.
 MEASURED_TRAFFIC = {
-    "decode_bf16": {"gemm_src_sha256_16": "49faeb91d41e53b5", "bytes": 5555619606},
-    "prefill_skew_bf16": {"gemm_src_sha256_16": "49faeb91d41e53b5", "bytes": 8296622205},
-    "deepseek_v3_bf16": {"gemm_src_sha256_16": "49faeb91d41e53b5", "bytes": 23007011565},
-    "ragged_stress_bf16": {"gemm_src_sha256_16": "49faeb91d41e53b5", "bytes": 14069722682},
-    "decode_fp8w": {"gemm_src_sha256_16": "49faeb91d41e53b5", "bytes": 2779700052},
-    "prefill_skew_fp8w": {"gemm_src_sha256_16": "49faeb91d41e53b5", "bytes": 4075577945},
-    "deepseek_v3_fp8w": {"gemm_src_sha256_16": "49faeb91d41e53b5", "bytes": 13126936196},
-    "ragged_stress_fp8w": {"gemm_src_sha256_16": "49faeb91d41e53b5", "bytes": 10773917313},
+    "decode_bf16": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 5550466394},
+    "prefill_skew_bf16": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 7854199676},
+    "deepseek_v3_bf16": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 22786563914},
+    "ragged_stress_bf16": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 13625183535},
+    "decode_fp8w": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 2779344480},
+    "prefill_skew_fp8w": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 3680642898},
+    "deepseek_v3_fp8w": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 12647503250},
+    "ragged_stress_fp8w": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 9917944184},
+    "decode_w8a8": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 2775067376},
+    "prefill_skew_w8a8": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 4122422406},
+    "deepseek_v3_w8a8": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 12040771206},
+    "ragged_stress_w8a8": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 7704044077},
 }
 
 
