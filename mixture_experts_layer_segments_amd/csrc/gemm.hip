@@ -842,8 +842,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 #define MOE_DECODE_ROWS 16  // mean rows per segment up to which the decode tiles are used
 #endif
 // One activation fragment of the decode tiles, 8 consecutive K elements of
-// row `arow` starting at element offset `off` (K index k): bf16 as stored,
-// or (WF = 2) 8 E4M3 codes times their 1 x 128 scale, exactly, as bf16.
+// row `arow` starting at element offset `off` (K index k), as loaded: bf16,
+// or (WF = 2) 8 E4M3 codes in .x/.y with their 1 x 128 piece scale's bits in
+// .z.  decode_a_bf16 turns a loaded fragment into the MFMA operand (codes
+// times scale, exact); loads and conversions are apart so that the
+// one-stage-ahead prefetch does not wait for its own loads.
 template <int WF>
 __device__ __forceinline__ u32x4 decode_a_frag(const GemmProblem& P, bool ok, uint32_t off,
                                                int arow, int k) {
@@ -851,10 +854,15 @@ __device__ __forceinline__ u32x4 decode_a_frag(const GemmProblem& P, bool ok, ui
   if constexpr (WF == 2) {
     const u32x2 c = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(P.A) + off);
     const float sc = P.a_scale[(size_t)arow * (P.K / 128) + k / 128];
-    return __builtin_bit_cast(u32x4, fp8x8_to_bf16(c.x, c.y, sc));
+    return u32x4{c.x, c.y, __float_as_uint(sc), 0u};
   } else {
     return *reinterpret_cast<const u32x4*>(P.A + off);
   }
+}
+template <int WF>
+__device__ __forceinline__ u32x4 decode_a_bf16(u32x4 f) {
+  if constexpr (WF == 2) return __builtin_bit_cast(u32x4, fp8x8_to_bf16(f.x, f.y, __uint_as_float(f.z)));
+  else return f;
 }
 
 // WF = 1: E4M3 weights with 128 x 128 block scales, loaded as 16-byte chunks
@@ -976,7 +984,7 @@ void gemm_decode_kernel(GemmArgs args) {
 #pragma unroll
       for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
-        for (int jj = 0; jj < KPW; ++jj) ac[mi][jj] = ra[mi][jj];
+        for (int jj = 0; jj < KPW; ++jj) ac[mi][jj] = decode_a_bf16<WF>(ra[mi][jj]);
       if (kt + 1 < KT) {
         const int koff = (kt + 1) * BK;
 #pragma unroll
