@@ -17,6 +17,8 @@
 // conflicts.  fp32 path: a plain FMA kernel (the fp32 layer is tiny).
 #include <math.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -1074,24 +1076,30 @@ template <int WF> constexpr int decode_bk2() { return WF ? MOE_DBK_F8 : DBK2; }
 // refuses some large-LDS kernels that launch fine) is cleared so that it is
 // not reported as a launch failure; `fallback` workgroups per CU are used
 // then.  Results are cached per kernel and LDS size.
+// (The cache is shared by every host thread that calls the library: guarded.)
 template <typename Kern>
 int persistent_grid(Kern kernel, size_t dyn_lds, int fallback, int threads = 256) {
   struct Entry { const void* k; size_t lds; int dev; int per_cu; };
-  static Entry cache[32];
+  static Entry cache[64];
   static int n_cache = 0;
+  static std::mutex mu;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   const void* key = reinterpret_cast<const void*>(kernel);
   int per_cu = 0;
-  for (int i = 0; i < n_cache; ++i)
-    if (cache[i].k == key && cache[i].lds == dyn_lds && cache[i].dev == dev) per_cu = cache[i].per_cu;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < n_cache; ++i)
+      if (cache[i].k == key && cache[i].lds == dyn_lds && cache[i].dev == dev) per_cu = cache[i].per_cu;
+  }
   if (per_cu == 0) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, dyn_lds) != hipSuccess ||
         per_cu < 1) {
       (void)hipGetLastError();
       per_cu = fallback;
     }
-    if (n_cache < 32) cache[n_cache++] = Entry{key, dyn_lds, dev, per_cu};
+    std::lock_guard<std::mutex> lock(mu);
+    if (n_cache < 64) cache[n_cache++] = Entry{key, dyn_lds, dev, per_cu};
   }
   const int g = device_cu_count() * per_cu / 8 * 8;
   return g > 8 ? g : 8;

@@ -4,6 +4,8 @@
 // one).
 #include <string.h>
 
+#include <atomic>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -55,17 +57,17 @@ Layout make_layout(const moe_config& c) {
 }
 
 int device_cu_count() {
-  static int cache[64];
+  static std::atomic<int> cache[64];   // per device; any thread may fill it (same value)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
       n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 namespace {
