@@ -5,64 +5,21 @@
 //
 // One workgroup per 128 x 128 block: the block maximum picks the power-of-two
 // scale 2^s (the smallest s with max <= 448 * 2^s), then every element is
-// rounded to the nearest E4M3 value of w / 2^s, ties to even.  All of it is
-// exact integer work on the fp32 bits (a bf16 value and a power-of-two
-// division are exact in fp32), so the codes are a pure function of the input.
+// rounded to the nearest E4M3 value of w / 2^s, ties to even (the hardware
+// conversion; w / 2^s is exact in fp32 and at most 448 in magnitude), so the
+// codes are a pure function of the input.
 #include <math.h>
 
+#include "fp8_dev.h"
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
+using namespace fp8_dev;
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-// E4M3 code of y (exact fp32), round to nearest even, saturating at 448.
-__device__ __forceinline__ uint32_t e4m3_rne(float y) {
-  const uint32_t b = __float_as_uint(y);
-  const uint32_t sign = (b >> 24) & 0x80u;
-  const uint32_t a = b & 0x7fffffffu;
-  const float af = __uint_as_float(a);
-  if (!(af < 448.0f)) return sign | 0x7Eu;   // 448 itself, and beyond (saturate)
-  if (af < 0.015625f) {                      // below 2^-6: quantum 2^-9
-    // af * 512 is exact and below 8; v_rndne rounds halves to even
-    return sign | (uint32_t)__builtin_rintf(af * 512.0f);
-  }
-  int E = (int)(a >> 23) - 127;              // -6 .. 8
-  uint32_t m3 = (a >> 20) & 7u;
-  const uint32_t rem = a & 0xfffffu;
-  m3 += (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) ? 1u : 0u;
-  if (m3 == 8u) {
-    m3 = 0u;
-    ++E;
-  }
-  if (E > 8 || (E == 8 && m3 == 7u)) return sign | 0x7Eu;
-  return sign | ((uint32_t)(E + 7) << 3) | m3;
-}
-
-// Smallest s with amax <= 448 * 2^s (amax finite, >= 0); 0 for amax == 0;
-// kept in [-127, 127], the range of the 8-bit power-of-two (E8M0) scales the
-// FP8 matrix instructions take.  amax = (1 + m / 2^23) * 2^E and
-// 448 = 1.75 * 2^8, so s = E - 8 when the mantissa is at most 0.75
-// (m <= 0x600000), else E - 7.
-__device__ __forceinline__ int block_exponent(float amax) {
-  if (amax == 0.0f) return 0;
-  int adj = 0;
-  if (amax < 1.17549435e-38f) {              // fp32 subnormal: normalise exactly
-    amax *= 18446744073709551616.0f;         // 2^64
-    adj = -64;
-  }
-  const uint32_t b = __float_as_uint(amax);
-  const int E = (int)(b >> 23) - 127;
-  const int s = E - 8 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0) + adj;
-  return max(-127, min(127, s));
-}
-
-// 2^s for s in [-127, 127], exactly (ldexpf of 1 would do; this states it).
-__device__ __forceinline__ float pow2(int s) {
-  return s >= -126 ? __uint_as_float((uint32_t)(s + 127) << 23) : __uint_as_float(0x00400000u);
-}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -103,11 +60,9 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t* __res
   for (int i = 0; i < 8; ++i) {
 #pragma unroll
     for (int j = 0; j < 4; j += 2) {
-      const uint32_t c0 = e4m3_rne(ldexpf(bf16_lo(v[i][j]), -s));
-      const uint32_t c1 = e4m3_rne(ldexpf(bf16_hi(v[i][j]), -s));
-      const uint32_t c2 = e4m3_rne(ldexpf(bf16_lo(v[i][j + 1]), -s));
-      const uint32_t c3 = e4m3_rne(ldexpf(bf16_hi(v[i][j + 1]), -s));
-      out[i * 2 + j / 2] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+      out[i * 2 + j / 2] = e4m3x4(ldexpf(bf16_lo(v[i][j]), -s), ldexpf(bf16_hi(v[i][j]), -s),
+                                  ldexpf(bf16_lo(v[i][j + 1]), -s),
+                                  ldexpf(bf16_hi(v[i][j + 1]), -s));
     }
   }
 #pragma unroll
@@ -142,11 +97,8 @@ __global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(const uint16_t* 
   uint32_t w[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const uint32_t c0 = e4m3_rne(ldexpf(bf16_lo(v[2 * j]), -s));
-    const uint32_t c1 = e4m3_rne(ldexpf(bf16_hi(v[2 * j]), -s));
-    const uint32_t c2 = e4m3_rne(ldexpf(bf16_lo(v[2 * j + 1]), -s));
-    const uint32_t c3 = e4m3_rne(ldexpf(bf16_hi(v[2 * j + 1]), -s));
-    w[j] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    w[j] = e4m3x4(ldexpf(bf16_lo(v[2 * j]), -s), ldexpf(bf16_hi(v[2 * j]), -s),
+                  ldexpf(bf16_lo(v[2 * j + 1]), -s), ldexpf(bf16_hi(v[2 * j + 1]), -s));
   }
   *reinterpret_cast<u32x2*>(q + at) = u32x2{w[0], w[1]};
 }

@@ -19,6 +19,7 @@
 
 #include <mutex>
 
+#include "fp8_dev.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -47,6 +48,10 @@ struct GemmProblem {
   const float* b_scale;     // FP8 weights: [n_w][NB/128][K/128] block scales (else unused)
   int64_t s_stride;         // floats per expert in b_scale
   const float* a_scale;     // FP8 activations: [A rows][K/128] scales of the A codes
+  // FP8 activations, GEMM 1 on ring tiles: h leaves the tile as E4M3 codes
+  // [rows, N] with one scale per 1 x 128 piece [rows, N/128] (C is unused)
+  uint8_t* Cq;
+  float* c_scale;
 };
 
 struct GemmArgs {
@@ -444,7 +449,12 @@ __device__ __forceinline__ void ring_kloop(
   using C = RingCfg<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>;
   constexpr int KCH = C::KCH, KCHB = C::KCHB, A_CH = C::A_CH, STAGE_CH = C::STAGE_CH;
   constexpr int TM = C::TM, TN = C::TN, WM = C::WM, WN = C::WN, LPI = C::LPI;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int tid = threadIdx.x;
+  // (FP8 activations: the lane's row addresses are computed per tile, not
+  // kept live across the tile loop, where the quantizing epilogue needs the
+  // registers)
+  if constexpr (WF == 2) asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wv = tid >> 6;
   const int wvs = __builtin_amdgcn_readfirstlane(wv);
   const int wm = wv / C::WAVES_N, wn = wv % C::WAVES_N;
   int brow_of[TN];
@@ -671,6 +681,90 @@ __device__ __forceinline__ void ring_store(
   }
 }
 
+// GEMM 1 with E4M3 activations: a tile's BN / 2 = 128 h columns (n0 is a
+// multiple of 128) are exactly one 1 x 128 piece of each of its rows, so the
+// tile quantizes h itself and GEMM 2 reads the codes: no bf16 h round trip
+// through HBM and no quantizer launch between the GEMMs.  The bf16 h values
+// are staged as in ring_store; after a barrier, 8 lanes take one row (16
+// columns each, two staged chunks), reduce the row's maximum with lane
+// shuffles, and write its 128 codes as 16-byte pieces of one 128-byte line
+// and its power-of-two scale.  The codes are those a separate quantizer would
+// give on the bf16 h this tile would have written.
+template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
+__device__ __forceinline__ void ring_store_q(
+    const RingTileState<RingCfg<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>::LPI>& t,
+    const u32x2* out, u32x4* ring) {
+  using C = RingCfg<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>;
+  constexpr int TM = C::TM, WM = C::WM, WN = C::WN, NPM = C::TN / 2;
+  constexpr int COUT = WN / 2;                    // h columns of a wave
+  constexpr int CPR = COUT / 8;                   // 16-byte chunks per staged row
+  constexpr int RPP = NTHR / 8;                   // rows per pass
+  static_assert(MODE == 0 && WF == 2 && BN == 256, "one 1 x 128 piece per row of a tile");
+  static_assert(BM % RPP == 0 && 16 % CPR == 0, "row pass shape");
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  const int wv = threadIdx.x >> 6;
+  u32x4* reg = ring + (size_t)wv * WM * CPR;
+#pragma unroll
+  for (int mi = 0; mi < TM; ++mi) {
+    const int r = mi * 16 + (lane & 15);
+#pragma unroll
+    for (int ni = 0; ni < NPM; ++ni) {
+      const int c = ni * 2 + ((lane >> 4) >> 1);
+      reinterpret_cast<u32x2*>(reg + r * CPR + (c ^ (r % CPR)))[(lane >> 4) & 1] =
+          out[mi * NPM + ni];
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  raw_barrier();   // every wave's rows are staged
+  const GemmProblem& P = *t.P;
+  const int N = P.N;
+  const __amdgpu_buffer_rsrc_t rq =
+      buffer_rsrc(P.Cq + (size_t)t.r0 * N, (uint32_t)((size_t)t.len * N));
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int sub = tid & 7;
+#pragma unroll
+  for (int it = 0; it < BM / RPP; ++it) {
+    const int R = it * RPP + (tid >> 3);          // row of the tile
+    const int wm = R / WM, r = R % WM;
+    u32x4 v[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int cc = sub * 2 + j;                 // chunk of the row's 16
+      const int wn = cc / CPR, c = cc % CPR;
+      v[j] = ring[(size_t)(wm * C::WAVES_N + wn) * WM * CPR + r * CPR + (c ^ (r % CPR))];
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(v[j][w] << 16)),
+                                 fabsf(__uint_as_float(v[j][w] & 0xffff0000u))));
+#pragma unroll
+    for (int off = 4; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 8));
+    const int sx = fp8_dev::block_exponent(amax);
+    u32x4 codes;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const uint32_t a = v[j][2 * w], b = v[j][2 * w + 1];
+        codes[2 * j + w] = fp8_dev::e4m3x4(ldexpf(__uint_as_float(a << 16), -sx),
+                                           ldexpf(__uint_as_float(a & 0xffff0000u), -sx),
+                                           ldexpf(__uint_as_float(b << 16), -sx),
+                                           ldexpf(__uint_as_float(b & 0xffff0000u), -sx));
+      }
+    const int row = t.m0 + R;
+    const uint32_t off =
+        row < t.len ? (uint32_t)row * (uint32_t)N + (uint32_t)(t.n0 + sub * 16) : 0xFFFFFFF0u;
+    __builtin_amdgcn_raw_buffer_store_b128(codes, rq, off, 0, 0);
+    if (sub == 0 && row < t.len)
+      P.c_scale[(size_t)(t.r0 + row) * (N / 128) + t.n0 / 128] = fp8_dev::pow2(sx);
+  }
+}
+
 // Persistent schedule: workgroup l (XCD-remapped) takes tiles l, l + G, ...
 template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES, int OCC>
 __global__ __launch_bounds__(NTHR, OCC) void gemm_ring_kernel(GemmArgs args) {
@@ -713,7 +807,10 @@ __global__ __launch_bounds__(NTHR, OCC) void gemm_ring_kernel(GemmArgs args) {
       ring_pack<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(acc, rsc, outv);
     }
     raw_barrier();   // every wave is done reading the ring: it takes the output
-    ring_store<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, outv, ring);
+    if constexpr (MODE == 0 && WF == 2)
+      ring_store_q<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, outv, ring);
+    else
+      ring_store<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, outv, ring);
   }
 }
 
@@ -1201,7 +1298,7 @@ void launch_mfma_pair(const moe_config& c, const FfnProblem* probs, int n_probs,
   if (deep1) launch_ring<0, WF, M1::kBM, M1::kBN, M1::kBK, M1::kThreads, M1::kWM, M1::kStages>(m1, s);
   else launch_ring<0, WF, M1::kBM, M1::kBN, M1::kBK, M1::kThreads, M1::kWM, 2>(m1, s);
   if (any_big) launch_ring<0, WF, BG::kBM, BG::kBN, BG::kBK, BG::kThreads, BG::kWM, BG::kStages>(b1, s);
-  quantize_h<WF>(probs, n_probs, s);
+  // (FP8 activations: the ring tiles of GEMM 1 wrote h quantized)
   if (deep2) launch_ring<1, WF, M2::kBM, M2::kBN, M2::kBK, M2::kThreads, M2::kWM, M2::kStages>(m2, s);
   else launch_ring<1, WF, M2::kBM, M2::kBN, M2::kBK, M2::kThreads, M2::kWM, 2>(m2, s);
   if (any_big) launch_ring<1, WF, BG::kBM, BG::kBN, BG::kBK, BG::kThreads, BG::kWM, BG::kStages>(b2, s);
@@ -1250,10 +1347,14 @@ void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_prob
     a.b_scale = P.w13_scale;
     a.s_stride = (int64_t)(2 * P.Iw / 128) * (H / 128);
     a.a_scale = P.a_scale;
+    a.Cq = P.h_q;
+    a.c_scale = P.h_scale;
     GemmProblem& b = g2.p[p];
     b = a;
     b.A = (const uint16_t*)(P.a_fp8 ? (const void*)P.h_q : P.h);
     b.a_scale = P.h_scale;
+    b.Cq = nullptr;
+    b.c_scale = nullptr;
     b.a_rows = nullptr;
     b.a_ld_rows = P.rows;
     b.B = (const uint16_t*)P.w2;
