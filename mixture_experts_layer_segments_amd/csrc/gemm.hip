@@ -410,18 +410,63 @@ __device__ __forceinline__ void ring_scales(
                                 : min(t.n0 / 128 + g, nrb - 1);
       scl[i] = Sb[rb_ * KB + kb];
     }
-    if constexpr (WF == 2) {
-      // and the E8M0 exponents of its activation rows' scales, a byte each
-      uint8_t* ascl = reinterpret_cast<uint8_t*>(scl + 2 * KB);
-      for (int i = tid; i < BM * KB; i += nthr) {
-        const int row = i / KB, kb = i % KB;
-        const int ar = t.r0 + min(t.m0 + row, t.len - 1);
-        const int grow = P.a_rows ? P.a_rows[ar] : ar;
-        ascl[i] = (uint8_t)(__float_as_uint(P.a_scale[(size_t)grow * KB + kb]) >> 23);
-      }
-    }
   }
 }
+
+// FP8 activations: the E8M0 exponents of the tile's BM activation rows'
+// scales, a byte each, go into LDS after the weight-block scales.  TPR
+// threads take one row (its source row looked up once) and a run of its KB
+// scales each.  The first RUN of a thread's loads are issued together, with
+// indices clamped into the run instead of branches, before the tile's first
+// ring copies (act_scales_load); the bytes are written after them
+// (act_scales_store), so the scale loads' latency overlaps the copies'.
+// A run longer than RUN (K above RUN * TPR * 128) finishes in further passes.
+template <int BM, int NTHR, int RUN>
+struct ActScales {
+  static constexpr int TPR = NTHR / BM;
+  static_assert(NTHR % BM == 0, "threads per activation row");
+  uint32_t v[RUN];
+  const float* src;
+  int k0, k1;
+};
+
+template <int BM, int NTHR, int RUN, typename TS>
+__device__ __forceinline__ void act_scales_load(const TS& t, int KB, ActScales<BM, NTHR, RUN>& a) {
+  constexpr int TPR = ActScales<BM, NTHR, RUN>::TPR;
+  const GemmProblem& P = *t.P;
+  const int row = threadIdx.x / TPR, part = threadIdx.x % TPR;
+  const int per = (KB + TPR - 1) / TPR;
+  a.k0 = min(KB, part * per);
+  a.k1 = min(KB, a.k0 + per);
+  const int ar = t.r0 + min(t.m0 + row, t.len - 1);
+  const int grow = P.a_rows ? P.a_rows[ar] : ar;
+  a.src = P.a_scale + (size_t)grow * KB;
+  const int last = a.k1 - 1;   // >= 0 (KB >= 1); a thread past the row's end re-reads its last scale
+#pragma unroll
+  for (int i = 0; i < RUN; ++i) a.v[i] = __float_as_uint(a.src[min(a.k0 + i, last)]);
+}
+
+template <int BM, int NTHR, int RUN>
+__device__ __forceinline__ void act_scales_store(ActScales<BM, NTHR, RUN>& a, uint8_t* ascl,
+                                                 int KB) {
+  constexpr int TPR = ActScales<BM, NTHR, RUN>::TPR;
+  uint8_t* dst = ascl + (threadIdx.x / TPR) * KB;
+  for (int base = a.k0;;) {
+#pragma unroll
+    for (int i = 0; i < RUN; ++i)
+      if (base + i < a.k1) dst[base + i] = (uint8_t)(a.v[i] >> 23);
+    base += RUN;
+    if (base >= a.k1) break;
+    const int last = a.k1 - 1;
+#pragma unroll
+    for (int i = 0; i < RUN; ++i) a.v[i] = __float_as_uint(a.src[min(base + i, last)]);
+  }
+}
+
+#ifndef MOE_ACT_RUN
+#define MOE_ACT_RUN 16
+#endif
+constexpr int kActRun = MOE_ACT_RUN;   // activation-scale loads in flight per thread
 
 // The first STAGES - 1 stages of a tile's ring (issuing waves).
 template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
@@ -791,7 +836,15 @@ __global__ __launch_bounds__(NTHR, OCC) void gemm_ring_kernel(GemmArgs args) {
     ring_setup<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(args, tiles_l, tile, cur);
     raw_barrier();   // the ring and the scales are free (the previous tile's output is out)
     ring_scales<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, scl, threadIdx.x, NTHR);
-    ring_prologue<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, ring);
+    if constexpr (WF == 2) {
+      const int KB = cur.P->K / 128;
+      ActScales<BM, NTHR, kActRun> as;
+      act_scales_load(cur, KB, as);
+      ring_prologue<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, ring);
+      act_scales_store(as, reinterpret_cast<uint8_t*>(scl + 2 * KB), KB);
+    } else {
+      ring_prologue<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, ring);
+    }
     u32x2 outv[C::TM * NPM];
     {
       f32x4 acc[C::TM][C::TN];
