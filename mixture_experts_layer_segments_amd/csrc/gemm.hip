@@ -463,6 +463,9 @@ __device__ __forceinline__ void act_scales_store(ActScales<BM, NTHR, RUN>& a, ui
   }
 }
 
+#ifndef MOE_W8A8_INTERLEAVE
+#define MOE_W8A8_INTERLEAVE 2
+#endif
 #ifndef MOE_ACT_RUN
 #define MOE_ACT_RUN 16
 #endif
@@ -563,13 +566,32 @@ __device__ __forceinline__ void ring_kloop(
         bq[ni] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
       // weights as the first operand: lane l gets output row l % 16 and
-      // columns 4 (l / 16) .. +3 of each 16 x 16 piece (row-wise stores)
+      // columns 4 (l / 16) .. +3 of each 16 x 16 piece (row-wise stores).
+      // Weight fragment by weight fragment, so that the first MFMAs need only
+      // the scales, the activation fragments and the first weight fragment;
+      // the scheduler is told to place each later weight fragment's two reads
+      // among the MFMAs of the one before.
 #pragma unroll
-      for (int mi = 0; mi < TM; ++mi)
+      for (int ni = 0; ni < TN; ++ni)
 #pragma unroll
-        for (int ni = 0; ni < TN; ++ni)
+        for (int mi = 0; mi < TM; ++mi)
           acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               bq[ni], af[mi], acc[mi][ni], 0, 0, 0, sb[ni], 0, sa[mi]);
+#if MOE_W8A8_INTERLEAVE
+      constexpr int AHEAD = MOE_W8A8_INTERLEAVE;   // weight fragments read ahead
+      __builtin_amdgcn_sched_group_barrier(0x100, TM + (MODE == 0 ? 2 : 1) + 2 * TM + 2 * AHEAD, 0);
+#pragma unroll
+      for (int ni = 0; ni < TN; ++ni) {
+        if (ni + AHEAD < TN) {
+          __builtin_amdgcn_sched_group_barrier(0x008, TM / 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, TM - TM / 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, TM, 0);
+        }
+      }
+#endif
     } else {
       float sc0 = 1.0f, sc1 = 1.0f;
       if (WF) {
