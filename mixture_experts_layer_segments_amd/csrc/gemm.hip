@@ -463,6 +463,9 @@ __device__ __forceinline__ void act_scales_store(ActScales<BM, NTHR, RUN>& a, ui
   }
 }
 
+#ifndef MOE_BF16_NMAJOR
+#define MOE_BF16_NMAJOR 1
+#endif
 #ifndef MOE_W8A8_INTERLEAVE
 #define MOE_W8A8_INTERLEAVE 2
 #endif
@@ -639,6 +642,35 @@ __device__ __forceinline__ void ring_kloop(
             bfr[cur][ni] = fp8x8_to_bf16(b8[cur][ni][0], b8[cur][ni][1],
                                          (MODE == 0 && ni >= TN / 2) ? sc1 : sc0);
         }
+        if constexpr (WF == 0 && MOE_BF16_NMAJOR) {
+          // weight fragment by weight fragment: the step's first MFMAs need
+          // only its activation fragments and its first two weight fragments,
+          // the rest of its reads (and the next step's) go among the MFMAs
+#pragma unroll
+          for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+            for (int mi = 0; mi < TM; ++mi)
+              acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[cur][ni], af[cur][mi],
+                                                                    acc[mi][ni], 0, 0, 0);
+          constexpr int first = TM + 2;
+          const int rest = (kk == 0 ? TN - 2 : 0) + (kk + 1 < BK / 32 ? TM + TN : 0);
+          if (kk == 0) __builtin_amdgcn_sched_group_barrier(0x100, first, 0);
+          if (rest > 0) {
+            constexpr int R0 = TN - 2 + TM + TN;   // kk == 0 (BK / 32 > 1)
+            constexpr int per0 = (TM * TN) / R0;
+            static_assert(BK / 32 == 2, "two K steps per stage");
+            if (kk == 0) {
+#pragma unroll
+              for (int i = 0; i < R0; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, per0, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+              }
+              __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - per0 * R0, 0);
+            }
+          } else {
+            __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
+          }
+        } else {
 #pragma unroll
         for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
@@ -659,6 +691,7 @@ __device__ __forceinline__ void ring_kloop(
           __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - per * (TM + TN), 0);
         } else {
           __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
+        }
         }
       }
     }
