@@ -35,10 +35,10 @@ GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_segments_amd", "csrc", "gem
 # what it reads for a plain 1 GiB device copy), keyed by workload.  An entry
 # only applies while gemm.hip still has the hash it was measured with.
 MEASURED_TRAFFIC = {
-    "decode_bf16": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 5550466394},
+    "decode_bf16": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 5550334838},
     "prefill_skew_bf16": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 7854199676},
     "deepseek_v3_bf16": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 22786563914},
-    "ragged_stress_bf16": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 13625183535},
+    "ragged_stress_bf16": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 13505345625},
     "decode_fp8w": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 2779344480},
     "prefill_skew_fp8w": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 3680642898},
     "deepseek_v3_fp8w": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 12647503250},
