@@ -160,13 +160,14 @@ def device_inputs(cfg):
 
 
 # ------------------------------------------------------------------ cpu baseline
-def cpu_baseline(cfg, logits, budget_s=20.0):
+def cpu_baseline(cfg, logits, budget_s=20.0, min_s=10.0):
     """The float64 oracle as it stands, on the host cores: routing,
     permutation and combine of every token, and the expert MLP of active
     experts in a spread order until ~budget_s of MLP time (all of them when
     that fits).  Expert weights are regenerated and converted to float64
     outside the timed region (they are the oracle's inputs).  The MLP time
-    is scaled to all active experts."""
+    is scaled to all active experts.  A layer whose MLPs take well under
+    min_s has each expert's MLP timed several times and averaged."""
     from threadpoolctl import threadpool_limits
 
     from oracle import fp8 as ofp8
@@ -189,6 +190,8 @@ def cpu_baseline(cfg, logits, budget_s=20.0):
         t_ffn, done = [0.0], []
         y = np.zeros((len(p["row_to_token"]), cfg.H))
 
+        reps = [0]
+
         def run(e, a, b):
             if t_ffn[0] > budget_s:
                 return
@@ -196,23 +199,40 @@ def cpu_baseline(cfg, logits, budget_s=20.0):
             if cfg.weights == "fp8":   # the oracle's own quantization, untimed like generation
                 w13 = ofp8.dequantize_blocks(*ofp8.quantize_blocks(w13))
                 w2 = ofp8.dequantize_blocks(*ofp8.quantize_blocks(w2))
-            t1 = time.perf_counter()
-            for s in np.nonzero(seg_exp == e)[0]:
-                r0, r1 = int(seg_off[s]), int(seg_off[s + 1])
-                if r1 > r0:
-                    y[r0:r1] = expert(x_perm[r0:r1], w13, w2)
-            t_ffn[0] += time.perf_counter() - t1
+
+            def once():
+                t1 = time.perf_counter()
+                for s in np.nonzero(seg_exp == e)[0]:
+                    r0, r1 = int(seg_off[s]), int(seg_off[s + 1])
+                    if r1 > r0:
+                        y[r0:r1] = expert(x_perm[r0:r1], w13, w2)
+                return time.perf_counter() - t1
+
+            dt = once()
+            if not reps[0]:
+                # a layer far below min_s of CPU work is timed several times over
+                reps[0] = int(min(50, max(1, np.ceil(min_s / max(dt * n, 1e-6)))))
+            for _ in range(reps[0] - 1):
+                dt += once()
+            t_ffn[0] += dt / reps[0]
             done.append(e)
 
         for i in range(0, n, 8):
             if t_ffn[0] > budget_s:
                 break
-            mi.for_each_expert(cfg, run, experts=order[i:i + 8])
+            # the chunk's weights are generated first (in a thread pool), so
+            # that no generation runs beside the timed MLPs
+            got = []
+            mi.for_each_expert(cfg, lambda e, a, b: got.append((e, a, b)), experts=order[i:i + 8])
+            for args_ in got:
+                run(*args_)
+            del got
         t0 = time.perf_counter()
         orc.combine(y, p["assign_to_row"], w)
         t_comb = time.perf_counter() - t0
     est = t_route + t_ffn[0] * n / max(1, len(done)) + t_comb
-    scope = ("the whole layer" if len(done) == n else
+    reps_note = f", each expert MLP timed {reps[0]} times and averaged" if reps[0] > 1 else ""
+    scope = ("the whole layer" + reps_note if len(done) == n else
              f"expert MLP of {len(done)} of {n} active experts ({t_ffn[0]:.1f} s), "
              f"scaled by {n}/{len(done)}")
     return {"value": cfg.T / est, "unit": "tokens/s", "cores": threads, "kind": "oracle",
