@@ -35,18 +35,18 @@ GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_segments_amd", "csrc", "gem
 # what it reads for a plain 1 GiB device copy), keyed by workload.  An entry
 # only applies while gemm.hip still has the hash it was measured with.
 MEASURED_TRAFFIC = {
-    "decode_bf16": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 5550334838},
-    "prefill_skew_bf16": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 7854199676},
-    "deepseek_v3_bf16": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 22786563914},
-    "ragged_stress_bf16": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 13505345625},
-    "decode_fp8w": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 2779344480},
-    "prefill_skew_fp8w": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 3680642898},
-    "deepseek_v3_fp8w": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 12647503250},
-    "ragged_stress_fp8w": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 9917944184},
-    "decode_w8a8": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 2775067376},
-    "prefill_skew_w8a8": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 4122422406},
-    "deepseek_v3_w8a8": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 12040771206},
-    "ragged_stress_w8a8": {"gemm_src_sha256_16": "f94e5fb7134d7f02", "bytes": 7704044077},
+    "decode_bf16": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 5550459133},
+    "prefill_skew_bf16": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 7887849765},
+    "deepseek_v3_bf16": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 22483526462},
+    "ragged_stress_bf16": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 13554176428},
+    "decode_fp8w": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 2779342928},
+    "prefill_skew_fp8w": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 3701500243},
+    "deepseek_v3_fp8w": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 12640237499},
+    "ragged_stress_fp8w": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 9903362383},
+    "decode_w8a8": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 2777682263},
+    "prefill_skew_w8a8": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 3995564577},
+    "deepseek_v3_w8a8": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 11685020648},
+    "ragged_stress_w8a8": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 7382592806},
 }
 
 
