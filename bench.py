@@ -211,7 +211,7 @@ def cpu_baseline(cfg, logits, budget_s=20.0, min_s=10.0):
             dt = once()
             if not reps[0]:
                 # a layer far below min_s of CPU work is timed several times over
-                reps[0] = int(min(50, max(1, np.ceil(min_s / max(dt * n, 1e-6)))))
+                reps[0] = int(min(200, max(1, np.ceil(min_s / max(dt * n, 1e-6)))))
             for _ in range(reps[0] - 1):
                 dt += once()
             t_ffn[0] += dt / reps[0]

@@ -8,6 +8,8 @@
 namespace moe {
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ void unpack_bf16x8(const uint4& u, float* f) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -32,6 +34,28 @@ __device__ __forceinline__ uint4 pack_bf16x8(const float* f) {
   return u;
 }
 
+// y_perm rows are read once and out is written once, so both go through
+// non-temporal accesses, and each thread issues the loads of 4 rows at a
+// time.  Measured: the layer 0.4-3% faster across the workloads (most on the
+// prefill and ragged ones), bit-identical outputs.
+#ifndef MOE_COMBINE_ROWS
+#define MOE_COMBINE_ROWS 4
+#endif
+#ifndef MOE_COMBINE_NT
+#define MOE_COMBINE_NT 1
+#endif
+constexpr int kCombineRows = MOE_COMBINE_ROWS;   // y rows loaded together per output chunk
+
+// A 16-byte chunk of a y_perm row.
+__device__ __forceinline__ uint4 load_row_chunk(const uint4* p) {
+  if constexpr (MOE_COMBINE_NT) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return uint4{v.x, v.y, v.z, v.w};
+  } else {
+    return *p;
+  }
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ y,
                                                       const int32_t* __restrict__ a2r,
@@ -50,22 +74,35 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
     float acc[EPC];
 #pragma unroll
     for (int i = 0; i < EPC; ++i) acc[i] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const int r = rows[j];
-      if (r < 0) continue;
-      const float wj = wt ? wt[j] : 1.0f;
-      const uint4 u = y[(size_t)r * row_chunks + c];
-      float f[EPC];
-      if constexpr (BF16) {
-        unpack_bf16x8(u, f);
-      } else {
-        f[0] = __uint_as_float(u.x);
-        f[1] = __uint_as_float(u.y);
-        f[2] = __uint_as_float(u.z);
-        f[3] = __uint_as_float(u.w);
+    // CU rows at a time: their loads are issued together, then summed in
+    // slot order (the same fp32 operations in the same order as one by one)
+    for (int j0 = 0; j0 < k; j0 += kCombineRows) {
+      uint4 u[kCombineRows];
+      float wj[kCombineRows];
+      bool ok[kCombineRows];
+#pragma unroll
+      for (int q = 0; q < kCombineRows; ++q) {
+        const int j = j0 + q;
+        const int r = j < k ? rows[j] : -1;
+        ok[q] = r >= 0;
+        wj[q] = (ok[q] && wt) ? wt[j] : 1.0f;
+        u[q] = ok[q] ? load_row_chunk(y + (size_t)r * row_chunks + c) : uint4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
-      for (int i = 0; i < EPC; ++i) acc[i] = fmaf(wj, f[i], acc[i]);
+      for (int q = 0; q < kCombineRows; ++q) {
+        if (!ok[q]) continue;
+        float f[EPC];
+        if constexpr (BF16) {
+          unpack_bf16x8(u[q], f);
+        } else {
+          f[0] = __uint_as_float(u[q].x);
+          f[1] = __uint_as_float(u[q].y);
+          f[2] = __uint_as_float(u[q].z);
+          f[3] = __uint_as_float(u[q].w);
+        }
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) acc[i] = fmaf(wj[q], f[i], acc[i]);
+      }
     }
     if (shared_y) {
       const uint4 u = shared_y[(size_t)t * row_chunks + c];
@@ -90,7 +127,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
       o.z = __float_as_uint(acc[2]);
       o.w = __float_as_uint(acc[3]);
     }
-    out[(size_t)t * row_chunks + c] = o;
+    if constexpr (MOE_COMBINE_NT)
+      __builtin_nontemporal_store(u32x4{o.x, o.y, o.z, o.w},
+                                  reinterpret_cast<u32x4*>(out + (size_t)t * row_chunks + c));
+    else
+      out[(size_t)t * row_chunks + c] = o;
   }
 }
 
