@@ -35,18 +35,18 @@ GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_segments_amd", "csrc", "gem
 # what it reads for a plain 1 GiB device copy), keyed by workload.  An entry
 # only applies while gemm.hip still has the hash it was measured with.
 MEASURED_TRAFFIC = {
-    "decode_bf16": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 5550459133},
-    "prefill_skew_bf16": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 7887849765},
-    "deepseek_v3_bf16": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 22483526462},
-    "ragged_stress_bf16": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 13554176428},
-    "decode_fp8w": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 2779342928},
-    "prefill_skew_fp8w": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 3701500243},
-    "deepseek_v3_fp8w": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 12640237499},
-    "ragged_stress_fp8w": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 9903362383},
-    "decode_w8a8": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 2777682263},
-    "prefill_skew_w8a8": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 3995564577},
-    "deepseek_v3_w8a8": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 11685020648},
-    "ragged_stress_w8a8": {"gemm_src_sha256_16": "f3bb115dedeb1eb7", "bytes": 7382592806},
+    "decode_bf16": {"gemm_src_sha256_16": "8a0c45f72b87d9c9", "bytes": 5542930245},
+    "prefill_skew_bf16": {"gemm_src_sha256_16": "8a0c45f72b87d9c9", "bytes": 7685739629},
+    "deepseek_v3_bf16": {"gemm_src_sha256_16": "8a0c45f72b87d9c9", "bytes": 22520310581},
+    "ragged_stress_bf16": {"gemm_src_sha256_16": "8a0c45f72b87d9c9", "bytes": 13388686139},
+    "decode_fp8w": {"gemm_src_sha256_16": "8a0c45f72b87d9c9", "bytes": 2774802920},
+    "prefill_skew_fp8w": {"gemm_src_sha256_16": "8a0c45f72b87d9c9", "bytes": 3643862020},
+    "deepseek_v3_fp8w": {"gemm_src_sha256_16": "8a0c45f72b87d9c9", "bytes": 12648739953},
+    "ragged_stress_fp8w": {"gemm_src_sha256_16": "8a0c45f72b87d9c9", "bytes": 9800606855},
+    "decode_w8a8": {"gemm_src_sha256_16": "8a0c45f72b87d9c9", "bytes": 2774586083},
+    "prefill_skew_w8a8": {"gemm_src_sha256_16": "8a0c45f72b87d9c9", "bytes": 4024754273},
+    "deepseek_v3_w8a8": {"gemm_src_sha256_16": "8a0c45f72b87d9c9", "bytes": 11697170997},
+    "ragged_stress_w8a8": {"gemm_src_sha256_16": "8a0c45f72b87d9c9", "bytes": 7330217133},
 }
 
 
