@@ -159,18 +159,48 @@ __global__ __launch_bounds__(1024) void route_permute_small_kernel(
   const int A = T * k;
   for (int i = tid; i < E * bin_ways; i += 1024) L.tot[i] = 0;
   __syncthreads();
-  for (int t = wv; t < T; t += 16) {
-    int my_id;
-    float my_w;
-    route_dev::route_token<VPL>(logits + (size_t)t * E, E, k, score, n_group, topk_group, topn,
-                                renorm, lane, my_id, my_w);
-    if (lane < k) {
-      const int a = t * k + lane;
-      ids[a] = my_id;
-      w[a] = my_w;
-      id_a[a] = my_id;
-      w_a[a] = my_w;
-      atomicAdd(&L.tot[my_id * bin_ways + t % bin_ways], 1);
+  // a wave's tokens PF at a time: their logit loads are issued together, so
+  // the wave waits on memory once per PF tokens
+  // (wide rows, E > 256, keep one token at a time: their registers are taken)
+  constexpr int PF = VPL <= 4 ? 4 : 1;
+  for (int t0 = wv; t0 < T; t0 += 16 * PF) {
+    if constexpr (PF == 1) {
+      int my_id;
+      float my_w;
+      route_dev::route_token<VPL>(logits + (size_t)t0 * E, E, k, score, n_group, topk_group,
+                                  topn, renorm, lane, my_id, my_w);
+      if (lane < k) {
+        const int a = t0 * k + lane;
+        ids[a] = my_id;
+        w[a] = my_w;
+        id_a[a] = my_id;
+        w_a[a] = my_w;
+        atomicAdd(&L.tot[my_id * bin_ways + t0 % bin_ways], 1);
+      }
+      continue;
+    }
+    float v[PF][VPL];
+#pragma unroll
+    for (int c = 0; c < PF; ++c) {
+      const int t = t0 + 16 * c;
+      if (t < T) route_dev::load_logits<VPL>(logits + (size_t)t * E, E, lane, v[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < PF; ++c) {
+      const int t = t0 + 16 * c;
+      if (t >= T) break;
+      int my_id;
+      float my_w;
+      route_dev::route_token_vals<VPL>(v[c], E, k, score, n_group, topk_group, topn, renorm,
+                                       lane, my_id, my_w);
+      if (lane < k) {
+        const int a = t * k + lane;
+        ids[a] = my_id;
+        w[a] = my_w;
+        id_a[a] = my_id;
+        w_a[a] = my_w;
+        atomicAdd(&L.tot[my_id * bin_ways + t % bin_ways], 1);
+      }
     }
   }
   __syncthreads();

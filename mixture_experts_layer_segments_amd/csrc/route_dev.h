@@ -48,17 +48,30 @@ __device__ __forceinline__ double wave_sum(double x) {
 
 // Routes the token whose logits start at `row`.  Lane j < k returns slot j:
 // its expert id in my_id and its weight (fp64 math rounded once) in my_w.
+// This lane's logits of one token row (expert lane + 64 i in slot i, -inf
+// past E); the loads of several rows can be issued before any is routed.
 template <int VPL>
-__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k,
-                                            int score, int n_group, int topk_group, int topn,
-                                            int renorm, int lane, int& my_id_out,
-                                            float& my_w_out) {
+__device__ __forceinline__ void load_logits(const float* __restrict__ row, int E, int lane,
+                                            float (&v)[VPL]) {
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < E ? row[e] : -INFINITY;
+  }
+}
+
+// Routes one token from its loaded logits (load_logits).
+template <int VPL>
+__device__ __forceinline__ void route_token_vals(const float (&vin)[VPL], int E, int k,
+                                                 int score, int n_group, int topk_group,
+                                                 int topn, int renorm, int lane,
+                                                 int& my_id_out, float& my_w_out) {
   float v[VPL];
   bool avail[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     int e = lane + 64 * i;
-    float x = e < E ? row[e] : -INFINITY;
+    float x = vin[i];
     if (x != x) x = -INFINITY;  // a NaN logit never wins over a number
     v[i] = x;
     avail[i] = e < E;
@@ -169,6 +182,18 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
   }
   my_id_out = my_id;
   my_w_out = (float)p;
+}
+
+// Routes one token whose logit row is `row`.
+template <int VPL>
+__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k,
+                                            int score, int n_group, int topk_group, int topn,
+                                            int renorm, int lane, int& my_id_out,
+                                            float& my_w_out) {
+  float v[VPL];
+  load_logits<VPL>(row, E, lane, v);
+  route_token_vals<VPL>(v, E, k, score, n_group, topk_group, topn, renorm, lane, my_id_out,
+                        my_w_out);
 }
 
 }  // namespace route_dev
