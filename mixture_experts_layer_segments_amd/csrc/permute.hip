@@ -49,13 +49,30 @@ __global__ __launch_bounds__(1024) void plan_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nbins = E * bin_ways;
 
-  // bin totals: one wave per bin, coalesced over chunks
-  for (int bin = wv; bin < nbins; bin += 16) {
-    int s = 0;
-    for (int b = lane; b < nb; b += 64) s += cnt_bin[(size_t)bin * nb + b];
+  // bin totals: a wave takes 4 bins at a time, coalesced over chunks, and
+  // issues all their loads (nb <= 256 chunks: 4 per lane and bin) before
+  // adding, so it waits on memory once per 4 bins, not once per 64 chunks
+  // of every bin
+  for (int bin0 = wv; bin0 < nbins; bin0 += 16 * 4) {
+    int v[4][4];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-    if (lane == 0) L.tot[bin] = s;
+    for (int q = 0; q < 4; ++q) {
+      const int bin = bin0 + 16 * q;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int b = lane + 64 * r;
+        v[q][r] = (bin < nbins && b < nb) ? cnt_bin[(size_t)bin * nb + b] : 0;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int bin = bin0 + 16 * q;
+      int s = v[q][0] + v[q][1] + v[q][2] + v[q][3];
+      for (int b = lane + 256; bin < nbins && b < nb; b += 64) s += cnt_bin[(size_t)bin * nb + b];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+      if (lane == 0 && bin < nbins) L.tot[bin] = s;
+    }
   }
   __syncthreads();
   const int S = cap > 0 ? plan_dev::plan_capacity(L, E, cap, counts, seg_offsets, seg_expert,
@@ -74,8 +91,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(
     const int f = L.seg_first[e];
     const bool per_replica = L.seg_first[e + 1] - f > 1 && bin_ways > 1;
     int carry = L.seg_off[s];
-    for (int b0 = 0; b0 < nb; b0 += 64) {
-      const int b = b0 + lane;
+    // the segment's chunk counts are loaded together (nb <= 256: 4 per
+    // lane), then scanned 64 chunks at a time
+    auto count = [&](int b) {
       int v = 0;
       if (b < nb) {
         if (per_replica) {
@@ -83,6 +101,19 @@ __global__ __launch_bounds__(1024) void plan_kernel(
         } else {
           for (int p = 0; p < bin_ways; ++p) v += cnt_bin[(size_t)(e * bin_ways + p) * nb + b];
         }
+      }
+      return v;
+    };
+    int vq[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vq[r] = count(64 * r + lane);
+    for (int b0 = 0; b0 < nb; b0 += 64) {
+      const int b = b0 + lane;
+      int v = b0 < 256 ? vq[0] : count(b);
+      if (b0 < 256) {   // rotate the preloaded counts
+        vq[0] = vq[1];
+        vq[1] = vq[2];
+        vq[2] = vq[3];
       }
       const int incl = plan_dev::wave_incl_scan(v, lane);
       if (b < nb) blk_off[(size_t)s * nb + b] = carry + incl - v;
@@ -107,31 +138,47 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ id
   __syncthreads();
   const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   const int a_end = min(A, (b + 1) * chunk);
-  for (int a0 = b * chunk; a0 < a_end; a0 += 64) {
-    const int a = a0 + lane;
-    int seg = -1, e = -1;
-    if (a < a_end) {
-      e = ids[a];
-      if (e >= 0 && e < E) seg = seg_of_bin[e * ways + (a / k) % ways];
+  // RB rounds of 64 assignments at a time: their ids, then their segments,
+  // are loaded together, so the wave waits on memory twice per RB rounds
+  constexpr int RB = 8;
+  int e_pre[RB], seg_pre[RB];
+  for (int a00 = b * chunk; a00 < a_end; a00 += 64 * RB) {
+    #pragma unroll
+    for (int q = 0; q < RB; ++q) {
+      const int a = a00 + 64 * q + lane;
+      e_pre[q] = a < a_end ? ids[a] : -1;
     }
-    int row = -1;
-    uint64_t pending = __ballot(seg >= 0);
-    while (pending) {
-      const int leader = __ffsll((unsigned long long)pending) - 1;
-      const int sl = __shfl(seg, leader);
-      const uint64_t m = __ballot(seg == sl);
-      const int base = run[sl];
-      if (seg == sl) row = base + __popcll(m & lt);
-      if (lane == leader) run[sl] = base + __popcll(m);
-      pending &= ~m;
+    #pragma unroll
+    for (int q = 0; q < RB; ++q) {
+      const int a = a00 + 64 * q + lane;
+      const int e = e_pre[q];
+      seg_pre[q] = (a < a_end && e >= 0 && e < E) ? seg_of_bin[e * ways + (a / k) % ways] : -1;
     }
-    // fixed capacity: an assignment past its expert's last slot is dropped
-    if (cap > 0 && row >= (e + 1) * cap) row = -1;
-    if (a < a_end) {
-      a2r[a] = row;
-      if (row >= 0) {
-        r2t[row] = a / k;
-        if (row_w) row_w[row] = w[a];
+    #pragma unroll
+    for (int q = 0; q < RB; ++q) {
+      const int a0 = a00 + 64 * q;
+      if (a0 >= a_end) break;
+      const int a = a0 + lane;
+      const int seg = seg_pre[q], e = e_pre[q];
+      int row = -1;
+      uint64_t pending = __ballot(seg >= 0);
+      while (pending) {
+        const int leader = __ffsll((unsigned long long)pending) - 1;
+        const int sl = __shfl(seg, leader);
+        const uint64_t m = __ballot(seg == sl);
+        const int base = run[sl];
+        if (seg == sl) row = base + __popcll(m & lt);
+        if (lane == leader) run[sl] = base + __popcll(m);
+        pending &= ~m;
+      }
+      // fixed capacity: an assignment past its expert's last slot is dropped
+      if (cap > 0 && row >= (e + 1) * cap) row = -1;
+      if (a < a_end) {
+        a2r[a] = row;
+        if (row >= 0) {
+          r2t[row] = a / k;
+          if (row_w) row_w[row] = w[a];
+        }
       }
     }
   }
