@@ -75,6 +75,18 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t* __res
 // of 16 lanes takes one piece (8 elements a lane, one 16-byte load), so a
 // 256-thread block quantizes 16 pieces; the piece maximum is reduced over
 // the group with lane shuffles.
+// 8 E4M3 codes (byte j of word w = element 4w + j) times a power-of-two
+// scale, as 8 bf16 (exact).
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi, float sc) {
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, true)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, true))};
+}
+
+// FAKE: instead of codes and scales, write each value back (to src, in
+// place) as its code times its scale: the bf16 value the codes stand for.
+template <bool FAKE>
 __global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(const uint16_t* __restrict__ src,
                                                                 uint8_t* __restrict__ q,
                                                                 float* __restrict__ scale,
@@ -93,14 +105,33 @@ __global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(const uint16_t* 
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
   const int s = block_exponent(amax);
-  if (sub == 0) scale[piece] = pow2(s);
+  if (!FAKE && sub == 0) scale[piece] = pow2(s);
   uint32_t w[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     w[j] = e4m3x4(ldexpf(bf16_lo(v[2 * j]), -s), ldexpf(bf16_hi(v[2 * j]), -s),
                   ldexpf(bf16_lo(v[2 * j + 1]), -s), ldexpf(bf16_hi(v[2 * j + 1]), -s));
   }
-  *reinterpret_cast<u32x2*>(q + at) = u32x2{w[0], w[1]};
+  if constexpr (FAKE)
+    *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(src) + at) = e4m3x8_to_bf16(w[0], w[1], pow2(s));
+  else
+    *reinterpret_cast<u32x2*>(q + at) = u32x2{w[0], w[1]};
+}
+
+// bf16 dst = codes times their 1 x 128 scales, 8 elements per thread.
+__global__ __launch_bounds__(256) void dequantize_rows_fp8_kernel(const uint8_t* __restrict__ q,
+                                                                  const float* __restrict__ scale,
+                                                                  uint16_t* __restrict__ dst,
+                                                                  int64_t pieces, int cols) {
+  const int64_t piece = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (piece >= pieces) return;
+  const int sub = threadIdx.x & 15;
+  const int pr = cols / 128;
+  const int64_t row = piece / pr;
+  const int col = (int)(piece % pr) * 128 + sub * 8;
+  const size_t at = (size_t)row * cols + col;
+  const u32x2 c = *reinterpret_cast<const u32x2*>(q + at);
+  *reinterpret_cast<u32x4*>(dst + at) = e4m3x8_to_bf16(c.x, c.y, scale[piece]);
 }
 
 }  // namespace
@@ -109,8 +140,23 @@ void launch_quantize_rows_fp8(int64_t rows, int cols, const void* src, uint8_t* 
                               hipStream_t s) {
   const int64_t pieces = rows * (cols / 128);
   if (pieces == 0) return;
-  quantize_rows_fp8_kernel<<<(unsigned)((pieces + 15) / 16), 256, 0, s>>>(
+  quantize_rows_fp8_kernel<false><<<(unsigned)((pieces + 15) / 16), 256, 0, s>>>(
       (const uint16_t*)src, q, scale, pieces, cols);
+}
+
+void launch_dequantize_rows_fp8(int64_t rows, int cols, const uint8_t* q, const float* scale,
+                                void* dst, hipStream_t s) {
+  const int64_t pieces = rows * (cols / 128);
+  if (pieces == 0) return;
+  dequantize_rows_fp8_kernel<<<(unsigned)((pieces + 15) / 16), 256, 0, s>>>(
+      q, scale, (uint16_t*)dst, pieces, cols);
+}
+
+void launch_fake_quant_rows_fp8(int64_t rows, int cols, void* data, hipStream_t s) {
+  const int64_t pieces = rows * (cols / 128);
+  if (pieces == 0) return;
+  quantize_rows_fp8_kernel<true><<<(unsigned)((pieces + 15) / 16), 256, 0, s>>>(
+      (const uint16_t*)data, nullptr, nullptr, pieces, cols);
 }
 
 void launch_quantize_fp8(int n_mat, int rows, int cols, const void* src, uint8_t* q,

@@ -1082,14 +1082,14 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 #ifndef MOE_DWAVES
 #define MOE_DWAVES 6
 #endif
+#ifndef MOE_W8A8_DECODE_DEQ
+#define MOE_W8A8_DECODE_DEQ 1
+#endif
 #ifndef MOE_DWAVES_F8
 #define MOE_DWAVES_F8 5     // E4M3 weights (codes in LDS)
 #endif
 #ifndef MOE_DWAVES_W8A8
 #define MOE_DWAVES_W8A8 4   // E4M3 weights and activations
-#endif
-#ifndef MOE_DECODE_ROWS
-#define MOE_DECODE_ROWS 16  // mean rows per segment up to which the decode tiles are used
 #endif
 // One activation fragment of the decode tiles, 8 consecutive K elements of
 // row `arow` starting at element offset `off` (K index k), as loaded: bf16,
@@ -1480,6 +1480,45 @@ void quantize_h(const FfnProblem* probs, int n_probs, hipStream_t s) {
   }
 }
 
+// FP8 activations on the decode tiles: the activation codes are dequantized
+// to bf16 once (E4M3 value times its power-of-two scale, exact), h is
+// rounded through E4M3 in place between the launches, and the FP8-weight
+// decode tiles run on them.  Those are the bf16 operands the E4M3-activation
+// decode tiles form fragment by fragment, in the same K order, so the
+// results are the same bit for bit; the FP8-weight tiles read 16-byte
+// activation fragments without per-fragment scale loads (measured ~10%
+// faster).  Needs the a_deq scratch and one activation matrix for all
+// problems (the layer's routed and shared problems both read x); returns
+// false otherwise, and the E4M3-activation decode tiles run.
+bool w8a8_on_fp8w_decode(const moe_config& c, const FfnProblem* probs, int n_probs,
+                         const GemmArgs& g1, const GemmArgs& g2, size_t lds_tiles,
+                         hipStream_t s) {
+  if (!MOE_W8A8_DECODE_DEQ || !probs[0].a_deq) return false;
+  for (int p = 1; p < n_probs; ++p)
+    if (probs[p].A != probs[0].A || probs[p].a_scale != probs[0].a_scale) return false;
+  int64_t a_rows = 0;
+  for (int p = 0; p < n_probs; ++p)
+    a_rows = g1.p[p].a_ld_rows > a_rows ? g1.p[p].a_ld_rows : a_rows;
+  if ((size_t)a_rows * c.H * 2 > probs[0].a_deq_bytes) return false;
+  launch_dequantize_rows_fp8(a_rows, c.H, (const uint8_t*)probs[0].A, probs[0].a_scale,
+                             probs[0].a_deq, s);
+  GemmArgs d1 = g1, d2 = g2;
+  for (int p = 0; p < n_probs; ++p) {
+    d1.p[p].A = (const uint16_t*)probs[0].a_deq;
+    d1.p[p].a_scale = nullptr;
+    d2.p[p].A = (const uint16_t*)probs[p].h;
+    d2.p[p].a_scale = nullptr;
+  }
+  auto k1 = gemm_decode_kernel<0, 1, DBN1, decode_bk1<1>(), 1, MOE_DWAVES_F8>;
+  auto k2 = gemm_decode_kernel<1, 1, DBN2, decode_bk2<1>(), 1, MOE_DWAVES_F8>;
+  k1<<<persistent_grid(k1, lds_tiles, 4), 256, lds_tiles, s>>>(cover(d1, 16, DBN1 / 2, 1, kAll));
+  for (int p = 0; p < n_probs; ++p)
+    launch_fake_quant_rows_fp8(probs[p].rows, probs[p].Iw, probs[p].h, s);
+  k2<<<persistent_grid(k2, lds_tiles, 4), 256, lds_tiles, s>>>(cover(d2, 16, DBN2, 1, kAll));
+  MOE_DBG("grouped gemms (W8A8 on the FP8-weight decode tiles)");
+  return true;
+}
+
 // The GEMM pair for operand format WF (0: bf16; 1: E4M3 weights with block
 // scales, bf16 activations; 2: E4M3 weights and activations).
 template <int WF>
@@ -1495,7 +1534,10 @@ void launch_mfma_pair(const moe_config& c, const FfnProblem* probs, int n_probs,
   }
   const size_t lds_tiles = (size_t)(nst + 1) * sizeof(int);
   // Few rows per segment on average: weight streaming with 16-row tiles.
-  if (k_ok && (int64_t)max_rows <= (int64_t)MOE_DECODE_ROWS * nst) {
+  if (k_ok && uses_decode_tiles(max_rows, nst)) {
+    if constexpr (WF == 2) {
+      if (w8a8_on_fp8w_decode(c, probs, n_probs, g1, g2, lds_tiles, s)) return;
+    }
     constexpr int DW = WF == 0 ? MOE_DWAVES : WF == 1 ? MOE_DWAVES_F8 : MOE_DWAVES_W8A8;
     auto k1 = gemm_decode_kernel<0, WF, DBN1, BK1, 1, DW>;
     auto k2 = gemm_decode_kernel<1, WF, DBN2, BK2, 1, DW>;

@@ -42,6 +42,14 @@ Layout make_layout(const moe_config& c) {
   L.h_s = take(R * ib * 4);
   L.shared_hq = take((size_t)c.T * c.shared_I);
   L.shared_hs = take((size_t)c.T * sb * 4);
+  {
+    // bf16 copy of FP8 activations for the decode tiles: x (T rows) in the
+    // layer, x_perm (R rows) in the grouped FFN, when the launch takes them
+    const int64_t rows = (int64_t)R + (c.shared_I > 0 ? c.T : 0);
+    const int64_t segs = (int64_t)S + (c.shared_I > 0 ? 1 : 0);
+    const bool dec = c.act_dtype == MOE_DT_BF16 && uses_decode_tiles(rows, segs);
+    L.a_deq = take(dec ? std::max((size_t)c.T, R) * c.H * 2 : 0);
+  }
   L.g_end = o;
   L.y_perm = take(R * c.H * eb);
   L.shared_y = take(c.shared_I > 0 ? (size_t)c.T * c.H * eb : 0);
@@ -189,6 +197,8 @@ moe_status grouped_ffn(const moe_config* cfg, const void* x_perm, const float* x
   p.a_scale = x_perm_scale;
   p.h_q = (uint8_t*)(ws + L.h_q);
   p.h_scale = (float*)(ws + L.h_s);
+  p.a_deq = ws + L.a_deq;
+  p.a_deq_bytes = L.g_end - L.a_deq;
   launch_grouped_ffn(*cfg, &p, 1, (hipStream_t)stream);
   return launch_status();
 }
@@ -246,6 +256,8 @@ moe_status layer_forward(const moe_config* cfg, const float* logits, const void*
   p[0].a_scale = xs;
   p[0].h_q = (uint8_t*)(ws + L.h_q);
   p[0].h_scale = (float*)(ws + L.h_s);
+  p[0].a_deq = ws + L.a_deq;
+  p[0].a_deq_bytes = L.g_end - L.a_deq;
   p[0].a_rows = r2t;
   p[0].w13 = w.w13;
   p[0].w2 = w.w2;
@@ -267,6 +279,8 @@ moe_status layer_forward(const moe_config* cfg, const float* logits, const void*
     p[1].a_scale = xs;
     p[1].h_q = (uint8_t*)(ws + L.shared_hq);
     p[1].h_scale = (float*)(ws + L.shared_hs);
+    p[1].a_deq = ws + L.a_deq;
+    p[1].a_deq_bytes = L.g_end - L.a_deq;
     p[1].w13 = sw.w13;
     p[1].w2 = sw.w2;
     p[1].w_fp8 = sw.fp8;

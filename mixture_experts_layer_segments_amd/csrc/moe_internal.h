@@ -64,12 +64,23 @@ inline int chunk_len(int64_t A) {
 }
 inline int num_chunks(int64_t A) { return (int)((A + chunk_len(A) - 1) / chunk_len(A)); }
 
+// The grouped GEMMs take the weight-streaming decode tiles when a launch's
+// rows are at most MOE_DECODE_ROWS per segment on average.
+#ifndef MOE_DECODE_ROWS
+#define MOE_DECODE_ROWS 16
+#endif
+inline bool uses_decode_tiles(int64_t rows, int64_t segments) {
+  return rows <= (int64_t)MOE_DECODE_ROWS * segments;
+}
+
 // Offsets of the workspace regions (bytes).  P: permutation scratch;
 // G: grouped-FFN scratch (h); L: layer intermediates.
 struct Layout {
   size_t cnt_bin, blk_off, seg_of_bin, p_end;                 // region P
   size_t h, shared_h,                                         // region G
-      h_q, h_s, shared_hq, shared_hs, g_end;                  //   (FP8 activations: h quantized)
+      h_q, h_s, shared_hq, shared_hs,                         //   (FP8 activations: h quantized)
+      a_deq, g_end;                                           //   (FP8 activations, decode tiles:
+                                                              //    the activations in bf16)
   size_t y_perm, shared_y, seg_offsets, seg_expert,           // region L
       assign_to_row, row_to_token, row_w,
       x_q, x_s, l_end;                                        //   (FP8 activations: x quantized)
@@ -119,6 +130,10 @@ struct FfnProblem {
   const float* a_scale;
   uint8_t* h_q;
   float* h_scale;
+  // FP8 activations on the decode tiles: scratch for A in bf16 [A rows, K1]
+  // of a_deq_bytes (too small or null: the E4M3 decode tiles read the codes)
+  void* a_deq;
+  size_t a_deq_bytes;
 };
 void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_probs,
                         hipStream_t s);
@@ -129,6 +144,12 @@ void launch_quantize_fp8(int n_mat, int rows, int cols, const void* src, uint8_t
 // 1 x 128 pieces: codes [rows, cols] and scales [rows, cols / 128].
 void launch_quantize_rows_fp8(int64_t rows, int cols, const void* src, uint8_t* q,
                               float* scale, hipStream_t s);
+// bf16 dst = E4M3 codes q times their 1 x 128 scales (exact), [rows, cols].
+void launch_dequantize_rows_fp8(int64_t rows, int cols, const uint8_t* q, const float* scale,
+                                void* dst, hipStream_t s);
+// bf16 rows rounded through E4M3 in place: each value becomes what the
+// row quantizer's code and scale for it dequantize to.
+void launch_fake_quant_rows_fp8(int64_t rows, int cols, void* data, hipStream_t s);
 void launch_combine(const moe_config& c, const void* y_perm, const int32_t* a2r,
                     const float* w, const void* shared_y, void* out, hipStream_t s);
 
