@@ -35,18 +35,18 @@ GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_segments_amd", "csrc", "gem
 # what it reads for a plain 1 GiB device copy), keyed by workload.  An entry
 # only applies while gemm.hip still has the hash it was measured with.
 MEASURED_TRAFFIC = {
-    "decode_bf16": {"gemm_src_sha256_16": "b4f2f55b95fa037c", "bytes": 5542934074},
-    "prefill_skew_bf16": {"gemm_src_sha256_16": "b4f2f55b95fa037c", "bytes": 7775493787},
-    "deepseek_v3_bf16": {"gemm_src_sha256_16": "b4f2f55b95fa037c", "bytes": 22448859850},
-    "ragged_stress_bf16": {"gemm_src_sha256_16": "b4f2f55b95fa037c", "bytes": 13518369838},
-    "decode_fp8w": {"gemm_src_sha256_16": "b4f2f55b95fa037c", "bytes": 2776283149},
-    "prefill_skew_fp8w": {"gemm_src_sha256_16": "b4f2f55b95fa037c", "bytes": 3678172710},
-    "deepseek_v3_fp8w": {"gemm_src_sha256_16": "b4f2f55b95fa037c", "bytes": 12656619561},
-    "ragged_stress_fp8w": {"gemm_src_sha256_16": "b4f2f55b95fa037c", "bytes": 9791051692},
-    "decode_w8a8": {"gemm_src_sha256_16": "b4f2f55b95fa037c", "bytes": 2774559713},
-    "prefill_skew_w8a8": {"gemm_src_sha256_16": "b4f2f55b95fa037c", "bytes": 4020583375},
-    "deepseek_v3_w8a8": {"gemm_src_sha256_16": "b4f2f55b95fa037c", "bytes": 11680719919},
-    "ragged_stress_w8a8": {"gemm_src_sha256_16": "b4f2f55b95fa037c", "bytes": 7333526924},
+    "decode_bf16": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 5542936994},
+    "prefill_skew_bf16": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 7767546027},
+    "deepseek_v3_bf16": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 22387721636},
+    "ragged_stress_bf16": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 13475333526},
+    "decode_fp8w": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 2776273067},
+    "prefill_skew_fp8w": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 3653058955},
+    "deepseek_v3_fp8w": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 12659297664},
+    "ragged_stress_fp8w": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 9844721947},
+    "decode_w8a8": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 2781442905},
+    "prefill_skew_w8a8": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 3995230343},
+    "deepseek_v3_w8a8": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 11644868909},
+    "ragged_stress_w8a8": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 7331109955},
 }
 
 
