@@ -71,10 +71,6 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t* __res
         u32x4{out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]};
 }
 
-// Activations: one power-of-two scale per 1 x 128 piece of a row.  A group
-// of 16 lanes takes one piece (8 elements a lane, one 16-byte load), so a
-// 256-thread block quantizes 16 pieces; the piece maximum is reduced over
-// the group with lane shuffles.
 // 8 E4M3 codes (byte j of word w = element 4w + j) times a power-of-two
 // scale, as 8 bf16 (exact).
 __device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi, float sc) {
@@ -84,12 +80,18 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi, float 
                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, true))};
 }
 
-// FAKE: instead of codes and scales, write each value back (to src, in
-// place) as its code times its scale: the bf16 value the codes stand for.
+// Activations: one power-of-two scale per 1 x 128 piece of a row.  A group
+// of 16 lanes takes one piece (8 elements a lane, one 16-byte load), so a
+// 256-thread block quantizes 16 pieces; the piece maximum is reduced over
+// the group with lane shuffles.
+// FAKE: instead of codes and scales, write each value to dst (which may be
+// src: every element is read and written by the same lane) as its code
+// times its scale, the bf16 value the codes stand for.
 template <bool FAKE>
-__global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(const uint16_t* __restrict__ src,
+__global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(const uint16_t* src,
                                                                 uint8_t* __restrict__ q,
                                                                 float* __restrict__ scale,
+                                                                uint16_t* dst,
                                                                 int64_t pieces, int cols) {
   const int64_t piece = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   if (piece >= pieces) return;                      // whole groups of 16 leave together
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(const uint16_t* 
                   ldexpf(bf16_lo(v[2 * j + 1]), -s), ldexpf(bf16_hi(v[2 * j + 1]), -s));
   }
   if constexpr (FAKE)
-    *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(src) + at) = e4m3x8_to_bf16(w[0], w[1], pow2(s));
+    *reinterpret_cast<u32x4*>(dst + at) = e4m3x8_to_bf16(w[0], w[1], pow2(s));
   else
     *reinterpret_cast<u32x2*>(q + at) = u32x2{w[0], w[1]};
 }
@@ -141,7 +143,7 @@ void launch_quantize_rows_fp8(int64_t rows, int cols, const void* src, uint8_t* 
   const int64_t pieces = rows * (cols / 128);
   if (pieces == 0) return;
   quantize_rows_fp8_kernel<false><<<(unsigned)((pieces + 15) / 16), 256, 0, s>>>(
-      (const uint16_t*)src, q, scale, pieces, cols);
+      (const uint16_t*)src, q, scale, nullptr, pieces, cols);
 }
 
 void launch_dequantize_rows_fp8(int64_t rows, int cols, const uint8_t* q, const float* scale,
@@ -156,7 +158,7 @@ void launch_fake_quant_rows_fp8(int64_t rows, int cols, void* data, hipStream_t 
   const int64_t pieces = rows * (cols / 128);
   if (pieces == 0) return;
   quantize_rows_fp8_kernel<true><<<(unsigned)((pieces + 15) / 16), 256, 0, s>>>(
-      (const uint16_t*)data, nullptr, nullptr, pieces, cols);
+      (const uint16_t*)data, nullptr, nullptr, (uint16_t*)data, pieces, cols);
 }
 
 void launch_quantize_fp8(int n_mat, int rows, int cols, const void* src, uint8_t* q,
