@@ -54,12 +54,15 @@ inline int64_t num_rows(const moe_config& c) {
   return c.capacity_factor_permille > 0 ? c.E * capacity(c) : (int64_t)c.T * c.k;
 }
 
-// Assignment chunk of one histogram / rank block: a multiple of 64, at least
-// 256, grown so that there are at most ~256 chunks.
+// Assignment chunk of one histogram / rank block: a multiple of 64, grown so
+// that there are at most 256 chunks.  A rank block is one wave ranking its
+// chunk 64 assignments at a time, serially, so small batches take 64-long
+// chunks and more blocks (with 256-long ones, a 4000-token top-2 batch ran
+// 32 waves of 4 rounds each).
 inline int chunk_len(int64_t A) {
   int64_t c = (A + 255) / 256;
   c = (c + 63) / 64 * 64;
-  if (c < 256) c = 256;
+  if (c < 64) c = 64;
   return (int)c;
 }
 inline int num_chunks(int64_t A) { return (int)((A + chunk_len(A) - 1) / chunk_len(A)); }
