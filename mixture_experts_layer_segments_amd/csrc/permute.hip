@@ -80,44 +80,39 @@ __global__ __launch_bounds__(1024) void plan_kernel(
                         : plan_dev::plan_segments(L, E, bin_ways, ways, n_hot, c, counts,
                                                   seg_offsets, seg_expert, seg_of_bin, bal);
 
-  // per-(segment, chunk) bases: one wave per segment scans over chunks.  In
-  // the load-bounded split only the first segment of a hot expert is ever
-  // looked up (its rows run on through the later ones); the later replica
-  // segments get bases too, which nothing reads.  Padding segments of the
-  // fixed-capacity layout (expert -1) get none.
-  for (int s = wv; s < S; s += 16) {
-    const int e = L.seg_exp[s];
+  // per-(segment, chunk) bases: a wave scans a segment's chunk counts, lane l
+  // taking chunks 4l .. 4l + 3 (nb <= 256), so one wave scan covers the
+  // segment.  In the load-bounded split only the first segment of a hot
+  // expert is ever looked up (its rows run on through the later ones); the
+  // later replica segments get bases too, which nothing reads.  Padding
+  // segments of the fixed-capacity layout (expert -1) get none.
+  for (int sg = wv; sg < S; sg += 16) {
+    const int e = L.seg_exp[sg];
     if (e < 0) continue;
     const int f = L.seg_first[e];
     const bool per_replica = L.seg_first[e + 1] - f > 1 && bin_ways > 1;
-    int carry = L.seg_off[s];
-    // the segment's chunk counts are loaded together (nb <= 256: 4 per
-    // lane), then scanned 64 chunks at a time
     auto count = [&](int b) {
       int v = 0;
       if (b < nb) {
         if (per_replica) {
-          v = cnt_bin[(size_t)(e * bin_ways + (s - f)) * nb + b];
+          v = cnt_bin[(size_t)(e * bin_ways + (sg - f)) * nb + b];
         } else {
           for (int p = 0; p < bin_ways; ++p) v += cnt_bin[(size_t)(e * bin_ways + p) * nb + b];
         }
       }
       return v;
     };
-    int vq[4];
+    int v[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) vq[r] = count(64 * r + lane);
-    for (int b0 = 0; b0 < nb; b0 += 64) {
-      const int b = b0 + lane;
-      int v = b0 < 256 ? vq[0] : count(b);
-      if (b0 < 256) {   // rotate the preloaded counts
-        vq[0] = vq[1];
-        vq[1] = vq[2];
-        vq[2] = vq[3];
-      }
-      const int incl = plan_dev::wave_incl_scan(v, lane);
-      if (b < nb) blk_off[(size_t)s * nb + b] = carry + incl - v;
-      carry += __shfl(incl, 63);
+    for (int r = 0; r < 4; ++r) v[r] = count(4 * lane + r);
+    const int local = v[0] + v[1] + v[2] + v[3];
+    const int incl = plan_dev::wave_incl_scan(local, lane);
+    int run = L.seg_off[sg] + incl - local;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int b = 4 * lane + r;
+      if (b < nb) blk_off[(size_t)sg * nb + b] = run;
+      run += v[r];
     }
   }
 }
