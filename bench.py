@@ -35,18 +35,18 @@ GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_segments_amd", "csrc", "gem
 # what it reads for a plain 1 GiB device copy), keyed by workload.  An entry
 # only applies while gemm.hip still has the hash it was measured with.
 MEASURED_TRAFFIC = {
-    "decode_bf16": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 5542936994},
-    "prefill_skew_bf16": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 7767546027},
-    "deepseek_v3_bf16": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 22387721636},
-    "ragged_stress_bf16": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 13475333526},
-    "decode_fp8w": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 2776273067},
-    "prefill_skew_fp8w": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 3653058955},
-    "deepseek_v3_fp8w": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 12659297664},
-    "ragged_stress_fp8w": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 9844721947},
-    "decode_w8a8": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 2781442905},
-    "prefill_skew_w8a8": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 3995230343},
-    "deepseek_v3_w8a8": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 11644868909},
-    "ragged_stress_w8a8": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 7331109955},
+    "decode_bf16": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 5542936319},
+    "prefill_skew_bf16": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 7649083292},
+    "deepseek_v3_bf16": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 22466081716},
+    "ragged_stress_bf16": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 13501005067},
+    "decode_fp8w": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 2776273441},
+    "prefill_skew_fp8w": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 3655580077},
+    "deepseek_v3_fp8w": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 12676606059},
+    "ragged_stress_fp8w": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 9799088690},
+    "decode_w8a8": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 2781414063},
+    "prefill_skew_w8a8": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 4044629670},
+    "deepseek_v3_w8a8": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 11667204101},
+    "ragged_stress_w8a8": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 7330972608},
 }
 
 
