@@ -98,6 +98,12 @@ SHAPES = {
     "w8a8_decode_shared_grouped": mi.MoEShape("a2", T=24, H=2048, E=16, k=2, I=512,
                                               score="sigmoid", n_group=4, topk_group=2,
                                               shared_I=1024, weights="fp8", acts="fp8", seed=52),
+    # the grouped FFN alone takes the decode tiles (120 rows over 8 segments)
+    # but the workspace, sized for the layer with its shared expert (180 rows
+    # over 9 segments: ring tiles), holds no bf16 copy of the activations, so
+    # the E4M3-activation decode tiles run
+    "w8a8_decode_codes": mi.MoEShape("a7", T=60, H=512, E=8, k=2, I=512, shared_I=512,
+                                     weights="fp8", acts="fp8", seed=57),
     # FP8 x FP8 ring tiles: 128 x 256 with replica splits and N / K tails
     "w8a8_mid_split": mi.MoEShape("a3", T=300, H=640, E=16, k=4, I=384, zipf_s=1.2,
                                   n_hot_split=3, split_ways=2, weights="fp8", acts="fp8",
