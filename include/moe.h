@@ -133,7 +133,7 @@ int32_t moe_num_rows(const moe_config* cfg);
 size_t moe_workspace_size(const moe_config* cfg);
 
 /* Step 1 -- top-k gating ("Follow one token through an MoE layer": the router
- * gives expert ids and weights for every token; the MoE inference blog's
+ * picks each token's experts and their weights; the MoE inference blog's
  * "MoE architecture recap": top-k experts, or a few expert groups first and
  * then the top experts inside them).
  *   logits   [T, E] fp32, finite.

@@ -19,8 +19,9 @@ blocking or fusion.  Sources (the pages' titles and sections):
   balancing" (blog), section "MoE architecture recap": top-k experts per
   token from a router; grouped routing picks a few expert groups first, then
   the top experts inside them; shared experts process every token.
-* Zepp paper, section 4.1: replicas preserve the model's logical expert
-  selections and routing weights (replica segments do not change the math).
+* Zepp paper, section 4.1: a replica changes where an expert runs, never
+  which experts or weights a token gets (replica segments do not change the
+  math).
 
 Readings where the pages are silent (they are listed with reasons in the
 design notes of the repository): weights are renormalised over the k winners;
@@ -106,8 +107,8 @@ def group_scores_f32(logits: np.ndarray, n_group: int, topn: int) -> np.ndarray:
 
 def route_grouped(logits: np.ndarray, k: int, n_group: int, topk_group: int,
                   topn: int = 2, renormalize: bool = True):
-    """Group-limited routing ("MoE architecture recap": pick a limited number
-    of expert groups, then the top experts within them).
+    """Group-limited routing ("MoE architecture recap": a few expert groups
+    are chosen first, and the experts are then taken from inside them).
 
     Scores are sigmoid(logit).  Groups are contiguous blocks of E/n_group
     experts; the ``topk_group`` best groups by ``group_scores_f32`` are kept
@@ -134,9 +135,16 @@ def route_grouped(logits: np.ndarray, k: int, n_group: int, topk_group: int,
         cand = [e for g in sorted(kept) for e in range(g * per, (g + 1) * per)]
         order = sorted(cand, key=lambda e: (-l[t, e], e))[:k]
         ids[t] = order
-        s = sigmoid_f64(l[t, order])
-        w[t] = s / s.sum() if renormalize else s
+    w = sigmoid_weights(logits, ids, renormalize)
     return ids, w, gap
+
+
+def sigmoid_weights(logits: np.ndarray, ids: np.ndarray, renormalize: bool = True):
+    """Weights of chosen experts in sigmoid mode: s_j = sigmoid(logit) of each
+    winner, divided by their sum when renormalised (float64)."""
+    l = np.asarray(logits, dtype=np.float32).astype(np.float64)
+    s = sigmoid_f64(np.take_along_axis(l, np.asarray(ids, dtype=np.int64), axis=1))
+    return s / s.sum(axis=1, keepdims=True) if renormalize else s
 
 
 # ------------------------------------------------------------------ segments
@@ -298,8 +306,12 @@ def capacity_plan(ids: np.ndarray, E: int, cap: int):
 
 def balancedness(loads) -> np.float32:
     """mean(loads) / max(loads) ("The slowest expert sets the pace"), in
-    float64, rounded once to fp32.  Zero loads count in the mean."""
+    float64, rounded once to fp32.  Zero loads count in the mean.  A batch
+    with no load at all (every id dropped) has no slowest expert and the
+    ratio is 0/0; it is read as 0 (the pages are silent)."""
     loads = np.asarray(loads, dtype=np.float64)
+    if loads.max() == 0.0:
+        return np.float32(0.0)
     return np.float32(loads.mean() / loads.max())
 
 

@@ -58,7 +58,8 @@ def test_token_flow_printed_example():
     assert r["y_perm"].shape[0] == g["expert_executions"]
     assert r["out"].shape[0] == g["outputs_combined_into"]
     assert int(r["seg_offsets"][-1]) == 16
-    # "roughly 3 percent of its expert parameters" per token
+    # each token uses about 3% of the expert weights (book, "Follow one token
+    # through an MoE layer")
     assert abs(cfg.k / cfg.E - _gold("serving_moe_token_flow.json")["expert_fraction_per_token_approx"]) < 0.005
 
 
@@ -84,8 +85,9 @@ def test_balancedness_worked_example():
 
 
 def test_uniform_routing_balancedness_is_one():
-    """A perfectly balanced deployment logs 1.0 ("The slowest expert sets
-    the pace"): token t routed to experts 2t mod E and 2t+1 mod E."""
+    """Balancedness is 1.0 when every expert carries the same load ("The
+    slowest expert sets the pace"): token t routed to experts 2t mod E and
+    2t+1 mod E."""
     T, E, k = 64, 16, 2
     lg = np.empty((T, E), dtype=np.float32)
     for t in range(T):
@@ -97,6 +99,26 @@ def test_uniform_routing_balancedness_is_one():
     c = o.expert_counts(ids, E)
     assert (c == T * k // E).all()
     assert o.balancedness(c) == np.float32(1.0)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_balancedness_is_a_fraction_and_scale_free(seed):
+    """For any loads with a positive maximum, mean/max lies in [1/E, 1]: it is
+    1/E exactly when one expert holds everything, and it does not change when
+    every load is multiplied by the same factor.  With no load at all (every
+    id dropped) the ratio is 0/0 and reads as 0, below every defined value, so
+    an empty batch never looks balanced."""
+    rng = np.random.default_rng(seed)
+    E = int(rng.integers(1, 40))
+    c = rng.integers(0, 50, size=E)
+    c[rng.integers(0, E)] += 1
+    b = float(o.balancedness(c))
+    assert 1.0 / E - 1e-7 <= b <= 1.0
+    assert o.balancedness(3 * c) == o.balancedness(c)
+    one = np.zeros(E, dtype=np.int64)
+    one[rng.integers(0, E)] = 7
+    assert o.balancedness(one) == np.float32(1.0 / E)
+    assert o.balancedness(np.zeros(E, dtype=np.int64)) == np.float32(0.0)
 
 
 def test_empty_experts_are_normal():
@@ -172,6 +194,20 @@ def test_route_grouped_one_group_is_flat_sigmoid_topk():
     s = scipy.special.expit(lg.astype(np.float64))
     sel = np.take_along_axis(s, ids_f.astype(np.int64), 1)
     np.testing.assert_allclose(w_g, sel / sel.sum(1, keepdims=True), rtol=1e-14)
+
+
+def test_sigmoid_weights_of_given_ids():
+    """The weights of any chosen ids (used where the GPU's group choice sits
+    on a tie): sigmoid of each winner's logit (scipy's expit), divided by
+    their sum when renormalised; for the routed ids they are route_grouped's."""
+    rng = np.random.default_rng(7)
+    lg = _distinct_logits(rng, 25, 32)
+    ids = np.stack([rng.permutation(32)[:4] for _ in range(25)]).astype(np.int32)
+    s = np.take_along_axis(scipy.special.expit(lg.astype(np.float64)), ids.astype(np.int64), 1)
+    np.testing.assert_allclose(o.sigmoid_weights(lg, ids, False), s, rtol=1e-14)
+    np.testing.assert_allclose(o.sigmoid_weights(lg, ids), s / s.sum(1, keepdims=True), rtol=1e-14)
+    ids_g, w_g, _ = o.route_grouped(lg, 4, n_group=4, topk_group=2)
+    assert np.array_equal(o.sigmoid_weights(lg, ids_g), w_g)
 
 
 def test_group_scores_are_fp32_sums_of_best_members():
@@ -321,7 +357,7 @@ def _ids_with_counts(counts, k):
 
 
 def test_capacity_worked_example():
-    """1.25 x the mean of 8 gives 10 slots per expert, 80 slots for 64
+    """1.25 x the mean of 8 gives 10 slots per expert (80 in all) for the 64
     assignments, and expert 0 (22 assignments) overflows by 12; sizing every
     expert for the busiest gives 22 x 8 = 176 slots, about two thirds of them
     padding ("Capacity, padding, and the drop decision")."""
@@ -457,9 +493,9 @@ def test_identity_experts_recover_tokens():
 
 
 def test_replica_segments_do_not_change_the_output():
-    """Replication "preserves the model's logical expert selections and
-    routing weights" (Zepp section 4.1): splitting hot experts by token parity
-    gives the same output, bit for bit, in the oracle."""
+    """Replication changes where an expert runs, not which experts or
+    weights a token gets (Zepp section 4.1): splitting hot experts by token
+    parity gives the same output, bit for bit, in the oracle."""
     cfg, lg, x, w13, w2 = _tiny(T=45, E=6, k=3, n_hot_split=2, split_ways=2)
     a = o.layer_forward(cfg, lg, x, w13, w2)
     b = o.layer_forward(cfg.replace(n_hot_split=0, split_ways=1), lg, x, w13, w2)
