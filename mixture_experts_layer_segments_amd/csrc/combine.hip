@@ -38,22 +38,12 @@ __device__ __forceinline__ uint4 pack_bf16x8(const float* f) {
 // non-temporal accesses, and each thread issues the loads of 4 rows at a
 // time.  Measured: the layer 0.4-3% faster across the workloads (most on the
 // prefill and ragged ones), bit-identical outputs.
-#ifndef MOE_COMBINE_ROWS
-#define MOE_COMBINE_ROWS 4
-#endif
-#ifndef MOE_COMBINE_NT
-#define MOE_COMBINE_NT 1
-#endif
-constexpr int kCombineRows = MOE_COMBINE_ROWS;   // y rows loaded together per output chunk
+constexpr int kCombineRows = 4;   // y rows loaded together per output chunk
 
 // A 16-byte chunk of a y_perm row.
 __device__ __forceinline__ uint4 load_row_chunk(const uint4* p) {
-  if constexpr (MOE_COMBINE_NT) {
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    return uint4{v.x, v.y, v.z, v.w};
-  } else {
-    return *p;
-  }
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return uint4{v.x, v.y, v.z, v.w};
 }
 
 template <bool BF16>
@@ -127,11 +117,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
       o.z = __float_as_uint(acc[2]);
       o.w = __float_as_uint(acc[3]);
     }
-    if constexpr (MOE_COMBINE_NT)
-      __builtin_nontemporal_store(u32x4{o.x, o.y, o.z, o.w},
-                                  reinterpret_cast<u32x4*>(out + (size_t)t * row_chunks + c));
-    else
-      out[(size_t)t * row_chunks + c] = o;
+    __builtin_nontemporal_store(u32x4{o.x, o.y, o.z, o.w},
+                                reinterpret_cast<u32x4*>(out + (size_t)t * row_chunks + c));
   }
 }
 

@@ -76,19 +76,16 @@ __device__ __forceinline__ void seg_range(const GemmProblem& P, int s, int& r0, 
   }
 }
 
-#ifndef MOE_GROUP_M
-#define MOE_GROUP_M 8
-#endif
-#ifndef MOE_XCD_REMAP
-#define MOE_XCD_REMAP 1
-#endif
-constexpr int kGroupM = MOE_GROUP_M;
-constexpr size_t kMaxLdsBytes = 160 * 1024;  // LDS per workgroup on gfx950  // row tiles that share a weight slice in the tile order
+// Row tiles that share a weight slice in the tile order (groups of 4, 16 or
+// 32 measured 0.5-3% slower on the ragged layers).
+constexpr int kGroupM = 8;
+constexpr size_t kMaxLdsBytes = 160 * 1024;  // LDS per workgroup on gfx950
 
 // Workgroup ids are dealt round-robin to the 8 XCDs; renumber them so that
-// consecutive logical ids share an XCD (and its L2).
+// consecutive logical ids share an XCD (and its L2).  Measured 2-5% faster
+// than the plain order on the ragged and DeepSeek-shaped layers.
 __device__ __forceinline__ int xcd_logical(int bid, int G) {
-  return MOE_XCD_REMAP ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  return (bid % 8) * (G / 8) + bid / 8;
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
@@ -100,18 +97,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)to_bf16(lo) | ((uint32_t)to_bf16(hi) << 16);
 }
 
-// 16 E4M3 weights (byte j of word w = element 4w + j) times their block's
-// power-of-two scale, as 16 bf16 in two 16-byte chunks (exact: an E4M3 value
-// times a power of two is a bf16 value).
+// Two E4M3 codes (the low or upper half-word of w) times a power-of-two
+// scale, as two bf16 (exact: an E4M3 value times a power of two is a bf16
+// value).
 template <bool UPPER>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16(uint32_t w, float sc) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, sc, UPPER));
-}
-__device__ __forceinline__ void fp8x16_to_bf16(u32x4 src, float sc, u32x4& lo, u32x4& hi) {
-  lo = u32x4{fp8x2_to_bf16<false>(src.x, sc), fp8x2_to_bf16<true>(src.x, sc),
-             fp8x2_to_bf16<false>(src.y, sc), fp8x2_to_bf16<true>(src.y, sc)};
-  hi = u32x4{fp8x2_to_bf16<false>(src.z, sc), fp8x2_to_bf16<true>(src.z, sc),
-             fp8x2_to_bf16<false>(src.w, sc), fp8x2_to_bf16<true>(src.w, sc)};
 }
 
 // ---------------------------------------------------------------- tile tables
@@ -198,12 +189,6 @@ __device__ void build_tile_table(const GemmArgs& a, int* tiles_l, int* wsum) {
 // once per fragment -- left to itself the compiler reloads one fragment at a
 // time to save registers (measured 3-6% faster on the large tiles).
 #define MOE_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
-#ifndef MOE_COPY_WAVES
-#define MOE_COPY_WAVES 4
-#endif
-#ifndef MOE_SWZ8
-#define MOE_SWZ8(row) (((row) >> 1) & 7)
-#endif
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -230,7 +215,7 @@ __device__ __forceinline__ void wait_stages(int later) {
 // (measured 3-9% faster than swizzling by row & 7).
 template <int KCH>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (KCH == 8) return MOE_SWZ8(row);
+  if constexpr (KCH == 8) return (row >> 1) & 7;
   else return (row >> 2) & 3;
 }
 
@@ -313,15 +298,7 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi, float 
 // non-temporal.  y_perm is written once and read once by the combine, and
 // keeping it out of L2 leaves L2 to the tiles' operands: measured 1-2.5%
 // faster grouped FFN on the bf16 prefill, DeepSeek-shaped and ragged layers.
-#ifndef MOE_Y_STORE_AUX
-#define MOE_Y_STORE_AUX 2
-#endif
-#ifndef MOE_MID_B_AUX
-#define MOE_MID_B_AUX 2
-#endif
-#ifndef MOE_MID_NT_ALL
-#define MOE_MID_NT_ALL 0
-#endif
+constexpr int kAuxNT = 2;   // the gfx950 "nt" bit of a buffer access's aux operand
 template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
 struct RingCfg {
   using RS = RingShape<WF, BM, BN, BK, STAGES>;
@@ -337,12 +314,13 @@ struct RingCfg {
   // With 8 waves only one wave per SIMD (waves 0-3) issues the copies, so
   // that its partner never stalls behind the copy issue and keeps the SIMD's
   // matrix core fed.
-  static constexpr int NI = (NW == 8 && MOE_COPY_WAVES == 4) ? 4 : NW;   // issuing waves
+  // (measured 2-5% faster than all eight waves issuing)
+  static constexpr int NI = NW == 8 ? 4 : NW;   // issuing waves
   static constexpr int A_IT = BM / RPB / NI;   // A copies per issuing wave per stage
   static constexpr int LPI = A_IT + BN / RPBB / NI;   // all copies per issuing wave per stage
   // cache policy of the weight copies of single-row-tile segments (bf16
-  // weights on the 128-row tiles; see MOE_MID_B_AUX)
-  static constexpr int B_AUX = (BM < 256 && WF == 0) ? MOE_MID_B_AUX : 0;
+  // weights on the 128-row tiles, as above)
+  static constexpr int B_AUX = (BM < 256 && WF == 0) ? kAuxNT : 0;
   static_assert(WF == 2 ? BK == 128 : (BK == 32 || BK == 64), "row piece of 64 or 128 bytes");
   static_assert(WF != 1 || BK == 64, "E4M3 weights: 64-byte row pieces");
   static_assert((BM / RPB) % NI == 0 && (BN / RPBB) % NI == 0, "copy blocks per wave");
@@ -382,7 +360,7 @@ __device__ __forceinline__ void ring_setup(const GemmArgs& args, const int* tile
   seg_range(P, gs - (pi ? args.p[0].n_seg : 0), t.r0, t.len, t.e);
   const int mt = (t.len + BM - 1) / BM;
   // weights that no other row tile of the segment reads again
-  t.stream = MOE_MID_NT_ALL || mt == 1;
+  t.stream = mt == 1;
   const int ncols = MODE == 0 ? BN / 2 : BN;
   const int nt = (P.N + ncols - 1) / ncols;
   const int local = tile - tiles_l[gs];
@@ -491,16 +469,7 @@ __device__ __forceinline__ void act_scales_store(ActScales<BM, NTHR, RUN>& a, ui
   }
 }
 
-#ifndef MOE_BF16_NMAJOR
-#define MOE_BF16_NMAJOR 1
-#endif
-#ifndef MOE_W8A8_INTERLEAVE
-#define MOE_W8A8_INTERLEAVE 2
-#endif
-#ifndef MOE_ACT_RUN
-#define MOE_ACT_RUN 16
-#endif
-constexpr int kActRun = MOE_ACT_RUN;   // activation-scale loads in flight per thread
+constexpr int kActRun = 16;   // activation-scale loads in flight per thread
 
 // The first STAGES - 1 stages of a tile's ring (issuing waves).
 template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
@@ -512,14 +481,15 @@ __device__ __forceinline__ void ring_prologue(
   const int KT = t.P->K / BK;
   if (wvs >= C::NI) return;
 #pragma unroll
-  for (int st = 0; st < STAGES - 1; ++st)
-    if (st < KT)
-      if (C::B_AUX && t.stream)
-        ring_issue<C::LPI, C::NI, STAGES, C::STAGE_CH, C::A_CH, BK, C::A_IT, C::WB, C::AB, C::B_AUX>(
-            t.ra, t.rb, t.voff, ring, st, wvs);
-      else
-        ring_issue<C::LPI, C::NI, STAGES, C::STAGE_CH, C::A_CH, BK, C::A_IT, C::WB, C::AB, 0>(
-            t.ra, t.rb, t.voff, ring, st, wvs);
+  for (int st = 0; st < STAGES - 1; ++st) {
+    if (st >= KT) break;
+    if (C::B_AUX && t.stream)
+      ring_issue<C::LPI, C::NI, STAGES, C::STAGE_CH, C::A_CH, BK, C::A_IT, C::WB, C::AB, C::B_AUX>(
+          t.ra, t.rb, t.voff, ring, st, wvs);
+    else
+      ring_issue<C::LPI, C::NI, STAGES, C::STAGE_CH, C::A_CH, BK, C::A_IT, C::WB, C::AB, 0>(
+          t.ra, t.rb, t.voff, ring, st, wvs);
+  }
 }
 
 // The K loop of one tile into `acc`.
@@ -617,8 +587,7 @@ __device__ __forceinline__ void ring_kloop(
         for (int mi = 0; mi < TM; ++mi)
           acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               bq[ni], af[mi], acc[mi][ni], 0, 0, 0, sb[ni], 0, sa[mi]);
-#if MOE_W8A8_INTERLEAVE
-      constexpr int AHEAD = MOE_W8A8_INTERLEAVE;   // weight fragments read ahead
+      constexpr int AHEAD = 2;   // weight fragments read ahead
       __builtin_amdgcn_sched_group_barrier(0x100, TM + (MODE == 0 ? 2 : 1) + 2 * TM + 2 * AHEAD, 0);
 #pragma unroll
       for (int ni = 0; ni < TN; ++ni) {
@@ -631,7 +600,6 @@ __device__ __forceinline__ void ring_kloop(
           __builtin_amdgcn_sched_group_barrier(0x008, TM, 0);
         }
       }
-#endif
     } else {
       float sc0 = 1.0f, sc1 = 1.0f;
       if (WF) {
@@ -679,7 +647,7 @@ __device__ __forceinline__ void ring_kloop(
             bfr[cur][ni] = fp8x8_to_bf16(b8[cur][ni][0], b8[cur][ni][1],
                                          (MODE == 0 && ni >= TN / 2) ? sc1 : sc0);
         }
-        if constexpr (WF == 0 && MOE_BF16_NMAJOR) {
+        if constexpr (WF == 0) {
           // weight fragment by weight fragment: the step's first MFMAs need
           // only its activation fragments and its first two weight fragments,
           // the rest of its reads (and the next step's) go among the MFMAs
@@ -708,6 +676,8 @@ __device__ __forceinline__ void ring_kloop(
             __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
           }
         } else {
+        // E4M3 weights: activation fragment by activation fragment, the
+        // step's dequantized weight fragments all formed first
 #pragma unroll
         for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
@@ -814,7 +784,7 @@ __device__ __forceinline__ void ring_store(
     const uint32_t off = (row < t.len && col < N)
                              ? ((uint32_t)row * (uint32_t)N + (uint32_t)col) * 2u
                              : 0xFFFFFFF0u;
-    __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, MODE == 1 ? MOE_Y_STORE_AUX : 0);
+    __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, MODE == 1 ? kAuxNT : 0);
   }
 }
 
@@ -961,24 +931,8 @@ __global__ __launch_bounds__(NTHR, OCC) void gemm_ring_kernel(GemmArgs args) {
 
 
 // Ring-tile shapes: BM, BN, BK, threads, waves along M, ring stages.  "big"
-// for segments of at least MOE_BIG_ROWS rows, "mid" for the rest.
-#ifndef MOE_MID_TILE
-#define MOE_MID_TILE 128, 256, 64, 512, 2, 3   // 2 x 4 waves of 64 x 64
-#endif
-#ifndef MOE_BIG_TILE
-#define MOE_BIG_TILE 256, 256, 64, 512, 4, 2   // 4 x 2 waves of 64 x 128
-#endif
-// E4M3 weights: the weight rows of a stage take half the bytes, so the same
-// tiles hold one more stage.
-#ifndef MOE_MID_TILE_F8
-#define MOE_MID_TILE_F8 128, 256, 64, 512, 2, 4
-#endif
-#ifndef MOE_BIG_TILE_F8
-#define MOE_BIG_TILE_F8 256, 256, 64, 512, 4, 3
-#endif
-#ifndef MOE_BIG_ROWS
-#define MOE_BIG_ROWS 256
-#endif
+// for segments of at least kBigRows rows, "mid" for the rest.
+constexpr int kBigRows = 256;
 
 template <int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
 struct TileCfg {
@@ -986,36 +940,23 @@ struct TileCfg {
   static constexpr int kThreads = NTHR;
   static constexpr int kBM = BM, kBN = BN, kBK = BK, kWM = WAVES_M, kStages = STAGES;
 };
-#ifndef MOE_MID1_TILE
-#define MOE_MID1_TILE MOE_MID_TILE
-#endif
-#ifndef MOE_MID2_TILE
-#define MOE_MID2_TILE MOE_MID_TILE
-#endif
-// tile shapes per weight format: [0] bf16, [1] E4M3
+// tile shapes per operand format
 template <int WF> struct Tiles;
-template <> struct Tiles<0> {
-  using Mid1 = TileCfg<0, MOE_MID1_TILE>;   // GEMM 1 and GEMM 2 may differ
-  using Mid2 = TileCfg<0, MOE_MID2_TILE>;
-  using Big = TileCfg<0, MOE_BIG_TILE>;
+template <> struct Tiles<0> {                              // bf16
+  using Mid = TileCfg<0, 128, 256, 64, 512, 2, 3>;         // 2 x 4 waves of 64 x 64
+  using Big = TileCfg<0, 256, 256, 64, 512, 4, 2>;         // 4 x 2 waves of 64 x 128
 };
+// E4M3 weights: the weight rows of a stage take half the bytes, so the same
+// tiles hold one more stage.
 template <> struct Tiles<1> {
-  using Mid1 = TileCfg<1, MOE_MID_TILE_F8>;
-  using Mid2 = TileCfg<1, MOE_MID_TILE_F8>;
-  using Big = TileCfg<1, MOE_BIG_TILE_F8>;
+  using Mid = TileCfg<1, 128, 256, 64, 512, 2, 4>;
+  using Big = TileCfg<1, 256, 256, 64, 512, 4, 3>;
 };
 // E4M3 activations and weights: 128-deep stages (128-byte row pieces, as the
 // bf16 tiles' 64-deep ones), one scaled FP8 MFMA K step each.
-#ifndef MOE_MID_TILE_W8A8
-#define MOE_MID_TILE_W8A8 128, 256, 128, 512, 2, 3
-#endif
-#ifndef MOE_BIG_TILE_W8A8
-#define MOE_BIG_TILE_W8A8 256, 256, 128, 512, 4, 2
-#endif
 template <> struct Tiles<2> {
-  using Mid1 = TileCfg<2, MOE_MID_TILE_W8A8>;
-  using Mid2 = TileCfg<2, MOE_MID_TILE_W8A8>;
-  using Big = TileCfg<2, MOE_BIG_TILE_W8A8>;
+  using Mid = TileCfg<2, 128, 256, 128, 512, 2, 3>;
+  using Big = TileCfg<2, 256, 256, 128, 512, 4, 2>;
 };
 
 
@@ -1079,18 +1020,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 // registers (rows past the segment end are never loaded).  The four waves
 // split each stage's K and reduce their partial sums through LDS at the end
 // of the tile, so every wave issues MFMAs even on one-row segments.
-#ifndef MOE_DWAVES
-#define MOE_DWAVES 6
-#endif
-#ifndef MOE_W8A8_DECODE_DEQ
-#define MOE_W8A8_DECODE_DEQ 1
-#endif
-#ifndef MOE_DWAVES_F8
-#define MOE_DWAVES_F8 5     // E4M3 weights (codes in LDS)
-#endif
-#ifndef MOE_DWAVES_W8A8
-#define MOE_DWAVES_W8A8 4   // E4M3 weights and activations
-#endif
+// Waves per SIMD of the decode tiles (their register budgets keep the K loop
+// free of spills): bf16 6 (8 spilled, 6% slower); E4M3 weights 5 (codes in
+// LDS); E4M3 weights and activations 4.
+constexpr int kDecodeWaves = 6, kDecodeWavesF8 = 5, kDecodeWavesW8A8 = 4;
 // One activation fragment of the decode tiles, 8 consecutive K elements of
 // row `arow` starting at element offset `off` (K index k), as loaded: bf16,
 // or (WF = 2) 8 E4M3 codes in .x/.y with their 1 x 128 piece scale's bits in
@@ -1100,27 +1033,14 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 // Weight chunks of the decode tiles are read once per layer call, so they
 // are loaded non-temporal: measured 7% faster on the bf16 decode layer (6.4
 // against 6.0 TB/s), 10% with E4M3 weights, bit-identical results.
-#ifndef MOE_DECODE_NT
-#define MOE_DECODE_NT 1
-#endif
 // E4M3 weights in the decode tiles: the codes go into LDS as they are and are
 // dequantized at the operand read, so a 512-deep stage takes 16 KiB of LDS
 // (as a bf16 256-deep one) instead of 32 KiB of dequantized bf16, which had
-// held a CU to 4 workgroups.  Measured with the waves per SIMD below (their
-// register budgets keep the K loop free of spills): FP8-weight decode FFN 7%
-// faster, W8A8 6%, bit-identical.
-#ifndef MOE_DECODE_F8_LDS
-#define MOE_DECODE_F8_LDS 1
-#endif
-#ifndef MOE_DECODE_W8A8_LDS
-#define MOE_DECODE_W8A8_LDS 1
-#endif
-// A weight chunk of the decode tiles.
+// held a CU to 4 workgroups.  Measured with the waves per SIMD above: FP8-weight
+// decode FFN 7% faster, W8A8 6%, bit-identical.
+// A weight chunk of the decode tiles (non-temporal, as above).
 __device__ __forceinline__ u32x4 decode_w_chunk(const uint8_t* p) {
-  if constexpr (MOE_DECODE_NT)
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  else
-    return *reinterpret_cast<const u32x4*>(p);
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 template <int WF>
 __device__ __forceinline__ u32x4 decode_a_frag(const GemmProblem& P, bool ok, uint32_t off,
@@ -1141,8 +1061,8 @@ __device__ __forceinline__ u32x4 decode_a_bf16(u32x4 f) {
 }
 
 // WF = 1: E4M3 weights with 128 x 128 block scales, loaded as 16-byte chunks
-// of 16 codes and dequantized (exactly) to bf16 on their way into LDS.
-// WF = 2: E4M3 activations too (see decode_a_frag).
+// of 16 codes, kept as codes in LDS and dequantized (exactly) to bf16 at the
+// operand read.  WF = 2: E4M3 activations too (see decode_a_frag).
 template <int MODE, int WF, int BN, int BK, int MT, int WAVES>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES)))
 void gemm_decode_kernel(GemmArgs args) {
@@ -1158,8 +1078,8 @@ void gemm_decode_kernel(GemmArgs args) {
   // E4M3 weights stay codes in LDS (LDS_CH chunks of 16 codes per row) and
   // are dequantized at the operand read, so a stage takes as much LDS as a
   // bf16 one and as many workgroups fit per CU
-  constexpr bool F8LDS = (WF == 1 && MOE_DECODE_F8_LDS) || (WF == 2 && MOE_DECODE_W8A8_LDS);
-  constexpr int LDS_CH = F8LDS ? LCH : KCH;
+  constexpr bool F8LDS = WF >= 1;
+  constexpr int LDS_CH = LCH;
   static_assert(!F8LDS || KPW * 32 == 128, "a wave's K steps of a stage share one scale block");
   __shared__ __attribute__((aligned(1024))) u32x4 Bs[BN * LDS_CH];   // swizzled rows: keep banks
   extern __shared__ int tiles_l[];
@@ -1195,10 +1115,8 @@ void gemm_decode_kernel(GemmArgs args) {
     const uint8_t* Bb = reinterpret_cast<const uint8_t*>(P.B) + (size_t)e * P.b_stride * WB;
     const float* Sb = WF ? P.b_scale + (size_t)e * P.s_stride : nullptr;
 
-    // byte offsets (within this expert's matrix) of this thread's chunks,
-    // and (WF) the index of their block scale at k = 0
+    // byte offsets (within this expert's matrix) of this thread's chunks
     uint32_t b_off[B_CH];
-    int b_sc[B_CH];
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
       const int c = tid + 256 * i, row = c / LCH, kc = c % LCH;
@@ -1210,11 +1128,10 @@ void gemm_decode_kernel(GemmArgs args) {
         brow = min(n0 + row, N - 1);
       }
       b_off[i] = ((uint32_t)brow * (uint32_t)K + kc * (16 / WB)) * WB;
-      if (WF) b_sc[i] = (brow / 128) * (K / 128) + (kc * 16) / 128;
     }
     // this lane's activation row and its K offsets inside a stage (WF = 2:
     // E4M3 codes, dequantized with their 1 x 128 scale on the way to the MFMA)
-    // F8LDS: the scale index at k = 0 of each 16-row group's 128-row block
+    // WF: the scale index at k = 0 of each 16-row group's 128-row block
     // (GEMM 1: the gate rows n0.., the up rows up_off + n0..; GEMM 2: rows
     // n0 + 16 j.., all in one block since n0 is a multiple of BN and N of
     // 128); wave wv reads K block wv of every stage.  Uniform over the wave,
@@ -1243,13 +1160,9 @@ void gemm_decode_kernel(GemmArgs args) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[mi][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     u32x4 rb[B_CH], ra[MT][KPW];
-    float rs[B_CH];
     float gsc[TN];
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      rb[i] = decode_w_chunk(Bb + b_off[i]);
-      if (WF && !F8LDS) rs[i] = Sb[b_sc[i]];
-    }
+    for (int i = 0; i < B_CH; ++i) rb[i] = decode_w_chunk(Bb + b_off[i]);
     if constexpr (F8LDS) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) gsc[j] = Sb[g_sc[j]];
@@ -1267,16 +1180,7 @@ void gemm_decode_kernel(GemmArgs args) {
 #pragma unroll
       for (int i = 0; i < B_CH; ++i) {
         const int c = tid + 256 * i, row = c / LCH, kc = c % LCH;
-        if (F8LDS) {
-          Bs[row * LDS_CH + (kc ^ (row & 7))] = rb[i];
-        } else if (WF) {
-          u32x4 lo, hi;
-          fp8x16_to_bf16(rb[i], rs[i], lo, hi);
-          Bs[row * KCH + ((2 * kc) ^ (row & 7))] = lo;
-          Bs[row * KCH + ((2 * kc + 1) ^ (row & 7))] = hi;
-        } else {
-          Bs[row * KCH + (kc ^ (row & 7))] = rb[i];
-        }
+        Bs[row * LDS_CH + (kc ^ (row & 7))] = rb[i];
       }
       __syncthreads();
       float sc[TN];
@@ -1290,10 +1194,7 @@ void gemm_decode_kernel(GemmArgs args) {
       if (kt + 1 < KT) {
         const int koff = (kt + 1) * BK;
 #pragma unroll
-        for (int i = 0; i < B_CH; ++i) {
-          rb[i] = decode_w_chunk(Bb + b_off[i] + koff * WB);
-          if (WF && !F8LDS) rs[i] = Sb[b_sc[i] + koff / 128];
-        }
+        for (int i = 0; i < B_CH; ++i) rb[i] = decode_w_chunk(Bb + b_off[i] + koff * WB);
         if constexpr (F8LDS) {
 #pragma unroll
           for (int j = 0; j < TN; ++j) gsc[j] = Sb[g_sc[j] + koff / 128];
@@ -1385,20 +1286,13 @@ void gemm_decode_kernel(GemmArgs args) {
 }
 
 // decode tiles: GEMM 1 32 weight rows (16 h columns) x K 256; GEMM 2 32 rows x K 256
-#ifndef MOE_DBN1
-#define MOE_DBN1 32
-#define MOE_DBK1 256
-#define MOE_DBN2 32
-#define MOE_DBK2 256
-#endif
-constexpr int DBN1 = MOE_DBN1, DBK1 = MOE_DBK1, DBN2 = MOE_DBN2, DBK2 = MOE_DBK2;
+// (512-deep bf16 stages measured 0.5% slower)
+constexpr int DBN1 = 32, DBK1 = 256, DBN2 = 32, DBK2 = 256;
 // E4M3 weights: twice the K per stage, so that a stage moves as many bytes
-// (and keeps as many in flight) as with bf16 weights
-#ifndef MOE_DBK_F8
-#define MOE_DBK_F8 512
-#endif
-template <int WF> constexpr int decode_bk1() { return WF ? MOE_DBK_F8 : DBK1; }
-template <int WF> constexpr int decode_bk2() { return WF ? MOE_DBK_F8 : DBK2; }
+// (and keeps as many in flight) as with bf16 weights (256-deep: 4% slower)
+constexpr int kDbkF8 = 512;
+template <int WF> constexpr int decode_bk1() { return WF ? kDbkF8 : DBK1; }
+template <int WF> constexpr int decode_bk2() { return WF ? kDbkF8 : DBK2; }
 
 // Persistent grid: as many workgroups as can be resident at once (a larger
 // grid would run its excess only after others finish), a multiple of 8 so
@@ -1493,7 +1387,7 @@ void quantize_h(const FfnProblem* probs, int n_probs, hipStream_t s) {
 bool w8a8_on_fp8w_decode(const moe_config& c, const FfnProblem* probs, int n_probs,
                          const GemmArgs& g1, const GemmArgs& g2, size_t lds_tiles,
                          hipStream_t s) {
-  if (!MOE_W8A8_DECODE_DEQ || !probs[0].a_deq) return false;
+  if (!probs[0].a_deq) return false;
   for (int p = 1; p < n_probs; ++p)
     if (probs[p].A != probs[0].A || probs[p].a_scale != probs[0].a_scale) return false;
   int64_t a_rows = 0;
@@ -1509,8 +1403,8 @@ bool w8a8_on_fp8w_decode(const moe_config& c, const FfnProblem* probs, int n_pro
     d2.p[p].A = (const uint16_t*)probs[p].h;
     d2.p[p].a_scale = nullptr;
   }
-  auto k1 = gemm_decode_kernel<0, 1, DBN1, decode_bk1<1>(), 1, MOE_DWAVES_F8>;
-  auto k2 = gemm_decode_kernel<1, 1, DBN2, decode_bk2<1>(), 1, MOE_DWAVES_F8>;
+  auto k1 = gemm_decode_kernel<0, 1, DBN1, decode_bk1<1>(), 1, kDecodeWavesF8>;
+  auto k2 = gemm_decode_kernel<1, 1, DBN2, decode_bk2<1>(), 1, kDecodeWavesF8>;
   k1<<<persistent_grid(k1, lds_tiles, 4), 256, lds_tiles, s>>>(cover(d1, 16, DBN1 / 2, 1, kAll));
   for (int p = 0; p < n_probs; ++p)
     launch_fake_quant_rows_fp8(probs[p].rows, probs[p].Iw, probs[p].h, s);
@@ -1538,7 +1432,7 @@ void launch_mfma_pair(const moe_config& c, const FfnProblem* probs, int n_probs,
     if constexpr (WF == 2) {
       if (w8a8_on_fp8w_decode(c, probs, n_probs, g1, g2, lds_tiles, s)) return;
     }
-    constexpr int DW = WF == 0 ? MOE_DWAVES : WF == 1 ? MOE_DWAVES_F8 : MOE_DWAVES_W8A8;
+    constexpr int DW = WF == 0 ? kDecodeWaves : WF == 1 ? kDecodeWavesF8 : kDecodeWavesW8A8;
     auto k1 = gemm_decode_kernel<0, WF, DBN1, BK1, 1, DW>;
     auto k2 = gemm_decode_kernel<1, WF, DBN2, BK2, 1, DW>;
     k1<<<persistent_grid(k1, lds_tiles, 4), 256, lds_tiles, s>>>(cover(g1, 16, DBN1 / 2, 1, kAll));
@@ -1547,36 +1441,37 @@ void launch_mfma_pair(const moe_config& c, const FfnProblem* probs, int n_probs,
     MOE_DBG("grouped gemms");
     return;
   }
-  // Segments of MOE_BIG_ROWS rows or more take 256 x 256 tiles (half the
-  // weight re-reads of their many row tiles), the rest 128 x 256 tiles: one
-  // launch per shape, each covering its own segments.  The mid ring is cut
-  // to 2 stages if the 3-stage one leaves no room for the tile table (and
-  // the scales), and the mid tiles take the long segments too if the big
-  // ring does not fit beside them.  A segment holds at most one row per
-  // token of its problem, so the big launches may be skipped.
-  using M1 = typename Tiles<WF>::Mid1;
-  using M2 = typename Tiles<WF>::Mid2;
+  // Segments of kBigRows rows or more take 256 x 256 tiles (half the weight
+  // re-reads of their many row tiles), the rest 128 x 256 tiles: one launch
+  // per shape, each covering its own segments.  The mid ring is cut to 2
+  // stages if the 3-stage one leaves no room for the tile table (and the
+  // scales), and the mid tiles take the long segments too if the big ring
+  // does not fit beside them.  The big launches are skipped when no segment
+  // can reach kBigRows rows (each problem states the longest a segment of it
+  // can be).
+  using MT = typename Tiles<WF>::Mid;
   using BG = typename Tiles<WF>::Big;
   constexpr size_t kMargin = 64;
   const bool big_fits = ring_dyn_lds(g1, WF, BG::kBM) + BG::kRingBytes + kMargin <= kMaxLdsBytes &&
                         ring_dyn_lds(g2, WF, BG::kBM) + BG::kRingBytes + kMargin <= kMaxLdsBytes;
-  const int mid_hi = big_fits ? MOE_BIG_ROWS : kAll;
-  const GemmArgs m1 = cover(g1, M1::kBM, M1::kBN / 2, 1, mid_hi);
-  const GemmArgs m2 = cover(g2, M2::kBM, M2::kBN, 1, mid_hi);
-  const GemmArgs b1 = cover(g1, BG::kBM, BG::kBN / 2, MOE_BIG_ROWS, kAll);
-  const GemmArgs b2 = cover(g2, BG::kBM, BG::kBN, MOE_BIG_ROWS, kAll);
-  const bool deep1 = ring_dyn_lds(g1, WF, M1::kBM) + M1::kRingBytes + kMargin <= kMaxLdsBytes;
-  const bool deep2 = ring_dyn_lds(g2, WF, M2::kBM) + M2::kRingBytes + kMargin <= kMaxLdsBytes;
+  const int mid_hi = big_fits ? kBigRows : kAll;
+  const GemmArgs m1 = cover(g1, MT::kBM, MT::kBN / 2, 1, mid_hi);
+  const GemmArgs m2 = cover(g2, MT::kBM, MT::kBN, 1, mid_hi);
+  const GemmArgs b1 = cover(g1, BG::kBM, BG::kBN / 2, kBigRows, kAll);
+  const GemmArgs b2 = cover(g2, BG::kBM, BG::kBN, kBigRows, kAll);
+  const bool deep1 = ring_dyn_lds(g1, WF, MT::kBM) + MT::kRingBytes + kMargin <= kMaxLdsBytes;
+  const bool deep2 = ring_dyn_lds(g2, WF, MT::kBM) + MT::kRingBytes + kMargin <= kMaxLdsBytes;
   int longest = 0;
-  for (int p = 0; p < n_probs; ++p) longest = probs[p].rows > longest ? probs[p].rows : longest;
-  const bool any_big = big_fits && longest >= MOE_BIG_ROWS && c.T >= MOE_BIG_ROWS;
+  for (int p = 0; p < n_probs; ++p)
+    longest = probs[p].max_seg_rows > longest ? probs[p].max_seg_rows : longest;
+  const bool any_big = big_fits && longest >= kBigRows;
   // (a 2-stage ring of the mid shape always fits beside the largest table)
-  if (deep1) launch_ring<0, WF, M1::kBM, M1::kBN, M1::kBK, M1::kThreads, M1::kWM, M1::kStages>(m1, s);
-  else launch_ring<0, WF, M1::kBM, M1::kBN, M1::kBK, M1::kThreads, M1::kWM, 2>(m1, s);
+  if (deep1) launch_ring<0, WF, MT::kBM, MT::kBN, MT::kBK, MT::kThreads, MT::kWM, MT::kStages>(m1, s);
+  else launch_ring<0, WF, MT::kBM, MT::kBN, MT::kBK, MT::kThreads, MT::kWM, 2>(m1, s);
   if (any_big) launch_ring<0, WF, BG::kBM, BG::kBN, BG::kBK, BG::kThreads, BG::kWM, BG::kStages>(b1, s);
   // (FP8 activations: the ring tiles of GEMM 1 wrote h quantized)
-  if (deep2) launch_ring<1, WF, M2::kBM, M2::kBN, M2::kBK, M2::kThreads, M2::kWM, M2::kStages>(m2, s);
-  else launch_ring<1, WF, M2::kBM, M2::kBN, M2::kBK, M2::kThreads, M2::kWM, 2>(m2, s);
+  if (deep2) launch_ring<1, WF, MT::kBM, MT::kBN, MT::kBK, MT::kThreads, MT::kWM, MT::kStages>(m2, s);
+  else launch_ring<1, WF, MT::kBM, MT::kBN, MT::kBK, MT::kThreads, MT::kWM, 2>(m2, s);
   if (any_big) launch_ring<1, WF, BG::kBM, BG::kBN, BG::kBK, BG::kThreads, BG::kWM, BG::kStages>(b2, s);
   MOE_DBG("grouped gemms");
 }

@@ -191,6 +191,7 @@ moe_status grouped_ffn(const moe_config* cfg, const void* x_perm, const float* x
   p.seg_expert = seg_expert;
   p.n_seg = num_segments(*cfg);
   p.rows = (int32_t)num_rows(*cfg);
+  p.max_seg_rows = p.rows;   // any segment lengths (ids may repeat within a token)
   p.n_w = cfg->E;
   p.Iw = cfg->I;
   p.a_fp8 = w.acts_fp8;
@@ -271,6 +272,9 @@ moe_status layer_forward(const moe_config* cfg, const float* logits, const void*
   p[0].seg_expert = seg_expert;
   p[0].n_seg = num_segments(*cfg);
   p[0].rows = (int32_t)num_rows(*cfg);
+  // routing gives every token k distinct experts: a segment holds at most one
+  // row per token
+  p[0].max_seg_rows = p[0].rows < cfg->T ? p[0].rows : cfg->T;
   p[0].n_w = cfg->E;
   p[0].Iw = cfg->I;
   if (shared) {
@@ -293,6 +297,7 @@ moe_status layer_forward(const moe_config* cfg, const float* logits, const void*
     p[1].seg_expert = nullptr;
     p[1].n_seg = 1;
     p[1].rows = cfg->T;
+    p[1].max_seg_rows = cfg->T;
     p[1].n_w = 1;
     p[1].Iw = cfg->shared_I;
   }

@@ -68,12 +68,11 @@ inline int chunk_len(int64_t A) {
 inline int num_chunks(int64_t A) { return (int)((A + chunk_len(A) - 1) / chunk_len(A)); }
 
 // The grouped GEMMs take the weight-streaming decode tiles when a launch's
-// rows are at most MOE_DECODE_ROWS per segment on average.
-#ifndef MOE_DECODE_ROWS
-#define MOE_DECODE_ROWS 16
-#endif
+// rows are at most kDecodeRows per segment on average (the host never sees
+// the segment lengths, so it decides from the mean).
+constexpr int64_t kDecodeRows = 16;
 inline bool uses_decode_tiles(int64_t rows, int64_t segments) {
-  return rows <= (int64_t)MOE_DECODE_ROWS * segments;
+  return rows <= kDecodeRows * segments;
 }
 
 // Offsets of the workspace regions (bytes).  P: permutation scratch;
@@ -121,6 +120,8 @@ struct FfnProblem {
   const int32_t* a_rows;  // nullable: GEMM 1 reads row a_rows[r] of A for row r
   int32_t n_seg;          // segments (1 for shared)
   int32_t rows;           // rows of h / y (and of A unless a_rows gathers)
+  int32_t max_seg_rows;   // no segment is longer (rows, or the tokens when every
+                          // token has at most one row in a segment)
   int32_t n_w;            // experts in w13 / w2; segments of other experts are skipped
   int32_t Iw;             // intermediate size of this problem
   int32_t w_fp8;          // 1: w13 / w2 are E4M3 codes with the block scales below

@@ -247,3 +247,56 @@ def test_empty_batch_is_a_noop(moe):
     moe.moe_route_topk(cfg, None, sentinel, None)
     torch.cuda.synchronize()
     assert (sentinel.cpu() == 7).all()
+
+
+@pytest.mark.parametrize("T,k,E,n_ids", [(100, 4, 4, 1), (150, 4, 3, 2)])
+def test_repeated_ids_make_segments_longer_than_the_batch(moe, T, k, E, n_ids):
+    """moe_permute takes ids that repeat within a token, so a segment may hold
+    more rows than there are tokens (all ids 0: one segment of T*k rows).
+    moe_grouped_ffn on that permutation must compute every row, also when
+    the segment reaches the 256-row tiles while T is below 256."""
+    cfg = mi.MoEShape("rep", T=T, H=256, E=E, k=k, I=128, seed=34)
+    rng = np.random.default_rng(T)
+    ids = rng.integers(0, n_ids, size=(T, k)).astype(np.int32)
+    x = mi.x(cfg)
+    w13b = np.stack([mi.w13(cfg, e) for e in range(E)])
+    w2b = np.stack([mi.w2(cfg, e) for e in range(E)])
+    g = gu.run_permute(moe, cfg, gu.to_dev(x, cfg.dtype), torch.from_numpy(ids).to(gu.dev()))
+    counts = orc.expert_counts(ids, E)
+    assert counts.max() > T
+    se, sr = orc.segment_list(counts, 0, 1)
+    seg = orc.segment_of_assignments(ids, se, sr, 1)
+    so, r2a, a2r, r2t = orc.permutation(seg, len(se), k)
+    p = dict(counts=counts, seg_offsets=so, seg_expert=se, assign_to_row=a2r,
+             row_to_token=r2t, balancedness=orc.balancedness(counts))
+    gu.check_plan(g, p)
+    y = gu.empty((T * k, cfg.H), torch.bfloat16)
+    y.fill_(0)
+    ws = gu.empty((moe.moe_workspace_size(cfg),), torch.uint8)
+    moe.moe_grouped_ffn(cfg, g["x_perm"], g["seg_offsets"], g["seg_expert"],
+                        gu.to_dev(w13b, "bf16"), gu.to_dev(w2b, "bf16"), None, y, ws)
+    torch.cuda.synchronize()
+    x64 = mi.values_f64(x, "bf16")
+    ref = orc.grouped_ffn(x64[r2t], so, se, mi.values_f64(w13b, "bf16"),
+                          mi.values_f64(w2b, "bf16"))
+    got = gu.host_f64(y)
+    err = gu.rel_err(got, ref)
+    print(f"  longest segment {counts.max()} rows of {T} tokens: rel err {err:.3e}")
+    assert err <= gu.BF16_REL, err
+    # every row was written (a skipped segment would leave the zero fill)
+    assert (np.abs(got).max(axis=1) > 0).all()
+
+
+@pytest.mark.parametrize("T", [40, 400])
+def test_every_id_dropped(moe, T):
+    """Every id outside [0, E): no row in any segment, every assign_to_row
+    -1, zero counts, and balancedness 0 (the oracle's reading of 0/0)."""
+    cfg = mi.MoEShape("alldrop", T=T, H=128, E=6, k=3, I=64, seed=35)
+    ids = np.where(np.arange(T * cfg.k).reshape(T, cfg.k) % 2 == 0, -1, cfg.E).astype(np.int32)
+    g = gu.run_permute(moe, cfg, gu.to_dev(mi.x(cfg), cfg.dtype),
+                       torch.from_numpy(ids).to(gu.dev()))
+    counts = np.zeros(cfg.E, dtype=np.int64)
+    assert (g["counts"].cpu().numpy() == counts).all()
+    assert (g["seg_offsets"].cpu().numpy() == 0).all()
+    assert (g["a2r"].cpu().numpy() == -1).all()
+    assert g["bal"].cpu().numpy()[0] == orc.balancedness(counts)
