@@ -148,17 +148,57 @@ def w8a8_slack(case) -> np.ndarray:
     return out
 
 
+# At most this fraction of the output elements may carry an h-code slack
+# larger than the plain tolerance itself (measured on the small W8A8 layers:
+# 0 to 0.41%); a looser slack would stop the check from meaning anything.
+W8A8_BIG_SLACK_FRAC = 0.01
+
+
 def check_w8a8_out(got, ref, slack, name=""):
     """|got - ref| within the bf16 layer tolerance plus the per-element
-    h-code slack; returns the largest error beyond the slack, relative."""
+    h-code slack; returns the largest error beyond the slack, relative.
+    Fails too when more than W8A8_BIG_SLACK_FRAC of the elements carry a
+    slack above the plain tolerance."""
     m = np.abs(ref).max()
     excess = (np.abs(got - ref) - slack) / m
     worst = float(excess.max())
     flagged = int((slack > 0).any(axis=1).sum())
+    big = float(np.mean(slack > BF16_REL * m))
     print(f"  {name}: error beyond the h-code slack {worst:.3e} (raw "
-          f"{np.abs(got - ref).max() / m:.3e}; {flagged} of {len(ref)} rows with slack)", flush=True)
+          f"{np.abs(got - ref).max() / m:.3e}; {flagged} of {len(ref)} rows with slack, "
+          f"{100 * big:.3f}% of elements with slack above the tolerance)", flush=True)
+    assert big <= W8A8_BIG_SLACK_FRAC, big
     assert worst <= BF16_REL, worst
     return worst
+
+
+def quantize_blocks_strips(w64, threads=None):
+    """The oracle's quantize_blocks on a matrix, one strip of 128 rows at a
+    time in a thread pool (numpy releases the GIL in its kernels).  Every
+    128 x 128 block is quantized on its own, so this is the same result as
+    one call on the whole matrix (a CPU test checks that), only faster."""
+    from concurrent.futures import ThreadPoolExecutor
+    R = w64.shape[0]
+    strips = [w64[i:i + 128] for i in range(0, R, 128)]
+    with ThreadPoolExecutor(max_workers=threads or mi.default_threads()) as pool:
+        parts = list(pool.map(ofp8.quantize_blocks, strips))
+    return (np.concatenate([c for c, _ in parts]), np.concatenate([s for _, s in parts]))
+
+
+def segment_sample_rows(plan, rng, tile=256):
+    """Rows of y_perm to compare when not all of them are: the first and last
+    row of every computed segment, and one random row inside every 256-row
+    tile of it (the big tiles' row blocks)."""
+    so, se = plan["seg_offsets"], plan["seg_expert"]
+    rows = set()
+    for s in range(len(se)):
+        r0, r1 = int(so[s]), int(so[s + 1])
+        if r1 <= r0 or se[s] < 0:
+            continue
+        rows.update((r0, r1 - 1))
+        for t0 in range(r0, r1, tile):
+            rows.add(int(rng.integers(t0, min(t0 + tile, r1))))
+    return np.array(sorted(rows), dtype=np.int64)
 
 
 def quantize_act(moe, x):
