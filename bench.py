@@ -7,10 +7,15 @@ are resident in HBM before timing starts.  Prints one JSON line.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--no-cpu-baseline]
 
-The roofline object is for the grouped expert FFN (the two persistent
-grouped-GEMM launches that dominate the step), timed live with HIP events on
-the stream it runs on.  The cpu_baseline object times the float64 CPU oracle
-on a bounded sample of the same workload on the host cores.
+The default workload is the heavy-skew ragged layer (16384 tokens, hidden
+4096, 128 experts, top-8, intermediate 1536), the largest single-GPU
+configuration and the one bound by the matrix cores.  The roofline object is
+for the grouped expert FFN (the persistent grouped-GEMM launches that
+dominate the step), timed live with HIP events on the stream it runs on.
+The cpu_baseline object times the float64 CPU oracle on a bounded sample of
+the same workload on the host cores; practical_ceilings holds a device copy
+and hipBLASLt (torch.matmul) on the same GEMM shapes, measured in the same
+run outside the timed steps.
 """
 from __future__ import annotations
 
@@ -28,39 +33,38 @@ sys.path.insert(0, ROOT)
 import moe_inputs as mi  # noqa: E402
 
 METRIC = "MoE-layer tokens/s and grouped-GEMM TFLOP/s (% MFMA/HBM roofline), 1 MI355X"
-GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_segments_amd", "csrc", "gemm.hip")
+CSRC = os.path.join(ROOT, "mixture_experts_layer_segments_amd", "csrc")
 
 # HBM bytes per grouped-FFN call measured with rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE (summed over the GEMM kernels of one call, each counter scaled by
 # what it reads for a plain 1 GiB device copy), keyed by workload.  An entry
-# only applies while gemm.hip still has the hash it was measured with.
+# only applies while the library's sources (every file under csrc/) still
+# hash to the value it was measured with.
 MEASURED_TRAFFIC = {
-    "decode_bf16": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 5542936319},
-    "prefill_skew_bf16": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 7649083292},
-    "deepseek_v3_bf16": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 22466081716},
-    "ragged_stress_bf16": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 13501005067},
-    "decode_fp8w": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 2776273441},
-    "prefill_skew_fp8w": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 3655580077},
-    "deepseek_v3_fp8w": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 12676606059},
-    "ragged_stress_fp8w": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 9799088690},
-    "decode_w8a8": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 2781414063},
-    "prefill_skew_w8a8": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 4044629670},
-    "deepseek_v3_w8a8": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 11667204101},
-    "ragged_stress_w8a8": {"gemm_src_sha256_16": "9b839bea42fa6f05", "bytes": 7330972608},
 }
 
 
-def _src_hash(path=GEMM_SRC) -> str:
+def src_hash(root=CSRC) -> str:
+    """sha256 over every source file of the library (names and contents, in
+    name order), first 16 hex digits."""
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(root)):
+        path = os.path.join(root, name)
+        if os.path.isfile(path) and name.endswith((".hip", ".h")):
+            h.update(name.encode() + b"\0")
+            with open(path, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
     m = MEASURED_TRAFFIC.get(workload)
-    if m is None or m["gemm_src_sha256_16"] != _src_hash():
+    if m is None or m["csrc_sha256_16"] != src_hash():
         return None
     return m["bytes"]
+
+
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, published
@@ -172,7 +176,7 @@ def cpu_baseline(cfg, logits, budget_s=20.0, min_s=10.0):
 
     from oracle import fp8 as ofp8
     from oracle import moe_oracle as orc
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads = host_threads()
     with threadpool_limits(limits=threads):
         x64 = mi.values_f64(mi.x(cfg), cfg.dtype)
         t0 = time.perf_counter()
@@ -236,10 +240,85 @@ def cpu_baseline(cfg, logits, budget_s=20.0, min_s=10.0):
              f"expert MLP of {len(done)} of {n} active experts ({t_ffn[0]:.1f} s), "
              f"scaled by {n}/{len(done)}")
     return {"value": cfg.T / est, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu": cpu_identity(threads),
             "sample": (f"{cfg.name}: float64 numpy oracle, routing + permutation + combine of all "
                        f"{cfg.T} tokens and {scope}; {est:.2f} s per layer (weight generation"
                        f"{', FP8 quantization' if cfg.weights == 'fp8' else ''} "
                        f"and bf16->f64 conversion untimed)")}
+
+
+def host_threads() -> int:
+    """Threads the oracle's BLAS may use: every CPU this process may run on,
+    unless the environment caps the thread pools (OMP_NUM_THREADS, which the
+    GPU machines set to their CPU share)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def cpu_identity(threads: int) -> dict:
+    """Where the oracle baseline ran: CPU model, os.cpu_count(), the threads
+    used and the BLAS library numpy calls."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
+    except Exception:  # noqa: BLE001 (identity only)
+        pass
+    return {"model": model, "os_cpu_count": os.cpu_count(), "threads_used": threads,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"), "blas": blas}
+
+
+def practical_ceilings(dev, reps=10):
+    """Ceilings measured in the same run, outside the timed steps: a plain
+    1 GiB device copy (bytes read + written per second) and torch.matmul in
+    bf16 (hipBLASLt) on the ragged layer's two dense GEMM shapes."""
+    import torch
+    out = {}
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    out["device_copy_1GiB_GBs"] = round(2 * (1 << 30) / (ms * 1e-3) / 1e9, 1)
+    del src, dst
+    for m_, n_, k_ in ((16384, 3072, 4096), (16384, 4096, 1536)):
+        a = torch.randn((m_, k_), dtype=torch.bfloat16, device=dev)
+        b = torch.randn((k_, n_), dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            torch.matmul(a, b)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[f"matmul_bf16_{m_}x{n_}x{k_}_TFLOPs"] = round(2 * m_ * n_ * k_ / (ms * 1e-3) / 1e12, 1)
+        del a, b
+    torch.cuda.empty_cache()
+    return out
 
 
 def calibrate_copy(nbytes=1 << 30, reps=5):
@@ -264,8 +343,10 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode_bf16", choices=sorted(mi.WORKLOADS))
+    ap.add_argument("--workload", default="ragged_stress_bf16", choices=sorted(mi.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the device-copy and torch.matmul ceilings (profiling runs)")
     ap.add_argument("--launch", choices=("eager", "graph"), default="eager",
                     help="run the timed steps as eager calls, or as replays of one HIP graph "
                          "captured from a step (the other mode is timed too and reported)")
@@ -346,19 +427,26 @@ def main(argv=None):
     torch.cuda.synchronize()
 
     def timed(run):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        """Mean over exactly K steps (events around all of them), and the
+        median and min of per-step events recorded between the steps."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        e0.record(stream)
-        for _ in range(args.steps):
+        ev[0].record(stream)
+        for i in range(args.steps):
             run()
-        e1.record(stream)
+            ev[i + 1].record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps, time.perf_counter() - t0
+        per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
+        return (ev[0].elapsed_time(ev[-1]) / args.steps, time.perf_counter() - t0,
+                float(np.median(per)), float(per.min()))
 
-    ms_eager, wall_eager = timed(step)
-    ms_graph, wall_graph = timed(graph.replay)
-    ms, wall = (ms_graph, wall_graph) if args.launch == "graph" else (ms_eager, wall_eager)
+    ms_eager, wall_eager, med_eager, min_eager = timed(step)
+    ms_graph, wall_graph, med_graph, min_graph = timed(graph.replay)
+    if args.launch == "graph":
+        ms, wall, med, mn = ms_graph, wall_graph, med_graph, min_graph
+    else:
+        ms, wall, med, mn = ms_eager, wall_eager, med_eager, min_eager
     counts_h = counts.cpu().numpy()
     active = int((counts_h > 0).sum())   # experts whose weights the step must read
     cap = moe.moe_num_rows(cfg) // cfg.E if cfg.capacity_factor_permille else cfg.A
@@ -380,14 +468,7 @@ def main(argv=None):
         moe.moe_quantize_act_fp8(x_perm, xq, xs)
     for _ in range(2):
         ffn()
-    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    f0.record(stream)
-    for _ in range(args.steps):
-        ffn()
-    f1.record(stream)
-    torch.cuda.synchronize()
-    ffn_ms = f0.elapsed_time(f1) / args.steps
+    ffn_ms, _, ffn_med, ffn_min = timed(ffn)
 
     routed = cfg.replace(shared_I=0)
     fl = ffn_flops(routed, computed)
@@ -404,17 +485,24 @@ def main(argv=None):
         roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": mfma_peak,
                 "unit": "TFLOP/s", "frac": round(tflops / mfma_peak, 4),
                 "traffic": measured_traffic(cfg.name)}
-    roof["kernel"] = ("grouped FFN: the two grouped-GEMM launches of one moe_grouped_ffn"
+    roof["kernel"] = ("grouped FFN: the grouped-GEMM launches of one moe_grouped_ffn"
                       + ("_w8a8" if w8a8 else "_fp8w" if fp8 else "")
-                      + " call (gate/up + SwiGLU, then down + row scale)")
+                      + " call (GEMM 1 gate/up + SwiGLU, then GEMM 2 down + row scale; each "
+                        "one launch per tile shape)")
     roof["ms_per_launch"] = round(ffn_ms, 4)
+    roof["ms_per_launch_median"] = round(ffn_med, 4)
+    roof["ms_per_launch_min"] = round(ffn_min, 4)
+    roof["traffic_source"] = ("rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE on these sources "
+                              f"(csrc sha256 {src_hash()})" if roof["traffic"] is not None else
+                              "not measured for the current sources")
     roof["algorithmic_bytes"] = by
     roof["algorithmic_flops"] = fl
 
     res = {
         "metric": METRIC, "value": round(cfg.T / (ms * 1e-3), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "ms_per_step": round(ms, 4), "ms_per_step_median": round(med, 4),
+        "ms_per_step_min": round(mn, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp8e4m3" if w8a8 else cfg.dtype,
         "data": "synthetic (seeded; random-init weights)",
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "experts": cfg.E,
@@ -440,6 +528,9 @@ def main(argv=None):
         "ms_per_step_graph_replay": round(ms_graph, 4),
         "roofline": roof,
     }
+    if not args.no_ceilings:
+        print("[bench] practical ceilings", file=sys.stderr, flush=True)
+        res["practical_ceilings"] = practical_ceilings(dev)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, mi.logits(cfg))

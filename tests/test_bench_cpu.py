@@ -25,3 +25,19 @@ def test_cpu_baseline_object_on_the_tiny_workload():
     assert cb["kind"] == "oracle" and cb["unit"] == "tokens/s"
     assert cb["value"] > 0 and cb["cores"] >= 1
     assert "tiny_fp32" in cb["sample"] and "whole layer" in cb["sample"]
+    cpu = cb["cpu"]
+    assert cpu["threads_used"] == cb["cores"] and cpu["os_cpu_count"] == os.cpu_count()
+    assert cpu["model"] and cpu["blas"]
+
+
+def test_traffic_entries_are_keyed_to_all_library_sources(tmp_path):
+    """The counter traffic applies only to the sources it was measured on:
+    a change to any csrc file changes the hash."""
+    sys.path.insert(0, ROOT)
+    import bench
+    for name in ("a.hip", "b.h"):
+        (tmp_path / name).write_text("x")
+    h0 = bench.src_hash(str(tmp_path))
+    (tmp_path / "b.h").write_text("y")
+    assert bench.src_hash(str(tmp_path)) != h0
+    assert len(bench.src_hash()) == 16
