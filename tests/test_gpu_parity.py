@@ -249,7 +249,7 @@ def test_empty_batch_is_a_noop(moe):
     assert (sentinel.cpu() == 7).all()
 
 
-@pytest.mark.parametrize("T,k,E,n_ids", [(100, 4, 4, 1), (150, 4, 3, 2)])
+@pytest.mark.parametrize("T,k,E,n_ids", [(100, 4, 4, 1), (150, 4, 4, 2)])
 def test_repeated_ids_make_segments_longer_than_the_batch(moe, T, k, E, n_ids):
     """moe_permute takes ids that repeat within a token, so a segment may hold
     more rows than there are tokens (all ids 0: one segment of T*k rows).
