@@ -232,6 +232,30 @@ moe_status moe_layer_forward(const moe_config* cfg, const float* logits, const v
                              float* topk_w, int32_t* counts, float* balancedness,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_layer_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same layer, the same kernels and the same results bit for
+ * bit, but the workspace is a device array inside the library, of
+ * MOE_STATIC_WORKSPACE_BYTES, one per GPU, held from the time the library's
+ * code is loaded on that GPU until the process ends.  The call allocates
+ * nothing: no hipMalloc, hipFree or allocating library routine.  The caller
+ * still passes every input and output, as for moe_layer_forward.
+ *   Returns MOE_ERR_WORKSPACE, before touching the GPU, when the layer needs
+ *   more workspace than that (moe_workspace_size(cfg) >
+ *   MOE_STATIC_WORKSPACE_BYTES: about T*k*(H + I)*2 bytes in bf16, so
+ *   decode-sized batches fit, e.g. 64 tokens at H = 8192 top-2 take ~6 MB);
+ *   MOE_ERR_HIP if the array's device address cannot be had.
+ *   Nothing in the array needs to start at zero (every kernel writes what it
+ *   later reads), and it keeps the last call's contents.  All calls on one
+ *   GPU share it: calls that overlap in time on one GPU (on different
+ *   streams or host threads) race and must be serialized by the caller. */
+#define MOE_STATIC_WORKSPACE_BYTES (64u * 1024u * 1024u)
+moe_status moe_layer_forward_static(const moe_config* cfg, const float* logits, const void* x,
+                                    const void* w13, const void* w2, const void* shared_w13,
+                                    const void* shared_w2, void* out, int32_t* topk_ids,
+                                    float* topk_w, int32_t* counts, float* balancedness,
+                                    void* stream);
+
 /* Where moe_layer_forward (and its _fp8w and _w8a8 forms) leave the
  * permutation they built inside their workspace, as byte offsets from its
  * start: offsets[0] seg_offsets [S+1], offsets[1] seg_expert [S],

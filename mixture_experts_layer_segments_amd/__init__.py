@@ -21,6 +21,6 @@ from ._lib import (  # noqa: F401
     moe_permute, moe_route_topk, moe_status_string, moe_unpermute_combine,
     moe_workspace_size, moe_quantize_fp8, moe_grouped_ffn_fp8w, moe_layer_forward_fp8w,
     moe_layer_plan_offsets, moe_num_rows, moe_quantize_act_fp8, moe_grouped_ffn_w8a8,
-    moe_layer_forward_w8a8,
+    moe_layer_forward_w8a8, moe_layer_forward_static, MOE_STATIC_WORKSPACE_BYTES,
     EXPORTED_SYMBOLS,
 )

@@ -21,8 +21,9 @@ EXPORTED_SYMBOLS = (
     "moe_permute", "moe_grouped_ffn", "moe_unpermute_combine", "moe_layer_forward",
     "moe_quantize_fp8", "moe_grouped_ffn_fp8w", "moe_layer_forward_fp8w",
     "moe_layer_plan_offsets", "moe_num_rows", "moe_quantize_act_fp8", "moe_grouped_ffn_w8a8",
-    "moe_layer_forward_w8a8",
+    "moe_layer_forward_w8a8", "moe_layer_forward_static",
 )
+MOE_STATIC_WORKSPACE_BYTES = 64 * 1024 * 1024   # include/moe.h
 
 
 class MoEConfig(ctypes.Structure):
@@ -80,6 +81,8 @@ lib.moe_grouped_ffn_w8a8.restype = ctypes.c_int
 lib.moe_grouped_ffn_w8a8.argtypes = [_cfgp] + [_p] * 11 + [ctypes.c_size_t, _p]
 lib.moe_layer_forward_w8a8.restype = ctypes.c_int
 lib.moe_layer_forward_w8a8.argtypes = [_cfgp] + [_p] * 16 + [ctypes.c_size_t, _p]
+lib.moe_layer_forward_static.restype = ctypes.c_int
+lib.moe_layer_forward_static.argtypes = [_cfgp] + [_p] * 12
 
 
 def make_config(shape) -> MoEConfig:
@@ -194,6 +197,17 @@ def moe_layer_forward(cfg, logits, x, w13, w2, shared_w13, shared_w2, out, topk_
                                  _ptr(topk_ids), _ptr(topk_w), _ptr(counts), _ptr(balancedness),
                                  _ptr(workspace), _nbytes(workspace), _stream(stream)),
            "moe_layer_forward")
+
+
+def moe_layer_forward_static(cfg, logits, x, w13, w2, shared_w13, shared_w2, out, topk_ids,
+                             topk_w, counts, balancedness, stream=None):
+    """moe_layer_forward on the library's own per-GPU workspace (allocates
+    nothing; overlapping calls on one GPU race)."""
+    _check(lib.moe_layer_forward_static(ctypes.byref(_cfg(cfg)), _ptr(logits), _ptr(x), _ptr(w13),
+                                        _ptr(w2), _ptr(shared_w13), _ptr(shared_w2), _ptr(out),
+                                        _ptr(topk_ids), _ptr(topk_w), _ptr(counts),
+                                        _ptr(balancedness), _stream(stream)),
+           "moe_layer_forward_static")
 
 
 def moe_quantize_fp8(src, q, scale, stream=None):

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -307,9 +308,60 @@ moe_status layer_forward(const moe_config* cfg, const float* logits, const void*
   return launch_status();
 }
 
+// ---- the entry point that allocates nothing ----
+// Its workspace is this file-scope device array.  Each GPU the library runs
+// on holds its own copy at its own address from the time the code object is
+// loaded there until the process ends.  In host code the name `scratch` is
+// only a host-side stand-in: its device address comes from
+// hipGetSymbolAddress, taken once per device (with that device current) and
+// kept in static_scratch_base.
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_WORKSPACE_BYTES];
+
+// Device address of `scratch` on the current device, nullptr if it cannot be
+// had (status in *err).
+void* static_scratch_base(moe_status* err) {
+  static std::mutex mu;
+  static void* base[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    *err = MOE_ERR_HIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!base[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      *err = MOE_ERR_HIP;
+      return nullptr;
+    }
+    base[dev] = p;
+  }
+  return base[dev];
+}
+
 }  // namespace
 
 extern "C" {
+
+moe_status moe_layer_forward_static(const moe_config* cfg, const float* logits, const void* x,
+                                    const void* w13, const void* w2, const void* shared_w13,
+                                    const void* shared_w2, void* out, int32_t* topk_ids,
+                                    float* topk_w, int32_t* counts, float* balancedness,
+                                    void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  // sizes beyond the static array: refused before anything touches the GPU
+  if (make_layout(*cfg).l_end > (size_t)MOE_STATIC_WORKSPACE_BYTES) return MOE_ERR_WORKSPACE;
+  if (cfg->T == 0) return MOE_OK;
+  void* ws = static_scratch_base(&st);
+  if (!ws) return st;
+  return layer_forward(cfg, logits, x, Weights{w13, w2, nullptr, nullptr, false},
+                       Weights{shared_w13, shared_w2, nullptr, nullptr, false}, out, topk_ids,
+                       topk_w, counts, balancedness, ws, (size_t)MOE_STATIC_WORKSPACE_BYTES,
+                       stream);
+}
 
 const char* moe_status_string(moe_status s) {
   switch (s) {

@@ -128,6 +128,26 @@ def test_null_misaligned_and_small_workspace(moe):
                                          None) == -1
 
 
+def test_static_workspace_limit_is_checked_on_the_host(moe):
+    """moe_layer_forward_static refuses, before any HIP call, a layer whose
+    workspace exceeds the library's static array, and invalid configs; the
+    limit in the binding is the header's."""
+    with open(os.path.join(ROOT, "include", "moe.h")) as f:
+        m = re.search(r"#define MOE_STATIC_WORKSPACE_BYTES \((\d+)u \* 1024u \* 1024u\)", f.read())
+    assert m and int(m.group(1)) * 1024 * 1024 == moe.MOE_STATIC_WORKSPACE_BYTES
+    big = mi.WORKLOADS["prefill_skew_bf16"]
+    assert moe.moe_workspace_size(big) > moe.MOE_STATIC_WORKSPACE_BYTES
+    assert moe.moe_workspace_size(mi.WORKLOADS["decode_bf16"]) <= moe.MOE_STATIC_WORKSPACE_BYTES
+    args = [FAKE] * 4 + [None, None] + [FAKE] * 5 + [None]
+    c = moe.make_config(big)
+    assert moe.lib.moe_layer_forward_static(ctypes.byref(c), *args) == -3
+    c = moe.make_config(mi.WORKLOADS["decode_bf16"])
+    c.E = 0
+    assert moe.lib.moe_layer_forward_static(ctypes.byref(c), *args) == -1
+    c = moe.make_config(mi.WORKLOADS["decode_bf16"].replace(T=0))
+    assert moe.lib.moe_layer_forward_static(ctypes.byref(c), *args) == 0
+
+
 def test_empty_batch_returns_ok_without_launching(moe):
     cfg = mi.WORKLOADS["decode_bf16"].replace(T=0)
     c = moe.make_config(cfg)
