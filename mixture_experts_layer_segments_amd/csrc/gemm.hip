@@ -112,25 +112,29 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16(uint32_t w, float sc) {
 // lengths never leave the device, no separate planning launch runs, and the
 // cost is one read of the offsets (L2-resident after the first workgroup)
 // and a block scan.
-__device__ __forceinline__ int seg_tiles(const GemmArgs& a, int g) {
+// Tiles of segment g (over both problems) for a cover of tiles bm rows x
+// ncols output columns over the segments of length in [min_len, max_len).
+__device__ __forceinline__ int seg_tiles(const GemmArgs& a, int g, int bm, int ncols,
+                                         int min_len, int max_len) {
   const int p = g < a.p[0].n_seg ? 0 : 1;
   const GemmProblem& P = a.p[p];
   const int s = g - (p ? a.p[0].n_seg : 0);
   const int len = P.seg_offsets ? P.seg_offsets[s + 1] - P.seg_offsets[s] : P.rows;
-  if (len < a.min_len || len >= a.max_len) return 0;
+  if (len < min_len || len >= max_len) return 0;
   if (P.seg_offsets && (unsigned)P.seg_expert[s] >= (unsigned)P.n_w) return 0;
-  return ((len + a.tile_bm - 1) / a.tile_bm) * ((P.N + a.tile_ncols - 1) / a.tile_ncols);
+  return ((len + bm - 1) / bm) * ((P.N + ncols - 1) / ncols);
 }
 
 // `wsum`: NTHR / 64 + 1 ints of LDS scratch.  Ends with a barrier.
 template <int NTHR>
-__device__ void build_tile_table(const GemmArgs& a, int* tiles_l, int* wsum) {
+__device__ void build_tile_table(const GemmArgs& a, int* tiles_l, int* wsum, int bm, int ncols,
+                                 int min_len, int max_len) {
   constexpr int NW = NTHR / 64;
   const int n = a.n_seg_total, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int per = (n + NTHR - 1) / NTHR;
   const int lo = min(n, tid * per), hi = min(n, lo + per);
   int sum = 0;
-  for (int g = lo; g < hi; ++g) sum += seg_tiles(a, g);
+  for (int g = lo; g < hi; ++g) sum += seg_tiles(a, g, bm, ncols, min_len, max_len);
   int incl = sum;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -152,7 +156,7 @@ __device__ void build_tile_table(const GemmArgs& a, int* tiles_l, int* wsum) {
   int run = wsum[wv] + incl - sum;
   for (int g = lo; g < hi; ++g) {
     tiles_l[g] = run;
-    run += seg_tiles(a, g);
+    run += seg_tiles(a, g, bm, ncols, min_len, max_len);
   }
   if (tid == 0) tiles_l[n] = wsum[NW];
   __syncthreads();
@@ -872,6 +876,52 @@ __device__ __forceinline__ void ring_store_q(
   }
 }
 
+// One ring tile: set up, issue its first stages, run `after_issue` (every
+// wave), the K loop, then the epilogue through the ring.  Starts with a
+// barrier after which the ring and the scales are free (the previous tile's
+// output is out).
+template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES,
+          typename Hook>
+__device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles_l, int tile,
+                                          u32x4* ring, float* scl, Hook after_issue) {
+  using C = RingCfg<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int wm = wv / C::WAVES_N;
+  constexpr int NPM = MODE == 0 ? C::TN / 2 : C::TN;
+  RingTileState<C::LPI> cur;
+  ring_setup<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(args, tiles_l, tile, cur);
+  raw_barrier();
+  ring_scales<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, scl, threadIdx.x, NTHR);
+  if constexpr (WF == 2) {
+    const int KB = cur.P->K / 128;
+    ActScales<BM, NTHR, kActRun> as;
+    act_scales_load(cur, KB, as);
+    ring_prologue<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, ring);
+    act_scales_store(as, reinterpret_cast<uint8_t*>(scl + 2 * KB), KB);
+  } else {
+    ring_prologue<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, ring);
+  }
+  after_issue();
+  u32x2 outv[C::TM * NPM];
+  {
+    f32x4 acc[C::TM][C::TN];
+    ring_kloop<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, ring, scl, acc);
+    // this tile's output scales (GEMM 2)
+    float rsc[C::TM];
+#pragma unroll
+    for (int mi = 0; mi < C::TM; ++mi) {
+      const int row = cur.m0 + wm * C::WM + mi * 16 + (lane & 15);
+      rsc[mi] = (MODE == 1 && cur.P->scale) ? cur.P->scale[cur.r0 + min(row, cur.len - 1)] : 1.0f;
+    }
+    ring_pack<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(acc, rsc, outv);
+  }
+  raw_barrier();   // every wave is done reading the ring: it takes the output
+  if constexpr (MODE == 0 && WF == 2)
+    ring_store_q<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, outv, ring);
+  else
+    ring_store<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, outv, ring);
+}
+
 // Persistent schedule: workgroup l (XCD-remapped) takes tiles l, l + G, ...
 template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES, int OCC>
 __global__ __launch_bounds__(NTHR, OCC) void gemm_ring_kernel(GemmArgs args) {
@@ -881,54 +931,17 @@ __global__ __launch_bounds__(NTHR, OCC) void gemm_ring_kernel(GemmArgs args) {
   // read (measured 15-30% slower).  The table build's scan scratch therefore
   // borrows the ring, which is idle until the first tile.
   // (WF: the dynamic LDS also holds a tile's block scales, after the table.)
-  using C = RingCfg<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>;
   __shared__ __attribute__((aligned(1024))) u32x4 ring[RingShape<WF, BM, BN, BK, STAGES>::RING_CH];
   extern __shared__ int tiles_l[];
-  build_tile_table<NTHR>(args, tiles_l, reinterpret_cast<int*>(ring));
+  build_tile_table<NTHR>(args, tiles_l, reinterpret_cast<int*>(ring), args.tile_bm,
+                         args.tile_ncols, args.min_len, args.max_len);
   const int total = tiles_l[args.n_seg_total];
   float* scl = reinterpret_cast<float*>(tiles_l + args.n_seg_total + 1);
   const int G = gridDim.x;
-  int tile = xcd_logical(blockIdx.x, G);
-  if (tile >= total) return;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int wm = wv / C::WAVES_N;
-  constexpr int NPM = MODE == 0 ? C::TN / 2 : C::TN;
-  RingTileState<C::LPI> cur;
-  for (; tile < total; tile += G) {
-    ring_setup<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(args, tiles_l, tile, cur);
-    raw_barrier();   // the ring and the scales are free (the previous tile's output is out)
-    ring_scales<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, scl, threadIdx.x, NTHR);
-    if constexpr (WF == 2) {
-      const int KB = cur.P->K / 128;
-      ActScales<BM, NTHR, kActRun> as;
-      act_scales_load(cur, KB, as);
-      ring_prologue<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, ring);
-      act_scales_store(as, reinterpret_cast<uint8_t*>(scl + 2 * KB), KB);
-    } else {
-      ring_prologue<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, ring);
-    }
-    u32x2 outv[C::TM * NPM];
-    {
-      f32x4 acc[C::TM][C::TN];
-      ring_kloop<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, ring, scl, acc);
-      // this tile's output scales (GEMM 2)
-      float rsc[C::TM];
-#pragma unroll
-      for (int mi = 0; mi < C::TM; ++mi) {
-        const int row = cur.m0 + wm * C::WM + mi * 16 + (lane & 15);
-        rsc[mi] =
-            (MODE == 1 && cur.P->scale) ? cur.P->scale[cur.r0 + min(row, cur.len - 1)] : 1.0f;
-      }
-      ring_pack<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(acc, rsc, outv);
-    }
-    raw_barrier();   // every wave is done reading the ring: it takes the output
-    if constexpr (MODE == 0 && WF == 2)
-      ring_store_q<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, outv, ring);
-    else
-      ring_store<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, outv, ring);
-  }
+  for (int tile = xcd_logical(blockIdx.x, G); tile < total; tile += G)
+    ring_tile<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(args, tiles_l, tile, ring, scl,
+                                                            [] {});
 }
-
 
 // Ring-tile shapes: BM, BN, BK, threads, waves along M, ring stages.  "big"
 // for segments of at least kBigRows rows, "mid" for the rest.
@@ -958,6 +971,7 @@ template <> struct Tiles<2> {
   using Mid = TileCfg<2, 128, 256, 128, 512, 2, 3>;
   using Big = TileCfg<2, 256, 256, 128, 512, 4, 2>;
 };
+
 
 
 // ---------------------------------------------------------------- fp32 path
@@ -1089,7 +1103,8 @@ void gemm_decode_kernel(GemmArgs args) {
   __shared__ int wsum[256 / 64 + 1];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nst = args.n_seg_total;
-  build_tile_table<256>(args, tiles_l, wsum);
+  build_tile_table<256>(args, tiles_l, wsum, args.tile_bm, args.tile_ncols, args.min_len,
+                        args.max_len);
   const int total = tiles_l[nst];
   const int G = gridDim.x;
   const int logical = xcd_logical(blockIdx.x, G);
