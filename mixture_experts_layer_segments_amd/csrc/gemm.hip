@@ -21,6 +21,7 @@
 
 #include "fp8_dev.h"
 #include "moe_internal.h"
+#include "wave_dev.h"
 
 namespace moe {
 namespace {
@@ -135,12 +136,7 @@ __device__ void build_tile_table(const GemmArgs& a, int* tiles_l, int* wsum, int
   const int lo = min(n, tid * per), hi = min(n, lo + per);
   int sum = 0;
   for (int g = lo; g < hi; ++g) sum += seg_tiles(a, g, bm, ncols, min_len, max_len);
-  int incl = sum;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
+  const int incl = wave_dev::incl_scan(sum);
   if (lane == 63) wsum[wv] = incl;
   __syncthreads();
   if (tid == 0) {

@@ -24,7 +24,7 @@ Layout make_layout(const moe_config& c) {
   const size_t R = (size_t)num_rows(c);
   const size_t eb = c.act_dtype == MOE_DT_F32 ? 4 : 2;
   const size_t nbins = (size_t)c.E * bin_ways(c);
-  const size_t nb = (size_t)num_chunks((int64_t)A);
+  const size_t nb = (size_t)chunk_stride((int64_t)A);
   const size_t S = (size_t)num_segments(c);
   size_t o = 0;
   auto take = [&](size_t bytes) {

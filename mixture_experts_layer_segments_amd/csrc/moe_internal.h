@@ -66,6 +66,10 @@ inline int chunk_len(int64_t A) {
   return (int)c;
 }
 inline int num_chunks(int64_t A) { return (int)((A + chunk_len(A) - 1) / chunk_len(A)); }
+// Row stride (ints) of the per-chunk count and base tables: the chunks
+// rounded up to a multiple of 4, so that a lane moves 4 chunks in one
+// 16-byte access.
+inline int chunk_stride(int64_t A) { return (num_chunks(A) + 3) & ~3; }
 
 // The grouped GEMMs take the weight-streaming decode tiles when a launch's
 // rows are at most kDecodeRows per segment on average (the host never sees

@@ -13,8 +13,9 @@
 //             blk_off[s][b] = seg_offsets[s] + rows of s in chunks < b, and
 //             balancedness ("The slowest expert sets the pace").
 //  3. rank:   one wave per chunk walks its assignments in order, 64 at a
-//             time; lanes of one segment get consecutive rows from a ballot
-//             mask, so rows of a segment are in increasing assignment order.
+//             time; lanes of one segment get consecutive rows from their
+//             peer mask (one ballot per bit of the segment number), so rows
+//             of a segment are in increasing assignment order.
 //  4. gather: x_perm[r] = x[row_to_token[r]] with 16-byte loads and stores.
 #include "plan_dev.h"
 #include "route_dev.h"
@@ -23,7 +24,7 @@ namespace moe {
 namespace {
 
 __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ ids, int A,
-                                                   int k, int E, int ways, int chunk, int nb,
+                                                   int k, int E, int ways, int chunk, int ns,
                                                    int32_t* __restrict__ cnt_bin) {
   __shared__ int h[kMaxBins];
   const int nbins = E * ways;
@@ -37,11 +38,16 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
     if (e >= 0 && e < E) atomicAdd(&h[e * ways + (a / k) % ways], 1);
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < nbins; i += blockDim.x) cnt_bin[(size_t)i * nb + b] = h[i];
+  for (int i = threadIdx.x; i < nbins; i += blockDim.x) {
+    cnt_bin[(size_t)i * ns + b] = h[i];
+    // the last chunk's block zeroes the row's padding (chunks nb .. ns-1)
+    if (b == (int)gridDim.x - 1)
+      for (int j = b + 1; j < ns; ++j) cnt_bin[(size_t)i * ns + j] = 0;
+  }
 }
 
 __global__ __launch_bounds__(1024) void plan_kernel(
-    const int32_t* __restrict__ cnt_bin, int nb, int E, int bin_ways, int ways, int n_hot,
+    const int32_t* __restrict__ cnt_bin, int nb, int ns, int E, int bin_ways, int ways, int n_hot,
     int c, int cap, int32_t* __restrict__ counts, int32_t* __restrict__ seg_offsets,
     int32_t* __restrict__ seg_expert, int32_t* __restrict__ seg_of_bin,
     int32_t* __restrict__ blk_off, int32_t* __restrict__ r2t, float* __restrict__ bal) {
@@ -49,28 +55,27 @@ __global__ __launch_bounds__(1024) void plan_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nbins = E * bin_ways;
 
-  // bin totals: a wave takes 4 bins at a time, coalesced over chunks, and
-  // issues all their loads (nb <= 256 chunks: 4 per lane and bin) before
-  // adding, so it waits on memory once per 4 bins, not once per 64 chunks
-  // of every bin
-  for (int bin0 = wv; bin0 < nbins; bin0 += 16 * 4) {
-    int v[4][4];
+  // Rows of the count tables are ns ints (nb chunks, zero-padded to a
+  // multiple of 4): lane l holds chunks 4l .. 4l + 3 of a row in one 16-byte
+  // access (nb <= 256).
+  // bin totals: wave w takes bins w, w + 16, ... (QB at a time) and issues
+  // all their loads before adding, so it waits on memory once per 16 * QB
+  // bins
+  constexpr int QB = 16;
+  const bool in_row = 4 * lane < nb;
+  for (int bin0 = wv; bin0 < nbins; bin0 += 16 * QB) {
+    int4 v[QB];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < QB; ++q) {
       const int bin = bin0 + 16 * q;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int b = lane + 64 * r;
-        v[q][r] = (bin < nbins && b < nb) ? cnt_bin[(size_t)bin * nb + b] : 0;
-      }
+      v[q] = (bin < nbins && in_row)
+                 ? reinterpret_cast<const int4*>(cnt_bin + (size_t)bin * ns)[lane]
+                 : int4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < QB; ++q) {
       const int bin = bin0 + 16 * q;
-      int s = v[q][0] + v[q][1] + v[q][2] + v[q][3];
-      for (int b = lane + 256; bin < nbins && b < nb; b += 64) s += cnt_bin[(size_t)bin * nb + b];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+      const int s = wave_dev::sum(v[q].x + v[q].y + v[q].z + v[q].w);
       if (lane == 0 && bin < nbins) L.tot[bin] = s;
     }
   }
@@ -81,44 +86,56 @@ __global__ __launch_bounds__(1024) void plan_kernel(
                                                   seg_offsets, seg_expert, seg_of_bin, bal);
 
   // per-(segment, chunk) bases: a wave scans a segment's chunk counts, lane l
-  // taking chunks 4l .. 4l + 3 (nb <= 256), so one wave scan covers the
-  // segment.  In the load-bounded split only the first segment of a hot
+  // taking chunks 4l .. 4l + 3, so one wave scan covers the segment; wave w
+  // takes segments w, w + 16, ... (QS at a time) and issues all their loads (a chunk count is the
+  // segment's one bin, or the sum over its expert's bins) before scanning
+  // and storing.  In the load-bounded split only the first segment of a hot
   // expert is ever looked up (its rows run on through the later ones); the
   // later replica segments get bases too, which nothing reads.  Padding
   // segments of the fixed-capacity layout (expert -1) get none.
-  for (int sg = wv; sg < S; sg += 16) {
-    const int e = L.seg_exp[sg];
-    if (e < 0) continue;
-    const int f = L.seg_first[e];
-    const bool per_replica = L.seg_first[e + 1] - f > 1 && bin_ways > 1;
-    auto count = [&](int b) {
-      int v = 0;
-      if (b < nb) {
-        if (per_replica) {
-          v = cnt_bin[(size_t)(e * bin_ways + (sg - f)) * nb + b];
-        } else {
-          for (int p = 0; p < bin_ways; ++p) v += cnt_bin[(size_t)(e * bin_ways + p) * nb + b];
+  constexpr int QS = 16;
+  for (int sg0 = wv; sg0 < S; sg0 += 16 * QS) {
+    int4 v[QS];
+#pragma unroll
+    for (int q = 0; q < QS; ++q) {
+      const int sg = sg0 + 16 * q;
+      const int e = sg < S ? L.seg_exp[sg] : -1;
+      // the bins counted: bin0 .. bin0 + nbin - 1
+      int bin0 = 0, nbin = 0;
+      if (e >= 0) {
+        const int f = L.seg_first[e];
+        const bool per_replica = L.seg_first[e + 1] - f > 1 && bin_ways > 1;
+        bin0 = e * bin_ways + (per_replica ? sg - f : 0);
+        nbin = per_replica ? 1 : bin_ways;
+      }
+      int4 c = {0, 0, 0, 0};
+#pragma unroll
+      for (int p = 0; p < kMaxWays; ++p) {
+        if (p < nbin && in_row) {
+          const int4 u = reinterpret_cast<const int4*>(cnt_bin + (size_t)(bin0 + p) * ns)[lane];
+          c.x += u.x;
+          c.y += u.y;
+          c.z += u.z;
+          c.w += u.w;
         }
       }
-      return v;
-    };
-    int v[4];
+      v[q] = c;
+    }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = count(4 * lane + r);
-    const int local = v[0] + v[1] + v[2] + v[3];
-    const int incl = plan_dev::wave_incl_scan(local, lane);
-    int run = L.seg_off[sg] + incl - local;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int b = 4 * lane + r;
-      if (b < nb) blk_off[(size_t)sg * nb + b] = run;
-      run += v[r];
+    for (int q = 0; q < QS; ++q) {
+      const int sg = sg0 + 16 * q;
+      if (sg >= S || L.seg_exp[sg] < 0) continue;
+      const int local = v[q].x + v[q].y + v[q].z + v[q].w;
+      const int incl = plan_dev::wave_incl_scan(local, lane);
+      const int r0 = L.seg_off[sg] + incl - local;
+      const int4 o = {r0, r0 + v[q].x, r0 + v[q].x + v[q].y, r0 + v[q].x + v[q].y + v[q].z};
+      if (in_row) reinterpret_cast<int4*>(blk_off + (size_t)sg * ns)[lane] = o;
     }
   }
 }
 
 __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ ids, int A, int k,
-                                                  int E, int ways, int chunk, int nb, int S,
+                                                  int E, int ways, int chunk, int ns, int S,
                                                   int cap,
                                                   const int32_t* __restrict__ seg_of_bin,
                                                   const int32_t* __restrict__ blk_off,
@@ -129,9 +146,9 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ id
   extern __shared__ int run[];  // [S] next free row of each segment
   const int lane = threadIdx.x;
   const int b = blockIdx.x;
-  for (int s = lane; s < S; s += 64) run[s] = blk_off[(size_t)s * nb + b];
+  for (int s = lane; s < S; s += 64) run[s] = blk_off[(size_t)s * ns + b];
   __syncthreads();
-  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  const int nbits = plan_dev::segment_bits(S);
   const int a_end = min(A, (b + 1) * chunk);
   // RB rounds of 64 assignments at a time: their ids, then their segments,
   // are loaded together, so the wave waits on memory twice per RB rounds
@@ -155,17 +172,7 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ id
       if (a0 >= a_end) break;
       const int a = a0 + lane;
       const int seg = seg_pre[q], e = e_pre[q];
-      int row = -1;
-      uint64_t pending = __ballot(seg >= 0);
-      while (pending) {
-        const int leader = __ffsll((unsigned long long)pending) - 1;
-        const int sl = __shfl(seg, leader);
-        const uint64_t m = __ballot(seg == sl);
-        const int base = run[sl];
-        if (seg == sl) row = base + __popcll(m & lt);
-        if (lane == leader) run[sl] = base + __popcll(m);
-        pending &= ~m;
-      }
+      int row = plan_dev::wave_rank_round(seg, nbits, run);
       // fixed capacity: an assignment past its expert's last slot is dropped
       if (cap > 0 && row >= (e + 1) * cap) row = -1;
       if (a < a_end) {
@@ -182,10 +189,9 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ id
 // Small batches (decode): routing, histogram, plan and the stable rank in one
 // workgroup -- one launch instead of four.  Each wave routes tokens; every
 // assignment is binned by LDS atomics (counts do not depend on the order);
-// the plan is the one above; and the row of assignment a is its segment's
-// offset plus the number of earlier assignments in the same segment, counted
-// directly over the at most kSmallA assignments.
-template <int VPL>
+// the plan is the one above; and one wave ranks the at most kSmallA
+// assignments in order, 64 at a time, as the rank kernel does.
+template <int G, int VPL>
 __global__ __launch_bounds__(1024) void route_permute_small_kernel(
     const float* __restrict__ logits, int T, int E, int k, int score, int n_group,
     int topk_group, int topn, int renorm, int bin_ways, int ways, int n_hot, int c, int cap,
@@ -201,11 +207,32 @@ __global__ __launch_bounds__(1024) void route_permute_small_kernel(
   const int A = T * k;
   for (int i = tid; i < E * bin_ways; i += 1024) L.tot[i] = 0;
   __syncthreads();
+  if constexpr (G > 0) {
+    // flat routing on G lanes per token: a wave routes 64 / G tokens at once
+    constexpr int TPW = 64 / G;
+    const int j = lane % G;
+    for (int tb = wv * TPW; tb < T; tb += 16 * TPW) {
+      const int t = tb + lane / G;
+      float v[VPL];
+      route_dev::load_logits_group<G, VPL>(t < T ? logits + (size_t)t * E : nullptr, E, j, v);
+      int my_id;
+      float my_w;
+      route_dev::route_group_vals<G, VPL>(v, E, k, score, renorm, j, my_id, my_w);
+      if (t < T && j < k) {
+        const int a = t * k + j;
+        ids[a] = my_id;
+        w[a] = my_w;
+        id_a[a] = my_id;
+        w_a[a] = my_w;
+        atomicAdd(&L.tot[my_id * bin_ways + t % bin_ways], 1);
+      }
+    }
+  }
   // a wave's tokens PF at a time: their logit loads are issued together, so
   // the wave waits on memory once per PF tokens
   // (wide rows, E > 256, keep one token at a time: their registers are taken)
   constexpr int PF = VPL <= 4 ? 4 : 1;
-  for (int t0 = wv; t0 < T; t0 += 16 * PF) {
+  for (int t0 = wv; G == 0 && t0 < T; t0 += 16 * PF) {
     if constexpr (PF == 1) {
       int my_id;
       float my_w;
@@ -246,26 +273,33 @@ __global__ __launch_bounds__(1024) void route_permute_small_kernel(
     }
   }
   __syncthreads();
-  if (cap > 0)
-    plan_dev::plan_capacity(L, E, cap, counts, seg_offsets, seg_expert, seg_of_bin, r2t, bal);
-  else
-    plan_dev::plan_segments(L, E, bin_ways, ways, n_hot, c, counts, seg_offsets, seg_expert,
-                            seg_of_bin, bal);
+  const int S =
+      cap > 0 ? plan_dev::plan_capacity(L, E, cap, counts, seg_offsets, seg_expert, seg_of_bin,
+                                        r2t, bal)
+              : plan_dev::plan_segments(L, E, bin_ways, ways, n_hot, c, counts, seg_offsets,
+                                        seg_expert, seg_of_bin, bal);
+  // the bin totals are spent: L.tot becomes the next free row of each segment
+  int* run = L.tot;
+  for (int s = tid; s < S; s += 1024) run[s] = L.seg_off[s];
   for (int a = tid; a < A; a += 1024)
     id_a[a] = seg_of_bin[id_a[a] * bin_ways + (a / k) % bin_ways];
   __syncthreads();
-  for (int a = tid; a < A; a += 1024) {
-    const int sa = id_a[a];
-    int before = 0;
-    for (int b = 0; b < a; ++b) before += id_a[b] == sa;
-    if (cap > 0 && before >= cap) {   // fixed capacity: the expert's slots are full
-      a2r[a] = -1;
-      continue;
+  // one wave ranks every assignment, 64 at a time in assignment order
+  if (wv == 0) {
+    const int nbits = plan_dev::segment_bits(S);
+    for (int a0 = 0; a0 < A; a0 += 64) {
+      const int a = a0 + lane;
+      const int sa = a < A ? id_a[a] : -1;
+      const int row = plan_dev::wave_rank_round(sa, nbits, run);
+      if (a >= A) continue;
+      if (cap > 0 && row - L.seg_off[sa] >= cap) {   // fixed capacity: the expert's slots are full
+        a2r[a] = -1;
+        continue;
+      }
+      a2r[a] = row;
+      r2t[row] = a / k;
+      row_w[row] = w_a[a];
     }
-    const int row = L.seg_off[sa] + before;
-    a2r[a] = row;
-    r2t[row] = a / k;
-    row_w[row] = w_a[a];
   }
 }
 
@@ -293,15 +327,35 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x
   for (; c < row_chunks; c += 64) dst[c] = src[c];
 }
 
-template <int VPL>
+template <int G, int VPL>
 void launch_small_vpl(const moe_config& c, const float* logits, int32_t* ids, float* w,
                       int32_t* counts, int32_t* seg_offsets, int32_t* seg_expert, int32_t* a2r,
                       int32_t* r2t, float* row_w, float* bal, hipStream_t s) {
-  route_permute_small_kernel<VPL><<<1, 1024, 0, s>>>(
+  route_permute_small_kernel<G, VPL><<<1, 1024, 0, s>>>(
       logits, c.T, c.E, c.k, c.score, c.n_group, c.topk_group, c.group_score_topn,
       c.renormalize, bin_ways(c), split_ways(c), c.n_hot_split, c.split_c_permille,
       (int)capacity(c), ids, w, counts, seg_offsets, seg_expert, a2r, r2t,
       row_w, bal);
+}
+
+// Kernel variant for G lanes per token (0: one wave per token) and ceil(E / lanes)
+// logits per lane.
+template <int G>
+void launch_small_g(const moe_config& c, const float* logits, int32_t* ids, float* w,
+                    int32_t* counts, int32_t* seg_offsets, int32_t* seg_expert, int32_t* a2r,
+                    int32_t* r2t, float* row_w, float* bal, hipStream_t s) {
+  const int lanes = G > 0 ? G : 64;
+  const int vpl = (c.E + lanes - 1) / lanes;
+  if (vpl <= 1)
+    launch_small_vpl<G, 1>(c, logits, ids, w, counts, seg_offsets, seg_expert, a2r, r2t, row_w, bal, s);
+  else if (vpl <= 2)
+    launch_small_vpl<G, 2>(c, logits, ids, w, counts, seg_offsets, seg_expert, a2r, r2t, row_w, bal, s);
+  else if (vpl <= 4)
+    launch_small_vpl<G, 4>(c, logits, ids, w, counts, seg_offsets, seg_expert, a2r, r2t, row_w, bal, s);
+  else if (vpl <= 8)
+    launch_small_vpl<G, 8>(c, logits, ids, w, counts, seg_offsets, seg_expert, a2r, r2t, row_w, bal, s);
+  else
+    launch_small_vpl<G, 16>(c, logits, ids, w, counts, seg_offsets, seg_expert, a2r, r2t, row_w, bal, s);
 }
 
 }  // namespace
@@ -310,17 +364,13 @@ void launch_route_permute_small(const moe_config& c, const float* logits, int32_
                                 float* w, int32_t* counts, int32_t* seg_offsets,
                                 int32_t* seg_expert, int32_t* a2r, int32_t* r2t, float* row_w,
                                 float* bal, hipStream_t s) {
-  const int vpl = (c.E + 63) / 64;
-  if (vpl <= 1)
-    launch_small_vpl<1>(c, logits, ids, w, counts, seg_offsets, seg_expert, a2r, r2t, row_w, bal, s);
-  else if (vpl <= 2)
-    launch_small_vpl<2>(c, logits, ids, w, counts, seg_offsets, seg_expert, a2r, r2t, row_w, bal, s);
-  else if (vpl <= 4)
-    launch_small_vpl<4>(c, logits, ids, w, counts, seg_offsets, seg_expert, a2r, r2t, row_w, bal, s);
-  else if (vpl <= 8)
-    launch_small_vpl<8>(c, logits, ids, w, counts, seg_offsets, seg_expert, a2r, r2t, row_w, bal, s);
+  const int g = route_dev::flat_group_lanes(c.E, c.k, c.n_group);
+  if (g == 16)
+    launch_small_g<16>(c, logits, ids, w, counts, seg_offsets, seg_expert, a2r, r2t, row_w, bal, s);
+  else if (g == 32)
+    launch_small_g<32>(c, logits, ids, w, counts, seg_offsets, seg_expert, a2r, r2t, row_w, bal, s);
   else
-    launch_small_vpl<16>(c, logits, ids, w, counts, seg_offsets, seg_expert, a2r, r2t, row_w, bal, s);
+    launch_small_g<0>(c, logits, ids, w, counts, seg_offsets, seg_expert, a2r, r2t, row_w, bal, s);
 }
 
 void launch_permute(const moe_config& c, const void* x, const int32_t* ids, void* x_perm,
@@ -330,17 +380,17 @@ void launch_permute(const moe_config& c, const void* x, const int32_t* ids, void
   const int A = c.T * c.k;
   const int bw = bin_ways(c);
   const int chunk = chunk_len(A);
-  const int nb = num_chunks(A);
+  const int nb = num_chunks(A), ns = chunk_stride(A);
   const int S = num_segments(c);
   int32_t* cnt_bin = reinterpret_cast<int32_t*>(ws + L.cnt_bin);
   int32_t* blk_off = reinterpret_cast<int32_t*>(ws + L.blk_off);
   int32_t* seg_of_bin = reinterpret_cast<int32_t*>(ws + L.seg_of_bin);
-  hist_kernel<<<nb, 256, 0, s>>>(ids, A, c.k, c.E, bw, chunk, nb, cnt_bin);
+  hist_kernel<<<nb, 256, 0, s>>>(ids, A, c.k, c.E, bw, chunk, ns, cnt_bin);
   const int cap = (int)capacity(c);
-  plan_kernel<<<1, 1024, 0, s>>>(cnt_bin, nb, c.E, bw, split_ways(c), c.n_hot_split,
+  plan_kernel<<<1, 1024, 0, s>>>(cnt_bin, nb, ns, c.E, bw, split_ways(c), c.n_hot_split,
                                  c.split_c_permille, cap, counts, seg_offsets, seg_expert,
                                  seg_of_bin, blk_off, r2t, bal);
-  rank_kernel<<<nb, 64, S * sizeof(int), s>>>(ids, A, c.k, c.E, bw, chunk, nb, S, cap,
+  rank_kernel<<<nb, 64, S * sizeof(int), s>>>(ids, A, c.k, c.E, bw, chunk, ns, S, cap,
                                               seg_of_bin, blk_off, a2r, r2t, w, row_w);
   if (!x_perm) return;  // the caller reads rows of x through row_to_token
   const int eb = c.act_dtype == MOE_DT_F32 ? 4 : 2;

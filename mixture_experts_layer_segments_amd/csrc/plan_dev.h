@@ -5,19 +5,15 @@
 // function here is called by all 1024 threads of one workgroup.
 #pragma once
 
+#include <type_traits>
+
 #include "moe_internal.h"
+#include "wave_dev.h"
 
 namespace moe {
 namespace plan_dev {
 
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int o = __shfl_up(v, off);
-    if (lane >= off) v += o;
-  }
-  return v;
-}
+__device__ __forceinline__ int wave_incl_scan(int v, int) { return wave_dev::incl_scan(v); }
 
 // In-place exclusive scan of n <= 4096 ints in LDS by 1024 threads; returns
 // the total to every thread.
@@ -46,6 +42,36 @@ __device__ inline int block_exclusive_scan(int* data, int n, int* wave_tot) {
   const int total = wave_tot[16];
   __syncthreads();
   return total;
+}
+
+// Bits of a segment number below S (0 for S <= 1).
+__device__ __forceinline__ int segment_bits(int S) {
+  int n = 0;
+  while ((1 << n) < S) ++n;
+  return n;
+}
+
+// Stable rows of one round of 64 assignments (segment `seg` per lane, -1 for
+// none) against run[] (LDS, the next free row of each segment): the lanes of
+// one segment take consecutive rows in lane order, and run[] of the segment
+// advances by their number.  A lane's peers (lanes of its segment) come from
+// one ballot per bit of the segment number -- the lanes that agree with it on
+// every bit -- so all segments of the round are ranked at once.  Returns the
+// row, -1 for seg < 0.  Called by a whole wave.
+__device__ __forceinline__ int wave_rank_round(int seg, int nbits, int* run) {
+  const int lane = threadIdx.x & 63;
+  uint64_t peers = __ballot(seg >= 0);
+  for (int j = 0; j < nbits; ++j) {
+    const bool bit = (seg >> j) & 1;
+    const uint64_t bj = __ballot(bit);
+    peers &= bit ? bj : ~bj;
+  }
+  if (seg < 0) return -1;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  const int before = __popcll(peers & below);
+  const int base = run[seg];
+  if (before == 0) run[seg] = base + __popcll(peers);
+  return base + before;
 }
 
 // LDS scratch of plan_segments, declared by the calling kernel.
@@ -87,11 +113,8 @@ __device__ inline void balancedness(PlanLds& L, int E, float* __restrict__ bal) 
     mx = max(mx, L.cnt_e[e]);
     sm += L.cnt_e[e];
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    mx = max(mx, __shfl_xor(mx, off));
-    sm += __shfl_xor(sm, off);
-  }
+  mx = wave_dev::max(mx);
+  sm = wave_dev::sum(sm);
   if (lane == 0) {
     L.red[0][wv] = mx;
     L.red[1][wv] = sm;
@@ -132,18 +155,31 @@ __device__ inline int plan_segments(PlanLds& L, int E, int bin_ways, int ways, i
   __syncthreads();
 
   const bool split = n_hot > 0 && ways > 1;
-  for (int e = tid; e < E; e += 1024) {
-    int nseg = 1;
-    if (split) {
-      const int ce = L.cnt_e[e];
-      int rank = 0;
-      for (int o = 0; o < E; ++o) {
-        const int co = L.cnt_e[o];
-        rank += (co > ce) || (co == ce && o < e);
+  if (split) {
+    // rank of each expert among the counts (higher first, lower id on a
+    // tie): G adjacent lanes share an expert, each comparing every G-th
+    // other expert, and their partial ranks are summed in registers
+    auto hot_ranks = [&](auto g_tag) {
+      constexpr int G = decltype(g_tag)::value;
+      for (int e0 = 0; e0 < E; e0 += 1024 / G) {
+        const int e = e0 + tid / G;
+        const int ce = e < E ? L.cnt_e[e] : 0;
+        int rank = 0;
+        if (e < E)
+          for (int o = tid % G; o < E; o += G) {
+            const int co = L.cnt_e[o];
+            rank += (co > ce) || (co == ce && o < e);
+          }
+        rank = wave_dev::group_sum<G>(rank);
+        if (e < E && tid % G == 0) L.seg_first[e] = rank < n_hot ? ways : 1;
       }
-      if (rank < n_hot) nseg = ways;
-    }
-    L.seg_first[e] = nseg;
+    };
+    if (E <= 64) hot_ranks(std::integral_constant<int, 16>{});
+    else if (E <= 128) hot_ranks(std::integral_constant<int, 8>{});
+    else if (E <= 256) hot_ranks(std::integral_constant<int, 4>{});
+    else hot_ranks(std::integral_constant<int, 2>{});
+  } else {
+    for (int e = tid; e < E; e += 1024) L.seg_first[e] = 1;
   }
   __syncthreads();
   const int S = block_exclusive_scan(L.seg_first, E, L.wave_tot);

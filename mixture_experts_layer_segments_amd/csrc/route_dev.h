@@ -27,17 +27,77 @@ __device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
   return av > bv || (av == bv && ai < bi);
 }
 
-// Wave-wide arg-max of (value desc, id asc); every lane returns the winner.
-__device__ __forceinline__ void wave_argmax(float& v, int& id) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    float ov = __shfl_xor(v, off);
-    int oi = __shfl_xor(id, off);
-    if (better(ov, oi, v, id)) {
-      v = ov;
-      id = oi;
-    }
+__device__ __forceinline__ void take_better(float& v, int& id, float ov, int oi) {
+  if (better(ov, oi, v, id)) {
+    v = ov;
+    id = oi;
   }
+}
+
+// One reduction step with the partner lane a DPP row permutation names.
+template <int CTRL>
+__device__ __forceinline__ void dpp_step(float& v, int& id) {
+  const float ov = __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+  const int oi = __builtin_amdgcn_update_dpp(0, id, CTRL, 0xF, 0xF, false);
+  take_better(v, id, ov, oi);
+}
+
+// One step with the lane 16 (ROW32 false) or 32 (true) lanes away, by the
+// gfx950 row-swap moves: the pair they return holds this lane's own value and
+// its partner's, so taking the better of both is the partner step.  (Each
+// half of the result is copied into a plain integer before its bit cast:
+// bit-casting an element of the builtin's result directly reads element 0.)
+template <bool ROW32>
+__device__ __forceinline__ void swap_step(float& v, int& id) {
+  const uint32_t vb = __builtin_bit_cast(uint32_t, v), ib = (uint32_t)id;
+  uint32_t v0, v1, i0, i1;
+  if constexpr (ROW32) {
+    const auto a = __builtin_amdgcn_permlane32_swap(vb, vb, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(ib, ib, false, false);
+    v0 = a[0]; v1 = a[1]; i0 = b[0]; i1 = b[1];
+  } else {
+    const auto a = __builtin_amdgcn_permlane16_swap(vb, vb, false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(ib, ib, false, false);
+    v0 = a[0]; v1 = a[1]; i0 = b[0]; i1 = b[1];
+  }
+  take_better(v, id, __builtin_bit_cast(float, v0), (int)i0);
+  take_better(v, id, __builtin_bit_cast(float, v1), (int)i1);
+}
+
+// Wave-wide arg-max of (value desc, id asc); every lane returns the winner.
+// The partners double the reach each step -- lane l ^ 1, l ^ 2 (quad
+// permutations), the mirrored lane of its 8-lane half row and of its 16-lane
+// row, then the rows 16 and 32 lanes away -- all register-to-register moves
+// (a shuffle by index would go through the LDS unit and wait on it six times
+// per arg-max).  The order is total, so the winner is the same whatever the
+// reduction order.
+__device__ __forceinline__ void wave_argmax(float& v, int& id) {
+  dpp_step<0xB1>(v, id);    // quad_perm [1,0,3,2]
+  dpp_step<0x4E>(v, id);    // quad_perm [2,3,0,1]
+  dpp_step<0x141>(v, id);   // row_half_mirror
+  dpp_step<0x140>(v, id);   // row_mirror
+  swap_step<false>(v, id);
+  swap_step<true>(v, id);
+}
+
+// Lane `src` (wave-uniform) of x, to every lane.
+__device__ __forceinline__ float lane_value(float x, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), src));
+}
+__device__ __forceinline__ double lane_value(double x, int src) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, src);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), src);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum of x over lanes 0 .. n-1 (n wave-uniform, at most 64), in lane order,
+// to every lane.
+__device__ __forceinline__ double lanes_sum(double x, int n) {
+  double s = lane_value(x, 0);
+  for (int j = 1; j < n; ++j) s += lane_value(x, j);
+  return s;
 }
 
 __device__ __forceinline__ double wave_sum(double x) {
@@ -100,13 +160,14 @@ __device__ __forceinline__ void route_token_vals(const float (&vin)[VPL], int E,
           }
         }
         wave_argmax(bv, bi);
+        bi = __builtin_amdgcn_readfirstlane(bi);   // the same in every lane
         if (bi == kNoId) break;  // group smaller than topn
         const int slot = bi >> 6, owner = bi & 63;
         float mine = 0.0f;
 #pragma unroll
         for (int i = 0; i < VPL; ++i)
           if (i == slot) mine = s32[i];
-        acc = acc + __shfl(mine, owner);
+        acc = acc + lane_value(mine, owner);
         if (lane == owner) {
 #pragma unroll
           for (int i = 0; i < VPL; ++i)
@@ -122,6 +183,7 @@ __device__ __forceinline__ void route_token_vals(const float (&vin)[VPL], int E,
       float bv = (lane < n_group && !gtaken) ? my_gs : -INFINITY;
       int bi = (lane < n_group && !gtaken) ? lane : kNoId;
       wave_argmax(bv, bi);
+      bi = __builtin_amdgcn_readfirstlane(bi);
       if (bi == kNoId) break;
       kept |= 1ull << bi;
       if (lane == bi) gtaken = true;
@@ -148,6 +210,7 @@ __device__ __forceinline__ void route_token_vals(const float (&vin)[VPL], int E,
       }
     }
     wave_argmax(bv, bi);
+    bi = __builtin_amdgcn_readfirstlane(bi);
     if (lane == j) {
       my_id = bi;
       my_v = bv;
@@ -160,17 +223,17 @@ __device__ __forceinline__ void route_token_vals(const float (&vin)[VPL], int E,
     }
   }
 
-  // weights in fp64, rounded once
-  const double top0 = (double)__shfl(my_v, 0);
+  // weights in fp64, rounded once (the winners sit in lanes 0 .. k-1)
+  const double top0 = (double)lane_value(my_v, 0);
   double p = 0.0;
   if (score == MOE_SCORE_SIGMOID) {
     p = lane < k ? 1.0 / (1.0 + exp(-(double)my_v)) : 0.0;
-    if (renorm) p = p / wave_sum(p);
+    if (renorm) p = p / lanes_sum(p, k);
   } else {
     p = lane < k ? exp((double)my_v - top0) : 0.0;
     double denom;
     if (renorm) {
-      denom = wave_sum(p);
+      denom = lanes_sum(p, k);
     } else {
       double part = 0.0;
 #pragma unroll
@@ -194,6 +257,140 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
   load_logits<VPL>(row, E, lane, v);
   route_token_vals<VPL>(v, E, k, score, n_group, topk_group, topn, renorm, lane, my_id_out,
                         my_w_out);
+}
+
+
+// ---- flat routing by lane groups ----
+// Flat top-k (one expert group) on G = 16 or 32 lanes per token, 64 / G
+// tokens per wave: lane j of a group holds experts j + G i (i < VPL), each
+// arg-max round reduces inside the group (the first log2 G steps of
+// wave_argmax), and the weights of all the wave's tokens are formed together.
+// The winners and their order are those of route_token_vals (the order is
+// total); the weights' fp64 sum runs in another order (within rounding of the
+// same value).
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, true);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, true);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// x of the lane 16 lanes away (see swap_step).
+__device__ __forceinline__ double swap16_f64(double x) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)b, hi = (uint32_t)(b >> 32);
+  const auto rl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto rh = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  const uint32_t l0 = rl[0], l1 = rl[1], h0 = rh[0], h1 = rh[1];
+  const bool odd_row = threadIdx.x & 16;
+  return __builtin_bit_cast(double, ((uint64_t)(odd_row ? h0 : h1) << 32) | (odd_row ? l0 : l1));
+}
+
+template <int G>
+__device__ __forceinline__ void group_argmax(float& v, int& id) {
+  static_assert(G == 16 || G == 32, "a row or two rows per token");
+  dpp_step<0xB1>(v, id);
+  dpp_step<0x4E>(v, id);
+  dpp_step<0x141>(v, id);
+  dpp_step<0x140>(v, id);
+  if constexpr (G == 32) swap_step<false>(v, id);
+}
+
+template <int G>
+__device__ __forceinline__ double group_sum_f64(double x) {
+  x += dpp_f64<0xB1>(x);
+  x += dpp_f64<0x4E>(x);
+  x += dpp_f64<0x141>(x);
+  x += dpp_f64<0x140>(x);
+  if constexpr (G == 32) x += swap16_f64(x);
+  return x;
+}
+
+// This lane's logits of the token its group routes (`row`, null past the
+// batch: -inf everywhere).
+template <int G, int VPL>
+__device__ __forceinline__ void load_logits_group(const float* __restrict__ row, int E, int j,
+                                                  float (&v)[VPL]) {
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = j + G * i;
+    v[i] = (row && e < E) ? row[e] : -INFINITY;
+  }
+}
+
+// Routes the token of this lane's group from its loaded logits; lane j < k
+// of the group returns slot j.
+template <int G, int VPL>
+__device__ __forceinline__ void route_group_vals(const float (&vin)[VPL], int E, int k, int score,
+                                                 int renorm, int j, int& my_id_out,
+                                                 float& my_w_out) {
+  float v[VPL];
+  bool avail[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    float x = vin[i];
+    if (x != x) x = -INFINITY;  // a NaN logit never wins over a number
+    v[i] = x;
+    avail[i] = j + G * i < E;
+  }
+  int my_id = 0;
+  float my_v = 0.0f, top0 = 0.0f;
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int bi = kNoId;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = j + G * i;
+      if (avail[i] && better(v[i], e, bv, bi)) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+    group_argmax<G>(bv, bi);
+    if (r == 0) top0 = bv;
+    if (j == r) {
+      my_id = bi;
+      my_v = bv;
+    }
+    if (j == bi % G) {
+      const int slot = bi / G;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i)
+        if (i == slot) avail[i] = false;
+    }
+  }
+  // weights in fp64, rounded once (the winners sit in lanes 0 .. k-1 of the group)
+  double p = 0.0;
+  if (score == MOE_SCORE_SIGMOID) {
+    p = j < k ? 1.0 / (1.0 + exp(-(double)my_v)) : 0.0;
+    if (renorm) p = p / group_sum_f64<G>(p);
+  } else {
+    p = j < k ? exp((double)my_v - (double)top0) : 0.0;
+    double denom;
+    if (renorm) {
+      denom = group_sum_f64<G>(p);
+    } else {
+      double part = 0.0;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i)
+        if (j + G * i < E) part += exp((double)v[i] - (double)top0);
+      denom = group_sum_f64<G>(part);
+    }
+    p = p / denom;
+  }
+  my_id_out = my_id;
+  my_w_out = (float)p;
+}
+
+// Lanes per token of the flat routing (0: one wave per token, the general
+// path): the fewest that hold the k winners, with at most 16 logits per lane.
+inline int flat_group_lanes(int E, int k, int n_group) {
+  if (n_group > 1) return 0;
+  if (k <= 16 && E <= 16 * 16) return 16;
+  if (k <= 32 && E <= 16 * 32) return 32;
+  return 0;
 }
 
 }  // namespace route_dev
