@@ -112,7 +112,7 @@ typedef struct moe_config {
 /* Size limits (MOE_ERR_UNSUPPORTED beyond them): T*k <= 2^30; each of
  * T*k*H, T*k*I, T*shared_I, 2*I*H and 2*shared_I*H below 2^31 elements (the
  * kernels address every matrix with 32-bit byte offsets); bf16 needs H, I
- * and shared_I to be multiples of 64, fp32 needs H % 4 == 0. */
+ * and shared_I to be multiples of 8, fp32 needs H % 4 == 0. */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* moe_status_string(moe_status s);
@@ -200,7 +200,7 @@ moe_status moe_permute(const moe_config* cfg, const void* x, const int32_t* topk
  *   w2          [E, H, I]  act_dtype, W_down[e]^T.
  *   row_scale   [R] fp32 indexed by row, or NULL for 1.0.
  *   y_perm      [R, H] out (rows of computed segments).
- * bf16 needs H and I multiples of 64; all pointers 16-byte aligned. */
+ * bf16 needs H and I multiples of 8; all pointers 16-byte aligned. */
 moe_status moe_grouped_ffn(const moe_config* cfg, const void* x_perm,
                            const int32_t* seg_offsets, const int32_t* seg_expert,
                            const void* w13, const void* w2, const float* row_scale,

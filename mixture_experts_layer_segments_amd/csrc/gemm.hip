@@ -232,21 +232,61 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 // of the slot (bf16 weights: 128-byte row pieces; E4M3 codes: 64-byte
 // pieces, 16 rows per block).  `voff` holds each lane's byte offset of its
 // 16 bytes at k = 0; the stage's K offset goes in the scalar offset.
+//
+// K tail (bf16, K not a multiple of BK): in the last stage only the first
+// `kval` 16-byte chunks of each row piece lie inside K; the lanes that copy
+// a chunk past it take an offset past the buffer's range, so both operands
+// hold zeros there and add nothing.  (KCH, KCHB: chunks per A / B row piece;
+// RPB, RPBB: rows per 1 KiB block.)
 template <int LPI, int NI, int STAGES, int STAGE_CH, int A_CH, int BK, int A_IT, int WB, int AB,
-          int B_AUX = 0>
+          int B_AUX = 0, int KCH = 8, int KCHB = 8, int BM = 0>
 __device__ __forceinline__ void ring_issue(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                           const uint32_t* voff, u32x4* ring, int kt, int wv) {
+                                           const uint32_t* voff, u32x4* ring, int kt, int wv,
+                                           int kval = 64) {
   u32x4* slot = ring + (kt % STAGES) * STAGE_CH;
+  if (kval >= KCH && kval >= KCHB) {
 #pragma unroll
-  for (int i = 0; i < LPI; ++i) {
-    if (i < A_IT)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MOE_LDS_PTR(slot + (i * NI + wv) * 64), 16,
-                                               voff[i], kt * BK * AB, 0, 0);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rb, MOE_LDS_PTR(slot + A_CH + ((i - A_IT) * NI + wv) * 64), 16, voff[i],
-          kt * BK * WB, 0, B_AUX);
+    for (int i = 0; i < LPI; ++i) {
+      if (i < A_IT)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MOE_LDS_PTR(slot + (i * NI + wv) * 64), 16,
+                                                 voff[i], kt * BK * AB, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, MOE_LDS_PTR(slot + A_CH + ((i - A_IT) * NI + wv) * 64), 16, voff[i],
+            kt * BK * WB, 0, B_AUX);
+    }
+  } else {
+    const int lane = threadIdx.x & 63;
+    constexpr int RPB = 64 / KCH, RPBB = 64 / KCHB;
+#pragma unroll
+    for (int i = 0; i < LPI; ++i) {
+      if (i < A_IT) {
+        const int row = (i * NI + wv) * RPB + lane / KCH;
+        const int kc = (lane % KCH) ^ swz<KCH>(row);
+        const uint32_t off = kc < kval ? voff[i] : 0xFFFFFFF0u - (uint32_t)(kt * BK * AB);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MOE_LDS_PTR(slot + (i * NI + wv) * 64), 16,
+                                                 off, kt * BK * AB, 0, 0);
+      } else {
+        const int br = ((i - A_IT) * NI + wv) * RPBB + lane / KCHB;
+        const int kc = (lane % KCHB) ^ swz<KCHB>(BM + br);
+        const uint32_t off = kc < kval ? voff[i] : 0xFFFFFFF0u - (uint32_t)(kt * BK * WB);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, MOE_LDS_PTR(slot + A_CH + ((i - A_IT) * NI + wv) * 64), 16, off, kt * BK * WB,
+            0, B_AUX);
+      }
+    }
   }
+}
+
+// 16-byte chunks of stage kt's row pieces that lie inside K (64, i.e. all of
+// them, for a full stage).
+// (KTAIL false: K is a multiple of BK and every stage is full -- the launches
+// take the K-tail variant only when it is not.)
+template <int BK, int AB, bool KTAIL>
+__device__ __forceinline__ int ring_stage_chunks(int K, int kt) {
+  if constexpr (!KTAIL) return 64;
+  const int left = K - kt * BK;
+  return left >= BK ? 64 : left * AB / 16;
 }
 
 // Ring-tile geometry shared by the per-tile body and the kernels that size
@@ -472,28 +512,31 @@ __device__ __forceinline__ void act_scales_store(ActScales<BM, NTHR, RUN>& a, ui
 constexpr int kActRun = 16;   // activation-scale loads in flight per thread
 
 // The first STAGES - 1 stages of a tile's ring (issuing waves).
-template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
+template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES,
+          bool KTAIL>
 __device__ __forceinline__ void ring_prologue(
     const RingTileState<RingCfg<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>::LPI>& t,
     u32x4* ring) {
   using C = RingCfg<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>;
   const int wvs = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int KT = t.P->K / BK;
+  const int K = t.P->K, KT = KTAIL ? (K + BK - 1) / BK : K / BK;
   if (wvs >= C::NI) return;
 #pragma unroll
   for (int st = 0; st < STAGES - 1; ++st) {
     if (st >= KT) break;
+    const int kval = ring_stage_chunks<BK, C::AB, KTAIL>(K, st);
     if (C::B_AUX && t.stream)
-      ring_issue<C::LPI, C::NI, STAGES, C::STAGE_CH, C::A_CH, BK, C::A_IT, C::WB, C::AB, C::B_AUX>(
-          t.ra, t.rb, t.voff, ring, st, wvs);
+      ring_issue<C::LPI, C::NI, STAGES, C::STAGE_CH, C::A_CH, BK, C::A_IT, C::WB, C::AB, C::B_AUX,
+                 C::KCH, C::KCHB, BM>(t.ra, t.rb, t.voff, ring, st, wvs, kval);
     else
-      ring_issue<C::LPI, C::NI, STAGES, C::STAGE_CH, C::A_CH, BK, C::A_IT, C::WB, C::AB, 0>(
-          t.ra, t.rb, t.voff, ring, st, wvs);
+      ring_issue<C::LPI, C::NI, STAGES, C::STAGE_CH, C::A_CH, BK, C::A_IT, C::WB, C::AB, 0, C::KCH,
+                 C::KCHB, BM>(t.ra, t.rb, t.voff, ring, st, wvs, kval);
   }
 }
 
 // The K loop of one tile into `acc`.
-template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
+template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES,
+          bool KTAIL>
 __device__ __forceinline__ void ring_kloop(
     const RingTileState<RingCfg<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>::LPI>& t,
     u32x4* ring, const float* scl,
@@ -525,7 +568,7 @@ __device__ __forceinline__ void ring_kloop(
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int K = t.P->K;
-  const int KT = K / BK;
+  const int KT = KTAIL ? (K + BK - 1) / BK : K / BK;   // (KTAIL: the last stage is partial)
   const int KB = K / 128;               // WF: K blocks of the scales
   // WF: the scale group of this wave's weight fragments (GEMM 1: gate
   // fragments use group 0, up fragments group 1)
@@ -537,12 +580,13 @@ __device__ __forceinline__ void ring_kloop(
     if (WF) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the tile's scales are written
     raw_barrier();
     if (kt + STAGES - 1 < KT && wvs < C::NI) {
+      const int kval = ring_stage_chunks<BK, C::AB, KTAIL>(K, kt + STAGES - 1);
       if (C::B_AUX && t.stream)
-        ring_issue<LPI, C::NI, STAGES, STAGE_CH, A_CH, BK, C::A_IT, C::WB, C::AB, C::B_AUX>(
-            t.ra, t.rb, t.voff, ring, kt + STAGES - 1, wvs);
+        ring_issue<LPI, C::NI, STAGES, STAGE_CH, A_CH, BK, C::A_IT, C::WB, C::AB, C::B_AUX, KCH,
+                   KCHB, BM>(t.ra, t.rb, t.voff, ring, kt + STAGES - 1, wvs, kval);
       else
-        ring_issue<LPI, C::NI, STAGES, STAGE_CH, A_CH, BK, C::A_IT, C::WB, C::AB, 0>(
-            t.ra, t.rb, t.voff, ring, kt + STAGES - 1, wvs);
+        ring_issue<LPI, C::NI, STAGES, STAGE_CH, A_CH, BK, C::A_IT, C::WB, C::AB, 0, KCH, KCHB,
+                   BM>(t.ra, t.rb, t.voff, ring, kt + STAGES - 1, wvs, kval);
     }
     const u32x4* slot = ring + (kt % STAGES) * STAGE_CH;
     if constexpr (WF == 2) {
@@ -877,7 +921,7 @@ __device__ __forceinline__ void ring_store_q(
 // barrier after which the ring and the scales are free (the previous tile's
 // output is out).
 template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES,
-          typename Hook>
+          bool KTAIL, typename Hook>
 __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles_l, int tile,
                                           u32x4* ring, float* scl, Hook after_issue) {
   using C = RingCfg<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>;
@@ -892,16 +936,16 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
     const int KB = cur.P->K / 128;
     ActScales<BM, NTHR, kActRun> as;
     act_scales_load(cur, KB, as);
-    ring_prologue<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, ring);
+    ring_prologue<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES, KTAIL>(cur, ring);
     act_scales_store(as, reinterpret_cast<uint8_t*>(scl + 2 * KB), KB);
   } else {
-    ring_prologue<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, ring);
+    ring_prologue<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES, KTAIL>(cur, ring);
   }
   after_issue();
   u32x2 outv[C::TM * NPM];
   {
     f32x4 acc[C::TM][C::TN];
-    ring_kloop<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(cur, ring, scl, acc);
+    ring_kloop<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES, KTAIL>(cur, ring, scl, acc);
     // this tile's output scales (GEMM 2)
     float rsc[C::TM];
 #pragma unroll
@@ -919,7 +963,9 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& args, const int* tiles
 }
 
 // Persistent schedule: workgroup l (XCD-remapped) takes tiles l, l + G, ...
-template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES, int OCC>
+// KTAIL: some problem's K is not a multiple of BK (bf16 only).
+template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES, int OCC,
+          bool KTAIL>
 __global__ __launch_bounds__(NTHR, OCC) void gemm_ring_kernel(GemmArgs args) {
   // The ring and the tile table are this kernel's only LDS objects: with a
   // third one the compiler can no longer tell the operand reads from the
@@ -935,8 +981,8 @@ __global__ __launch_bounds__(NTHR, OCC) void gemm_ring_kernel(GemmArgs args) {
   float* scl = reinterpret_cast<float*>(tiles_l + args.n_seg_total + 1);
   const int G = gridDim.x;
   for (int tile = xcd_logical(blockIdx.x, G); tile < total; tile += G)
-    ring_tile<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES>(args, tiles_l, tile, ring, scl,
-                                                            [] {});
+    ring_tile<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES, KTAIL>(args, tiles_l, tile, ring,
+                                                                   scl, [] {});
 }
 
 // Ring-tile shapes: BM, BN, BK, threads, waves along M, ring stages.  "big"
@@ -1356,7 +1402,16 @@ inline size_t ring_dyn_lds(const GemmArgs& g, int wf, int bm) {
 template <int MODE, int WF, int BM, int BN, int BK, int NTHR, int WAVES_M, int STAGES>
 void launch_ring(const GemmArgs& g, hipStream_t s) {
   const size_t dyn = ring_dyn_lds(g, WF, BM);
-  auto k = gemm_ring_kernel<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES, 1>;
+  bool tail = false;
+  for (int p = 0; p < g.n_probs; ++p) tail = tail || g.p[p].K % BK != 0;
+  if constexpr (WF == 0) {
+    if (tail) {
+      auto k = gemm_ring_kernel<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES, 1, true>;
+      k<<<persistent_grid(k, dyn, 1, NTHR), NTHR, dyn, s>>>(g);
+      return;
+    }
+  }
+  auto k = gemm_ring_kernel<MODE, WF, BM, BN, BK, NTHR, WAVES_M, STAGES, 1, false>;
   k<<<persistent_grid(k, dyn, 1, NTHR), NTHR, dyn, s>>>(g);
 }
 

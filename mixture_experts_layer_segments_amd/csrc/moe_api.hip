@@ -118,7 +118,8 @@ moe_status check_config(const moe_config* c) {
       (int64_t)2 * c->I * c->H >= lim || (int64_t)2 * c->shared_I * c->H >= lim)
     return MOE_ERR_UNSUPPORTED;
   if (c->act_dtype == MOE_DT_BF16) {
-    if (c->H % 64 || c->I % 64 || c->shared_I % 64) return MOE_ERR_UNSUPPORTED;
+    // rows of 16-byte chunks (the GEMM copies, gather and combine move 8 bf16)
+    if (c->H % 8 || c->I % 8 || c->shared_I % 8) return MOE_ERR_UNSUPPORTED;
   } else {
     if (c->H % 4) return MOE_ERR_UNSUPPORTED;
   }

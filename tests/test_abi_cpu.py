@@ -88,8 +88,8 @@ def _layer(moe, cfg, ws_bytes=None, **override):
 @pytest.mark.parametrize("field,value,status", [
     ("E", 0, -1), ("k", 0, -1), ("H", -8, -1), ("I", 0, -1), ("T", -1, -1),
     ("k", 65, -2), ("E", 2048, -2), ("act_dtype", 7, -1), ("score", 3, -1),
-    ("n_group", 3, -1), ("split_ways", 9, -2), ("H", 100, -2), ("I", 96, -2),
-    ("shared_I", 32, -2), ("renormalize", 2, -1), ("split_mode", 2, -1),
+    ("n_group", 3, -1), ("split_ways", 9, -2), ("H", 100, -2), ("I", 100, -2),
+    ("shared_I", 36, -2), ("renormalize", 2, -1), ("split_mode", 2, -1),
     ("split_c_permille", -1, -1), ("split_c_permille", 100001, -1),
     ("capacity_factor_permille", -1, -1), ("capacity_factor_permille", 1000001, -1),
     ("H", 1 << 24, -2),   # T*k*H reaches 2^31 elements: beyond 32-bit byte offsets
@@ -100,6 +100,14 @@ def test_bad_config_is_rejected(moe, field, value, status):
     assert moe.lib.moe_route_topk(ctypes.byref(c), FAKE, FAKE, FAKE, None) == status
     assert moe.lib.moe_workspace_size(ctypes.byref(c)) == 0
     assert moe.lib.moe_num_segments(ctypes.byref(c)) == -1
+
+
+@pytest.mark.parametrize("H,I", [(200, 72), (8, 8), (4104, 1544)])
+def test_bf16_sizes_in_multiples_of_8_are_accepted(moe, H, I):
+    """bf16 rows are moved in 16-byte chunks, so H and I need only be
+    multiples of 8 (the GEMM tiles zero the K tail of their last stage)."""
+    c = moe.make_config(mi.WORKLOADS["decode_bf16"].replace(H=H, I=I))
+    assert moe.lib.moe_workspace_size(ctypes.byref(c)) > 0
 
 
 def test_grouped_softmax_and_bad_groups_are_rejected(moe):

@@ -65,6 +65,15 @@ SHAPES = {
                                 capacity_factor_permille=800, seed=32),
     "bf16_capacity_roomy": mi.MoEShape("t20", T=120, H=256, E=8, k=2, I=128, zipf_s=1.0,
                                        capacity_factor_permille=4000, seed=33),
+    # H and I multiples of 8 but not of the 64-deep stage: the last K stage of
+    # each GEMM is partial (128-row tiles; 256-row tiles; a single partial
+    # stage; a shared expert beside the routed ones)
+    "bf16_k_tail_mid": mi.MoEShape("t21", T=300, H=200, E=16, k=4, I=72, zipf_s=1.2, seed=34),
+    "bf16_k_tail_big": mi.MoEShape("t22", T=1100, H=264, E=3, k=1, I=136, zipf_s=1.0, seed=35),
+    "bf16_k_tail_one_stage": mi.MoEShape("t23", T=64, H=8, E=8, k=2, I=16, seed=36),
+    "bf16_k_tail_shared": mi.MoEShape("t24", T=200, H=136, E=32, k=4, I=72, score="sigmoid",
+                                      n_group=4, topk_group=2, shared_I=40, zipf_s=1.0,
+                                      seed=37),
 }
 
 
