@@ -74,6 +74,11 @@ SHAPES = {
     "bf16_k_tail_shared": mi.MoEShape("t24", T=200, H=136, E=32, k=4, I=72, score="sigmoid",
                                       n_group=4, topk_group=2, shared_I=40, zipf_s=1.0,
                                       seed=37),
+    # flat routing on 32 lanes per token: inside the one-workgroup planner
+    # (T*k <= 1024), and flat sigmoid weights through the four-kernel path
+    "bf16_wide_k_small": mi.MoEShape("t25", T=40, H=128, E=64, k=20, I=64, seed=38),
+    "bf16_flat_sigmoid_wide": mi.MoEShape("t26", T=60, H=128, E=40, k=18, I=64, score="sigmoid",
+                                          seed=39),
 }
 
 
@@ -235,8 +240,13 @@ def test_dropped_ids(moe, split_mode):
     assert g["bal"].cpu().numpy()[0] == orc.balancedness(counts)
 
 
+# flat routing runs on 16 lanes per token (k <= 16, E <= 256), 32 lanes
+# (k <= 32, E <= 512) or a whole wave; k equal to the group width, and 1 or 16
+# logits per lane, included
 @pytest.mark.parametrize("E,k,groups,topk_group", [(1024, 32, 1, 1), (100, 7, 1, 1),
-                                                   (256, 8, 64, 16), (130, 3, 1, 1)])
+                                                   (256, 8, 64, 16), (130, 3, 1, 1),
+                                                   (512, 20, 1, 1), (300, 16, 1, 1),
+                                                   (16, 16, 1, 1), (64, 32, 1, 1)])
 def test_route_extremes(moe, E, k, groups, topk_group):
     score = "sigmoid" if groups > 1 else "softmax"
     cfg = mi.MoEShape("rx", T=77, H=64, E=E, k=k, I=64, score=score, n_group=groups,
