@@ -79,6 +79,15 @@ SHAPES = {
     "bf16_wide_k_small": mi.MoEShape("t25", T=40, H=128, E=64, k=20, I=64, seed=38),
     "bf16_flat_sigmoid_wide": mi.MoEShape("t26", T=60, H=128, E=40, k=18, I=64, score="sigmoid",
                                           seed=39),
+    # many bins and segments: 1024 experts with 4-way parity replicas of the 8
+    # hottest (4096 bins, 1048 segments) through the four-kernel planner and
+    # the one-workgroup one, and a fixed-capacity layout of 2048 segments
+    "bf16_many_segments": mi.MoEShape("t27", T=600, H=64, E=1024, k=4, I=64, zipf_s=1.0,
+                                      n_hot_split=8, split_ways=4, seed=40),
+    "bf16_many_segments_small": mi.MoEShape("t28", T=200, H=64, E=1024, k=4, I=64, zipf_s=1.0,
+                                            n_hot_split=8, split_ways=4, seed=41),
+    "bf16_capacity_many": mi.MoEShape("t29", T=600, H=64, E=1024, k=2, I=64, zipf_s=1.0,
+                                      capacity_factor_permille=1000, seed=42),
 }
 
 

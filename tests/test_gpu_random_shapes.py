@@ -17,8 +17,10 @@ def _random_shape(rng, i):
     E = int(rng.choice([1, 2, 3, 5, 8, 13, 16, 32, 40, 64]))
     k = int(rng.integers(1, min(E, 6) + 1))
     T = int(rng.choice([1, 2, 7, 33, 64, 100, 257, 600, 1100]))
-    H = int(rng.choice([64, 128, 192, 320, 512, 1024]))
-    I = int(rng.choice([64, 128, 192, 256, 512]))
+    # (bf16 sizes in multiples of 8 that are not multiples of the 64-deep
+    # stage take the K-tail variants of the ring tiles)
+    H = int(rng.choice([64, 128, 192, 320, 512, 1024, 72, 200]))
+    I = int(rng.choice([64, 128, 192, 256, 512, 40, 136]))
     if dtype == "f32":
         H = int(rng.choice([4, 12, 64, 100]))
         I = int(rng.choice([3, 16, 70]))
@@ -36,7 +38,7 @@ def _random_shape(rng, i):
     elif rng.random() < 0.3:
         kw["capacity_factor_permille"] = int(rng.choice([500, 1000, 1250, 2000]))
     if dtype == "bf16" and rng.random() < 0.2:
-        kw["shared_I"] = int(rng.choice([64, 128, 256]))
+        kw["shared_I"] = int(rng.choice([64, 128, 256, 24]))
     if rng.random() < 0.2:
         kw["renormalize"] = 0
     return mi.MoEShape(f"rand{i}", T=T, H=H, E=E, k=k, I=I, dtype=dtype, seed=1000 + i,
