@@ -11,7 +11,9 @@
 // logits inside them; weights s_j / sum(s).  Sigmoid and weights are
 // evaluated in fp64 and rounded once, so the fp32 group scores (the values
 // that decide which groups are kept) are the correctly rounded sigmoid in all
-// but vanishingly rare cases.
+// but vanishingly rare cases.  When a group's experts are an aligned block of
+// lanes of one register slot (E / n_group divides 64), all groups are scored
+// at once, and only the groups' best members get a sigmoid.
 #pragma once
 
 #include <math.h>
@@ -81,6 +83,60 @@ __device__ __forceinline__ void wave_argmax(float& v, int& id) {
   swap_step<true>(v, id);
 }
 
+// Arg-max of (value desc, id asc) inside every aligned block of P lanes
+// (P a power of two up to 64), to every lane of the block: the first log2 P
+// steps of wave_argmax.
+template <int P>
+__device__ __forceinline__ void block_argmax(float& v, int& id) {
+  if constexpr (P >= 2) dpp_step<0xB1>(v, id);
+  if constexpr (P >= 4) dpp_step<0x4E>(v, id);
+  if constexpr (P >= 8) dpp_step<0x141>(v, id);
+  if constexpr (P >= 16) dpp_step<0x140>(v, id);
+  if constexpr (P >= 32) swap_step<false>(v, id);
+  if constexpr (P >= 64) swap_step<true>(v, id);
+}
+
+// Group scores when every group of P = E / n_group experts is an aligned
+// block of P lanes of one register slot (P divides 64; expert e = lane + 64 i
+// sits in slot i): each of the topn rounds takes every group's next best
+// member at once, one block arg-max per slot, and lane g (< n_group) adds the
+// sigmoid of its group's member -- the group's round-r winner fetched from
+// the group's lanes -- to its running score.  The score is the same fp32 sum,
+// in the same order of the same correctly rounded fp32 sigmoids, as the
+// one-group-at-a-time loop forms; lane g returns group g's score, the others
+// -inf.
+template <int VPL, int P>
+__device__ __forceinline__ float group_scores_blocked(const float (&v)[VPL],
+                                                      const bool (&avail)[VPL], int n_group,
+                                                      int topn, int lane) {
+  bool taken[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) taken[i] = false;
+  const int src = (lane * P) & 63, src_slot = (lane * P) >> 6;   // lane g's group
+  float acc = 0.0f;
+  for (int r = 0; r < topn; ++r) {
+    float win = 0.0f;
+    bool has = false;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = lane + 64 * i;
+      const bool c = avail[i] && !taken[i];
+      float bv = c ? v[i] : -INFINITY;
+      int bi = c ? e : kNoId;
+      block_argmax<P>(bv, bi);
+      if (bi == e) taken[i] = true;   // the winner's own lane
+      const float wv = __shfl(bv, src);
+      const int wi = __shfl(bi, src);
+      if (src_slot == i) {
+        win = wv;
+        has = wi != kNoId;
+      }
+    }
+    if (lane < n_group && has) acc = acc + (float)(1.0 / (1.0 + exp(-(double)win)));
+  }
+  return lane < n_group ? acc : -INFINITY;
+}
+
 // Lane `src` (wave-uniform) of x, to every lane.
 __device__ __forceinline__ float lane_value(float x, int src) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), src));
@@ -139,11 +195,24 @@ __device__ __forceinline__ void route_token_vals(const float (&vin)[VPL], int E,
 
   if (score == MOE_SCORE_SIGMOID && n_group > 1) {
     const int per = E / n_group;
-    float s32[VPL];
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) s32[i] = (float)(1.0 / (1.0 + exp(-(double)v[i])));
     float my_gs = -INFINITY;  // lane g holds group g's score
-    for (int g = 0; g < n_group; ++g) {
+    switch (per) {
+      case 1: my_gs = group_scores_blocked<VPL, 1>(v, avail, n_group, topn, lane); break;
+      case 2: my_gs = group_scores_blocked<VPL, 2>(v, avail, n_group, topn, lane); break;
+      case 4: my_gs = group_scores_blocked<VPL, 4>(v, avail, n_group, topn, lane); break;
+      case 8: my_gs = group_scores_blocked<VPL, 8>(v, avail, n_group, topn, lane); break;
+      case 16: my_gs = group_scores_blocked<VPL, 16>(v, avail, n_group, topn, lane); break;
+      case 32: my_gs = group_scores_blocked<VPL, 32>(v, avail, n_group, topn, lane); break;
+      case 64: my_gs = group_scores_blocked<VPL, 64>(v, avail, n_group, topn, lane); break;
+      default: break;
+    }
+    // groups that are not lane blocks: one group at a time, over the wave
+    float s32[VPL];
+    if (64 % per != 0) {
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) s32[i] = (float)(1.0 / (1.0 + exp(-(double)v[i])));
+    }
+    for (int g = 0; 64 % per != 0 && g < n_group; ++g) {
       bool used[VPL];
 #pragma unroll
       for (int i = 0; i < VPL; ++i) used[i] = false;
