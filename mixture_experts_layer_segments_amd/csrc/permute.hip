@@ -143,28 +143,49 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ id
                                                   int32_t* __restrict__ r2t,
                                                   const float* __restrict__ w,
                                                   float* __restrict__ row_w) {
-  extern __shared__ int run[];  // [S] next free row of each segment
+  // LDS: run[S], the next free row of each segment; sob[bins], the bin ->
+  // segment map
+  extern __shared__ int lds[];
+  int* run = lds;
+  int* sob = lds + S;
   const int lane = threadIdx.x;
   const int b = blockIdx.x;
-  for (int s = lane; s < S; s += 64) run[s] = blk_off[(size_t)s * ns + b];
-  __syncthreads();
+  const int nbins = E * ways;
   const int nbits = plan_dev::segment_bits(S);
   const int a_end = min(A, (b + 1) * chunk);
-  // RB rounds of 64 assignments at a time: their ids, then their segments,
-  // are loaded together, so the wave waits on memory twice per RB rounds
+  // RB rounds of 64 assignments at a time.  The first RB rounds' ids and
+  // weights, the chunk's row bases and the bin -> segment map are all loaded
+  // before any is used (the loops issue four loads at a time), so the wave
+  // waits on memory once before its first round and once per later RB rounds.
   constexpr int RB = 8;
   int e_pre[RB], seg_pre[RB];
-  for (int a00 = b * chunk; a00 < a_end; a00 += 64 * RB) {
-    #pragma unroll
-    for (int q = 0; q < RB; ++q) {
-      const int a = a00 + 64 * q + lane;
-      e_pre[q] = a < a_end ? ids[a] : -1;
+  float w_pre[RB];
+  const int a_first = b * chunk;
+#pragma unroll
+  for (int q = 0; q < RB; ++q) {
+    const int a = a_first + 64 * q + lane;
+    e_pre[q] = a < a_end ? ids[a] : -1;
+    w_pre[q] = (row_w && a < a_end) ? w[a] : 0.0f;
+  }
+#pragma unroll 4
+  for (int s = lane; s < S; s += 64) run[s] = blk_off[(size_t)s * ns + b];
+#pragma unroll 4
+  for (int i = lane; i < nbins; i += 64) sob[i] = seg_of_bin[i];
+  __syncthreads();
+  for (int a00 = a_first; a00 < a_end; a00 += 64 * RB) {
+    if (a00 != a_first) {
+#pragma unroll
+      for (int q = 0; q < RB; ++q) {
+        const int a = a00 + 64 * q + lane;
+        e_pre[q] = a < a_end ? ids[a] : -1;
+        w_pre[q] = (row_w && a < a_end) ? w[a] : 0.0f;
+      }
     }
-    #pragma unroll
+#pragma unroll
     for (int q = 0; q < RB; ++q) {
       const int a = a00 + 64 * q + lane;
       const int e = e_pre[q];
-      seg_pre[q] = (a < a_end && e >= 0 && e < E) ? seg_of_bin[e * ways + (a / k) % ways] : -1;
+      seg_pre[q] = (a < a_end && e >= 0 && e < E) ? sob[e * ways + (a / k) % ways] : -1;
     }
     #pragma unroll
     for (int q = 0; q < RB; ++q) {
@@ -179,7 +200,7 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ id
         a2r[a] = row;
         if (row >= 0) {
           r2t[row] = a / k;
-          if (row_w) row_w[row] = w[a];
+          if (row_w) row_w[row] = w_pre[q];
         }
       }
     }
@@ -390,8 +411,9 @@ void launch_permute(const moe_config& c, const void* x, const int32_t* ids, void
   plan_kernel<<<1, 1024, 0, s>>>(cnt_bin, nb, ns, c.E, bw, split_ways(c), c.n_hot_split,
                                  c.split_c_permille, cap, counts, seg_offsets, seg_expert,
                                  seg_of_bin, blk_off, r2t, bal);
-  rank_kernel<<<nb, 64, S * sizeof(int), s>>>(ids, A, c.k, c.E, bw, chunk, ns, S, cap,
-                                              seg_of_bin, blk_off, a2r, r2t, w, row_w);
+  // (LDS: the segments' next free rows and the bin -> segment map)
+  rank_kernel<<<nb, 64, (size_t)(S + c.E * bw) * sizeof(int), s>>>(
+      ids, A, c.k, c.E, bw, chunk, ns, S, cap, seg_of_bin, blk_off, a2r, r2t, w, row_w);
   if (!x_perm) return;  // the caller reads rows of x through row_to_token
   const int eb = c.act_dtype == MOE_DT_F32 ? 4 : 2;
   const int row_chunks = c.H * eb / 16;
