@@ -33,9 +33,15 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
   const int b = blockIdx.x;
   const int a0 = b * chunk;
   const int a1 = min(A, a0 + chunk);
-  for (int a = a0 + threadIdx.x; a < a1; a += blockDim.x) {
-    const int e = ids[a];
-    if (e >= 0 && e < E) atomicAdd(&h[e * ways + (a / k) % ways], 1);
+  // four ids per thread loaded before any is counted (one wait on memory
+  // per 1024 assignments)
+  for (int a = a0 + threadIdx.x; a < a1; a += 4 * 256) {
+    int e[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) e[q] = a + 256 * q < a1 ? ids[a + 256 * q] : -1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (e[q] >= 0 && e[q] < E) atomicAdd(&h[e[q] * ways + ((a + 256 * q) / k) % ways], 1);
   }
   __syncthreads();
   for (int i = threadIdx.x; i < nbins; i += blockDim.x) {
@@ -43,6 +49,71 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
     // the last chunk's block zeroes the row's padding (chunks nb .. ns-1)
     if (b == (int)gridDim.x - 1)
       for (int j = b + 1; j < ns; ++j) cnt_bin[(size_t)i * ns + j] = 0;
+  }
+}
+
+// Per-(segment, chunk) bases of the plan: blk_off[s][b] = seg_offsets[s] +
+// rows of segment s in chunks < b.  A wave scans a segment's chunk counts,
+// lane l taking chunks 4l .. 4l + 3 (rows of the count tables are ns ints,
+// nb chunks zero-padded to a multiple of 4), so one wave scan covers the
+// segment; wave w takes segments w, w + 16, ...  A chunk count is the
+// segment's one bin (a replica of the parity split) or the sum over its
+// expert's BW bins.  The loads of QS segments are issued unconditionally,
+// from in-range addresses (row 0, the lane's last in-row chunk group) where
+// a bin or lane is unused, and masked afterwards: as branches, every load
+// waited for its data before the next was issued.  In the load-bounded split
+// only the first segment of a hot expert is ever looked up (its rows run on
+// through the later ones); the later replica segments get bases too, which
+// nothing reads.  Padding segments of the fixed-capacity layout (expert -1)
+// get none.
+template <int BW>
+__device__ inline void segment_bases(const plan_dev::PlanLds& L, const int32_t* __restrict__ cnt_bin,
+                                     int S, int nb, int ns, int32_t* __restrict__ blk_off) {
+  constexpr int QS = 16 / BW;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const bool in_row = 4 * lane < nb;
+  const int lc = min(lane, ns / 4 - 1);
+  for (int sg0 = wv; sg0 < S; sg0 += 16 * QS) {
+    int4 u[QS][BW];
+    int nbin[QS];
+#pragma unroll
+    for (int q = 0; q < QS; ++q) {
+      const int sg = sg0 + 16 * q;
+      const int e = sg < S ? L.seg_exp[sg] : -1;
+      int bin0 = 0;
+      nbin[q] = 0;
+      if (e >= 0) {
+        const int f = L.seg_first[e];
+        const bool per_replica = BW > 1 && L.seg_first[e + 1] - f > 1;
+        bin0 = e * BW + (per_replica ? sg - f : 0);
+        nbin[q] = per_replica ? 1 : BW;
+      }
+      if (!in_row) nbin[q] = 0;
+#pragma unroll
+      for (int p = 0; p < BW; ++p) {
+        const int row = p < nbin[q] ? bin0 + p : 0;
+        u[q][p] = reinterpret_cast<const int4*>(cnt_bin + (size_t)row * ns)[lc];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < QS; ++q) {
+      const int sg = sg0 + 16 * q;
+      if (sg >= S || L.seg_exp[sg] < 0) continue;
+      int4 c = {0, 0, 0, 0};
+#pragma unroll
+      for (int p = 0; p < BW; ++p)
+        if (p < nbin[q]) {
+          c.x += u[q][p].x;
+          c.y += u[q][p].y;
+          c.z += u[q][p].z;
+          c.w += u[q][p].w;
+        }
+      const int local = c.x + c.y + c.z + c.w;
+      const int incl = plan_dev::wave_incl_scan(local, lane);
+      const int r0 = L.seg_off[sg] + incl - local;
+      const int4 o = {r0, r0 + c.x, r0 + c.x + c.y, r0 + c.x + c.y + c.z};
+      if (in_row) reinterpret_cast<int4*>(blk_off + (size_t)sg * ns)[lane] = o;
+    }
   }
 }
 
@@ -85,52 +156,11 @@ __global__ __launch_bounds__(1024) void plan_kernel(
                         : plan_dev::plan_segments(L, E, bin_ways, ways, n_hot, c, counts,
                                                   seg_offsets, seg_expert, seg_of_bin, bal);
 
-  // per-(segment, chunk) bases: a wave scans a segment's chunk counts, lane l
-  // taking chunks 4l .. 4l + 3, so one wave scan covers the segment; wave w
-  // takes segments w, w + 16, ... (QS at a time) and issues all their loads (a chunk count is the
-  // segment's one bin, or the sum over its expert's bins) before scanning
-  // and storing.  In the load-bounded split only the first segment of a hot
-  // expert is ever looked up (its rows run on through the later ones); the
-  // later replica segments get bases too, which nothing reads.  Padding
-  // segments of the fixed-capacity layout (expert -1) get none.
-  constexpr int QS = 16;
-  for (int sg0 = wv; sg0 < S; sg0 += 16 * QS) {
-    int4 v[QS];
-#pragma unroll
-    for (int q = 0; q < QS; ++q) {
-      const int sg = sg0 + 16 * q;
-      const int e = sg < S ? L.seg_exp[sg] : -1;
-      // the bins counted: bin0 .. bin0 + nbin - 1
-      int bin0 = 0, nbin = 0;
-      if (e >= 0) {
-        const int f = L.seg_first[e];
-        const bool per_replica = L.seg_first[e + 1] - f > 1 && bin_ways > 1;
-        bin0 = e * bin_ways + (per_replica ? sg - f : 0);
-        nbin = per_replica ? 1 : bin_ways;
-      }
-      int4 c = {0, 0, 0, 0};
-#pragma unroll
-      for (int p = 0; p < kMaxWays; ++p) {
-        if (p < nbin && in_row) {
-          const int4 u = reinterpret_cast<const int4*>(cnt_bin + (size_t)(bin0 + p) * ns)[lane];
-          c.x += u.x;
-          c.y += u.y;
-          c.z += u.z;
-          c.w += u.w;
-        }
-      }
-      v[q] = c;
-    }
-#pragma unroll
-    for (int q = 0; q < QS; ++q) {
-      const int sg = sg0 + 16 * q;
-      if (sg >= S || L.seg_exp[sg] < 0) continue;
-      const int local = v[q].x + v[q].y + v[q].z + v[q].w;
-      const int incl = plan_dev::wave_incl_scan(local, lane);
-      const int r0 = L.seg_off[sg] + incl - local;
-      const int4 o = {r0, r0 + v[q].x, r0 + v[q].x + v[q].y, r0 + v[q].x + v[q].y + v[q].z};
-      if (in_row) reinterpret_cast<int4*>(blk_off + (size_t)sg * ns)[lane] = o;
-    }
+  switch (bin_ways) {
+    case 1: segment_bases<1>(L, cnt_bin, S, nb, ns, blk_off); break;
+    case 2: segment_bases<2>(L, cnt_bin, S, nb, ns, blk_off); break;
+    case 3: segment_bases<3>(L, cnt_bin, S, nb, ns, blk_off); break;
+    default: segment_bases<4>(L, cnt_bin, S, nb, ns, blk_off); break;
   }
 }
 
