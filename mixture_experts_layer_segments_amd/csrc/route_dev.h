@@ -3,7 +3,8 @@
 //
 // The token's logits are held in registers (VPL = ceil(E/64) per lane,
 // expert e = lane + 64*i) and k rounds of a wave-wide (value desc, id asc)
-// arg-max butterfly pick the winners.  Flat mode: the k largest logits;
+// arg-max butterfly pick the winners; each candidate is one 64-bit key whose
+// integer order is that order (sel_key), so a butterfly step is one compare.  Flat mode: the k largest logits;
 // weights softmax over the winners.  Grouped mode (the MoE inference blog,
 // "MoE architecture recap": a few expert groups first, then the top experts
 // inside them): sigmoid scores, each group scored by the fp32 sum of its best
@@ -23,116 +24,111 @@
 namespace moe {
 namespace route_dev {
 
-constexpr int kNoId = 0x7fffffff;
-
-__device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
-  return av > bv || (av == bv && ai < bi);
+// Selection keys: one 64-bit integer per (value, id) whose unsigned order is
+// the routing order -- value descending, then id ascending -- so picking the
+// better of two is one integer compare, and the key also carries the value
+// and the id.  The high word is the value's bits mapped to an
+// order-preserving unsigned integer (+0 and -0 are first made one value, as
+// they tie as floats; NaN has already become -inf), so it is at least
+// 0x007FFFFF (-inf); the low word is the complement of the id (ids are below
+// 2^31).  0 lies below every key and marks a value already taken, a slot past
+// the experts or a group not kept.
+__device__ __forceinline__ uint64_t sel_key(float x, int id) {
+  const uint32_t u = __float_as_uint(x == 0.0f ? 0.0f : x);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)~(uint32_t)id;
 }
-
-__device__ __forceinline__ void take_better(float& v, int& id, float ov, int oi) {
-  if (better(ov, oi, v, id)) {
-    v = ov;
-    id = oi;
-  }
+__device__ __forceinline__ float key_hi_value(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
+__device__ __forceinline__ float key_value(uint64_t key) { return key_hi_value((uint32_t)(key >> 32)); }
+__device__ __forceinline__ int key_id(uint64_t key) { return (int)~(uint32_t)key; }
+__device__ __forceinline__ uint64_t key_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
-// One reduction step with the partner lane a DPP row permutation names.
+// The key of the lane a DPP row permutation names (both words moved).
 template <int CTRL>
-__device__ __forceinline__ void dpp_step(float& v, int& id) {
-  const float ov = __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-  const int oi = __builtin_amdgcn_update_dpp(0, id, CTRL, 0xF, 0xF, false);
-  take_better(v, id, ov, oi);
+__device__ __forceinline__ uint64_t dpp_key(uint64_t k) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, 0xF, 0xF, false);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
 }
 
-// One step with the lane 16 (ROW32 false) or 32 (true) lanes away, by the
-// gfx950 row-swap moves: the pair they return holds this lane's own value and
-// its partner's, so taking the better of both is the partner step.  (Each
-// half of the result is copied into a plain integer before its bit cast:
-// bit-casting an element of the builtin's result directly reads element 0.)
+// The larger of this lane's key and that of the lane 16 (ROW32 false) or 32
+// (true) lanes away, by the gfx950 row-swap moves: the pair they return holds
+// both.  (Each half of the result is copied into a plain integer before use:
+// reading an element of the builtin's result inside a wider expression has
+// read element 0.)
 template <bool ROW32>
-__device__ __forceinline__ void swap_step(float& v, int& id) {
-  const uint32_t vb = __builtin_bit_cast(uint32_t, v), ib = (uint32_t)id;
-  uint32_t v0, v1, i0, i1;
+__device__ __forceinline__ uint64_t swap_max_key(uint64_t k) {
+  const uint32_t lo = (uint32_t)k, hi = (uint32_t)(k >> 32);
+  uint32_t l0, l1, h0, h1;
   if constexpr (ROW32) {
-    const auto a = __builtin_amdgcn_permlane32_swap(vb, vb, false, false);
-    const auto b = __builtin_amdgcn_permlane32_swap(ib, ib, false, false);
-    v0 = a[0]; v1 = a[1]; i0 = b[0]; i1 = b[1];
+    const auto a = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    l0 = a[0]; l1 = a[1]; h0 = b[0]; h1 = b[1];
   } else {
-    const auto a = __builtin_amdgcn_permlane16_swap(vb, vb, false, false);
-    const auto b = __builtin_amdgcn_permlane16_swap(ib, ib, false, false);
-    v0 = a[0]; v1 = a[1]; i0 = b[0]; i1 = b[1];
+    const auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    l0 = a[0]; l1 = a[1]; h0 = b[0]; h1 = b[1];
   }
-  take_better(v, id, __builtin_bit_cast(float, v0), (int)i0);
-  take_better(v, id, __builtin_bit_cast(float, v1), (int)i1);
+  return key_max(((uint64_t)h0 << 32) | l0, ((uint64_t)h1 << 32) | l1);
 }
 
-// Wave-wide arg-max of (value desc, id asc); every lane returns the winner.
-// The partners double the reach each step -- lane l ^ 1, l ^ 2 (quad
-// permutations), the mirrored lane of its 8-lane half row and of its 16-lane
-// row, then the rows 16 and 32 lanes away -- all register-to-register moves
-// (a shuffle by index would go through the LDS unit and wait on it six times
-// per arg-max).  The order is total, so the winner is the same whatever the
-// reduction order.
-__device__ __forceinline__ void wave_argmax(float& v, int& id) {
-  dpp_step<0xB1>(v, id);    // quad_perm [1,0,3,2]
-  dpp_step<0x4E>(v, id);    // quad_perm [2,3,0,1]
-  dpp_step<0x141>(v, id);   // row_half_mirror
-  dpp_step<0x140>(v, id);   // row_mirror
-  swap_step<false>(v, id);
-  swap_step<true>(v, id);
-}
-
-// Arg-max of (value desc, id asc) inside every aligned block of P lanes
-// (P a power of two up to 64), to every lane of the block: the first log2 P
-// steps of wave_argmax.
+// Largest key inside every aligned block of P lanes (P a power of two up to
+// 64), to every lane of the block.  The partners double the reach each step
+// -- lane l ^ 1, l ^ 2 (quad permutations), the mirrored lane of its 8-lane
+// half row and of its 16-lane row, then the rows 16 and 32 lanes away -- all
+// register-to-register moves (a shuffle by index would go through the LDS
+// unit).  The order is total, so the result does not depend on the order of
+// the steps.
 template <int P>
-__device__ __forceinline__ void block_argmax(float& v, int& id) {
-  if constexpr (P >= 2) dpp_step<0xB1>(v, id);
-  if constexpr (P >= 4) dpp_step<0x4E>(v, id);
-  if constexpr (P >= 8) dpp_step<0x141>(v, id);
-  if constexpr (P >= 16) dpp_step<0x140>(v, id);
-  if constexpr (P >= 32) swap_step<false>(v, id);
-  if constexpr (P >= 64) swap_step<true>(v, id);
+__device__ __forceinline__ uint64_t block_max_key(uint64_t k) {
+  if constexpr (P >= 2) k = key_max(k, dpp_key<0xB1>(k));    // quad_perm [1,0,3,2]
+  if constexpr (P >= 4) k = key_max(k, dpp_key<0x4E>(k));    // quad_perm [2,3,0,1]
+  if constexpr (P >= 8) k = key_max(k, dpp_key<0x141>(k));   // row_half_mirror
+  if constexpr (P >= 16) k = key_max(k, dpp_key<0x140>(k));  // row_mirror
+  if constexpr (P >= 32) k = swap_max_key<false>(k);
+  if constexpr (P >= 64) k = swap_max_key<true>(k);
+  return k;
+}
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) { return block_max_key<64>(k); }
+
+// The same key in every lane, as a wave-uniform (scalar) value.
+__device__ __forceinline__ uint64_t uniform_key(uint64_t k) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)k);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(k >> 32));
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // Group scores when every group of P = E / n_group experts is an aligned
 // block of P lanes of one register slot (P divides 64; expert e = lane + 64 i
 // sits in slot i): each of the topn rounds takes every group's next best
-// member at once, one block arg-max per slot, and lane g (< n_group) adds the
-// sigmoid of its group's member -- the group's round-r winner fetched from
-// the group's lanes -- to its running score.  The score is the same fp32 sum,
-// in the same order of the same correctly rounded fp32 sigmoids, as the
-// one-group-at-a-time loop forms; lane g returns group g's score, the others
-// -inf.
+// member at once, one block key maximum per slot, and lane g (< n_group)
+// adds the sigmoid of its group's member -- the high word of the group's
+// round-r winner, fetched from the group's lanes -- to its running score.
+// The score is the same fp32 sum, in the same order of the same correctly
+// rounded fp32 sigmoids, as the one-group-at-a-time loop forms; lane g
+// returns group g's score, the others -inf.
 template <int VPL, int P>
-__device__ __forceinline__ float group_scores_blocked(const float (&v)[VPL],
-                                                      const bool (&avail)[VPL], int n_group,
+__device__ __forceinline__ float group_scores_blocked(const uint64_t (&key)[VPL], int n_group,
                                                       int topn, int lane) {
-  bool taken[VPL];
+  uint64_t kk[VPL];
 #pragma unroll
-  for (int i = 0; i < VPL; ++i) taken[i] = false;
+  for (int i = 0; i < VPL; ++i) kk[i] = key[i];
   const int src = (lane * P) & 63, src_slot = (lane * P) >> 6;   // lane g's group
   float acc = 0.0f;
   for (int r = 0; r < topn; ++r) {
-    float win = 0.0f;
-    bool has = false;
+    uint32_t win = 0;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-      const int e = lane + 64 * i;
-      const bool c = avail[i] && !taken[i];
-      float bv = c ? v[i] : -INFINITY;
-      int bi = c ? e : kNoId;
-      block_argmax<P>(bv, bi);
-      if (bi == e) taken[i] = true;   // the winner's own lane
-      const float wv = __shfl(bv, src);
-      const int wi = __shfl(bi, src);
-      if (src_slot == i) {
-        win = wv;
-        has = wi != kNoId;
-      }
+      const uint64_t best = block_max_key<P>(kk[i]);
+      kk[i] = kk[i] == best ? 0 : kk[i];   // the winner's own lane
+      const uint32_t w = (uint32_t)__shfl((int)(uint32_t)(best >> 32), src);
+      if (src_slot == i) win = w;
     }
-    if (lane < n_group && has) acc = acc + (float)(1.0 / (1.0 + exp(-(double)win)));
+    if (lane < n_group && win != 0)
+      acc = acc + (float)(1.0 / (1.0 + exp(-(double)key_hi_value(win))));
   }
   return lane < n_group ? acc : -INFINITY;
 }
@@ -183,113 +179,87 @@ __device__ __forceinline__ void route_token_vals(const float (&vin)[VPL], int E,
                                                  int topn, int renorm, int lane,
                                                  int& my_id_out, float& my_w_out) {
   float v[VPL];
-  bool avail[VPL];
+  uint64_t key[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
-    int e = lane + 64 * i;
+    const int e = lane + 64 * i;
     float x = vin[i];
     if (x != x) x = -INFINITY;  // a NaN logit never wins over a number
     v[i] = x;
-    avail[i] = e < E;
+    key[i] = e < E ? sel_key(x, e) : 0;
   }
 
   if (score == MOE_SCORE_SIGMOID && n_group > 1) {
     const int per = E / n_group;
     float my_gs = -INFINITY;  // lane g holds group g's score
     switch (per) {
-      case 1: my_gs = group_scores_blocked<VPL, 1>(v, avail, n_group, topn, lane); break;
-      case 2: my_gs = group_scores_blocked<VPL, 2>(v, avail, n_group, topn, lane); break;
-      case 4: my_gs = group_scores_blocked<VPL, 4>(v, avail, n_group, topn, lane); break;
-      case 8: my_gs = group_scores_blocked<VPL, 8>(v, avail, n_group, topn, lane); break;
-      case 16: my_gs = group_scores_blocked<VPL, 16>(v, avail, n_group, topn, lane); break;
-      case 32: my_gs = group_scores_blocked<VPL, 32>(v, avail, n_group, topn, lane); break;
-      case 64: my_gs = group_scores_blocked<VPL, 64>(v, avail, n_group, topn, lane); break;
+      case 1: my_gs = group_scores_blocked<VPL, 1>(key, n_group, topn, lane); break;
+      case 2: my_gs = group_scores_blocked<VPL, 2>(key, n_group, topn, lane); break;
+      case 4: my_gs = group_scores_blocked<VPL, 4>(key, n_group, topn, lane); break;
+      case 8: my_gs = group_scores_blocked<VPL, 8>(key, n_group, topn, lane); break;
+      case 16: my_gs = group_scores_blocked<VPL, 16>(key, n_group, topn, lane); break;
+      case 32: my_gs = group_scores_blocked<VPL, 32>(key, n_group, topn, lane); break;
+      case 64: my_gs = group_scores_blocked<VPL, 64>(key, n_group, topn, lane); break;
       default: break;
     }
     // groups that are not lane blocks: one group at a time, over the wave
-    float s32[VPL];
     if (64 % per != 0) {
+      float s32[VPL];
 #pragma unroll
       for (int i = 0; i < VPL; ++i) s32[i] = (float)(1.0 / (1.0 + exp(-(double)v[i])));
-    }
-    for (int g = 0; 64 % per != 0 && g < n_group; ++g) {
-      bool used[VPL];
+      for (int g = 0; g < n_group; ++g) {
+        uint64_t gk[VPL];
 #pragma unroll
-      for (int i = 0; i < VPL; ++i) used[i] = false;
-      float acc = 0.0f;
-      for (int r = 0; r < topn; ++r) {
-        float bv = -INFINITY;
-        int bi = kNoId;
+        for (int i = 0; i < VPL; ++i) gk[i] = (lane + 64 * i) / per == g ? key[i] : 0;
+        float acc = 0.0f;
+        for (int r = 0; r < topn; ++r) {
+          uint64_t best = gk[0];
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-          int e = lane + 64 * i;
-          if (avail[i] && !used[i] && e / per == g && better(v[i], e, bv, bi)) {
-            bv = v[i];
-            bi = e;
-          }
-        }
-        wave_argmax(bv, bi);
-        bi = __builtin_amdgcn_readfirstlane(bi);   // the same in every lane
-        if (bi == kNoId) break;  // group smaller than topn
-        const int slot = bi >> 6, owner = bi & 63;
-        float mine = 0.0f;
-#pragma unroll
-        for (int i = 0; i < VPL; ++i)
-          if (i == slot) mine = s32[i];
-        acc = acc + lane_value(mine, owner);
-        if (lane == owner) {
+          for (int i = 1; i < VPL; ++i) best = key_max(best, gk[i]);
+          best = uniform_key(wave_max_key(best));
+          if (best == 0) break;  // group smaller than topn
+          const int id = key_id(best);
+          const int slot = id >> 6, owner = id & 63;
+          float mine = 0.0f;
 #pragma unroll
           for (int i = 0; i < VPL; ++i)
-            if (i == slot) used[i] = true;
+            if (i == slot) mine = s32[i];
+          acc = acc + lane_value(mine, owner);
+#pragma unroll
+          for (int i = 0; i < VPL; ++i) gk[i] = gk[i] == best ? 0 : gk[i];
         }
+        if (lane == g) my_gs = acc;
       }
-      if (lane == g) my_gs = acc;
     }
-    // keep the topk_group best groups
+    // keep the topk_group best groups (scores ordered like logits: score
+    // desc, group id asc)
+    uint64_t gkey = lane < n_group ? sel_key(my_gs, lane) : 0;
     uint64_t kept = 0;
-    bool gtaken = false;
     for (int r = 0; r < topk_group; ++r) {
-      float bv = (lane < n_group && !gtaken) ? my_gs : -INFINITY;
-      int bi = (lane < n_group && !gtaken) ? lane : kNoId;
-      wave_argmax(bv, bi);
-      bi = __builtin_amdgcn_readfirstlane(bi);
-      if (bi == kNoId) break;
-      kept |= 1ull << bi;
-      if (lane == bi) gtaken = true;
+      const uint64_t best = uniform_key(wave_max_key(gkey));
+      if (best == 0) break;
+      kept |= 1ull << key_id(best);
+      gkey = gkey == best ? 0 : gkey;
     }
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      int e = lane + 64 * i;
-      if (avail[i] && !((kept >> (e / per)) & 1ull)) avail[i] = false;
-    }
+    for (int i = 0; i < VPL; ++i)
+      if (!((kept >> ((lane + 64 * i) / per)) & 1ull)) key[i] = 0;
   }
 
-  // k rounds of arg-max over the remaining experts
+  // k rounds: the wave's largest key is winner j; its lane clears that key
   int my_id = 0;
   float my_v = 0.0f;
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = kNoId;
+    uint64_t best = key[0];
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      int e = lane + 64 * i;
-      if (avail[i] && better(v[i], e, bv, bi)) {
-        bv = v[i];
-        bi = e;
-      }
-    }
-    wave_argmax(bv, bi);
-    bi = __builtin_amdgcn_readfirstlane(bi);
+    for (int i = 1; i < VPL; ++i) best = key_max(best, key[i]);
+    best = uniform_key(wave_max_key(best));
     if (lane == j) {
-      my_id = bi;
-      my_v = bv;
+      my_id = key_id(best);
+      my_v = key_value(best);
     }
-    if (lane == (bi & 63)) {
-      const int slot = bi >> 6;
 #pragma unroll
-      for (int i = 0; i < VPL; ++i)
-        if (i == slot) avail[i] = false;
-    }
+    for (int i = 0; i < VPL; ++i) key[i] = key[i] == best ? 0 : key[i];
   }
 
   // weights in fp64, rounded once (the winners sit in lanes 0 .. k-1)
@@ -328,12 +298,10 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
                         my_w_out);
 }
 
-
 // ---- flat routing by lane groups ----
 // Flat top-k (one expert group) on G = 16 or 32 lanes per token, 64 / G
 // tokens per wave: lane j of a group holds experts j + G i (i < VPL), each
-// arg-max round reduces inside the group (the first log2 G steps of
-// wave_argmax), and the weights of all the wave's tokens are formed together.
+// arg-max round reduces inside the group (block_max_key<G>), and the weights of all the wave's tokens are formed together.
 // The winners and their order are those of route_token_vals (the order is
 // total); the weights' fp64 sum runs in another order (within rounding of the
 // same value).
@@ -346,7 +314,8 @@ __device__ __forceinline__ double dpp_f64(double x) {
       (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, true);
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
-// x of the lane 16 lanes away (see swap_step).
+// x of the lane 16 lanes away (the pair the row-swap move returns holds
+// this lane's word and its partner's; which is which depends on the row).
 __device__ __forceinline__ double swap16_f64(double x) {
   const uint64_t b = __builtin_bit_cast(uint64_t, x);
   const uint32_t lo = (uint32_t)b, hi = (uint32_t)(b >> 32);
@@ -357,14 +326,11 @@ __device__ __forceinline__ double swap16_f64(double x) {
   return __builtin_bit_cast(double, ((uint64_t)(odd_row ? h0 : h1) << 32) | (odd_row ? l0 : l1));
 }
 
+// Largest key over the G lanes of this lane's group (a DPP row, or two).
 template <int G>
-__device__ __forceinline__ void group_argmax(float& v, int& id) {
+__device__ __forceinline__ uint64_t group_max_key(uint64_t k) {
   static_assert(G == 16 || G == 32, "a row or two rows per token");
-  dpp_step<0xB1>(v, id);
-  dpp_step<0x4E>(v, id);
-  dpp_step<0x141>(v, id);
-  dpp_step<0x140>(v, id);
-  if constexpr (G == 32) swap_step<false>(v, id);
+  return block_max_key<G>(k);
 }
 
 template <int G>
@@ -396,39 +362,30 @@ __device__ __forceinline__ void route_group_vals(const float (&vin)[VPL], int E,
                                                  int renorm, int j, int& my_id_out,
                                                  float& my_w_out) {
   float v[VPL];
-  bool avail[VPL];
+  uint64_t key[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     float x = vin[i];
     if (x != x) x = -INFINITY;  // a NaN logit never wins over a number
     v[i] = x;
-    avail[i] = j + G * i < E;
+    key[i] = j + G * i < E ? sel_key(x, j + G * i) : 0;
   }
+  // round r: the group's largest key is winner r; its lane clears that key
   int my_id = 0;
   float my_v = 0.0f, top0 = 0.0f;
   for (int r = 0; r < k; ++r) {
-    float bv = -INFINITY;
-    int bi = kNoId;
+    uint64_t best = key[0];
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int e = j + G * i;
-      if (avail[i] && better(v[i], e, bv, bi)) {
-        bv = v[i];
-        bi = e;
-      }
-    }
-    group_argmax<G>(bv, bi);
+    for (int i = 1; i < VPL; ++i) best = key_max(best, key[i]);
+    best = group_max_key<G>(best);
+    const float bv = key_value(best);
     if (r == 0) top0 = bv;
     if (j == r) {
-      my_id = bi;
+      my_id = key_id(best);
       my_v = bv;
     }
-    if (j == bi % G) {
-      const int slot = bi / G;
 #pragma unroll
-      for (int i = 0; i < VPL; ++i)
-        if (i == slot) avail[i] = false;
-    }
+    for (int i = 0; i < VPL; ++i) key[i] = key[i] == best ? 0 : key[i];
   }
   // weights in fp64, rounded once (the winners sit in lanes 0 .. k-1 of the group)
   double p = 0.0;

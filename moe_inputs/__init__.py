@@ -34,7 +34,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-T_NOISE, T_PERM, T_X, T_W13, T_W2, T_SW13, T_SW2 = range(7)
+T_NOISE, T_PERM, T_X, T_W13, T_W2, T_SW13, T_SW2, T_TIES = range(8)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -177,6 +177,19 @@ def logits(cfg: MoEShape) -> np.ndarray:
             later = np.setdiff1d(np.arange(cfg.E), first)
             noise[t, later] = rng.standard_normal(later.size)
             out[t, later] = (noise[t, later] + bias[later]).astype(np.float32)
+
+
+def tied_logits(cfg: MoEShape) -> np.ndarray:
+    """Router logits fp32 [T, E] made to tie: N(0,1) draws rounded to
+    multiples of 1/2 (so most rows repeat values, zero among them), about
+    half of the zeros stored as -0.0, and about 2% of the entries -inf."""
+    rng = _rng(cfg, T_TIES)
+    out = (np.round(rng.standard_normal((cfg.T, cfg.E)) * 2.0) / 2.0).astype(np.float32)
+    zero = out == 0
+    neg = zero & (rng.random((cfg.T, cfg.E)) < 0.5)
+    out[neg] = np.float32(-0.0)
+    out[rng.random((cfg.T, cfg.E)) < 0.02] = -np.inf
+    return out
 
 
 # ---------------------------------------------------------------- tensors

@@ -269,6 +269,25 @@ def test_route_extremes(moe, E, k, groups, topk_group):
     gu.check_routing(cfg, ids.cpu().numpy(), w.cpu().numpy(), ids_r, w_r, gap, lg)
 
 
+# exact ties (values on a 1/2 grid), zeros of both signs (they tie) and -inf
+# entries, through every routing path: 16 and 32 lanes per token, the whole
+# wave, groups that are lane blocks and groups that are not (12 experts)
+@pytest.mark.parametrize("E,k,groups,topk_group", [(128, 8, 1, 1), (512, 20, 1, 1),
+                                                   (1024, 32, 1, 1), (256, 8, 8, 4),
+                                                   (96, 6, 8, 3), (128, 4, 64, 8)])
+def test_route_ties_and_signed_zeros(moe, E, k, groups, topk_group):
+    score = "sigmoid" if groups > 1 else "softmax"
+    cfg = mi.MoEShape("rt", T=300, H=64, E=E, k=k, I=64, score=score, n_group=groups,
+                      topk_group=topk_group, seed=29)
+    lg = mi.tied_logits(cfg)
+    ids_r, w_r, gap = orc.route(cfg, lg)
+    ids = gu.empty((cfg.T, cfg.k), torch.int32)
+    w = gu.empty((cfg.T, cfg.k), torch.float32)
+    moe.moe_route_topk(cfg, torch.from_numpy(lg).to(gu.dev()), ids, w)
+    torch.cuda.synchronize()
+    gu.check_routing(cfg, ids.cpu().numpy(), w.cpu().numpy(), ids_r, w_r, gap, lg)
+
+
 def test_empty_batch_is_a_noop(moe):
     cfg = mi.MoEShape("empty", T=0, H=128, E=8, k=2, I=64)
     sentinel = torch.full((4,), 7, dtype=torch.int32, device=gu.dev())
