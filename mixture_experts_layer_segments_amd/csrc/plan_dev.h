@@ -16,9 +16,22 @@ namespace plan_dev {
 __device__ __forceinline__ int wave_incl_scan(int v, int) { return wave_dev::incl_scan(v); }
 
 // In-place exclusive scan of n <= 4096 ints in LDS by 1024 threads; returns
-// the total to every thread.
+// the total to every thread.  The caller has a barrier between its writes of
+// data and the call; n <= 64 (a decode batch's experts) is scanned by wave 0
+// alone behind one barrier, and then the next call must come after another
+// barrier (every thread reads the total from wave_tot).
 __device__ inline int block_exclusive_scan(int* data, int n, int* wave_tot) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (n <= 64) {
+    if (wv == 0) {
+      const int x = lane < n ? data[lane] : 0;
+      const int incl = wave_incl_scan(x, lane);
+      if (lane < n) data[lane] = incl - x;
+      if (lane == 63) wave_tot[16] = incl;
+    }
+    __syncthreads();
+    return wave_tot[16];
+  }
   const int per = (n + 1023) / 1024;
   const int lo = min(n, tid * per), hi = min(n, lo + per);
   int sum = 0;
