@@ -212,10 +212,13 @@ __device__ __forceinline__ void wait_stages(int later) {
 // XOR swizzle of the 16-byte chunk index inside a row piece of KCH chunks,
 // chosen so that the 16 lanes reading one MFMA operand column (16 rows, same
 // logical chunk) hit distinct 16-byte bank groups of a 256-byte bank row
-// (measured 3-9% faster than swizzling by row & 7).
+// (128-byte pieces: measured 3-9% faster than swizzling by row & 7; 256-byte
+// pieces, the bf16 activations of 128-deep stages, every row a whole bank row:
+// row & 15, 2-4% faster than row & 7).
 template <int KCH>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (KCH == 8) return (row >> 1) & 7;
+  if constexpr (KCH == 16) return row & 15;
+  else if constexpr (KCH == 8) return (row >> 1) & 7;
   else return (row >> 2) & 3;
 }
 
@@ -229,8 +232,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 // Copy K stage kt of this wave's LPI 1 KiB blocks into its ring slot: the
 // wave's first A_IT blocks are A blocks i * NI + w (RPB rows of 128-byte
 // pieces each), the rest B blocks (i - A_IT) * NI + w, starting at chunk A_CH
-// of the slot (bf16 weights: 128-byte row pieces; E4M3 codes: 64-byte
-// pieces, 16 rows per block).  `voff` holds each lane's byte offset of its
+// of the slot (bf16 weights and the 128-deep stages' E4M3 codes: 128-byte
+// row pieces; E4M3 codes of 64-deep stages: 64-byte pieces, 16 rows per
+// block).  `voff` holds each lane's byte offset of its
 // 16 bytes at k = 0; the stage's K offset goes in the scalar offset.
 //
 // K tail (bf16, K not a multiple of BK): in the last stage only the first
@@ -319,8 +323,8 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi, float 
 // a 256 x 256 tile's time; the staged form is 5-10% faster overall).
 //
 // WF = 1: the weights are E4M3 codes with 128 x 128 block scales.  The codes
-// travel into the ring as they are (half the bytes of bf16, so the ring holds
-// more stages) and are dequantized when a wave reads its MFMA operand: an
+// travel into the ring as they are (half the bytes of bf16, so a ring of the
+// same size holds more, or deeper, stages) and are dequantized when a wave reads its MFMA operand: an
 // 8-byte LDS read and four conversions with the block's scale.  The tile's
 // block scales (its two 128-row blocks of weights x K/128) are staged once
 // per tile into `scl`, LDS beside the tile table.
@@ -329,11 +333,13 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi, float 
 // Cache policy of the weight copies of a 128-row tile whose segment has no
 // other row tile (its weights are read once): 2 = non-temporal (gfx950 "nt").
 // Measured with bf16 weights: 2% faster on the prefill and DeepSeek-shaped
-// layers (streaming the weights past L2 leaves it to the activations).  Not
-// with E4M3 weights: their 64-byte row pieces split every 128-byte line over
-// two stages, and a streamed line is fetched twice (6-7% slower).  A segment
-// with several row tiles keeps the default policy, since its other row tiles
-// read the same weights (streaming them too was 11% slower on prefill).
+// layers (streaming the weights past L2 leaves it to the activations); with
+// E4M3 weights on 128-deep stages 1%, with E4M3 activations too 2-4% (the
+// 128-row launches).  Only where a stage's weight row piece is a whole
+// 128-byte line: 64-byte pieces split every line over two stages, and a
+// streamed line is fetched twice (6-7% slower).  A segment with several row
+// tiles keeps the default policy, since its other row tiles read the same
+// weights (streaming them too was 11% slower on prefill).
 // Cache policy of the ring tiles' GEMM 2 output (y_perm) stores: 2 =
 // non-temporal.  y_perm is written once and read once by the combine, and
 // keeping it out of L2 leaves L2 to the tiles' operands: measured 1-2.5%
@@ -358,11 +364,11 @@ struct RingCfg {
   static constexpr int NI = NW == 8 ? 4 : NW;   // issuing waves
   static constexpr int A_IT = BM / RPB / NI;   // A copies per issuing wave per stage
   static constexpr int LPI = A_IT + BN / RPBB / NI;   // all copies per issuing wave per stage
-  // cache policy of the weight copies of single-row-tile segments (bf16
-  // weights on the 128-row tiles, as above)
-  static constexpr int B_AUX = (BM < 256 && WF == 0) ? kAuxNT : 0;
-  static_assert(WF == 2 ? BK == 128 : (BK == 32 || BK == 64), "row piece of 64 or 128 bytes");
-  static_assert(WF != 1 || BK == 64, "E4M3 weights: 64-byte row pieces");
+  // cache policy of the weight copies of single-row-tile segments (the
+  // 128-row tiles whose weight row pieces are whole 128-byte lines, as above)
+  static constexpr int B_AUX = (BM < 256 && BK * WB == 128) ? kAuxNT : 0;
+  static_assert(WF == 2 ? BK == 128 : WF == 1 ? (BK == 64 || BK == 128) : (BK == 32 || BK == 64),
+                "row pieces of 64, 128 or 256 bytes");
   static_assert((BM / RPB) % NI == 0 && (BN / RPBB) % NI == 0, "copy blocks per wave");
   static_assert(STAGES >= 2 && STAGES <= 6, "ring shape");
   static_assert(LPI * (STAGES - 2) < 64, "vmcnt range");
@@ -668,7 +674,7 @@ __device__ __forceinline__ void ring_kloop(
         for (int ni = 0; ni < TN; ++ni) {
           const int br = brow_of[ni] + (lane & 15);
           if (WF) {
-            // codes of K kk*32 + q*8 .. +8: chunk 2*kk + q/2 of the 64-byte piece, half q % 2
+            // codes of K kk*32 + q*8 .. +8: chunk 2*kk + q/2 of the row piece, half q % 2
             const int c = kk * 2 + ((lane >> 4) >> 1);
             const u32x2 v = reinterpret_cast<const u32x2*>(
                 slot + A_CH + br * KCHB + (c ^ swz<KCHB>(BM + br)))[(lane >> 4) & 1];
@@ -1001,10 +1007,14 @@ template <> struct Tiles<0> {                              // bf16
   using Mid = TileCfg<0, 128, 256, 64, 512, 2, 3>;         // 2 x 4 waves of 64 x 64
   using Big = TileCfg<0, 256, 256, 64, 512, 4, 2>;         // 4 x 2 waves of 64 x 128
 };
-// E4M3 weights: the weight rows of a stage take half the bytes, so the same
-// tiles hold one more stage.
+// E4M3 weights: the weight rows of a stage take half the bytes.  The
+// 128-row tile takes 128-deep stages (two), so that a stage's weight row
+// piece is a whole 128-byte line rather than half of one (the other half
+// fetched again a stage later): 4-6% faster on its launches than four
+// 64-deep stages.  The 256-row tile keeps 64-deep stages, one more than
+// bf16 (128-deep ones would not fit twice).
 template <> struct Tiles<1> {
-  using Mid = TileCfg<1, 128, 256, 64, 512, 2, 4>;
+  using Mid = TileCfg<1, 128, 256, 128, 512, 2, 2>;
   using Big = TileCfg<1, 256, 256, 64, 512, 4, 3>;
 };
 // E4M3 activations and weights: 128-deep stages (128-byte row pieces, as the
