@@ -1012,10 +1012,15 @@ template <> struct Tiles<0> {                              // bf16
 // piece is a whole 128-byte line rather than half of one (the other half
 // fetched again a stage later): 4-6% faster on its launches than four
 // 64-deep stages.  The 256-row tile keeps 64-deep stages, one more than
-// bf16 (128-deep ones would not fit twice).
+// bf16 (128-deep ones would not fit twice), and 2 x 4 waves of 128 x 64
+// rather than bf16's 4 x 2 of 64 x 128: every wave dequantizes the weight
+// fragments it reads, so half as many weight columns per wave halves the
+// conversions (for 25% more activation reads): 4-9% faster on its launches.
+// (With bf16 weights the two layouts read the same LDS bytes and time the
+// same.)
 template <> struct Tiles<1> {
   using Mid = TileCfg<1, 128, 256, 128, 512, 2, 2>;
-  using Big = TileCfg<1, 256, 256, 64, 512, 4, 3>;
+  using Big = TileCfg<1, 256, 256, 64, 512, 2, 3>;   // 2 x 4 waves of 128 x 64
 };
 // E4M3 activations and weights: 128-deep stages (128-byte row pieces, as the
 // bf16 tiles' 64-deep ones), one scaled FP8 MFMA K step each.
