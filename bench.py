@@ -41,18 +41,18 @@ CSRC = os.path.join(ROOT, "mixture_experts_layer_segments_amd", "csrc")
 # only applies while the library's sources (every file under csrc/) still
 # hash to the value it was measured with.
 MEASURED_TRAFFIC = {
-    "ragged_stress_bf16": {"csrc_sha256_16": "5b28aadefa12fa20", "bytes": 13451513641},
-    "decode_bf16": {"csrc_sha256_16": "5b28aadefa12fa20", "bytes": 5542912696},
-    "prefill_skew_bf16": {"csrc_sha256_16": "5b28aadefa12fa20", "bytes": 7653777858},
-    "deepseek_v3_bf16": {"csrc_sha256_16": "5b28aadefa12fa20", "bytes": 22419582567},
-    "ragged_stress_fp8w": {"csrc_sha256_16": "5b28aadefa12fa20", "bytes": 9796880443},
-    "decode_fp8w": {"csrc_sha256_16": "5b28aadefa12fa20", "bytes": 2776253702},
-    "prefill_skew_fp8w": {"csrc_sha256_16": "5b28aadefa12fa20", "bytes": 3640330130},
-    "deepseek_v3_fp8w": {"csrc_sha256_16": "5b28aadefa12fa20", "bytes": 12654383779},
-    "ragged_stress_w8a8": {"csrc_sha256_16": "5b28aadefa12fa20", "bytes": 7330996896},
-    "decode_w8a8": {"csrc_sha256_16": "5b28aadefa12fa20", "bytes": 2781393600},
-    "prefill_skew_w8a8": {"csrc_sha256_16": "5b28aadefa12fa20", "bytes": 4012166511},
-    "deepseek_v3_w8a8": {"csrc_sha256_16": "5b28aadefa12fa20", "bytes": 11727352250},
+    "ragged_stress_bf16": {"csrc_sha256_16": "09f781c3d4bd359e", "bytes": 13317640533},
+    "decode_bf16": {"csrc_sha256_16": "09f781c3d4bd359e", "bytes": 5542965099},
+    "prefill_skew_bf16": {"csrc_sha256_16": "09f781c3d4bd359e", "bytes": 7687083308},
+    "deepseek_v3_bf16": {"csrc_sha256_16": "09f781c3d4bd359e", "bytes": 22477087027},
+    "ragged_stress_fp8w": {"csrc_sha256_16": "09f781c3d4bd359e", "bytes": 9746513750},
+    "decode_fp8w": {"csrc_sha256_16": "09f781c3d4bd359e", "bytes": 2776285080},
+    "prefill_skew_fp8w": {"csrc_sha256_16": "09f781c3d4bd359e", "bytes": 3963797065},
+    "deepseek_v3_fp8w": {"csrc_sha256_16": "09f781c3d4bd359e", "bytes": 12661003387},
+    "ragged_stress_w8a8": {"csrc_sha256_16": "09f781c3d4bd359e", "bytes": 7327066164},
+    "decode_w8a8": {"csrc_sha256_16": "09f781c3d4bd359e", "bytes": 2781426875},
+    "prefill_skew_w8a8": {"csrc_sha256_16": "09f781c3d4bd359e", "bytes": 3876789887},
+    "deepseek_v3_w8a8": {"csrc_sha256_16": "09f781c3d4bd359e", "bytes": 11673617688},
 }
 
 
