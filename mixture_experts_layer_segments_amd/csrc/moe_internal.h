@@ -42,6 +42,13 @@ inline int bin_ways(const moe_config& c) {
   return c.split_mode == MOE_SPLIT_PARITY ? split_ways(c) : 1;
 }
 
+// The one-wave planner applies: nothing split, at most 256 experts and the
+// dropless layout (one segment and one bin per expert).
+inline bool wave_plan(const moe_config& c) {
+  return c.E <= 256 && !(c.n_hot_split > 0 && c.split_ways > 1) &&
+         c.capacity_factor_permille <= 0;
+}
+
 // Slots per expert of the fixed-capacity layout, ceil(f * T*k / E) with
 // f = capacity_factor_permille / 1000; 0 for the dropless layout.
 inline int64_t capacity(const moe_config& c) {

@@ -65,14 +65,20 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
 // only the first segment of a hot expert is ever looked up (its rows run on
 // through the later ones); the later replica segments get bases too, which
 // nothing reads.  Padding segments of the fixed-capacity layout (expert -1)
-// get none.
-template <int BW>
-__device__ inline void segment_bases(const plan_dev::PlanLds& L, const int32_t* __restrict__ cnt_bin,
-                                     int S, int nb, int ns, int32_t* __restrict__ blk_off) {
+// get none.  `after_issue` runs once per wave, as soon as the wave's first
+// loads are issued (or at once, for a wave without segments): stores issued
+// there do not hold up the waits for those loads, which the wave's single
+// in-order memory counter would make them do if issued before.
+template <int BW, typename F>
+__device__ __forceinline__ void segment_bases(const plan_dev::PlanLds& L,
+                                              const int32_t* __restrict__ cnt_bin, int S, int nb,
+                                              int ns, int32_t* __restrict__ blk_off,
+                                              F&& after_issue) {
   constexpr int QS = 16 / BW;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const bool in_row = 4 * lane < nb;
   const int lc = min(lane, ns / 4 - 1);
+  bool pending = true;
   for (int sg0 = wv; sg0 < S; sg0 += 16 * QS) {
     int4 u[QS][BW];
     int nbin[QS];
@@ -95,6 +101,10 @@ __device__ inline void segment_bases(const plan_dev::PlanLds& L, const int32_t* 
         u[q][p] = reinterpret_cast<const int4*>(cnt_bin + (size_t)row * ns)[lc];
       }
     }
+    if (pending) {
+      after_issue();
+      pending = false;
+    }
 #pragma unroll
     for (int q = 0; q < QS; ++q) {
       const int sg = sg0 + 16 * q;
@@ -115,8 +125,10 @@ __device__ inline void segment_bases(const plan_dev::PlanLds& L, const int32_t* 
       if (in_row) reinterpret_cast<int4*>(blk_off + (size_t)sg * ns)[lane] = o;
     }
   }
+  if (pending) after_issue();
 }
 
+template <bool WAVE>
 __global__ __launch_bounds__(1024) void plan_kernel(
     const int32_t* __restrict__ cnt_bin, int nb, int ns, int E, int bin_ways, int ways, int n_hot,
     int c, int cap, int32_t* __restrict__ counts, int32_t* __restrict__ seg_offsets,
@@ -151,16 +163,27 @@ __global__ __launch_bounds__(1024) void plan_kernel(
     }
   }
   __syncthreads();
-  const int S = cap > 0 ? plan_dev::plan_capacity(L, E, cap, counts, seg_offsets, seg_expert,
-                                                  seg_of_bin, r2t, bal)
-                        : plan_dev::plan_segments(L, E, bin_ways, ways, n_hot, c, counts,
-                                                  seg_offsets, seg_expert, seg_of_bin, bal);
-
-  switch (bin_ways) {
-    case 1: segment_bases<1>(L, cnt_bin, S, nb, ns, blk_off); break;
-    case 2: segment_bases<2>(L, cnt_bin, S, nb, ns, blk_off); break;
-    case 3: segment_bases<3>(L, cnt_bin, S, nb, ns, blk_off); break;
-    default: segment_bases<4>(L, cnt_bin, S, nb, ns, blk_off); break;
+  if constexpr (WAVE) {
+    // one segment per expert, planned by one wave; its outputs go out while
+    // the bases' loads are in flight
+    __shared__ int sob[kMaxE];
+    __shared__ float bal_s;
+    const int S = plan_dev::plan_segments_by_wave(L, E, sob, &bal_s);
+    segment_bases<1>(L, cnt_bin, S, nb, ns, blk_off, [&] {
+      plan_dev::write_plan(L, E, counts, seg_offsets, seg_expert, sob, seg_of_bin, bal_s, bal);
+    });
+  } else {
+    const int S = cap > 0 ? plan_dev::plan_capacity(L, E, cap, counts, seg_offsets, seg_expert,
+                                                    seg_of_bin, r2t, bal)
+                          : plan_dev::plan_segments(L, E, bin_ways, ways, n_hot, c, counts,
+                                                    seg_offsets, seg_expert, seg_of_bin, bal);
+    auto none = [] {};
+    switch (bin_ways) {
+      case 1: segment_bases<1>(L, cnt_bin, S, nb, ns, blk_off, none); break;
+      case 2: segment_bases<2>(L, cnt_bin, S, nb, ns, blk_off, none); break;
+      case 3: segment_bases<3>(L, cnt_bin, S, nb, ns, blk_off, none); break;
+      default: segment_bases<4>(L, cnt_bin, S, nb, ns, blk_off, none); break;
+    }
   }
 }
 
@@ -242,7 +265,7 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ id
 // assignment is binned by LDS atomics (counts do not depend on the order);
 // the plan is the one above; and one wave ranks the at most kSmallA
 // assignments in order, 64 at a time, as the rank kernel does.
-template <int G, int VPL>
+template <int G, int VPL, bool WAVE>
 __global__ __launch_bounds__(1024) void route_permute_small_kernel(
     const float* __restrict__ logits, int T, int E, int k, int score, int n_group,
     int topk_group, int topn, int renorm, int bin_ways, int ways, int n_hot, int c, int cap,
@@ -252,6 +275,7 @@ __global__ __launch_bounds__(1024) void route_permute_small_kernel(
     float* __restrict__ row_w, float* __restrict__ bal) {
   __shared__ plan_dev::PlanLds L;
   __shared__ int seg_of_bin[kMaxBins];
+  __shared__ float bal_s;   // (the one-wave planner's balancedness)
   __shared__ int id_a[kSmallA];
   __shared__ float w_a[kSmallA];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -324,17 +348,22 @@ __global__ __launch_bounds__(1024) void route_permute_small_kernel(
     }
   }
   __syncthreads();
-  const int S =
-      cap > 0 ? plan_dev::plan_capacity(L, E, cap, counts, seg_offsets, seg_expert, seg_of_bin,
-                                        r2t, bal)
-              : plan_dev::plan_segments(L, E, bin_ways, ways, n_hot, c, counts, seg_offsets,
-                                        seg_expert, seg_of_bin, bal);
+  int S;
+  if constexpr (WAVE)
+    S = plan_dev::plan_segments_by_wave(L, E, seg_of_bin, &bal_s);
+  else
+    S = cap > 0 ? plan_dev::plan_capacity(L, E, cap, counts, seg_offsets, seg_expert, seg_of_bin,
+                                          r2t, bal)
+                : plan_dev::plan_segments(L, E, bin_ways, ways, n_hot, c, counts, seg_offsets,
+                                          seg_expert, seg_of_bin, bal);
   // the bin totals are spent: L.tot becomes the next free row of each segment
   int* run = L.tot;
   for (int s = tid; s < S; s += 1024) run[s] = L.seg_off[s];
   for (int a = tid; a < A; a += 1024)
     id_a[a] = seg_of_bin[id_a[a] * bin_ways + (a / k) % bin_ways];
   __syncthreads();
+  if constexpr (WAVE)
+    plan_dev::write_plan(L, E, counts, seg_offsets, seg_expert, seg_of_bin, nullptr, bal_s, bal);
   // one wave ranks every assignment, 64 at a time in assignment order
   if (wv == 0) {
     const int nbits = plan_dev::segment_bits(S);
@@ -382,11 +411,18 @@ template <int G, int VPL>
 void launch_small_vpl(const moe_config& c, const float* logits, int32_t* ids, float* w,
                       int32_t* counts, int32_t* seg_offsets, int32_t* seg_expert, int32_t* a2r,
                       int32_t* r2t, float* row_w, float* bal, hipStream_t s) {
-  route_permute_small_kernel<G, VPL><<<1, 1024, 0, s>>>(
-      logits, c.T, c.E, c.k, c.score, c.n_group, c.topk_group, c.group_score_topn,
-      c.renormalize, bin_ways(c), split_ways(c), c.n_hot_split, c.split_c_permille,
-      (int)capacity(c), ids, w, counts, seg_offsets, seg_expert, a2r, r2t,
-      row_w, bal);
+  auto go = [&](auto kernel) {
+    kernel<<<1, 1024, 0, s>>>(logits, c.T, c.E, c.k, c.score, c.n_group, c.topk_group,
+                              c.group_score_topn, c.renormalize, bin_ways(c), split_ways(c),
+                              c.n_hot_split, c.split_c_permille, (int)capacity(c), ids, w,
+                              counts, seg_offsets, seg_expert, a2r, r2t, row_w, bal);
+  };
+  // (the one-wave planner needs E <= 256: only layouts of fewer logits per
+  // token than 512 can have it)
+  if constexpr ((G > 0 ? G : 64) * VPL < 512) {
+    if (wave_plan(c)) return go(route_permute_small_kernel<G, VPL, true>);
+  }
+  go(route_permute_small_kernel<G, VPL, false>);
 }
 
 // Kernel variant for G lanes per token (0: one wave per token) and ceil(E / lanes)
@@ -438,9 +474,10 @@ void launch_permute(const moe_config& c, const void* x, const int32_t* ids, void
   int32_t* seg_of_bin = reinterpret_cast<int32_t*>(ws + L.seg_of_bin);
   hist_kernel<<<nb, 256, 0, s>>>(ids, A, c.k, c.E, bw, chunk, ns, cnt_bin);
   const int cap = (int)capacity(c);
-  plan_kernel<<<1, 1024, 0, s>>>(cnt_bin, nb, ns, c.E, bw, split_ways(c), c.n_hot_split,
-                                 c.split_c_permille, cap, counts, seg_offsets, seg_expert,
-                                 seg_of_bin, blk_off, r2t, bal);
+  auto plan = wave_plan(c) ? plan_kernel<true> : plan_kernel<false>;
+  plan<<<1, 1024, 0, s>>>(cnt_bin, nb, ns, c.E, bw, split_ways(c), c.n_hot_split,
+                          c.split_c_permille, cap, counts, seg_offsets, seg_expert, seg_of_bin,
+                          blk_off, r2t, bal);
   // (LDS: the segments' next free rows and the bin -> segment map)
   rank_kernel<<<nb, 64, (size_t)(S + c.E * bw) * sizeof(int), s>>>(
       ids, A, c.k, c.E, bw, chunk, ns, S, cap, seg_of_bin, blk_off, a2r, r2t, w, row_w);

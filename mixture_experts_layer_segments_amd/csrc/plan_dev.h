@@ -230,6 +230,87 @@ __device__ inline int plan_segments(PlanLds& L, int E, int bin_ways, int ways, i
   return S;
 }
 
+// The one-wave planner, for plans that split nothing with E <= 256 (the
+// host picks it, wave_plan(); a kernel holds one planner only, since the code
+// of the other, run past once by one workgroup, measurably slowed it).  Every
+// expert is one segment and one bin (segment e, bin e), so only the row
+// offsets need a scan: lane l owns experts l V .. l V + V - 1 (E <= 64 V),
+// whose rows are contiguous, and one wave scan of its rows gives them.  The
+// results equal plan_segments', without its dozen block barriers (a decode
+// batch's plan is latency, not work), and go to LDS only: L, sob (bin ->
+// segment) and *bal_s; write_plan() copies them out.  Called by wave 0.
+template <int V>
+__device__ inline void plan_segments_wave(PlanLds& L, int E, int* sob, float* bal_s) {
+  const int lane = threadIdx.x & 63;
+  const int e0 = lane * V;
+  int cnt[V];
+  int cmax = 0, csum = 0;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int e = e0 + i;
+    cnt[i] = e < E ? L.tot[e] : 0;
+    cmax = ::max(cmax, cnt[i]);
+    csum += cnt[i];
+  }
+  const int row_incl = wave_dev::incl_scan(csum);
+  const int total = __builtin_amdgcn_readlane(row_incl, 63);
+  int row = row_incl - csum;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int e = e0 + i;
+    if (e >= E) continue;
+    L.cnt_e[e] = cnt[i];
+    L.seg_first[e] = e;
+    L.seg_exp[e] = e;
+    L.seg_off[e] = row;
+    sob[e] = e;
+    row += cnt[i];
+  }
+  // balancedness = (sum/E) / max by one fp64 division of exact integers
+  const int m = wave_dev::max(cmax);
+  if (lane == 0) {
+    L.seg_first[E] = E;
+    L.seg_off[E] = total;
+    *bal_s = m > 0 ? (float)(((double)total / (double)E) / (double)m) : 0.0f;
+  }
+}
+
+// The one-wave planner by wave 0 of the workgroup; returns S (= E) to every
+// thread, after a barrier.
+__device__ inline int plan_segments_by_wave(PlanLds& L, int E, int* sob, float* bal_s) {
+  if (threadIdx.x < 64) {
+    switch ((E + 63) / 64) {
+      case 1: plan_segments_wave<1>(L, E, sob, bal_s); break;
+      case 2: plan_segments_wave<2>(L, E, sob, bal_s); break;
+      case 3: plan_segments_wave<3>(L, E, sob, bal_s); break;
+      default: plan_segments_wave<4>(L, E, sob, bal_s); break;
+    }
+  }
+  __syncthreads();
+  return E;
+}
+
+// The one-wave planner's outputs, by every thread (after a barrier):
+// counts[E], seg_offsets[E + 1], seg_expert[E], seg_of_bin[E] (nullable: the
+// small kernel keeps the map in LDS) and bal[0].  (A wave's loads and stores
+// share one in-order completion counter, so a store issued before a load
+// holds up the wait for that load: the callers issue these where no load
+// waits behind them.)
+__device__ inline void write_plan(const PlanLds& L, int E, int32_t* __restrict__ counts,
+                                  int32_t* __restrict__ seg_offsets,
+                                  int32_t* __restrict__ seg_expert, const int* sob,
+                                  int32_t* __restrict__ seg_of_bin, float bal_s,
+                                  float* __restrict__ bal) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 1024) {
+    counts[e] = L.cnt_e[e];
+    seg_expert[e] = L.seg_exp[e];
+    if (seg_of_bin) seg_of_bin[e] = sob[e];
+  }
+  for (int s = tid; s <= E; s += 1024) seg_offsets[s] = L.seg_off[s];
+  if (tid == 0) bal[0] = bal_s;
+}
+
 // Fixed-capacity layout (the book's "Capacity, padding, and the drop
 // decision"; the MoE inference blog's masked decode layout): expert e owns
 // rows [e*cap, (e+1)*cap); segment 2e holds its kept rows (the first
