@@ -128,7 +128,11 @@ __device__ __forceinline__ void segment_bases(const plan_dev::PlanLds& L,
   if (pending) after_issue();
 }
 
-template <bool WAVE>
+// WAVE: the one-wave planner (one bin per expert); otherwise the block
+// planner with BW bins per expert, or (CAP) the fixed-capacity layout.  Each
+// variant holds only the code it runs: one workgroup runs this kernel once,
+// and code compiled beside its path, though skipped, measurably slowed it.
+template <bool WAVE, int BW, bool CAP>
 __global__ __launch_bounds__(1024) void plan_kernel(
     const int32_t* __restrict__ cnt_bin, int nb, int ns, int E, int bin_ways, int ways, int n_hot,
     int c, int cap, int32_t* __restrict__ counts, int32_t* __restrict__ seg_offsets,
@@ -173,17 +177,14 @@ __global__ __launch_bounds__(1024) void plan_kernel(
       plan_dev::write_plan(L, E, counts, seg_offsets, seg_expert, sob, seg_of_bin, bal_s, bal);
     });
   } else {
-    const int S = cap > 0 ? plan_dev::plan_capacity(L, E, cap, counts, seg_offsets, seg_expert,
-                                                    seg_of_bin, r2t, bal)
-                          : plan_dev::plan_segments(L, E, bin_ways, ways, n_hot, c, counts,
-                                                    seg_offsets, seg_expert, seg_of_bin, bal);
-    auto none = [] {};
-    switch (bin_ways) {
-      case 1: segment_bases<1>(L, cnt_bin, S, nb, ns, blk_off, none); break;
-      case 2: segment_bases<2>(L, cnt_bin, S, nb, ns, blk_off, none); break;
-      case 3: segment_bases<3>(L, cnt_bin, S, nb, ns, blk_off, none); break;
-      default: segment_bases<4>(L, cnt_bin, S, nb, ns, blk_off, none); break;
-    }
+    int S;
+    if constexpr (CAP)
+      S = plan_dev::plan_capacity(L, E, cap, counts, seg_offsets, seg_expert, seg_of_bin, r2t,
+                                  bal);
+    else
+      S = plan_dev::plan_segments(L, E, BW, ways, n_hot, c, counts, seg_offsets, seg_expert,
+                                  seg_of_bin, bal);
+    segment_bases<BW>(L, cnt_bin, S, nb, ns, blk_off, [] {});
   }
 }
 
@@ -474,7 +475,12 @@ void launch_permute(const moe_config& c, const void* x, const int32_t* ids, void
   int32_t* seg_of_bin = reinterpret_cast<int32_t*>(ws + L.seg_of_bin);
   hist_kernel<<<nb, 256, 0, s>>>(ids, A, c.k, c.E, bw, chunk, ns, cnt_bin);
   const int cap = (int)capacity(c);
-  auto plan = wave_plan(c) ? plan_kernel<true> : plan_kernel<false>;
+  auto plan = wave_plan(c)      ? plan_kernel<true, 1, false>
+              : cap > 0         ? plan_kernel<false, 1, true>
+              : bw == 1         ? plan_kernel<false, 1, false>
+              : bw == 2         ? plan_kernel<false, 2, false>
+              : bw == 3         ? plan_kernel<false, 3, false>
+                                : plan_kernel<false, 4, false>;
   plan<<<1, 1024, 0, s>>>(cnt_bin, nb, ns, c.E, bw, split_ways(c), c.n_hot_split,
                           c.split_c_permille, cap, counts, seg_offsets, seg_expert, seg_of_bin,
                           blk_off, r2t, bal);
