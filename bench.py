@@ -41,18 +41,18 @@ CSRC = os.path.join(ROOT, "mixture_experts_layer_segments_amd", "csrc")
 # only applies while the library's sources (every file under csrc/) still
 # hash to the value it was measured with.
 MEASURED_TRAFFIC = {
-    "ragged_stress_bf16": {"csrc_sha256_16": "09f781c3d4bd359e", "bytes": 13317640533},
-    "decode_bf16": {"csrc_sha256_16": "09f781c3d4bd359e", "bytes": 5542965099},
-    "prefill_skew_bf16": {"csrc_sha256_16": "09f781c3d4bd359e", "bytes": 7687083308},
-    "deepseek_v3_bf16": {"csrc_sha256_16": "09f781c3d4bd359e", "bytes": 22477087027},
-    "ragged_stress_fp8w": {"csrc_sha256_16": "09f781c3d4bd359e", "bytes": 9746513750},
-    "decode_fp8w": {"csrc_sha256_16": "09f781c3d4bd359e", "bytes": 2776285080},
-    "prefill_skew_fp8w": {"csrc_sha256_16": "09f781c3d4bd359e", "bytes": 3963797065},
-    "deepseek_v3_fp8w": {"csrc_sha256_16": "09f781c3d4bd359e", "bytes": 12661003387},
-    "ragged_stress_w8a8": {"csrc_sha256_16": "09f781c3d4bd359e", "bytes": 7327066164},
-    "decode_w8a8": {"csrc_sha256_16": "09f781c3d4bd359e", "bytes": 2781426875},
-    "prefill_skew_w8a8": {"csrc_sha256_16": "09f781c3d4bd359e", "bytes": 3876789887},
-    "deepseek_v3_w8a8": {"csrc_sha256_16": "09f781c3d4bd359e", "bytes": 11673617688},
+    "ragged_stress_bf16": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 13173160541},
+    "decode_bf16": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 5542963436},
+    "prefill_skew_bf16": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 7633212334},
+    "deepseek_v3_bf16": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 22469393820},
+    "ragged_stress_fp8w": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 9768917010},
+    "decode_fp8w": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 2776273161},
+    "prefill_skew_fp8w": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 3965844740},
+    "deepseek_v3_fp8w": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 12677466468},
+    "ragged_stress_w8a8": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 7323374227},
+    "decode_w8a8": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 2781432224},
+    "prefill_skew_w8a8": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 3872924447},
+    "deepseek_v3_w8a8": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 11666412820},
 }
 
 
