@@ -88,6 +88,18 @@ SHAPES = {
                                             n_hot_split=8, split_ways=4, seed=41),
     "bf16_capacity_many": mi.MoEShape("t29", T=600, H=64, E=1024, k=2, I=64, zipf_s=1.0,
                                       capacity_factor_permille=1000, seed=42),
+    # unsplit dropless layers of 65-256 experts, planned by one wave with 2, 3
+    # or 4 experts per lane, through the planning kernel (T*k > 1024) and the
+    # one-workgroup kernel (T*k <= 1024; grouped routing on whole waves too)
+    "bf16_wave_plan_2": mi.MoEShape("t30", T=300, H=64, E=100, k=4, I=64, zipf_s=1.0, seed=43),
+    "bf16_wave_plan_3_small": mi.MoEShape("t31", T=100, H=64, E=160, k=6, I=64, zipf_s=1.0,
+                                          seed=44),
+    "bf16_wave_plan_4": mi.MoEShape("t32", T=200, H=64, E=256, k=8, I=64, zipf_s=1.0, seed=45),
+    "bf16_wave_plan_4_small": mi.MoEShape("t33", T=64, H=64, E=256, k=8, I=64, zipf_s=1.0,
+                                          seed=46),
+    "bf16_wave_plan_grouped_small": mi.MoEShape("t34", T=50, H=64, E=192, k=6, I=64,
+                                                score="sigmoid", n_group=8, topk_group=3,
+                                                seed=47),
 }
 
 
