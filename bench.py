@@ -36,23 +36,24 @@ METRIC = "MoE-layer tokens/s and grouped-GEMM TFLOP/s (% MFMA/HBM roofline), 1 M
 CSRC = os.path.join(ROOT, "mixture_experts_layer_segments_amd", "csrc")
 
 # HBM bytes per grouped-FFN call measured with rocprofv3 --pmc FETCH_SIZE and
-# WRITE_SIZE (summed over the GEMM kernels of one call, each counter scaled by
-# what it reads for a plain 1 GiB device copy), keyed by workload.  An entry
+# WRITE_SIZE (summed over the dispatches of this script's grouped-FFN calls,
+# per call, each counter scaled by what it reads for a plain 1 GiB device
+# copy), keyed by workload.  An entry
 # only applies while the library's sources (every file under csrc/) still
 # hash to the value it was measured with.
 MEASURED_TRAFFIC = {
-    "ragged_stress_bf16": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 13173160541},
-    "decode_bf16": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 5542963436},
-    "prefill_skew_bf16": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 7633212334},
-    "deepseek_v3_bf16": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 22469393820},
-    "ragged_stress_fp8w": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 9768917010},
-    "decode_fp8w": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 2776273161},
-    "prefill_skew_fp8w": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 3965844740},
-    "deepseek_v3_fp8w": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 12677466468},
-    "ragged_stress_w8a8": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 7323374227},
-    "decode_w8a8": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 2781432224},
-    "prefill_skew_w8a8": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 3872924447},
-    "deepseek_v3_w8a8": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 11666412820},
+    "ragged_stress_bf16": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 13255711856},
+    "decode_bf16": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 5543124656},
+    "prefill_skew_bf16": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 7421682925},
+    "deepseek_v3_bf16": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 22385578715},
+    "ragged_stress_fp8w": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 9745561767},
+    "decode_fp8w": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 2776458410},
+    "prefill_skew_fp8w": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 3916540892},
+    "deepseek_v3_fp8w": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 12378113712},
+    "ragged_stress_w8a8": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 6952856172},
+    "decode_w8a8": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 2780792023},
+    "prefill_skew_w8a8": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 3708819152},
+    "deepseek_v3_w8a8": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 11468292500},
 }
 
 
