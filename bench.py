@@ -297,8 +297,10 @@ def cpu_identity(threads: int) -> dict:
 
 def practical_ceilings(dev, reps=10):
     """Ceilings measured in the same run, outside the timed steps: a plain
-    1 GiB device copy (bytes read + written per second) and torch.matmul in
-    bf16 (hipBLASLt) on the ragged layer's two dense GEMM shapes."""
+    1 GiB device copy (bytes read + written per second), a weight stream
+    (torch.matmul in bf16, hipBLASLt, of 64 rows by a 1 GiB weight, 8192 x
+    65536: weight bytes read per second, the decode layers' regime) and
+    torch.matmul in bf16 on the ragged layer's two dense GEMM shapes."""
     import torch
     out = {}
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -316,6 +318,19 @@ def practical_ceilings(dev, reps=10):
     ms = e0.elapsed_time(e1) / reps
     out["device_copy_1GiB_GBs"] = round(2 * (1 << 30) / (ms * 1e-3) / 1e9, 1)
     del src, dst
+    a = torch.randn((64, 8192), dtype=torch.bfloat16, device=dev)
+    wt = torch.randn((8192, 65536), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        torch.matmul(a, wt)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, wt)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    out["matmul_bf16_64x65536x8192_weight_GBs"] = round(wt.numel() * 2 / (ms * 1e-3) / 1e9, 1)
+    del a, wt
     for m_, n_, k_ in ((16384, 3072, 4096), (16384, 4096, 1536)):
         a = torch.randn((m_, k_), dtype=torch.bfloat16, device=dev)
         b = torch.randn((k_, n_), dtype=torch.bfloat16, device=dev)
