@@ -29,6 +29,15 @@ CASES = {
                                         shared_I=256, zipf_s=1.0, seed=43),
     "decode_fp8": mi.MoEShape("g4", T=64, H=1024, E=32, k=2, I=512, zipf_s=1.0,
                               weights="fp8", seed=44),
+    # E4M3 weights on the ring tiles; E4M3 activations too, on the decode
+    # tiles (x and h quantized between launches) and on the ring tiles (h
+    # quantized in GEMM 1's epilogue)
+    "rings_fp8": mi.MoEShape("g5", T=300, H=256, E=32, k=4, I=128, zipf_s=1.0,
+                             weights="fp8", seed=45),
+    "decode_w8a8": mi.MoEShape("g6", T=64, H=1024, E=32, k=2, I=512, zipf_s=1.0,
+                               weights="fp8", acts="fp8", seed=46),
+    "rings_w8a8": mi.MoEShape("g7", T=300, H=256, E=32, k=4, I=128, zipf_s=1.0,
+                              weights="fp8", acts="fp8", seed=47),
 }
 
 
@@ -47,10 +56,10 @@ class Layer:
     def __call__(self):
         d, o, m = self.d, self.o, self.moe
         if self.cfg.weights == "fp8":
-            m.moe_layer_forward_fp8w(self.cfg, d["logits"], d["x"], d["w13"], d["w13_s"],
-                                     d["w2"], d["w2_s"], d["sw13"], d["sw13_s"], d["sw2"],
-                                     d["sw2_s"], o["out"], o["ids"], o["w"], o["counts"],
-                                     o["bal"], self.ws)
+            call = m.moe_layer_forward_w8a8 if self.cfg.acts == "fp8" else m.moe_layer_forward_fp8w
+            call(self.cfg, d["logits"], d["x"], d["w13"], d["w13_s"], d["w2"], d["w2_s"],
+                 d["sw13"], d["sw13_s"], d["sw2"], d["sw2_s"], o["out"], o["ids"], o["w"],
+                 o["counts"], o["bal"], self.ws)
         else:
             m.moe_layer_forward(self.cfg, d["logits"], d["x"], d["w13"], d["w2"], d["sw13"],
                                 d["sw2"], o["out"], o["ids"], o["w"], o["counts"], o["bal"],
@@ -114,6 +123,10 @@ def test_graph_replay_matches_eager(name):
                             r["w"], r["group_gap"], case.logits)
     assert mism.size == 0
     assert (got["counts"].cpu().numpy() == r["counts"]).all()
+    if cfg.acts == "fp8":
+        gu.check_w8a8_out(gu.host_f64(got["out"]), r["out"], gu.w8a8_slack(case),
+                          f"[graph] {name}: last replay vs oracle")
+        return
     err = gu.rel_err(gu.host_f64(got["out"]), r["out"])
     print(f"[graph] {name}: last replay vs oracle rel err {err:.3e}", flush=True)
     assert err <= gu.rel_tol(cfg), err
