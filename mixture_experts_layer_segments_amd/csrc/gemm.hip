@@ -579,6 +579,9 @@ __device__ __forceinline__ void ring_kloop(
   // WF: the scale group of this wave's weight fragments (GEMM 1: gate
   // fragments use group 0, up fragments group 1)
   const int g_down = MODE == 1 ? (wn * WN) / 128 : 0;
+  // a wave whose rows all lie past the segment's end (the last row tile of a
+  // segment) takes part in the copies and barriers only
+  const bool rows_here = t.m0 + (wvs / C::WAVES_N) * WM < t.len;
   for (int kt = 0; kt < KT; ++kt) {
     // stage kt has landed once only the copies of later stages remain; the
     // waves that issue no copies (and write the output) have nothing to wait for
@@ -594,6 +597,7 @@ __device__ __forceinline__ void ring_kloop(
         ring_issue<LPI, C::NI, STAGES, STAGE_CH, A_CH, BK, C::A_IT, C::WB, C::AB, 0, KCH, KCHB,
                    BM>(t.ra, t.rb, t.voff, ring, kt + STAGES - 1, wvs, kval);
     }
+    if (!rows_here) continue;
     const u32x4* slot = ring + (kt % STAGES) * STAGE_CH;
     if constexpr (WF == 2) {
       // E4M3 x E4M3: one 128-deep MFMA K step per stage.  Lane l supplies row
