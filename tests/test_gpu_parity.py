@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import moe_inputs as mi
+from oracle import fp8 as ofp8
 from oracle import moe_oracle as orc
 from tests import gpu_util as gu
 
@@ -344,6 +345,53 @@ def test_repeated_ids_make_segments_longer_than_the_batch(moe, T, k, E, n_ids):
     assert err <= gu.BF16_REL, err
     # every row was written (a skipped segment would leave the zero fill)
     assert (np.abs(got).max(axis=1) > 0).all()
+
+
+# Segment lengths whose last row tile ends on each side of the 64-row wave
+# blocks of the 128-row tiles (lengths under 256) and of the 256-row tiles:
+# a wave whose rows all lie past the segment's end skips its MFMAs, the
+# others compute.  Each expert holds one segment; the total is above 256,
+# so both tile launches run.
+WAVE_EDGE_LENS = [1, 63, 64, 65, 127, 128, 129, 191, 192, 193, 255,
+                  257, 319, 320, 321, 384, 385, 448, 449, 511, 512]
+
+
+@pytest.mark.parametrize("weights", ["bf16", "fp8"])
+def test_last_row_tile_wave_edges(moe, weights):
+    """moe_grouped_ffn (bf16 or FP8 weights) on segments of WAVE_EDGE_LENS
+    rows: every row of every segment against the oracle's expert MLP."""
+    lens = np.array(WAVE_EDGE_LENS, dtype=np.int64)
+    E, R = len(lens), int(lens.sum())
+    cfg = mi.MoEShape("edges", T=R, H=256, E=E, k=1, I=256, seed=37, weights=weights)
+    so = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    se = np.arange(E, dtype=np.int32)
+    x = mi.x(cfg)
+    w13b = np.stack([mi.w13(cfg, e) for e in range(E)])
+    w2b = np.stack([mi.w2(cfg, e) for e in range(E)])
+    w13_64, w2_64 = mi.values_f64(w13b, "bf16"), mi.values_f64(w2b, "bf16")
+    d13, d2 = gu.to_dev(w13b, "bf16"), gu.to_dev(w2b, "bf16")
+    y = gu.empty((R, cfg.H), torch.bfloat16)
+    y.fill_(0)
+    ws = gu.empty((moe.moe_workspace_size(cfg),), torch.uint8)
+    so_d, se_d = torch.from_numpy(so).to(gu.dev()), torch.from_numpy(se).to(gu.dev())
+    if weights == "fp8":
+        # the oracle runs on its own quantization of the same weights
+        w13_64 = np.stack([ofp8.dequantize_blocks(*ofp8.quantize_blocks(m)) for m in w13_64])
+        w2_64 = np.stack([ofp8.dequantize_blocks(*ofp8.quantize_blocks(m)) for m in w2_64])
+        q13, s13 = gu.quantize_fp8(moe, d13)
+        q2, s2 = gu.quantize_fp8(moe, d2)
+        moe.moe_grouped_ffn_fp8w(cfg, gu.to_dev(x, "bf16"), so_d, se_d, q13, s13, q2, s2, None,
+                                 y, ws)
+    else:
+        moe.moe_grouped_ffn(cfg, gu.to_dev(x, "bf16"), so_d, se_d, d13, d2, None, y, ws)
+    torch.cuda.synchronize()
+    ref = orc.grouped_ffn(mi.values_f64(x, "bf16"), so, se, w13_64, w2_64)
+    got = gu.host_f64(y)
+    for s in range(E):
+        r0, r1 = so[s], so[s + 1]
+        err = gu.rel_err(got[r0:r1], ref[r0:r1])
+        assert err <= gu.BF16_REL, (weights, int(lens[s]), err)
+    print(f"  {weights}: {E} segments, rel err {gu.rel_err(got, ref):.3e}")
 
 
 @pytest.mark.parametrize("T", [40, 400])
