@@ -42,18 +42,18 @@ CSRC = os.path.join(ROOT, "mixture_experts_layer_segments_amd", "csrc")
 # only applies while the library's sources (every file under csrc/) still
 # hash to the value it was measured with.
 MEASURED_TRAFFIC = {
-    "ragged_stress_bf16": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 13255711856},
-    "decode_bf16": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 5543124656},
-    "prefill_skew_bf16": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 7421682925},
-    "deepseek_v3_bf16": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 22385578715},
-    "ragged_stress_fp8w": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 9745561767},
-    "decode_fp8w": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 2776458410},
-    "prefill_skew_fp8w": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 3916540892},
-    "deepseek_v3_fp8w": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 12378113712},
-    "ragged_stress_w8a8": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 6952856172},
-    "decode_w8a8": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 2780792023},
-    "prefill_skew_w8a8": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 3708819152},
-    "deepseek_v3_w8a8": {"csrc_sha256_16": "fc5559b62b8cb318", "bytes": 11468292500},
+    "ragged_stress_bf16": {"csrc_sha256_16": "f713f24a819f5741", "bytes": 14184400843},
+    "decode_bf16": {"csrc_sha256_16": "f713f24a819f5741", "bytes": 5543123624},
+    "prefill_skew_bf16": {"csrc_sha256_16": "f713f24a819f5741", "bytes": 7549278118},
+    "deepseek_v3_bf16": {"csrc_sha256_16": "f713f24a819f5741", "bytes": 22313503210},
+    "ragged_stress_fp8w": {"csrc_sha256_16": "f713f24a819f5741", "bytes": 12775264391},
+    "decode_fp8w": {"csrc_sha256_16": "f713f24a819f5741", "bytes": 2776457723},
+    "prefill_skew_fp8w": {"csrc_sha256_16": "f713f24a819f5741", "bytes": 4282187373},
+    "deepseek_v3_fp8w": {"csrc_sha256_16": "f713f24a819f5741", "bytes": 14727794257},
+    "ragged_stress_w8a8": {"csrc_sha256_16": "f713f24a819f5741", "bytes": 7243055162},
+    "decode_w8a8": {"csrc_sha256_16": "f713f24a819f5741", "bytes": 2780792280},
+    "prefill_skew_w8a8": {"csrc_sha256_16": "f713f24a819f5741", "bytes": 3802872760},
+    "deepseek_v3_w8a8": {"csrc_sha256_16": "f713f24a819f5741", "bytes": 11705302416},
 }
 
 
