@@ -14,7 +14,7 @@
 // remapped so that consecutive tiles (which share weight slices and
 // activation rows) land on the same XCD and therefore the same L2.  The K loop double-buffers LDS tiles; operands
 // are XOR-swizzled in 16-byte chunks so that MFMA operand reads avoid bank
-// conflicts.  fp32 path: a plain FMA kernel (the fp32 layer is tiny).
+// conflicts.  fp32 path: a wave per output element (the fp32 layer is tiny).
 #include <math.h>
 
 #include <mutex>
@@ -1046,6 +1046,10 @@ __device__ int find_segment(const int32_t* off, int n, int r) {
   return lo;
 }
 
+// fp32 grouped GEMMs (the fp32 layer is tiny: a few rows per expert): one
+// wave per output element.  Its lanes stride K, so every load instruction
+// reads consecutive elements of an A row and of a weight row, and the wave
+// sums the 64 partial dot products in registers.
 template <int MODE>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A,
                                                        const float* __restrict__ B,
@@ -1056,8 +1060,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
                                                        const int32_t* __restrict__ a_rows,
                                                        int n_seg, int rows, int N, int K,
                                                        int up_off, int64_t b_stride, int n_w) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int row = (int)(idx / N), col = (int)(idx % N);
+  const int lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int row = (int)(w / N), col = (int)(w % N);
+  // (every exit below is taken by the whole wave: its row and column are
+  // the wave's)
   if (row >= rows) return;
   int e = 0;
   if (seg_offsets) {
@@ -1071,16 +1078,20 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
     const float* bg = b + (size_t)col * K;
     const float* bu = b + (size_t)(up_off + col) * K;
     float g = 0.f, u = 0.f;
-    for (int kk = 0; kk < K; ++kk) {
-      g = fmaf(a[kk], bg[kk], g);
-      u = fmaf(a[kk], bu[kk], u);
+    for (int kk = lane; kk < K; kk += 64) {
+      const float x = a[kk];
+      g = fmaf(x, bg[kk], g);
+      u = fmaf(x, bu[kk], u);
     }
-    C[(size_t)row * N + col] = silu(g) * u;
+    g = wave_dev::sum(g);
+    u = wave_dev::sum(u);
+    if (lane == 0) C[(size_t)row * N + col] = silu(g) * u;
   } else {
     const float* bd = b + (size_t)col * K;
     float y = 0.f;
-    for (int kk = 0; kk < K; ++kk) y = fmaf(a[kk], bd[kk], y);
-    C[(size_t)row * N + col] = y * (scale ? scale[row] : 1.0f);
+    for (int kk = lane; kk < K; kk += 64) y = fmaf(a[kk], bd[kk], y);
+    y = wave_dev::sum(y);
+    if (lane == 0) C[(size_t)row * N + col] = y * (scale ? scale[row] : 1.0f);
   }
 }
 
@@ -1571,10 +1582,10 @@ void launch_grouped_ffn(const moe_config& c, const FfnProblem* probs, int n_prob
       const FfnProblem& P = probs[p];
       const int Iw = P.Iw;
       int64_t n1 = (int64_t)P.rows * Iw, n2 = (int64_t)P.rows * H;
-      gemm_f32_kernel<0><<<(unsigned)((n1 + 255) / 256), 256, 0, s>>>(
+      gemm_f32_kernel<0><<<(unsigned)((n1 + 3) / 4), 256, 0, s>>>(
           (const float*)P.A, (const float*)P.w13, (float*)P.h, nullptr, P.seg_offsets,
           P.seg_expert, P.a_rows, P.n_seg, P.rows, Iw, H, Iw, (int64_t)2 * Iw * H, P.n_w);
-      gemm_f32_kernel<1><<<(unsigned)((n2 + 255) / 256), 256, 0, s>>>(
+      gemm_f32_kernel<1><<<(unsigned)((n2 + 3) / 4), 256, 0, s>>>(
           (const float*)P.h, (const float*)P.w2, (float*)P.y, P.row_scale, P.seg_offsets,
           P.seg_expert, nullptr, P.n_seg, P.rows, H, Iw, 0, (int64_t)H * Iw, P.n_w);
     }

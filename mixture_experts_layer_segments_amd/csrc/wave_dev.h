@@ -48,6 +48,20 @@ __device__ __forceinline__ int sum(int x) {
   return x;
 }
 
+// The same sum for fp32 values (bit patterns through the same moves; the
+// additions in the same order on every lane, so every lane gets the same
+// result).
+__device__ __forceinline__ float sum(float x) {
+  auto step = [](float v, int moved) { return v + __builtin_bit_cast(float, moved); };
+  x = step(x, dpp<0xB1>(__builtin_bit_cast(int, x)));
+  x = step(x, dpp<0x4E>(__builtin_bit_cast(int, x)));
+  x = step(x, dpp<0x141>(__builtin_bit_cast(int, x)));
+  x = step(x, dpp<0x140>(__builtin_bit_cast(int, x)));
+  x = step(x, swap_partner<false>(__builtin_bit_cast(int, x)));
+  x = step(x, swap_partner<true>(__builtin_bit_cast(int, x)));
+  return x;
+}
+
 // Sum of x over each aligned group of G lanes (G = 1, 2, 4, 8 or 16), to
 // every lane of the group: the first log2 G steps of sum().
 template <int G>
