@@ -262,8 +262,8 @@ def cpu_baseline(cfg, logits, budget_s=20.0, min_s=10.0):
 
 def host_threads() -> int:
     """Threads the oracle's BLAS may use: every CPU this process may run on,
-    unless the environment caps the thread pools (OMP_NUM_THREADS, which the
-    GPU machines set to their CPU share)."""
+    unless the environment caps the thread pools (OMP_NUM_THREADS, which a
+    shared machine may set to the process's CPU share)."""
     n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
     cap = os.environ.get("OMP_NUM_THREADS", "")
     if cap.isdigit() and int(cap) > 0:
