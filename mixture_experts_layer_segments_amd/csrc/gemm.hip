@@ -1007,9 +1007,13 @@ struct TileCfg {
 };
 // tile shapes per operand format
 template <int WF> struct Tiles;
+// kSmallRows: segments shorter than this take the Small shape in a launch of
+// their own (0: no such launch).
 template <> struct Tiles<0> {                              // bf16
   using Mid = TileCfg<0, 128, 256, 64, 512, 2, 3>;         // 2 x 4 waves of 64 x 64
   using Big = TileCfg<0, 256, 256, 64, 512, 4, 2>;         // 4 x 2 waves of 64 x 128
+  using Small = Mid;
+  static constexpr int kSmallRows = 0;
 };
 // E4M3 weights: the weight rows of a stage take half the bytes.  The
 // 128-row tile takes 128-deep stages (two), so that a stage's weight row
@@ -1021,22 +1025,32 @@ template <> struct Tiles<0> {                              // bf16
 // fragments it reads, so half as many weight columns per wave halves the
 // conversions (for 25% more activation reads): 4-9% faster on its launches.
 // (With bf16 weights the two layouts read the same LDS bytes and time the
-// same.)
+// same.)  Two 128-deep stages of the 128-row tile keep one stage of weights
+// in flight per CU, which holds its weight stream to 3.4-3.8 TB/s, where the
+// bf16 tile's three stages reach 5.7-6.6.  Segments of fewer than 64 rows
+// (most of the DeepSeek-shaped layer's) take a 64-row tile instead, whose
+// 48 KiB stages fit three times: 12-23% faster on those launches.  The
+// longer ones stay on the 128-row tile: as two 64-row tiles the prefill
+// layer's 100-260-row segments ran 10-22% slower.
 template <> struct Tiles<1> {
   using Mid = TileCfg<1, 128, 256, 128, 512, 2, 2>;
   using Big = TileCfg<1, 256, 256, 64, 512, 2, 3>;   // 2 x 4 waves of 128 x 64
+  using Small = TileCfg<1, 64, 256, 128, 512, 2, 3>;  // 2 x 4 waves of 32 x 64
+  static constexpr int kSmallRows = 64;
 };
 // E4M3 activations and weights: 128-deep stages (128-byte row pieces, as the
 // bf16 tiles' 64-deep ones), one scaled FP8 MFMA K step each.
 template <> struct Tiles<2> {
   using Mid = TileCfg<2, 128, 256, 128, 512, 2, 3>;
   using Big = TileCfg<2, 256, 256, 128, 512, 4, 2>;
+  using Small = Mid;
+  static constexpr int kSmallRows = 0;
 };
 
 
 
 // ---------------------------------------------------------------- fp32 path
-// One thread per output element.  GEMM 1 writes h, GEMM 2 writes y.
+// GEMM 1 writes h, GEMM 2 writes y.
 __device__ int find_segment(const int32_t* off, int n, int r) {
   int lo = 0, hi = n - 1;
   while (lo < hi) {
@@ -1544,28 +1558,45 @@ void launch_mfma_pair(const moe_config& c, const FfnProblem* probs, int n_probs,
   // scales), and the mid tiles take the long segments too if the big ring
   // does not fit beside them.  The big launches are skipped when no segment
   // can reach kBigRows rows (each problem states the longest a segment of it
-  // can be).
+  // can be).  With E4M3 weights the segments shorter than kSmallRows take
+  // a launch of 64-row tiles of their own.
   using MT = typename Tiles<WF>::Mid;
   using BG = typename Tiles<WF>::Big;
+  using SM = typename Tiles<WF>::Small;
+  constexpr int kSmall = Tiles<WF>::kSmallRows;
   constexpr size_t kMargin = 64;
   const bool big_fits = ring_dyn_lds(g1, WF, BG::kBM) + BG::kRingBytes + kMargin <= kMaxLdsBytes &&
                         ring_dyn_lds(g2, WF, BG::kBM) + BG::kRingBytes + kMargin <= kMaxLdsBytes;
   const int mid_hi = big_fits ? kBigRows : kAll;
-  const GemmArgs m1 = cover(g1, MT::kBM, MT::kBN / 2, 1, mid_hi);
-  const GemmArgs m2 = cover(g2, MT::kBM, MT::kBN, 1, mid_hi);
+  const int mid_lo = kSmall > 0 ? kSmall : 1;
+  const GemmArgs m1 = cover(g1, MT::kBM, MT::kBN / 2, mid_lo, mid_hi);
+  const GemmArgs m2 = cover(g2, MT::kBM, MT::kBN, mid_lo, mid_hi);
+  const GemmArgs s1 = cover(g1, SM::kBM, SM::kBN / 2, 1, mid_lo);
+  const GemmArgs s2 = cover(g2, SM::kBM, SM::kBN, 1, mid_lo);
   const GemmArgs b1 = cover(g1, BG::kBM, BG::kBN / 2, kBigRows, kAll);
   const GemmArgs b2 = cover(g2, BG::kBM, BG::kBN, kBigRows, kAll);
   const bool deep1 = ring_dyn_lds(g1, WF, MT::kBM) + MT::kRingBytes + kMargin <= kMaxLdsBytes;
   const bool deep2 = ring_dyn_lds(g2, WF, MT::kBM) + MT::kRingBytes + kMargin <= kMaxLdsBytes;
+  const bool sdeep1 = ring_dyn_lds(g1, WF, SM::kBM) + SM::kRingBytes + kMargin <= kMaxLdsBytes;
+  const bool sdeep2 = ring_dyn_lds(g2, WF, SM::kBM) + SM::kRingBytes + kMargin <= kMaxLdsBytes;
   int longest = 0;
   for (int p = 0; p < n_probs; ++p)
     longest = probs[p].max_seg_rows > longest ? probs[p].max_seg_rows : longest;
   const bool any_big = big_fits && longest >= kBigRows;
-  // (a 2-stage ring of the mid shape always fits beside the largest table)
+  // (a 2-stage ring of the mid and small shapes always fits beside the
+  // largest table)
+  if constexpr (kSmall > 0) {
+    if (sdeep1) launch_ring<0, WF, SM::kBM, SM::kBN, SM::kBK, SM::kThreads, SM::kWM, SM::kStages>(s1, s);
+    else launch_ring<0, WF, SM::kBM, SM::kBN, SM::kBK, SM::kThreads, SM::kWM, 2>(s1, s);
+  }
   if (deep1) launch_ring<0, WF, MT::kBM, MT::kBN, MT::kBK, MT::kThreads, MT::kWM, MT::kStages>(m1, s);
   else launch_ring<0, WF, MT::kBM, MT::kBN, MT::kBK, MT::kThreads, MT::kWM, 2>(m1, s);
   if (any_big) launch_ring<0, WF, BG::kBM, BG::kBN, BG::kBK, BG::kThreads, BG::kWM, BG::kStages>(b1, s);
   // (FP8 activations: the ring tiles of GEMM 1 wrote h quantized)
+  if constexpr (kSmall > 0) {
+    if (sdeep2) launch_ring<1, WF, SM::kBM, SM::kBN, SM::kBK, SM::kThreads, SM::kWM, SM::kStages>(s2, s);
+    else launch_ring<1, WF, SM::kBM, SM::kBN, SM::kBK, SM::kThreads, SM::kWM, 2>(s2, s);
+  }
   if (deep2) launch_ring<1, WF, MT::kBM, MT::kBN, MT::kBK, MT::kThreads, MT::kWM, MT::kStages>(m2, s);
   else launch_ring<1, WF, MT::kBM, MT::kBN, MT::kBK, MT::kThreads, MT::kWM, 2>(m2, s);
   if (any_big) launch_ring<1, WF, BG::kBM, BG::kBN, BG::kBK, BG::kThreads, BG::kWM, BG::kStages>(b2, s);

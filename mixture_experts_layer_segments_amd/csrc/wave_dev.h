@@ -48,9 +48,9 @@ __device__ __forceinline__ int sum(int x) {
   return x;
 }
 
-// The same sum for fp32 values (bit patterns through the same moves; the
-// additions in the same order on every lane, so every lane gets the same
-// result).
+// The same sum for fp32 values (bit patterns through the same moves).  At
+// each step two lanes add the same two partial sums, in either order, and
+// fp32 addition commutes: every lane ends with the same bits.
 __device__ __forceinline__ float sum(float x) {
   auto step = [](float v, int moved) { return v + __builtin_bit_cast(float, moved); };
   x = step(x, dpp<0xB1>(__builtin_bit_cast(int, x)));
