@@ -42,18 +42,18 @@ CSRC = os.path.join(ROOT, "mixture_experts_layer_segments_amd", "csrc")
 # only applies while the library's sources (every file under csrc/) still
 # hash to the value it was measured with.
 MEASURED_TRAFFIC = {
-    "ragged_stress_bf16": {"csrc_sha256_16": "ca3ce5590422185f", "bytes": 14109164742},
-    "decode_bf16": {"csrc_sha256_16": "ca3ce5590422185f", "bytes": 5543123574},
-    "prefill_skew_bf16": {"csrc_sha256_16": "ca3ce5590422185f", "bytes": 7534910999},
-    "deepseek_v3_bf16": {"csrc_sha256_16": "ca3ce5590422185f", "bytes": 22364757159},
-    "ragged_stress_fp8w": {"csrc_sha256_16": "ca3ce5590422185f", "bytes": 12736656594},
-    "decode_fp8w": {"csrc_sha256_16": "ca3ce5590422185f", "bytes": 2776453973},
-    "prefill_skew_fp8w": {"csrc_sha256_16": "ca3ce5590422185f", "bytes": 4232013563},
-    "deepseek_v3_fp8w": {"csrc_sha256_16": "ca3ce5590422185f", "bytes": 14734454710},
-    "ragged_stress_w8a8": {"csrc_sha256_16": "ca3ce5590422185f", "bytes": 7274219836},
-    "decode_w8a8": {"csrc_sha256_16": "ca3ce5590422185f", "bytes": 2780787889},
-    "prefill_skew_w8a8": {"csrc_sha256_16": "ca3ce5590422185f", "bytes": 3768667911},
-    "deepseek_v3_w8a8": {"csrc_sha256_16": "ca3ce5590422185f", "bytes": 11727790520},
+    "ragged_stress_bf16": {"csrc_sha256_16": "64052207510fdc96", "bytes": 14124661746},
+    "decode_bf16": {"csrc_sha256_16": "64052207510fdc96", "bytes": 5543121204},
+    "prefill_skew_bf16": {"csrc_sha256_16": "64052207510fdc96", "bytes": 7615149531},
+    "deepseek_v3_bf16": {"csrc_sha256_16": "64052207510fdc96", "bytes": 22227781714},
+    "ragged_stress_fp8w": {"csrc_sha256_16": "64052207510fdc96", "bytes": 12672361338},
+    "decode_fp8w": {"csrc_sha256_16": "64052207510fdc96", "bytes": 2776455370},
+    "prefill_skew_fp8w": {"csrc_sha256_16": "64052207510fdc96", "bytes": 4219636677},
+    "deepseek_v3_fp8w": {"csrc_sha256_16": "64052207510fdc96", "bytes": 14813379208},
+    "ragged_stress_w8a8": {"csrc_sha256_16": "64052207510fdc96", "bytes": 7275516679},
+    "decode_w8a8": {"csrc_sha256_16": "64052207510fdc96", "bytes": 2780790228},
+    "prefill_skew_w8a8": {"csrc_sha256_16": "64052207510fdc96", "bytes": 3773621020},
+    "deepseek_v3_w8a8": {"csrc_sha256_16": "64052207510fdc96", "bytes": 11769029962},
 }
 
 
